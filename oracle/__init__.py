@@ -1,0 +1,207 @@
+"""fp64 CPU oracle for one tensor-parallel rank's share of a Transformer block.
+
+TEST INFRASTRUCTURE ONLY: only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this package.  It never imports the HIP library
+and the HIP library never imports it.
+
+The arithmetic lives in ``tp_oracle.c`` (plain loops, float64, k ascending);
+this module converts the shared seeded inputs to float64 exactly and composes
+the C functions in the order the pages give:
+
+* ``mlp_shard``   -- Y_i = X·A_i (+a_i), GeLU locally, Z_i = GeLU(Y_i)·B_i
+  ("图解Transformer并行计算" (un.csdn.net/7y5fj9k05scw) §2.1, §2.2);
+* ``attn_shard_rows`` -- local heads' softmax(QK^T/sqrt d)·V, then the row
+  slice of W_o (same page §3.1, §3.2);
+* ``partial_sum`` -- Z = sum_r Z_r (+ bias) (+ residual): the all-reduce's
+  arithmetic (same page §1.1, §2.1);
+* ``block_rows``  -- the pre-LN block x + attn(LN1(x)), then + mlp(LN2(.)), as
+  assembled in section 3.3 of the PyTorch tensor-parallel tutorial
+  (hotelren.com/news/6074135), with every rank's share summed.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_dp = ctypes.POINTER(ctypes.c_double)
+_i64 = ctypes.c_int64
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        from . import build as _b
+        _b.build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    lib.orc_matmul.argtypes = [_dp, _i64, _dp, _i64, _dp, _dp, _i64, _i64, _i64, _i64]
+    lib.orc_gelu.argtypes = [ctypes.c_double]
+    lib.orc_gelu.restype = ctypes.c_double
+    lib.orc_gelu_inplace.argtypes = [_dp, _i64]
+    lib.orc_mlp_shard.argtypes = [_dp, _dp, _dp, _dp, _dp, _i64, _i64, _i64]
+    lib.orc_layernorm.argtypes = [_dp, _dp, _dp, ctypes.c_double, _dp, _i64, _i64]
+    lib.orc_attn_shard_rows.argtypes = [_dp, _i64, _i64, _i64, _dp, _dp, _i64, _i64,
+                                        ctypes.c_int, ctypes.POINTER(_i64), _i64, _dp]
+    lib.orc_partial_sum.argtypes = [_dp, _i64, _i64, _i64, _dp, _dp, _dp]
+    lib.orc_num_threads.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def num_threads() -> int:
+    """Host threads the oracle's loops use (OpenMP's count)."""
+    return int(_load().orc_num_threads())
+
+
+# ---------------------------------------------------------------- conversion
+def f64(t) -> np.ndarray:
+    """Exact float64 copy of a CPU tensor/array stored as bf16, fp32 or fp64.
+
+    bf16 is widened by placing its 16 bits in the top half of an IEEE binary32
+    word, which is exact; binary32 and binary64 widen exactly as well.
+    """
+    if t is None:
+        return None
+    try:
+        import torch
+        if isinstance(t, torch.Tensor):
+            t = t.detach().cpu().contiguous()
+            if t.dtype == torch.bfloat16:
+                bits = t.view(torch.int16).numpy().astype(np.uint16).astype(np.uint32)
+                return np.ascontiguousarray((bits << 16).view(np.float32).astype(np.float64))
+            return np.ascontiguousarray(t.numpy().astype(np.float64))
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(np.asarray(t, dtype=np.float64))
+
+
+def _p(a):
+    if a is None:
+        return None
+    assert a.dtype == np.float64 and a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(_dp)
+
+
+# ---------------------------------------------------------------- primitives
+def matmul(X, W, bias=None) -> np.ndarray:
+    """Y = X·W (+bias); X [M,K], W [K,N] (row-major, float64)."""
+    X, W, bias = f64(X), f64(W), f64(bias)
+    M, K = X.shape
+    K2, N = W.shape
+    assert K == K2
+    Y = np.empty((M, N), dtype=np.float64)
+    _load().orc_matmul(_p(X), K, _p(W), N, _p(bias), _p(Y), N, M, K, N)
+    return Y
+
+
+def gelu(x) -> np.ndarray:
+    """Exact-erf GeLU applied elementwise."""
+    y = np.array(f64(x), dtype=np.float64, copy=True, order="C")
+    _load().orc_gelu_inplace(_p(y), y.size)
+    return y
+
+
+def gelu_scalar(x: float) -> float:
+    return float(_load().orc_gelu(float(x)))
+
+
+def layernorm(x, gamma=None, beta=None, eps: float = 1e-5) -> np.ndarray:
+    """LayerNorm of each row of x [M,h] (population variance)."""
+    x, gamma, beta = f64(x), f64(gamma), f64(beta)
+    M, h = x.shape
+    y = np.empty_like(x)
+    _load().orc_layernorm(_p(x), _p(gamma), _p(beta), float(eps), _p(y), M, h)
+    return y
+
+
+def mlp_shard(X, A_i, B_i, a_i=None) -> np.ndarray:
+    """Z_i = GeLU(X·A_i + a_i)·B_i for one rank; X [M,h], A_i [h,f], B_i [f,h]."""
+    X, A_i, B_i, a_i = f64(X), f64(A_i), f64(B_i), f64(a_i)
+    M, h = X.shape
+    f = A_i.shape[1]
+    assert A_i.shape == (h, f) and B_i.shape == (f, h)
+    Z = np.empty((M, h), dtype=np.float64)
+    _load().orc_mlp_shard(_p(X), _p(A_i), _p(a_i), _p(B_i), _p(Z), M, h, f)
+    return Z
+
+
+def attn_shard_rows(X, b: int, s: int, Wqkv, Wo, Hl: int, d: int, causal: bool,
+                    rows=None) -> np.ndarray:
+    """One rank's attention partial Z_i = O_i·W_o,i for the token rows ``rows``.
+
+    X [b·s, h]; Wqkv [h, 3·Hl·d] laid out [W_q | W_k | W_v] (local heads,
+    head-major within each block); Wo [Hl·d, h].  Returns [len(rows), h].
+    """
+    X, Wqkv, Wo = f64(X), f64(Wqkv), f64(Wo)
+    h = X.shape[1]
+    assert X.shape[0] == b * s and Wqkv.shape == (h, 3 * Hl * d) and Wo.shape == (Hl * d, h)
+    if rows is None:
+        rows = np.arange(b * s, dtype=np.int64)
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    Z = np.empty((rows.size, h), dtype=np.float64)
+    _load().orc_attn_shard_rows(_p(X), b, s, h, _p(Wqkv), _p(Wo), Hl, d, int(bool(causal)),
+                                rows.ctypes.data_as(ctypes.POINTER(_i64)), rows.size, _p(Z))
+    return Z
+
+
+def partial_sum(parts, bias=None, residual=None) -> np.ndarray:
+    """Z = sum_r parts[r] (+bias per column) (+residual); parts [P, M, h]."""
+    parts = f64(parts)
+    P = parts.shape[0]
+    M, h = parts.shape[1], parts.shape[2]
+    bias, residual = f64(bias), f64(residual)
+    if residual is not None:
+        residual = np.ascontiguousarray(residual.reshape(M, h))
+    Z = np.empty((M, h), dtype=np.float64)
+    _load().orc_partial_sum(_p(parts), P, M, h, _p(bias), _p(residual), _p(Z))
+    return Z
+
+
+# ---------------------------------------------------------------- composites
+def block_rows(x, b: int, s: int, Wqkv_list, Wo_list, A_list, B_list, H: int, d: int,
+               rows=None, ln1=(None, None), ln2=(None, None), eps: float = 1e-5,
+               causal: bool = True):
+    """Pre-LN block with P ranks' shares summed, for the token rows ``rows``.
+
+      x1  = x  + sum_r Attn_r(LN1(x))
+      out = x1 + sum_r MLP_r(LN2(x1))
+
+    Returns (x1_rows, out_rows), both [len(rows), h] float64.  LN1 is taken over
+    exactly the prefix rows the sampled queries attend to; rows are independent
+    everywhere else.  Weights are converted one rank at a time.
+    """
+    P = len(Wqkv_list)
+    xf = f64(x)
+    h = xf.shape[1]
+    Hl = H // P
+    if rows is None:
+        rows = np.arange(b * s, dtype=np.int64)
+    rows = np.asarray(rows, dtype=np.int64)
+    # LN1 of the prefix rows each sampled query reads (all of its sequence
+    # when not causal); other rows are never read.
+    need = np.zeros(b * s, dtype=bool)
+    for m in rows:
+        beta, t = divmod(int(m), s)
+        need[beta * s: beta * s + (t + 1 if causal else s)] = True
+    idx = np.nonzero(need)[0]
+    xn = np.zeros_like(xf)
+    xn[idx] = layernorm(xf[idx], ln1[0], ln1[1], eps)
+    attn_parts = np.empty((P, rows.size, h), dtype=np.float64)
+    for r in range(P):
+        attn_parts[r] = attn_shard_rows(xn, b, s, f64(Wqkv_list[r]), f64(Wo_list[r]),
+                                        Hl, d, causal, rows)
+    x1 = partial_sum(attn_parts, None, xf[rows])
+    del attn_parts
+    xn2 = layernorm(x1, ln2[0], ln2[1], eps)
+    mlp_parts = np.empty((P, rows.size, h), dtype=np.float64)
+    for r in range(P):
+        mlp_parts[r] = mlp_shard(xn2, f64(A_list[r]), f64(B_list[r]))
+    out = partial_sum(mlp_parts, None, x1)
+    return x1, out

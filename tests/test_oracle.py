@@ -1,0 +1,412 @@
+"""Pins for the fp64 oracle, independent of the oracle itself (CPU only).
+
+Each test ties the oracle to something it does not compute the same way: the
+invariants of the tensor-parallel method ("图解Transformer并行计算"
+(un.csdn.net/7y5fj9k05scw) §1.1, §1.2, §2.1, §3.2), closed forms, textbook
+values, library routines in float64 and brute-force pure-Python loops over
+tiny inputs.  Every shape is non-square so a transposed operand cannot pass.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+RNG = np.random.default_rng(12345)
+
+
+def rel(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+# --------------------------------------------------------------- matmul
+def test_matmul_matches_library():
+    X = RNG.standard_normal((13, 29))
+    W = RNG.standard_normal((29, 11))
+    bias = RNG.standard_normal(11)
+    assert rel(oracle.matmul(X, W), X @ W) < 1e-14
+    assert rel(oracle.matmul(X, W, bias), X @ W + bias) < 1e-14
+
+
+def test_matmul_brute_force_exact_sums():
+    X = RNG.standard_normal((3, 5))
+    W = RNG.standard_normal((5, 4))
+    Y = oracle.matmul(X, W)
+    for m in range(3):
+        for n in range(4):
+            ref = math.fsum(X[m, k] * W[k, n] for k in range(5))
+            assert abs(Y[m, n] - ref) <= 1e-14 * (1 + abs(ref))
+
+
+def test_matmul_identity_gives_input():
+    X = RNG.standard_normal((6, 8))
+    assert np.array_equal(oracle.matmul(X, np.eye(8)), X)
+
+
+def test_column_split_concat_is_full_product_bitwise():
+    """§1.2: Y_r = X·W_r on column blocks; concatenation equals X·W exactly."""
+    X = RNG.standard_normal((10, 24))
+    W = RNG.standard_normal((24, 36))
+    full = oracle.matmul(X, W)
+    for P in (2, 3, 4):
+        c = 36 // P
+        parts = [oracle.matmul(X, np.ascontiguousarray(W[:, r * c:(r + 1) * c])) for r in range(P)]
+        assert np.array_equal(np.concatenate(parts, axis=1), full)
+
+
+def test_row_split_sum_is_full_product():
+    """§1.1: W split on rows, X split on columns; summing the partials gives X·W."""
+    X = RNG.standard_normal((9, 32))
+    W = RNG.standard_normal((32, 20))
+    full = oracle.matmul(X, W)
+    for P in (2, 4, 8):
+        c = 32 // P
+        parts = np.stack([oracle.matmul(np.ascontiguousarray(X[:, r * c:(r + 1) * c]),
+                                        np.ascontiguousarray(W[r * c:(r + 1) * c]))
+                          for r in range(P)])
+        assert rel(oracle.partial_sum(parts), full) < 1e-14
+
+
+def test_split_gather_reconstruction_is_exact():
+    """Splitting a weight into P blocks and concatenating them back is the identity."""
+    W = torch.randn(128, 256, dtype=torch.float64)
+    for dim in (0, 1):
+        parts = torch.split(W, W.shape[dim] // 4, dim=dim)
+        assert torch.equal(torch.cat(parts, dim=dim), W)
+
+
+# --------------------------------------------------------------- GeLU
+def _golden_phi():
+    rows = []
+    with open(os.path.join(HERE, "golden", "normal_cdf.txt")) as fh:
+        for line in fh:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                x, p = line.split()
+                rows.append((float(x), float(p)))
+    return rows
+
+
+def test_gelu_textbook_values():
+    for x, phi in _golden_phi():
+        assert abs(oracle.gelu_scalar(x) - x * phi) <= 1e-15 * max(1.0, abs(x))
+
+
+def test_gelu_closed_forms():
+    assert oracle.gelu_scalar(0.0) == 0.0
+    for x in np.linspace(-6, 6, 97):
+        # GeLU(x) - GeLU(-x) = x because erf is odd
+        assert abs(oracle.gelu_scalar(x) - oracle.gelu_scalar(-x) - x) <= 4e-16 * max(1, abs(x))
+    assert abs(oracle.gelu_scalar(12.0) - 12.0) < 1e-15
+    assert abs(oracle.gelu_scalar(-12.0)) < 1e-30
+
+
+def _erf_series(x):
+    # Maclaurin series erf(x) = 2/sqrt(pi) * sum_n (-1)^n x^(2n+1) / (n! (2n+1))
+    term, n = x, 0
+    terms = []
+    while True:
+        t = term / (2 * n + 1)
+        terms.append(t)
+        if abs(t) < 1e-30:
+            break
+        n += 1
+        term *= -x * x / n
+    return 2.0 / math.sqrt(math.pi) * math.fsum(terms)
+
+
+def test_gelu_matches_independent_erf_series():
+    for x in np.linspace(-3, 3, 61):
+        ref = 0.5 * x * (1.0 + _erf_series(x / math.sqrt(2.0)))
+        assert abs(oracle.gelu_scalar(x) - ref) <= 1e-13
+
+
+def test_gelu_vector_matches_torch_exact_gelu():
+    x = RNG.standard_normal(1000) * 3
+    ref = torch.nn.functional.gelu(torch.from_numpy(x), approximate="none").numpy()
+    assert np.max(np.abs(oracle.gelu(x) - ref)) < 1e-14
+    tanh = torch.nn.functional.gelu(torch.from_numpy(x), approximate="tanh").numpy()
+    assert np.max(np.abs(oracle.gelu(x) - tanh)) > 1e-5  # not the tanh form
+
+
+# --------------------------------------------------------------- MLP
+def _mlp_weights(M=12, h=16, F=48):
+    X = RNG.standard_normal((M, h))
+    A = RNG.standard_normal((h, F)) / math.sqrt(h)
+    B = RNG.standard_normal((F, h)) / math.sqrt(F)
+    a = RNG.standard_normal(F) * 0.1
+    return X, A, B, a
+
+
+def test_mlp_unsharded_matches_library():
+    X, A, B, a = _mlp_weights()
+    t = lambda v: torch.from_numpy(v)
+    ref = (torch.nn.functional.gelu(t(X) @ t(A) + t(a)) @ t(B)).numpy()
+    assert rel(oracle.mlp_shard(X, A, B, a), ref) < 1e-13
+
+
+@pytest.mark.parametrize("P", [2, 3, 4, 8])
+def test_mlp_shards_sum_to_unsharded(P):
+    """§2.1: column-split A, local GeLU, row-split B; Z = sum_i Z_i."""
+    X, A, B, a = _mlp_weights(F=48)
+    f = 48 // P
+    parts = np.stack([oracle.mlp_shard(X, np.ascontiguousarray(A[:, r * f:(r + 1) * f]),
+                                       np.ascontiguousarray(B[r * f:(r + 1) * f]),
+                                       a[r * f:(r + 1) * f]) for r in range(P)])
+    assert rel(oracle.partial_sum(parts), oracle.mlp_shard(X, A, B, a)) < 1e-13
+
+
+def test_mlp_row_split_first_layer_is_wrong():
+    """§2.1 negative control: splitting A by rows puts GeLU before the sum, which
+    gives a different answer (GeLU(Y1+Y2) != GeLU(Y1)+GeLU(Y2))."""
+    X, A, B, _ = _mlp_weights(F=48)
+    h = 16
+    wrong = sum(oracle.matmul(oracle.gelu(oracle.matmul(np.ascontiguousarray(X[:, r * 8:(r + 1) * 8]),
+                                                        np.ascontiguousarray(A[r * 8:(r + 1) * 8]))), B)
+                for r in range(h // 8))
+    assert rel(wrong, oracle.mlp_shard(X, A, B)) > 1e-2
+
+
+def test_mlp_brute_force():
+    M, h, f = 3, 4, 6
+    X = RNG.standard_normal((M, h))
+    A = RNG.standard_normal((h, f))
+    B = RNG.standard_normal((f, h))
+    a = RNG.standard_normal(f)
+    Z = oracle.mlp_shard(X, A, B, a)
+    for m in range(M):
+        g = []
+        for n in range(f):
+            y = math.fsum(X[m, k] * A[k, n] for k in range(h)) + a[n]
+            g.append(0.5 * y * (1 + math.erf(y / math.sqrt(2))))
+        for j in range(h):
+            ref = math.fsum(g[n] * B[n, j] for n in range(f))
+            assert abs(Z[m, j] - ref) <= 1e-13 * (1 + abs(ref))
+
+
+# --------------------------------------------------------------- attention
+def _attn_setup(b=2, s=7, H=4, d=3):
+    h = H * d
+    X = RNG.standard_normal((b * s, h))
+    Wq = RNG.standard_normal((h, H * d)) / math.sqrt(h)
+    Wk = RNG.standard_normal((h, H * d)) / math.sqrt(h)
+    Wv = RNG.standard_normal((h, H * d)) / math.sqrt(h)
+    Wo = RNG.standard_normal((H * d, h)) / math.sqrt(h)
+    return X, Wq, Wk, Wv, Wo
+
+
+def _rank_qkv(Wq, Wk, Wv, r, Hl, d):
+    sl = slice(r * Hl * d, (r + 1) * Hl * d)
+    return np.ascontiguousarray(np.concatenate([Wq[:, sl], Wk[:, sl], Wv[:, sl]], axis=1))
+
+
+def _torch_mha(X, Wq, Wk, Wv, Wo, b, s, H, d, causal):
+    t = lambda v: torch.from_numpy(v)
+    q = (t(X) @ t(Wq)).view(b, s, H, d).transpose(1, 2)
+    k = (t(X) @ t(Wk)).view(b, s, H, d).transpose(1, 2)
+    v = (t(X) @ t(Wv)).view(b, s, H, d).transpose(1, 2)
+    o = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=causal)
+    return (o.transpose(1, 2).reshape(b * s, H * d) @ t(Wo)).numpy()
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_attention_full_matches_library(causal):
+    b, s, H, d = 2, 7, 4, 3
+    X, Wq, Wk, Wv, Wo = _attn_setup(b, s, H, d)
+    ours = oracle.attn_shard_rows(X, b, s, _rank_qkv(Wq, Wk, Wv, 0, H, d), Wo, H, d, causal)
+    assert rel(ours, _torch_mha(X, Wq, Wk, Wv, Wo, b, s, H, d, causal)) < 1e-13
+
+
+@pytest.mark.parametrize("P", [2, 4])
+def test_head_sharded_attention_sums_to_full_mha(P):
+    """§3.2: each rank runs its H/P heads and multiplies by its row block of
+    W_o; the sum over ranks equals full multi-head attention."""
+    b, s, H, d = 2, 6, 4, 5
+    X, Wq, Wk, Wv, Wo = _attn_setup(b, s, H, d)
+    Hl = H // P
+    parts = np.stack([oracle.attn_shard_rows(X, b, s, _rank_qkv(Wq, Wk, Wv, r, Hl, d),
+                                             np.ascontiguousarray(Wo[r * Hl * d:(r + 1) * Hl * d]),
+                                             Hl, d, True) for r in range(P)])
+    full = oracle.attn_shard_rows(X, b, s, _rank_qkv(Wq, Wk, Wv, 0, H, d), Wo, H, d, True)
+    assert rel(oracle.partial_sum(parts), full) < 1e-13
+
+
+def test_attention_sampled_rows_equal_full_rows():
+    b, s, H, d = 3, 9, 2, 4
+    X, Wq, Wk, Wv, Wo = _attn_setup(b, s, H, d)
+    Wqkv = _rank_qkv(Wq, Wk, Wv, 0, H, d)
+    full = oracle.attn_shard_rows(X, b, s, Wqkv, Wo, H, d, True)
+    rows = np.array([26, 0, 9, 13, 17, 4])
+    assert np.array_equal(oracle.attn_shard_rows(X, b, s, Wqkv, Wo, H, d, True, rows), full[rows])
+
+
+def test_attention_single_token_returns_value_projection():
+    """s = 1: softmax over one key is 1, so O = V and Z = V·W_o."""
+    b, s, H, d = 4, 1, 2, 3
+    X, Wq, Wk, Wv, Wo = _attn_setup(b, s, H, d)
+    ours = oracle.attn_shard_rows(X, b, s, _rank_qkv(Wq, Wk, Wv, 0, H, d), Wo, H, d, True)
+    assert rel(ours, (X @ Wv) @ Wo) < 1e-14
+
+
+def test_attention_equal_scores_give_causal_running_mean():
+    """W_k = 0 makes every score 0: causal softmax weights are 1/(t+1) over
+    u <= t, so O_t is the running mean of v_0..v_t (pins the mask direction)."""
+    b, s, H, d = 2, 8, 2, 3
+    X, Wq, Wk, Wv, Wo = _attn_setup(b, s, H, d)
+    Wk = np.zeros_like(Wk)
+    O_ref = np.zeros((b * s, H * d))
+    V = X @ Wv
+    for beta in range(b):
+        for t in range(s):
+            O_ref[beta * s + t] = V[beta * s: beta * s + t + 1].mean(axis=0)
+    ours = oracle.attn_shard_rows(X, b, s, _rank_qkv(Wq, Wk, Wv, 0, H, d), np.eye(H * d), H, d, True)
+    assert rel(ours, O_ref) < 1e-14
+
+
+def test_attention_brute_force():
+    b, s, H, d = 1, 3, 2, 2
+    h = 4
+    X = RNG.standard_normal((s, h))
+    Wqkv = RNG.standard_normal((h, 3 * H * d))
+    Wo = RNG.standard_normal((H * d, h))
+    Z = oracle.attn_shard_rows(X, b, s, Wqkv, Wo, H, d, True)
+    proj = [[math.fsum(X[t, k] * Wqkv[k, n] for k in range(h)) for n in range(3 * H * d)] for t in range(s)]
+    for t in range(s):
+        o = []
+        for j in range(H):
+            q = proj[t][j * d:(j + 1) * d]
+            sc = []
+            for u in range(t + 1):
+                kv = proj[u][H * d + j * d: H * d + (j + 1) * d]
+                sc.append(math.fsum(q[c] * kv[c] for c in range(d)) / math.sqrt(d))
+            mx = max(sc)
+            w = [math.exp(v - mx) for v in sc]
+            den = math.fsum(w)
+            for c in range(d):
+                o.append(math.fsum(w[u] * proj[u][2 * H * d + j * d + c] for u in range(t + 1)) / den)
+        for n in range(h):
+            ref = math.fsum(o[k] * Wo[k, n] for k in range(H * d))
+            assert abs(Z[t, n] - ref) <= 1e-13 * (1 + abs(ref))
+
+
+# --------------------------------------------------------------- LayerNorm
+def test_layernorm_moments():
+    x = RNG.standard_normal((17, 40)) * 3 + 1.5
+    eps = 1e-5
+    y = oracle.layernorm(x, eps=eps)
+    var = x.var(axis=1)
+    assert np.max(np.abs(y.mean(axis=1))) < 1e-14
+    assert np.max(np.abs(y.var(axis=1) - var / (var + eps))) < 1e-13
+
+
+def test_layernorm_matches_library():
+    x = RNG.standard_normal((9, 24))
+    g = RNG.standard_normal(24)
+    bta = RNG.standard_normal(24)
+    ref = torch.nn.functional.layer_norm(torch.from_numpy(x), (24,), torch.from_numpy(g),
+                                         torch.from_numpy(bta), eps=1e-5).numpy()
+    assert rel(oracle.layernorm(x, g, bta, 1e-5), ref) < 1e-14
+
+
+# --------------------------------------------------------------- partial sum
+def test_partial_sum_exact_against_fsum():
+    P, M, h = 8, 5, 7
+    parts = RNG.standard_normal((P, M, h)) * 10.0 ** RNG.integers(-3, 4, size=(P, M, h))
+    bias = RNG.standard_normal(h)
+    res = RNG.standard_normal((M, h))
+    Z = oracle.partial_sum(parts, bias, res)
+    for m in range(M):
+        for c in range(h):
+            terms = [*parts[:, m, c], bias[c], res[m, c]]
+            ref = math.fsum(terms)
+            assert abs(Z[m, c] - ref) <= 1e-15 * 16 * math.fsum(abs(v) for v in terms)
+    # the bias is added once per element, not once per rank
+    Z0 = oracle.partial_sum(parts)
+    assert rel(Z - Z0, np.broadcast_to(bias, (M, h)) + res) < 1e-12
+
+
+# --------------------------------------------------------------- block
+def _block_weights(P, h, H, d, F, seed=7):
+    rng = np.random.default_rng(seed)
+    Wq = rng.standard_normal((h, H * d)) / math.sqrt(h)
+    Wk = rng.standard_normal((h, H * d)) / math.sqrt(h)
+    Wv = rng.standard_normal((h, H * d)) / math.sqrt(h)
+    Wo = rng.standard_normal((H * d, h)) / math.sqrt(H * d)
+    A = rng.standard_normal((h, F)) / math.sqrt(h)
+    B = rng.standard_normal((F, h)) / math.sqrt(F)
+    Hl, f = H // P, F // P
+    qkv = [_rank_qkv(Wq, Wk, Wv, r, Hl, d) for r in range(P)]
+    wo = [np.ascontiguousarray(Wo[r * Hl * d:(r + 1) * Hl * d]) for r in range(P)]
+    a = [np.ascontiguousarray(A[:, r * f:(r + 1) * f]) for r in range(P)]
+    bb = [np.ascontiguousarray(B[r * f:(r + 1) * f]) for r in range(P)]
+    return qkv, wo, a, bb
+
+
+def test_block_brute_force():
+    """A pure-Python pre-LN block on a tiny input (P=2, h=8, H=2, d=4, s=3, F=16)."""
+    P, b, s, H, d, F = 2, 2, 3, 2, 4, 16
+    h = H * d
+    x = RNG.standard_normal((b * s, h))
+    qkv, wo, A, B = _block_weights(P, h, H, d, F)
+    g1, b1 = RNG.standard_normal(h), RNG.standard_normal(h)
+    g2, b2 = RNG.standard_normal(h), RNG.standard_normal(h)
+    eps = 1e-5
+    x1_o, out_o = oracle.block_rows(x, b, s, qkv, wo, A, B, H, d, ln1=(g1, b1), ln2=(g2, b2), eps=eps)
+
+    def ln(row, g, bt):
+        mu = math.fsum(row) / len(row)
+        var = math.fsum((v - mu) ** 2 for v in row) / len(row)
+        return [(v - mu) / math.sqrt(var + eps) * g[i] + bt[i] for i, v in enumerate(row)]
+
+    def mm(vec, W):
+        return [math.fsum(vec[k] * W[k][n] for k in range(len(vec))) for n in range(len(W[0]))]
+
+    Hl, f = H // P, F // P
+    xn = [ln(list(x[m]), g1, b1) for m in range(b * s)]
+    x1 = [list(x[m]) for m in range(b * s)]
+    for r in range(P):
+        proj = [mm(xn[m], qkv[r].tolist()) for m in range(b * s)]
+        for m in range(b * s):
+            beta, t = divmod(m, s)
+            o = []
+            for j in range(Hl):
+                q = proj[m][j * d:(j + 1) * d]
+                sc = [math.fsum(q[c] * proj[beta * s + u][Hl * d + j * d + c] for c in range(d)) / math.sqrt(d)
+                      for u in range(t + 1)]
+                mx = max(sc)
+                w = [math.exp(v - mx) for v in sc]
+                den = math.fsum(w)
+                o += [math.fsum(w[u] * proj[beta * s + u][2 * Hl * d + j * d + c] for u in range(t + 1)) / den
+                      for c in range(d)]
+            z = mm(o, wo[r].tolist())
+            x1[m] = [x1[m][c] + z[c] for c in range(h)]
+    out = [row[:] for row in x1]
+    for m in range(b * s):
+        xn2 = ln(x1[m], g2, b2)
+        for r in range(P):
+            y = mm(xn2, A[r].tolist())
+            g = [0.5 * v * (1 + math.erf(v / math.sqrt(2))) for v in y]
+            z = mm(g, B[r].tolist())
+            out[m] = [out[m][c] + z[c] for c in range(h)]
+    assert rel(x1_o, np.array(x1)) < 1e-12
+    assert rel(out_o, np.array(out)) < 1e-12
+
+
+def test_block_ranks_sum_to_unsharded_block():
+    b, s, H, d, F = 2, 5, 4, 4, 64
+    h = H * d
+    x = RNG.standard_normal((b * s, h))
+    full = _block_weights(1, h, H, d, F, seed=3)
+    shard = _block_weights(4, h, H, d, F, seed=3)
+    x1a, outa = oracle.block_rows(x, b, s, *full, H, d)
+    x1b, outb = oracle.block_rows(x, b, s, *shard, H, d)
+    assert rel(x1a, x1b) < 1e-13 and rel(outa, outb) < 1e-13
+    rows = [9, 0, 6]
+    x1c, outc = oracle.block_rows(x, b, s, *shard, H, d, rows=rows)
+    assert rel(outc, outb[rows]) < 1e-14 and rel(x1c, x1b[rows]) < 1e-14
