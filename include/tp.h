@@ -1,0 +1,187 @@
+/*
+ * tp.h -- C ABI of libtp.so: one tensor-parallel rank's share of a
+ * Megatron-style Transformer block, computed on one MI355X (gfx950).
+ *
+ * Sources cited below by short name:
+ *   [Megatron explainer] "图解Transformer并行计算：从矩阵乘法切分到Megatron架构设计"
+ *       (un.csdn.net/7y5fj9k05scw): §1.1 row split, §1.2 column split,
+ *       §2.1/§2.2 the MLP, §3.1/§3.2 head-sharded attention.
+ *   [PyTorch TP tutorial] hotelren.com/news/6074135, section 3.3 (the
+ *       pre-LN block: x + attention(norm1(x)), then x + mlp(norm2(x))),
+ *       section 2.2 (heads per rank = num_heads / world_size) and section 3.2
+ *       (a shape that does not divide by the world size is rejected).
+ *
+ * Conventions shared by every entry point:
+ *  - Matrices are row-major with the X·W convention: a weight of a linear
+ *    layer has shape [in, out].  "M" is the token count b·s; token m is
+ *    position t = m % s of sequence m / s.
+ *  - Every tensor pointer is a DEVICE pointer (hipMalloc / PyTorch memory)
+ *    owned by the caller, 16-byte aligned.  Host pointers are only the arrays
+ *    of per-rank device pointers taken by tp_block_shard.
+ *  - The library never allocates, frees or synchronises.  All work is
+ *    enqueued asynchronously on `stream` (a hipStream_t; NULL = the null
+ *    stream); outputs are ready when that stream reaches this point.
+ *  - Arguments are validated before anything is launched; on any error the
+ *    call returns a non-zero tp_status and touches no memory.  TP_ERR_LAUNCH
+ *    reports a failed kernel launch (hipGetLastError after enqueueing), in
+ *    which case outputs are unspecified.
+ *  - Calls are reentrant; calls that share a workspace on different streams
+ *    race.
+ */
+#ifndef TP_H
+#define TP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum tp_status {
+    TP_OK = 0,
+    TP_ERR_NULL = 1,      /* a required pointer is NULL                          */
+    TP_ERR_SHAPE = 2,     /* a size is <= 0, does not divide, or is unsupported  */
+    TP_ERR_DTYPE = 3,     /* dtype code not accepted by this entry point         */
+    TP_ERR_ALIGN = 4,     /* a pointer is not 16-byte aligned                    */
+    TP_ERR_WORKSPACE = 5, /* workspace NULL or smaller than the *_workspace size */
+    TP_ERR_LAUNCH = 6     /* the HIP runtime rejected a kernel launch            */
+} tp_status;
+
+typedef enum tp_dtype {
+    TP_F32 = 0,   /* IEEE binary32                                   */
+    TP_BF16 = 1   /* bfloat16 (top 16 bits of binary32), RNE rounded */
+} tp_dtype;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* tp_status_string(int status);
+
+/* ABI version of this header: 1. */
+int tp_abi_version(void);
+
+/* ------------------------------------------------------------------------
+ * tp_mlp_shard -- one rank's MLP share.  [Megatron explainer] §2.1, §2.2:
+ * the first linear layer is split by columns, GeLU is applied locally, the
+ * second is split by rows, and the result is a partial sum that the
+ * all-reduce would add over ranks:
+ *     Y_i = X·A_i + a_i,    Y'_i = GeLU(Y_i) = Y_i/2·(1+erf(Y_i/sqrt 2)),
+ *     Z_i = Y'_i·B_i.
+ *   X   [M,h]  in dtype `in`          A_i [h,f] in dtype `in`
+ *   a_i [f]    f32, or NULL for none  B_i [f,h] in dtype `in`
+ *   Z_i [M,h]  in dtype `out` (accumulated in f32)
+ *   ws  >= tp_mlp_shard_workspace(M, f, in) bytes (holds Y'_i in dtype `in`).
+ * in: TP_BF16 (MFMA path, f32 accumulate, Y'_i rounded to bf16) or TP_F32
+ * (f32 FMA path).  out: TP_F32 or TP_BF16.  bf16 needs h % 8 == 0 and
+ * f % 8 == 0.
+ * ---------------------------------------------------------------------- */
+size_t tp_mlp_shard_workspace(int64_t M, int64_t f, int in);
+tp_status tp_mlp_shard(const void* X, const void* A_i, const void* a_i, const void* B_i,
+                       void* Z_i, void* ws, size_t ws_bytes,
+                       int64_t M, int64_t h, int64_t f, int in, int out, void* stream);
+
+/* ------------------------------------------------------------------------
+ * tp_attn_shard -- one rank's attention share.  [Megatron explainer] §3.1,
+ * §3.2: the Q, K and V projections are split by columns so that this rank
+ * owns H_l whole heads, each head computes softmax(Q·K^T/sqrt d)·V locally,
+ * and W_o is split by rows so the rank's output is a partial sum:
+ *     [Q|K|V] = X·W_qkv_i,   O_j = softmax(Q_j·K_j^T/sqrt(d) + mask)·V_j,
+ *     Z_i = [O_0|...|O_{H_l-1}]·W_o_i.
+ *   X       [b·s, h] bf16
+ *   W_qkv_i [h, 3·H_l·d] bf16, columns [W_q | W_k | W_v] of this rank's heads;
+ *           inside each block local head j owns columns j·d .. j·d+d-1
+ *   W_o_i   [H_l·d, h] bf16 (this rank's row block of W_o)
+ *   Z_i     [b·s, h] in dtype `out` (TP_F32 or TP_BF16)
+ *   causal  non-zero: key u is visible to query t iff u <= t
+ *   ws      >= tp_attn_shard_workspace(b, s, H_l, d) bytes
+ * d must be 128 (the kernel's head tile); h % 8 == 0.
+ * ---------------------------------------------------------------------- */
+size_t tp_attn_shard_workspace(int64_t b, int64_t s, int64_t H_l, int64_t d);
+tp_status tp_attn_shard(const void* X, const void* W_qkv_i, const void* W_o_i, void* Z_i,
+                        void* ws, size_t ws_bytes, int64_t b, int64_t s, int64_t h,
+                        int64_t H_l, int64_t d, int causal, int out, void* stream);
+
+/* ------------------------------------------------------------------------
+ * tp_partial_sum -- the arithmetic of the all-reduce on one GPU.
+ * [Megatron explainer] §1.1 (row split: the partial products are summed) and
+ * §2.1 (Z = Z1 + Z2):
+ *     Z = sum_{r=0}^{P-1} partials[r]  (+ bias[col])  (+ residual),
+ * summed in f32 in ascending r, so results are bit-reproducible.
+ *   partials  [P][M·h] contiguous, dtype `part` (TP_F32 or TP_BF16)
+ *   bias      [h] f32 or NULL (a row-parallel bias, added once)
+ *   residual  [M,h] dtype `res` or NULL
+ *   Z         [M,h] dtype `out`; may alias `residual` when both are f32.
+ * Needs h % 4 == 0.
+ * ---------------------------------------------------------------------- */
+tp_status tp_partial_sum(void* Z, int out, const void* partials, int part, int P,
+                         int64_t M, int64_t h, const void* bias,
+                         const void* residual, int res, void* stream);
+
+/* ------------------------------------------------------------------------
+ * tp_block_shard -- a whole pre-LN Transformer block with all P ranks'
+ * shares emulated one after another on this GPU ([PyTorch TP tutorial] 3.3):
+ *     x1  = x  + sum_r Attn_r(LN1(x))       (the attention all-reduce)
+ *     out = x1 + sum_r MLP_r(LN2(x1))       (the MLP all-reduce)
+ * with Attn_r and MLP_r the tp_attn_shard / tp_mlp_shard shares of rank r
+ * (H_l = H/P heads, f = F/P columns of A), causal attention, no biases.
+ *   x      [b·s, h] bf16           out  [b·s, h] dtype `out`
+ *   x1     [b·s, h] f32 or NULL    (if given, receives the residual stream
+ *                                   after attention)
+ *   ln*_g, ln*_b  [h] f32 or NULL (gamma=1, beta=0); eps > 0
+ *   W_qkv, W_o, A, B  HOST arrays of P device pointers: rank r's
+ *                     [h,3·H_l·d], [H_l·d,h], [h,f], [f,h] bf16 slices
+ *   ws     >= tp_block_shard_workspace(b, s, h, H, d, F, P) bytes
+ * Needs h == H·d, H % P == 0, F % P == 0, d == 128, h % 8 == 0, f % 8 == 0.
+ * ---------------------------------------------------------------------- */
+size_t tp_block_shard_workspace(int64_t b, int64_t s, int64_t h, int64_t H, int64_t d,
+                                int64_t F, int P);
+tp_status tp_block_shard(const void* x, void* out, int out_dtype, void* x1,
+                         const void* ln1_g, const void* ln1_b,
+                         const void* ln2_g, const void* ln2_b, float eps,
+                         const void* const* W_qkv, const void* const* W_o,
+                         const void* const* A, const void* const* B, int P,
+                         void* ws, size_t ws_bytes, int64_t b, int64_t s, int64_t h,
+                         int64_t H, int64_t d, int64_t F, void* stream);
+
+/* ========================================================================
+ * Component entry points: the individual steps of the path, exported so
+ * that each can be checked on its own.
+ * ====================================================================== */
+
+/* Epilogues of tp_linear. */
+typedef enum tp_epilogue {
+    TP_EPI_NONE = 0,  /* C = X·W (+bias)                                    */
+    TP_EPI_GELU = 1   /* C = GeLU(X·W + bias), exact erf form (§2.1's GeLU) */
+} tp_epilogue;
+
+/* tp_linear -- C[M,N] = epi(X[M,K]·W[K,N] + bias[N]) with an f32 accumulator.
+ * [Megatron explainer] §1: Y = X·W, the product every split applies to its
+ * block.  Row-major with leading dimensions ldx, ldw, ldc (in elements).
+ *   in : TP_BF16 (MFMA) or TP_F32;  out: TP_F32 or TP_BF16;  bias f32 or NULL.
+ * bf16 needs K % 8 == 0, N % 8 == 0 and leading dimensions that are
+ * multiples of 8. */
+tp_status tp_linear(const void* X, int64_t ldx, const void* W, int64_t ldw,
+                    const void* bias, void* C, int64_t ldc,
+                    int64_t M, int64_t N, int64_t K, int in, int out, int epilogue,
+                    void* stream);
+
+/* tp_attention_core -- per (sequence, local head) softmax(Q·K^T/sqrt d)·V
+ * ([Megatron explainer] §3.1) on projections already in memory.
+ *   qkv [b·s, ld_qkv] bf16: for local head j, Q at columns j·d, K at
+ *       H_l·d + j·d, V at 2·H_l·d + j·d (d contiguous columns each)
+ *   O   [b·s, H_l·d] bf16, heads concatenated along the feature axis.
+ * d must be 128; ld_qkv >= 3·H_l·d and a multiple of 8. */
+tp_status tp_attention_core(const void* qkv, int64_t ld_qkv, void* O,
+                            int64_t b, int64_t s, int64_t H_l, int64_t d, int causal,
+                            void* stream);
+
+/* tp_layernorm -- y = (x - mean)/sqrt(var + eps)·gamma + beta over each row of
+ * x [M,h] (population variance, f32 statistics), the block's nn.LayerNorm(h)
+ * ([PyTorch TP tutorial] 3.3).  x in TP_F32 or TP_BF16; y is bf16 [M,h];
+ * gamma/beta f32 [h] or NULL.  Needs h % 8 == 0. */
+tp_status tp_layernorm(const void* x, int in, void* y, const void* gamma,
+                       const void* beta, float eps, int64_t M, int64_t h, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TP_H */

@@ -4,9 +4,11 @@ TEST INFRASTRUCTURE ONLY: only the tests, the smoke check and the benchmark's
 CPU-baseline leg may import this package.  It never imports the HIP library
 and the HIP library never imports it.
 
-The arithmetic lives in ``tp_oracle.c`` (plain loops, float64, k ascending);
-this module converts the shared seeded inputs to float64 exactly and composes
-the C functions in the order the pages give:
+The matrix products X·W are float64 library matmuls (numpy / OpenBLAS); the
+other steps -- exact-erf GeLU, LayerNorm, the per-head softmax attention and
+the partial sum -- are plain float64 loops in ``tp_oracle.c``.  This module
+converts the shared seeded inputs to float64 exactly and composes those steps
+in the order the pages give:
 
 * ``mlp_shard``   -- Y_i = X·A_i (+a_i), GeLU locally, Z_i = GeLU(Y_i)·B_i
   ("图解Transformer并行计算" (un.csdn.net/7y5fj9k05scw) §2.1, §2.2);
@@ -41,14 +43,12 @@ def _load():
         from . import build as _b
         _b.build()
     lib = ctypes.CDLL(_LIB_PATH)
-    lib.orc_matmul.argtypes = [_dp, _i64, _dp, _i64, _dp, _dp, _i64, _i64, _i64, _i64]
     lib.orc_gelu.argtypes = [ctypes.c_double]
     lib.orc_gelu.restype = ctypes.c_double
     lib.orc_gelu_inplace.argtypes = [_dp, _i64]
-    lib.orc_mlp_shard.argtypes = [_dp, _dp, _dp, _dp, _dp, _i64, _i64, _i64]
     lib.orc_layernorm.argtypes = [_dp, _dp, _dp, ctypes.c_double, _dp, _i64, _i64]
-    lib.orc_attn_shard_rows.argtypes = [_dp, _i64, _i64, _i64, _dp, _dp, _i64, _i64,
-                                        ctypes.c_int, ctypes.POINTER(_i64), _i64, _dp]
+    lib.orc_attention_rows.argtypes = [_dp, _dp, _dp, ctypes.POINTER(_i64), _i64, _i64, _i64,
+                                       _i64, ctypes.c_int, _dp]
     lib.orc_partial_sum.argtypes = [_dp, _i64, _i64, _i64, _dp, _dp, _dp]
     lib.orc_num_threads.restype = ctypes.c_int
     _lib = lib
@@ -91,14 +91,17 @@ def _p(a):
 
 # ---------------------------------------------------------------- primitives
 def matmul(X, W, bias=None) -> np.ndarray:
-    """Y = X·W (+bias); X [M,K], W [K,N] (row-major, float64)."""
+    """Y = X·W (+bias) in float64; X [M,K], W [K,N].
+
+    "图解Transformer并行计算" §1: Y = X @ W with W of shape [h, h'].  The
+    product is a library float64 matmul (numpy); the bias is added after it.
+    """
     X, W, bias = f64(X), f64(W), f64(bias)
-    M, K = X.shape
-    K2, N = W.shape
-    assert K == K2
-    Y = np.empty((M, N), dtype=np.float64)
-    _load().orc_matmul(_p(X), K, _p(W), N, _p(bias), _p(Y), N, M, K, N)
-    return Y
+    assert X.ndim == 2 and W.ndim == 2 and X.shape[1] == W.shape[0]
+    Y = np.matmul(X, W)
+    if bias is not None:
+        Y += bias
+    return np.ascontiguousarray(Y)
 
 
 def gelu(x) -> np.ndarray:
@@ -122,33 +125,59 @@ def layernorm(x, gamma=None, beta=None, eps: float = 1e-5) -> np.ndarray:
 
 
 def mlp_shard(X, A_i, B_i, a_i=None) -> np.ndarray:
-    """Z_i = GeLU(X·A_i + a_i)·B_i for one rank; X [M,h], A_i [h,f], B_i [f,h]."""
-    X, A_i, B_i, a_i = f64(X), f64(A_i), f64(B_i), f64(a_i)
+    """One rank's MLP share, "图解Transformer并行计算" §2.1 / §2.2:
+    Y_i = X·A_i (+a_i), Y'_i = GeLU(Y_i) locally, Z_i = Y'_i·B_i (a partial
+    sum).  X [M,h], A_i [h,f], B_i [f,h]."""
+    X, A_i, B_i = f64(X), f64(A_i), f64(B_i)
     M, h = X.shape
     f = A_i.shape[1]
     assert A_i.shape == (h, f) and B_i.shape == (f, h)
-    Z = np.empty((M, h), dtype=np.float64)
-    _load().orc_mlp_shard(_p(X), _p(A_i), _p(a_i), _p(B_i), _p(Z), M, h, f)
-    return Z
+    return matmul(gelu(matmul(X, A_i, a_i)), B_i)
+
+
+def attention_rows(Q, K, V, tpos, Hl: int, d: int, causal: bool) -> np.ndarray:
+    """softmax(q·K^T/sqrt d)·V per local head for query rows of one sequence
+    (the C loop); Q [nq, Hl·d], K/V [L, Hl·d], tpos [nq] positions."""
+    Q, K, V = f64(Q), f64(K), f64(V)
+    tpos = np.ascontiguousarray(np.asarray(tpos, dtype=np.int64))
+    nq, L = Q.shape[0], K.shape[0]
+    assert Q.shape[1] == K.shape[1] == V.shape[1] == Hl * d and V.shape[0] == L
+    assert nq == 0 or (tpos.min() >= 0 and tpos.max() < L)
+    O = np.empty((nq, Hl * d), dtype=np.float64)
+    _load().orc_attention_rows(_p(Q), _p(K), _p(V), tpos.ctypes.data_as(ctypes.POINTER(_i64)),
+                               nq, L, Hl, d, int(bool(causal)), _p(O))
+    return O
 
 
 def attn_shard_rows(X, b: int, s: int, Wqkv, Wo, Hl: int, d: int, causal: bool,
                     rows=None) -> np.ndarray:
-    """One rank's attention partial Z_i = O_i·W_o,i for the token rows ``rows``.
+    """One rank's attention partial Z_i = O_i·W_o,i for the token rows ``rows``
+    ("图解Transformer并行计算" §3.1 / §3.2).
 
-    X [b·s, h]; Wqkv [h, 3·Hl·d] laid out [W_q | W_k | W_v] (local heads,
-    head-major within each block); Wo [Hl·d, h].  Returns [len(rows), h].
+    X [b·s, h] (token m = sequence m // s, position m % s); Wqkv [h, 3·Hl·d]
+    laid out [W_q | W_k | W_v] for the local heads, head-major within each
+    block; Wo [Hl·d, h].  The keys and values of each sequence are projected
+    over exactly the prefix the requested rows attend to (all s tokens when
+    not causal).  Returns [len(rows), h].
     """
     X, Wqkv, Wo = f64(X), f64(Wqkv), f64(Wo)
     h = X.shape[1]
-    assert X.shape[0] == b * s and Wqkv.shape == (h, 3 * Hl * d) and Wo.shape == (Hl * d, h)
+    HD = Hl * d
+    assert X.shape[0] == b * s and Wqkv.shape == (h, 3 * HD) and Wo.shape == (HD, h)
     if rows is None:
         rows = np.arange(b * s, dtype=np.int64)
-    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
-    Z = np.empty((rows.size, h), dtype=np.float64)
-    _load().orc_attn_shard_rows(_p(X), b, s, h, _p(Wqkv), _p(Wo), Hl, d, int(bool(causal)),
-                                rows.ctypes.data_as(ctypes.POINTER(_i64)), rows.size, _p(Z))
-    return Z
+    rows = np.asarray(rows, dtype=np.int64)
+    O = np.empty((rows.size, HD), dtype=np.float64)
+    for beta in np.unique(rows // s):
+        sel = np.nonzero(rows // s == beta)[0]
+        t = rows[sel] % s
+        L = int(t.max()) + 1 if causal else s
+        xs = X[beta * s: beta * s + L]
+        KV = matmul(xs, np.ascontiguousarray(Wqkv[:, HD:]))
+        Q = matmul(np.ascontiguousarray(X[rows[sel]]), np.ascontiguousarray(Wqkv[:, :HD]))
+        O[sel] = attention_rows(Q, np.ascontiguousarray(KV[:, :HD]),
+                                np.ascontiguousarray(KV[:, HD:]), t, Hl, d, causal)
+    return matmul(O, Wo)
 
 
 def partial_sum(parts, bias=None, residual=None) -> np.ndarray:

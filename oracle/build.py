@@ -12,7 +12,7 @@ LIB = os.path.join(HERE, "liboracle.so")
 
 def build(verbose: bool = False) -> str:
     # No -ffast-math: every sum keeps its written order and IEEE semantics.
-    cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared",
+    cmd = ["gcc", "-O2", "-std=c99", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
            "-fvisibility=hidden", SRC, "-o", LIB + ".tmp", "-lm"]
     if verbose:
         print(" ".join(cmd))

@@ -1,0 +1,111 @@
+"""The five synthetic workloads: shapes, value distributions and seeds.
+
+Every input is N(0, sigma^2), drawn by ``synth.normal``; weights use
+sigma = 1/sqrt(fan_in) with fan_in the UNSHARDED input width (h for A, W_qkv
+and W_o; F for B).  Single-rank workloads draw rank 0's slice directly at the
+slice shape.  Nothing here computes any part of the method; the FLOP counts
+are the matrix-product counts used to report throughput (2 per multiply-add;
+causal attention counts only the visible (query, key) pairs).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+from . import normal, fan_in_sigma, rank_seed
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    kind: str            # "mlp" | "attn" | "block"
+    seed: int
+    P: int               # tensor-parallel degree
+    b: int
+    s: int
+    h: int
+    F: int = 0           # full FFN width
+    H: int = 0           # total heads
+    d: int = 128         # head dimension
+    dtype: torch.dtype = torch.bfloat16
+    all_ranks: bool = False
+    description: str = ""
+
+    @property
+    def M(self) -> int:
+        return self.b * self.s
+
+    @property
+    def f(self) -> int:
+        return self.F // self.P
+
+    @property
+    def Hl(self) -> int:
+        return self.H // self.P
+
+    # ---- matrix FLOPs ----------------------------------------------------
+    def mlp_flops_rank(self) -> int:
+        return 4 * self.M * self.h * self.f
+
+    def attn_flops_rank(self) -> dict:
+        qkv = 2 * self.M * self.h * 3 * self.Hl * self.d
+        pairs = self.b * self.s * (self.s + 1) // 2
+        core = 4 * self.Hl * self.d * pairs
+        wo = 2 * self.M * self.Hl * self.d * self.h
+        return {"qkv": qkv, "core": core, "wo": wo, "total": qkv + core + wo}
+
+    def flops(self) -> int:
+        """Matrix FLOPs of one call of the workload's entry point."""
+        if self.kind == "mlp":
+            return self.mlp_flops_rank() * (self.P if self.all_ranks else 1)
+        if self.kind == "attn":
+            return self.attn_flops_rank()["total"]
+        return self.P * (self.mlp_flops_rank() + self.attn_flops_rank()["total"])
+
+
+WORKLOADS = {w.name: w for w in [
+    Workload("mlp_f32_h64_tp2", "mlp", 1000, P=2, b=2, s=16, h=64, F=256, dtype=torch.float32,
+             all_ranks=True,
+             description="fp32 MLP TP shard, tp=2 emulated sequentially, X [2,16,64]"),
+    Workload("mlp_bf16_h4096_tp8", "mlp", 1001, P=8, b=8, s=1024, h=4096, F=16384,
+             description="bf16 MLP, one rank of tp=8: A_i [4096,2048], B_i [2048,4096], 8192 tokens"),
+    Workload("mlp_bf16_h12288_tp8", "mlp", 1002, P=8, b=8, s=2048, h=12288, F=49152,
+             description="bf16 MLP, one rank of tp=8 at the 175B layer shape, 16384 tokens"),
+    Workload("attn_bf16_h4096_tp4", "attn", 1003, P=4, b=4, s=2048, h=4096, H=32,
+             description="bf16 causal self-attention, one rank of tp=4: 8 local heads of 128"),
+    Workload("block_bf16_h12288_tp8", "block", 1004, P=8, b=8, s=2048, h=12288, H=96, F=49152,
+             all_ranks=True,
+             description="bf16 pre-LN block at the 175B layer shape, all 8 ranks of tp=8 in turn"),
+]}
+
+
+def mlp_inputs(w: Workload):
+    """X and the full (all-rank) or rank-0 A/B of an MLP workload, on the CPU."""
+    X = normal((w.M, w.h), 1.0, w.seed, "x", w.dtype)
+    width = w.F if w.all_ranks else w.f
+    A = normal((w.h, width), fan_in_sigma(w.h), w.seed, "A", w.dtype)
+    B = normal((width, w.h), fan_in_sigma(w.F), w.seed, "B", w.dtype)
+    return X, A, B
+
+
+def attn_inputs(w: Workload):
+    """X, W_qkv_0 [h, 3·H_l·d] and W_o_0 [H_l·d, h] of an attention workload."""
+    X = normal((w.M, w.h), 1.0, w.seed, "x", w.dtype)
+    Wqkv = normal((w.h, 3 * w.Hl * w.d), fan_in_sigma(w.h), w.seed, "Wqkv", w.dtype)
+    Wo = normal((w.Hl * w.d, w.h), fan_in_sigma(w.h), w.seed, "Wo", w.dtype)
+    return X, Wqkv, Wo
+
+
+def block_input(w: Workload):
+    return normal((w.M, w.h), 1.0, w.seed, "x", w.dtype)
+
+
+def block_rank_weights(w: Workload, r: int):
+    """Rank r's W_qkv_r, W_o_r, A_r, B_r of a block workload, on the CPU."""
+    sd = rank_seed(w.seed, r)
+    Wqkv = normal((w.h, 3 * w.Hl * w.d), fan_in_sigma(w.h), sd, "Wqkv", w.dtype)
+    Wo = normal((w.Hl * w.d, w.h), fan_in_sigma(w.h), sd, "Wo", w.dtype)
+    A = normal((w.h, w.f), fan_in_sigma(w.h), sd, "A", w.dtype)
+    B = normal((w.f, w.h), fan_in_sigma(w.F), sd, "B", w.dtype)
+    return Wqkv, Wo, A, B

@@ -1,0 +1,159 @@
+"""The C ABI of libtp.so on the CPU: it loads, exports every symbol that
+include/tp.h declares, binds to torch's HIP runtime, and rejects bad
+arguments with the documented status before launching anything (no compute
+call is made here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import transformer_tensor_shard_amd as tts
+from transformer_tensor_shard_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tp.h")
+
+FAKE = ctypes.c_void_p(0x100000)        # aligned, never dereferenced
+FAKE_ODD = ctypes.c_void_p(0x100004)    # 4-byte aligned only
+BIG = 1 << 40
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tp_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    names = header_functions()
+    assert len(names) >= 12
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (tp_\w+)", out))
+    assert set(names) == exported, (set(names) ^ exported)
+    assert set(names) == set(_lib.SIGNATURES)
+
+
+def test_loads_and_reports_version():
+    L = tts.lib()
+    assert L.tp_abi_version() == 1
+    assert L.tp_status_string(0) == b"ok"
+    assert L.tp_status_string(99) == b"unknown status"
+
+
+def test_single_hip_runtime_mapped():
+    tts.lib()
+    maps = open("/proc/self/maps").read()
+    libs = {m for m in re.findall(r"(\S*libamdhip64[^\s]*)", maps)}
+    assert len({os.path.realpath(p) for p in libs}) == 1, libs
+
+
+def mlp(**kw):
+    a = dict(X=FAKE, A=FAKE, a=None, B=FAKE, Z=FAKE, ws=FAKE, wsb=BIG, M=64, h=64, f=32,
+             i=_lib.TP_BF16, o=_lib.TP_F32)
+    a.update(kw)
+    return tts.lib().tp_mlp_shard(a["X"], a["A"], a["a"], a["B"], a["Z"], a["ws"], a["wsb"],
+                                  a["M"], a["h"], a["f"], a["i"], a["o"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(X=None), _lib.TP_ERR_NULL),
+    (dict(B=None), _lib.TP_ERR_NULL),
+    (dict(M=0), _lib.TP_ERR_SHAPE),            # empty input is rejected, not launched
+    (dict(f=-8), _lib.TP_ERR_SHAPE),
+    (dict(h=12), _lib.TP_ERR_SHAPE),           # bf16 rows must be 16-byte multiples
+    (dict(i=7), _lib.TP_ERR_DTYPE),
+    (dict(o=2), _lib.TP_ERR_DTYPE),
+    (dict(A=FAKE_ODD), _lib.TP_ERR_ALIGN),
+    (dict(ws=None), _lib.TP_ERR_WORKSPACE),
+    (dict(wsb=16), _lib.TP_ERR_WORKSPACE),
+])
+def test_mlp_shard_rejects(kw, status):
+    assert mlp(**kw) == status
+
+
+def test_mlp_workspace_size():
+    L = tts.lib()
+    assert L.tp_mlp_shard_workspace(100, 64, _lib.TP_BF16) == 12800
+    assert L.tp_mlp_shard_workspace(100, 64, _lib.TP_F32) == 25600
+    assert L.tp_mlp_shard_workspace(0, 64, _lib.TP_F32) == 0
+
+
+def attn(**kw):
+    a = dict(X=FAKE, Wqkv=FAKE, Wo=FAKE, Z=FAKE, ws=FAKE, wsb=BIG, b=2, s=64, h=512, Hl=4, d=128,
+             causal=1, o=_lib.TP_F32)
+    a.update(kw)
+    return tts.lib().tp_attn_shard(a["X"], a["Wqkv"], a["Wo"], a["Z"], a["ws"], a["wsb"], a["b"],
+                                   a["s"], a["h"], a["Hl"], a["d"], a["causal"], a["o"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Wo=None), _lib.TP_ERR_NULL),
+    (dict(d=64), _lib.TP_ERR_SHAPE),            # the kernel's head tile is 128
+    (dict(s=0), _lib.TP_ERR_SHAPE),
+    (dict(h=500), _lib.TP_ERR_SHAPE),
+    (dict(o=3), _lib.TP_ERR_DTYPE),
+    (dict(Z=FAKE_ODD), _lib.TP_ERR_ALIGN),
+    (dict(wsb=1024), _lib.TP_ERR_WORKSPACE),
+])
+def test_attn_shard_rejects(kw, status):
+    assert attn(**kw) == status
+
+
+def test_partial_sum_rejects():
+    L = tts.lib()
+    assert L.tp_partial_sum(None, 0, FAKE, 0, 2, 4, 8, None, None, 0, None) == _lib.TP_ERR_NULL
+    assert L.tp_partial_sum(FAKE, 0, FAKE, 0, 0, 4, 8, None, None, 0, None) == _lib.TP_ERR_SHAPE
+    assert L.tp_partial_sum(FAKE, 0, FAKE, 0, 2, 4, 6, None, None, 0, None) == _lib.TP_ERR_SHAPE
+    assert L.tp_partial_sum(FAKE, 0, FAKE, 9, 2, 4, 8, None, None, 0, None) == _lib.TP_ERR_DTYPE
+    assert L.tp_partial_sum(FAKE, 0, FAKE, 0, 2, 4, 8, FAKE_ODD, None, 0, None) == _lib.TP_ERR_ALIGN
+
+
+def block(**kw):
+    P = kw.pop("P", 2)
+    arr = (ctypes.c_void_p * P)(*([FAKE.value] * P))
+    a = dict(x=FAKE, out=FAKE, x1=None, eps=1e-5, W=arr, ws=FAKE, wsb=BIG, b=1, s=64, h=512,
+             H=4, d=128, F=1024)
+    a.update(kw)
+    return tts.lib().tp_block_shard(a["x"], a["out"], _lib.TP_F32, a["x1"], None, None, None,
+                                    None, a["eps"], a["W"], a["W"], a["W"], a["W"], P, a["ws"],
+                                    a["wsb"], a["b"], a["s"], a["h"], a["H"], a["d"], a["F"], None)
+
+
+def test_block_shard_rejects():
+    assert block(h=640) == _lib.TP_ERR_SHAPE          # h != H*d
+    assert block(P=3) == _lib.TP_ERR_SHAPE             # H=4 does not divide by 3
+    assert block(F=1000) == _lib.TP_ERR_SHAPE
+    assert block(eps=0.0) == _lib.TP_ERR_SHAPE
+    arr = (ctypes.c_void_p * 2)(FAKE.value, None)
+    assert block(W=arr) == _lib.TP_ERR_NULL
+    assert block(wsb=100) == _lib.TP_ERR_WORKSPACE
+
+
+def test_block_workspace_grows_with_ranks():
+    L = tts.lib()
+    w2 = L.tp_block_shard_workspace(1, 64, 512, 4, 128, 1024, 2)
+    w4 = L.tp_block_shard_workspace(1, 64, 512, 4, 128, 1024, 4)
+    assert w4 > w2 > 0
+    assert L.tp_block_shard_workspace(1, 64, 512, 4, 128, 1024, 3) == 0
+
+
+def test_linear_and_layernorm_reject():
+    L = tts.lib()
+    assert L.tp_linear(FAKE, 8, FAKE, 8, None, FAKE, 8, 4, 8, 16, 1, 0, 0, None) == _lib.TP_ERR_SHAPE
+    assert L.tp_linear(FAKE, 16, FAKE, 8, None, FAKE, 8, 4, 8, 16, 1, 0, 5, None) == _lib.TP_ERR_DTYPE
+    assert L.tp_layernorm(FAKE, 1, FAKE, None, None, 1e-5, 4, 20, None) == _lib.TP_ERR_SHAPE
+    assert L.tp_layernorm(FAKE, 1, FAKE, None, None, 1e-5, 4, 1 << 20, None) == _lib.TP_ERR_SHAPE
+    assert L.tp_attention_core(FAKE, 100, FAKE, 1, 8, 1, 128, 1, None) == _lib.TP_ERR_SHAPE
+
+
+def test_python_binding_raises_valueerror_on_shape():
+    import torch
+    with pytest.raises(ValueError):
+        tts._check(_lib.TP_ERR_SHAPE, "x")
+    with pytest.raises(tts.TpError):
+        tts._check(_lib.TP_ERR_LAUNCH, "x")
+    with pytest.raises(ValueError):
+        tts._dev(torch.zeros(2), "cpu tensor")

@@ -1,0 +1,269 @@
+"""GPU parity: every step of the path through the C ABI against the fp64
+oracle, on seeded inputs that span several tiles and ragged tails.
+
+Sizes here finish in seconds on the oracle; the full workload shapes are in
+test_gpu_fullsize.py.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import transformer_tensor_shard_amd as tts
+from _tol import assert_bf16, assert_f32, errors
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def banner(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def gen(shape, sigma, seed, sub, dtype=torch.bfloat16):
+    return synth.normal(shape, sigma, seed, sub, dtype)
+
+
+# ------------------------------------------------------------------ GEMM
+@pytest.mark.parametrize("M,N,K", [(256, 256, 64), (512, 768, 320), (600, 520, 328),
+                                   (1, 8, 8), (37, 264, 1032), (1300, 40, 96)])
+def test_linear_bf16_f32out(M, N, K):
+    banner(f"linear bf16 M={M} N={N} K={K}")
+    X = gen((M, K), 1.0, 11, "x")
+    W = gen((K, N), 1 / math.sqrt(K), 11, "A")
+    C = tts.tp_linear(X.to(DEV), W.to(DEV), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = oracle.matmul(X, W)
+    # identical bf16 inputs on both sides: only f32 accumulation differs
+    e = assert_f32(C, ref, bar=1e-4)
+    assert e["fro"] < 1e-5, e
+
+
+@pytest.mark.parametrize("M,N,K", [(512, 512, 256), (333, 264, 200)])
+def test_linear_bf16_bias_gelu_bf16out(M, N, K):
+    banner(f"linear bf16+bias+gelu M={M} N={N} K={K}")
+    X = gen((M, K), 1.0, 12, "x")
+    W = gen((K, N), 1 / math.sqrt(K), 12, "A")
+    bias = gen((N,), 0.5, 12, "bias", torch.float32)
+    C = tts.tp_linear(X.to(DEV), W.to(DEV), bias.to(DEV), gelu=True, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    ref = oracle.gelu(oracle.matmul(X, W, bias))
+    e = assert_bf16(C, ref, stored_bf16=True)
+    assert e["fro"] < 5e-3, e   # one bf16 rounding of the output
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 64, 64), (100, 36, 52)])
+def test_linear_f32(M, N, K):
+    banner(f"linear f32 M={M} N={N} K={K}")
+    X = gen((M, K), 1.0, 13, "x", torch.float32)
+    W = gen((K, N), 1 / math.sqrt(K), 13, "A", torch.float32)
+    bias = gen((N,), 0.5, 13, "bias", torch.float32)
+    C = tts.tp_linear(X.to(DEV), W.to(DEV), bias.to(DEV), gelu=True)
+    torch.cuda.synchronize()
+    assert_f32(C, oracle.gelu(oracle.matmul(X, W, bias)))
+
+
+def test_linear_deterministic():
+    X = gen((700, 512), 1.0, 14, "x").to(DEV)
+    W = gen((512, 640), 1 / math.sqrt(512), 14, "A").to(DEV)
+    a = tts.tp_linear(X, W)
+    b = tts.tp_linear(X, W)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_linear_nan_propagates():
+    X = gen((300, 128), 1.0, 15, "x")
+    X[7, 3] = float("nan")
+    W = gen((128, 256), 1 / math.sqrt(128), 15, "A")
+    C = tts.tp_linear(X.to(DEV), W.to(DEV)).cpu()
+    assert torch.isnan(C[7]).all()
+    C[7] = 0
+    assert torch.isfinite(C).all()
+
+
+# ------------------------------------------------------------------ MLP
+def test_mlp_f32_tp2_sums_to_unsharded():
+    """fp32 MLP TP shard, tp=2 emulated sequentially: X [2,16,64], A [64,256],
+    B [256,64], zero bias; Z = Z_0 + Z_1 against the unsharded MLP."""
+    banner("mlp f32 tp=2")
+    seed, P, h, F = 1000, 2, 64, 256
+    X = gen((32, h), 1.0, seed, "x", torch.float32)
+    A = gen((h, F), 1 / math.sqrt(h), seed, "A", torch.float32)
+    B = gen((F, h), 1 / math.sqrt(F), seed, "B", torch.float32)
+    f = F // P
+    Xd = X.to(DEV)
+    parts = torch.empty(P, 32, h, dtype=torch.float32, device=DEV)
+    for r in range(P):
+        tts.tp_mlp_shard(Xd, A[:, r * f:(r + 1) * f].contiguous().to(DEV),
+                         B[r * f:(r + 1) * f].contiguous().to(DEV), out=parts[r])
+    Z = tts.tp_partial_sum(parts)
+    torch.cuda.synchronize()
+    assert_f32(Z, oracle.mlp_shard(X, A, B))
+    for r in range(P):
+        assert_f32(parts[r], oracle.mlp_shard(X, A[:, r * f:(r + 1) * f], B[r * f:(r + 1) * f]))
+
+
+@pytest.mark.parametrize("M,h,f,bias", [(512, 256, 512, False), (300, 264, 136, True),
+                                        (17, 512, 256, False)])
+def test_mlp_bf16_small(M, h, f, bias):
+    banner(f"mlp bf16 M={M} h={h} f={f} bias={bias}")
+    X = gen((M, h), 1.0, 21, "x")
+    A = gen((h, f), 1 / math.sqrt(h), 21, "A")
+    B = gen((f, h), 1 / math.sqrt(4 * h), 21, "B")
+    a = gen((f,), 0.1, 21, "bias", torch.float32) if bias else None
+    Z = tts.tp_mlp_shard(X.to(DEV), A.to(DEV), B.to(DEV), a.to(DEV) if bias else None)
+    Zb = tts.tp_mlp_shard(X.to(DEV), A.to(DEV), B.to(DEV), a.to(DEV) if bias else None,
+                          out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    ref = oracle.mlp_shard(X, A, B, a)
+    assert_bf16(Z, ref)
+    assert_bf16(Zb, ref, stored_bf16=True)
+
+
+# ------------------------------------------------------------------ partial sum
+@pytest.mark.parametrize("P,M,h", [(8, 33, 520), (1, 5, 4), (3, 1000, 64)])
+def test_partial_sum_f32(P, M, h):
+    banner(f"partial sum f32 P={P} M={M} h={h}")
+    parts = gen((P, M, h), 1.0, 31, "partials", torch.float32)
+    bias = gen((h,), 1.0, 31, "bias", torch.float32)
+    res = gen((M, h), 1.0, 31, "residual", torch.float32)
+    Z = tts.tp_partial_sum(parts.to(DEV), bias.to(DEV), res.to(DEV))
+    Z0 = tts.tp_partial_sum(parts.to(DEV))
+    torch.cuda.synchronize()
+    assert_f32(Z, oracle.partial_sum(parts, bias, res), bar=1e-5)
+    assert_f32(Z0, oracle.partial_sum(parts), bar=1e-5)
+    # ascending-rank f32 order: bit-identical to the same-order host sum
+    host = parts[0].clone()
+    for r in range(1, P):
+        host += parts[r]
+    assert torch.equal(Z0.cpu(), host)
+
+
+def test_partial_sum_mixed_dtypes_and_alias():
+    banner("partial sum bf16 parts / bf16 residual / aliasing")
+    P, M, h = 4, 64, 256
+    parts = gen((P, M, h), 1.0, 32, "partials")
+    res = gen((M, h), 1.0, 32, "residual")
+    Z = tts.tp_partial_sum(parts.to(DEV), None, res.to(DEV), out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert_bf16(Z, oracle.partial_sum(parts, None, res), fro=4e-3, stored_bf16=True)
+    r32 = gen((M, h), 1.0, 32, "residual", torch.float32).to(DEV)
+    p32 = gen((P, M, h), 1.0, 33, "partials", torch.float32)
+    ref = oracle.partial_sum(p32, None, r32.cpu())
+    tts.tp_partial_sum(p32.to(DEV), None, r32, out=r32)   # Z aliases the residual
+    torch.cuda.synchronize()
+    assert_f32(r32, ref, bar=1e-5)
+
+
+# ------------------------------------------------------------------ LayerNorm
+@pytest.mark.parametrize("M,h,dtype,affine", [(64, 4096, torch.bfloat16, False),
+                                              (37, 520, torch.float32, True),
+                                              (3, 12288, torch.float32, False)])
+def test_layernorm(M, h, dtype, affine):
+    banner(f"layernorm M={M} h={h} {dtype} affine={affine}")
+    x = gen((M, h), 2.0, 41, "x", dtype) + 0.5
+    g = gen((h,), 1.0, 41, "gamma", torch.float32) if affine else None
+    b = gen((h,), 1.0, 41, "beta", torch.float32) if affine else None
+    y = tts.tp_layernorm(x.to(DEV), g.to(DEV) if affine else None, b.to(DEV) if affine else None)
+    torch.cuda.synchronize()
+    e = assert_bf16(y, oracle.layernorm(x, g, b, 1e-5), stored_bf16=True)
+    assert e["fro"] < 4e-3, e   # one bf16 rounding of the output
+
+
+# ------------------------------------------------------------------ attention
+def _qkv_weights(h, Hl, d, seed):
+    Wqkv = gen((h, 3 * Hl * d), 1 / math.sqrt(h), seed, "Wqkv")
+    Wo = gen((Hl * d, h), 1 / math.sqrt(h), seed, "Wo")
+    return Wqkv, Wo
+
+
+@pytest.mark.parametrize("b,s,Hl,causal", [(2, 256, 2, True), (1, 200, 3, True),
+                                           (2, 130, 1, False), (3, 1, 2, True),
+                                           (1, 64, 1, True)])
+def test_attention_core(b, s, Hl, causal):
+    """The attention step alone: with W_qkv = I and W_o = [I | 0] the oracle's
+    shard returns O itself."""
+    banner(f"attention core b={b} s={s} Hl={Hl} causal={causal}")
+    d = 128
+    n3 = 3 * Hl * d
+    qkv = gen((b * s, n3), 1.0, 51, "x")
+    O = tts.tp_attention_core(qkv.to(DEV), b, s, Hl, d, causal)
+    torch.cuda.synchronize()
+    eye = np.eye(n3)
+    ref = oracle.attn_shard_rows(qkv, b, s, eye, np.ascontiguousarray(eye[:Hl * d]), Hl, d,
+                                 causal)[:, :Hl * d]
+    assert_bf16(O, ref, stored_bf16=True)
+
+
+def test_attention_single_token_is_value():
+    banner("attention s=1")
+    b, s, Hl, d = 5, 1, 2, 128
+    qkv = gen((b * s, 3 * Hl * d), 1.0, 52, "x")
+    O = tts.tp_attention_core(qkv.to(DEV), b, s, Hl, d, True).cpu()
+    assert torch.equal(O, qkv[:, 2 * Hl * d:])
+
+
+@pytest.mark.parametrize("b,s,h,Hl", [(2, 192, 512, 2), (1, 300, 264, 1)])
+def test_attn_shard_small(b, s, h, Hl):
+    banner(f"attn shard b={b} s={s} h={h} Hl={Hl}")
+    d = 128
+    X = gen((b * s, h), 1.0, 53, "x")
+    Wqkv, Wo = _qkv_weights(h, Hl, d, 53)
+    Z = tts.tp_attn_shard(X.to(DEV), Wqkv.to(DEV), Wo.to(DEV), b, s, Hl, d, True)
+    torch.cuda.synchronize()
+    assert_bf16(Z, oracle.attn_shard_rows(X, b, s, Wqkv, Wo, Hl, d, True))
+
+
+def test_attn_heads_sum_to_full_mha():
+    """§3.2: rank partials of head-sharded attention, summed on the GPU, match
+    the oracle's unsharded multi-head attention."""
+    banner("attn tp=2 sum vs full MHA")
+    b, s, H, d, P = 2, 160, 4, 128, 2
+    h = H * d
+    Hl = H // P
+    X = gen((b * s, h), 1.0, 54, "x")
+    Wq = gen((h, H * d), 1 / math.sqrt(h), 54, "Wqkv")
+    Wk = gen((h, H * d), 1 / math.sqrt(h), 55, "Wqkv")
+    Wv = gen((h, H * d), 1 / math.sqrt(h), 56, "Wqkv")
+    Wo = gen((H * d, h), 1 / math.sqrt(h), 54, "Wo")
+    parts = torch.empty(P, b * s, h, device=DEV)
+    for r in range(P):
+        sl = slice(r * Hl * d, (r + 1) * Hl * d)
+        Wqkv_r = torch.cat([Wq[:, sl], Wk[:, sl], Wv[:, sl]], dim=1).contiguous()
+        tts.tp_attn_shard(X.to(DEV), Wqkv_r.to(DEV), Wo[sl].contiguous().to(DEV), b, s, Hl, d,
+                          True, out=parts[r])
+    Z = tts.tp_partial_sum(parts)
+    torch.cuda.synchronize()
+    full = oracle.attn_shard_rows(X, b, s, torch.cat([Wq, Wk, Wv], 1), Wo, H, d, True)
+    assert_bf16(Z, full)
+
+
+# ------------------------------------------------------------------ block
+def test_block_small_all_ranks():
+    banner("block P=2 small")
+    P, b, s, H, d, F = 2, 2, 160, 4, 128, 1024
+    h = H * d
+    seed = 61
+    x = gen((b * s, h), 1.0, seed, "x")
+    Wqkv = [gen((h, 3 * (H // P) * d), 1 / math.sqrt(h), synth.rank_seed(seed, r), "Wqkv")
+            for r in range(P)]
+    Wo = [gen(((H // P) * d, h), 1 / math.sqrt(h), synth.rank_seed(seed, r), "Wo") for r in range(P)]
+    A = [gen((h, F // P), 1 / math.sqrt(h), synth.rank_seed(seed, r), "A") for r in range(P)]
+    B = [gen((F // P, h), 1 / math.sqrt(F), synth.rank_seed(seed, r), "B") for r in range(P)]
+    g1 = gen((h,), 1.0, seed, "gamma", torch.float32)
+    b1 = gen((h,), 1.0, seed, "beta", torch.float32)
+    x1 = torch.empty(b * s, h, device=DEV)
+    dev = lambda ts: [t.to(DEV) for t in ts]
+    out = tts.tp_block_shard(x.to(DEV), dev(Wqkv), dev(Wo), dev(A), dev(B), b, s, H, d,
+                             ln1=(g1.to(DEV), b1.to(DEV)), x1=x1)
+    torch.cuda.synchronize()
+    x1_ref, out_ref = oracle.block_rows(x, b, s, Wqkv, Wo, A, B, H, d, ln1=(g1, b1))
+    assert_bf16(x1, x1_ref)
+    assert_bf16(out, out_ref)
+    # the residual dominates out: check the block's own contributions too
+    assert_bf16(x1.cpu().double() - oracle.f64(x), x1_ref - oracle.f64(x))
+    assert_bf16(out.cpu().double() - x1.cpu().double(), out_ref - x1_ref)

@@ -49,15 +49,16 @@ def test_matmul_identity_gives_input():
     assert np.array_equal(oracle.matmul(X, np.eye(8)), X)
 
 
-def test_column_split_concat_is_full_product_bitwise():
-    """§1.2: Y_r = X·W_r on column blocks; concatenation equals X·W exactly."""
+def test_column_split_concat_is_full_product():
+    """§1.2: Y_r = X·W_r on column blocks; concatenation equals X·W (up to the
+    library's summation order)."""
     X = RNG.standard_normal((10, 24))
     W = RNG.standard_normal((24, 36))
     full = oracle.matmul(X, W)
     for P in (2, 3, 4):
         c = 36 // P
         parts = [oracle.matmul(X, np.ascontiguousarray(W[:, r * c:(r + 1) * c])) for r in range(P)]
-        assert np.array_equal(np.concatenate(parts, axis=1), full)
+        assert rel(np.concatenate(parts, axis=1), full) < 1e-15
 
 
 def test_row_split_sum_is_full_product():
@@ -243,7 +244,7 @@ def test_attention_sampled_rows_equal_full_rows():
     Wqkv = _rank_qkv(Wq, Wk, Wv, 0, H, d)
     full = oracle.attn_shard_rows(X, b, s, Wqkv, Wo, H, d, True)
     rows = np.array([26, 0, 9, 13, 17, 4])
-    assert np.array_equal(oracle.attn_shard_rows(X, b, s, Wqkv, Wo, H, d, True, rows), full[rows])
+    assert rel(oracle.attn_shard_rows(X, b, s, Wqkv, Wo, H, d, True, rows), full[rows]) < 1e-14
 
 
 def test_attention_single_token_returns_value_projection():

@@ -1,0 +1,208 @@
+"""transformer_tensor_shard_amd -- one tensor-parallel rank's share of a
+Megatron-style Transformer block on one MI355X (gfx950).
+
+Python face of libtp.so.  Each function has the name of the C entry point it
+wraps (include/tp.h) and only marshals arguments: output and workspace tensors
+are allocated with torch when the caller does not pass them, pointers and
+dtype codes are handed to the library, and a non-zero status becomes an
+exception (ValueError for unsupported shapes, the pages' convention for a
+size that does not divide; TpError otherwise).
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Sequence
+
+import torch
+
+from . import _lib
+from ._lib import TP_BF16, TP_EPI_GELU, TP_EPI_NONE, TP_F32
+
+__all__ = [
+    "TpError", "tp_abi_version", "tp_mlp_shard", "tp_mlp_shard_workspace", "tp_attn_shard",
+    "tp_attn_shard_workspace", "tp_partial_sum", "tp_block_shard", "tp_block_shard_workspace",
+    "tp_linear", "tp_attention_core", "tp_layernorm", "lib",
+]
+
+
+class TpError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _lib.load().tp_status_string(status).decode()
+        super().__init__(f"{where}: status {status} ({msg})")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libtp.so (raw C ABI)."""
+    return _lib.load()
+
+
+def _check(status: int, where: str) -> None:
+    if status == _lib.TP_OK:
+        return
+    if status == _lib.TP_ERR_SHAPE:
+        raise ValueError(f"{where}: {_lib.load().tp_status_string(status).decode()}")
+    raise TpError(status, where)
+
+
+def _code(dtype: torch.dtype) -> int:
+    if dtype == torch.float32:
+        return TP_F32
+    if dtype == torch.bfloat16:
+        return TP_BF16
+    raise TypeError(f"unsupported dtype {dtype}: float32 or bfloat16")
+
+
+def _dev(t: Optional[torch.Tensor], name: str):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ws(ws: Optional[torch.Tensor], nbytes: int, device) -> torch.Tensor:
+    if ws is None:
+        ws = torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+    return ws
+
+
+def _bytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
+
+
+def tp_abi_version() -> int:
+    return int(_lib.load().tp_abi_version())
+
+
+# ------------------------------------------------------------------ MLP
+def tp_mlp_shard_workspace(M: int, f: int, in_dtype=torch.bfloat16) -> int:
+    return int(_lib.load().tp_mlp_shard_workspace(M, f, _code(in_dtype)))
+
+
+def tp_mlp_shard(X, A_i, B_i, a_i=None, *, out=None, out_dtype=torch.float32, ws=None,
+                 stream=None):
+    """Z_i = GeLU(X·A_i + a_i)·B_i for one rank; returns Z_i [M,h]."""
+    M, h = X.shape
+    f = A_i.shape[1]
+    if out is None:
+        out = torch.empty(M, h, dtype=out_dtype, device=X.device)
+    ws = _ws(ws, tp_mlp_shard_workspace(M, f, X.dtype), X.device)
+    st = _lib.load().tp_mlp_shard(_dev(X, "X"), _dev(A_i, "A_i"), _dev(a_i, "a_i"),
+                                  _dev(B_i, "B_i"), _dev(out, "out"), _dev(ws, "ws"), _bytes(ws),
+                                  M, h, f, _code(X.dtype), _code(out.dtype), _stream(stream))
+    _check(st, "tp_mlp_shard")
+    return out
+
+
+# ------------------------------------------------------------------ attention
+def tp_attn_shard_workspace(b: int, s: int, H_l: int, d: int = 128) -> int:
+    return int(_lib.load().tp_attn_shard_workspace(b, s, H_l, d))
+
+
+def tp_attn_shard(X, W_qkv_i, W_o_i, b: int, s: int, H_l: int, d: int = 128, causal=True, *,
+                  out=None, out_dtype=torch.float32, ws=None, stream=None):
+    """Z_i = MHA over this rank's H_l heads, times its row block of W_o."""
+    h = X.shape[1]
+    if out is None:
+        out = torch.empty(b * s, h, dtype=out_dtype, device=X.device)
+    ws = _ws(ws, tp_attn_shard_workspace(b, s, H_l, d), X.device)
+    st = _lib.load().tp_attn_shard(_dev(X, "X"), _dev(W_qkv_i, "W_qkv_i"), _dev(W_o_i, "W_o_i"),
+                                   _dev(out, "out"), _dev(ws, "ws"), _bytes(ws), b, s, h, H_l, d,
+                                   int(bool(causal)), _code(out.dtype), _stream(stream))
+    _check(st, "tp_attn_shard")
+    return out
+
+
+# ------------------------------------------------------------------ partial sum
+def tp_partial_sum(partials, bias=None, residual=None, *, out=None, out_dtype=torch.float32,
+                   stream=None):
+    """Z = sum_r partials[r] (+bias) (+residual); partials is [P, M, h]."""
+    P, M, h = partials.shape
+    if out is None:
+        out = torch.empty(M, h, dtype=out_dtype, device=partials.device)
+    res_code = _code(residual.dtype) if residual is not None else TP_F32
+    st = _lib.load().tp_partial_sum(_dev(out, "out"), _code(out.dtype), _dev(partials, "partials"),
+                                    _code(partials.dtype), P, M, h, _dev(bias, "bias"),
+                                    _dev(residual, "residual"), res_code, _stream(stream))
+    _check(st, "tp_partial_sum")
+    return out
+
+
+# ------------------------------------------------------------------ block
+def tp_block_shard_workspace(b, s, h, H, d, F, P) -> int:
+    return int(_lib.load().tp_block_shard_workspace(b, s, h, H, d, F, P))
+
+
+def _ptr_array(ts: Sequence[torch.Tensor], name: str):
+    arr = (ctypes.c_void_p * len(ts))()
+    for i, t in enumerate(ts):
+        arr[i] = _dev(t, f"{name}[{i}]").value
+    return arr
+
+
+def tp_block_shard(x, W_qkv: Sequence, W_o: Sequence, A: Sequence, B: Sequence, b: int, s: int,
+                   H: int, d: int = 128, *, ln1=(None, None), ln2=(None, None), eps=1e-5,
+                   out=None, out_dtype=torch.float32, x1=None, ws=None, stream=None):
+    """Pre-LN block with every rank's share run in turn on this GPU.
+
+    Returns out [b·s, h]; pass an f32 ``x1`` tensor to also receive the
+    residual stream after attention."""
+    P = len(W_qkv)
+    h = x.shape[1]
+    F = A[0].shape[1] * P
+    if out is None:
+        out = torch.empty(b * s, h, dtype=out_dtype, device=x.device)
+    ws = _ws(ws, tp_block_shard_workspace(b, s, h, H, d, F, P), x.device)
+    st = _lib.load().tp_block_shard(
+        _dev(x, "x"), _dev(out, "out"), _code(out.dtype), _dev(x1, "x1"),
+        _dev(ln1[0], "ln1_g"), _dev(ln1[1], "ln1_b"), _dev(ln2[0], "ln2_g"), _dev(ln2[1], "ln2_b"),
+        float(eps), _ptr_array(W_qkv, "W_qkv"), _ptr_array(W_o, "W_o"), _ptr_array(A, "A"),
+        _ptr_array(B, "B"), P, _dev(ws, "ws"), _bytes(ws), b, s, h, H, d, F, _stream(stream))
+    _check(st, "tp_block_shard")
+    return out
+
+
+# ------------------------------------------------------------------ components
+def tp_linear(X, W, bias=None, *, gelu=False, out=None, out_dtype=torch.float32, stream=None):
+    """C = epi(X·W + bias); X [M,K], W [K,N]."""
+    M, K = X.shape
+    N = W.shape[1]
+    if out is None:
+        out = torch.empty(M, N, dtype=out_dtype, device=X.device)
+    st = _lib.load().tp_linear(_dev(X, "X"), K, _dev(W, "W"), N, _dev(bias, "bias"),
+                               _dev(out, "out"), N, M, N, K, _code(X.dtype), _code(out.dtype),
+                               TP_EPI_GELU if gelu else TP_EPI_NONE, _stream(stream))
+    _check(st, "tp_linear")
+    return out
+
+
+def tp_attention_core(qkv, b: int, s: int, H_l: int, d: int = 128, causal=True, *, out=None,
+                      stream=None):
+    """O = softmax(QK^T/sqrt d)·V per (sequence, head); qkv [b·s, ld] bf16."""
+    if out is None:
+        out = torch.empty(b * s, H_l * d, dtype=torch.bfloat16, device=qkv.device)
+    st = _lib.load().tp_attention_core(_dev(qkv, "qkv"), qkv.shape[1], _dev(out, "out"), b, s,
+                                       H_l, d, int(bool(causal)), _stream(stream))
+    _check(st, "tp_attention_core")
+    return out
+
+
+def tp_layernorm(x, gamma=None, beta=None, eps=1e-5, *, out=None, stream=None):
+    """bf16 LayerNorm of each row of x [M,h] (x in f32 or bf16)."""
+    M, h = x.shape
+    if out is None:
+        out = torch.empty(M, h, dtype=torch.bfloat16, device=x.device)
+    st = _lib.load().tp_layernorm(_dev(x, "x"), _code(x.dtype), _dev(out, "out"),
+                                  _dev(gamma, "gamma"), _dev(beta, "beta"), float(eps), M, h,
+                                  _stream(stream))
+    _check(st, "tp_layernorm")
+    return out

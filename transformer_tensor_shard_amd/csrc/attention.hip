@@ -1,0 +1,257 @@
+// Head-sharded attention core for gfx950: for every (sequence, local head)
+// O = softmax(Q·K^T / sqrt(d) + mask)·V with d = 128, bf16 in, bf16 out,
+// f32 softmax statistics and accumulators ("图解Transformer并行计算" §3.1;
+// each rank runs whole heads locally, §3.2).
+//
+// Design (flash-style, scores never reach HBM):
+//  * one workgroup = 4 waves = 128 queries of one (sequence, head); grid order
+//    puts the longest causal rows first so the tail of the launch is short;
+//  * keys/values stream through LDS in 64-key tiles, double-buffered, the next
+//    tile's global loads in flight during this tile's MFMAs;
+//  * each wave owns 32 queries and computes S^T = K·Q^T with MFMA 32x32x16
+//    (A operand = K rows from LDS, B operand = Q held in registers), so every
+//    lane ends up holding the scores of ONE query: the online-softmax max and
+//    sum need only the lane's own values plus one swap with lane ^ 32;
+//  * the probabilities are rounded to bf16 in registers and used directly as
+//    the B operand of O^T += V^T·P^T (the row sum is taken over the same
+//    rounded values, so the weights applied to V sum exactly to one); the V^T operand comes from the
+//    row-major V tile via the gfx950 LDS transpose read (ds_read_b64_tr_b16);
+//  * exp uses exp2 with log2(e)/sqrt(d) folded into the score scale;
+//  * LDS tiles are XOR-swizzled in 16-byte units (64 banks, conflict-free for
+//    the 16-byte K reads and the transpose V reads);
+//  * the output block is staged through LDS and written with 16-byte stores.
+#include "tp_kernels.h"
+
+#include <math.h>
+
+namespace tpk {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+constexpr int D = 128, BQ = 128, BKV = 64;
+constexpr int TILE_BYTES = BKV * D * 2;      // 16 KiB (64 rows x 256 B)
+constexpr int STAGE_BYTES = 2 * TILE_BYTES;  // K tile + V tile
+constexpr unsigned OOB = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                             0x7ffffff0, 0x00020000);
+}
+
+__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
+    const __bf16* __restrict__ qkv, int64_t ld, __bf16* __restrict__ O, int64_t ldo,
+    int s, int Hl, int nqb, int n_bh, int causal, float scale_log2)
+{
+    __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE_BYTES];
+
+    const int id = blockIdx.x;
+    const int qb = nqb - 1 - id / n_bh;          // heaviest query blocks first
+    const int bh = id % n_bh;
+    const int beta = bh / Hl, head = bh % Hl;
+    const int q0 = qb * BQ;
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int l32 = lane & 31, hi = lane >> 5;
+
+    const __bf16* seq = qkv + (int64_t)beta * s * ld;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(seq);
+    const int qcol = head * D, kcol = Hl * D + head * D, vcol = 2 * Hl * D + head * D;
+
+    // ---- Q operand in registers: lane = query (q0 + 32w + l32), 8 k-steps of
+    // 16 head dims, lane half `hi` holds dims 8*hi..8*hi+7 of each step.
+    const int qrow = q0 + 32 * w + l32;
+    bf16x8 qf[8];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+        const unsigned off = (qrow < s) ? (unsigned)((int64_t)qrow * ld + qcol + kk * 16 + 8 * hi) * 2u : OOB;
+        u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+        qf[kk] = __builtin_bit_cast(bf16x8, v);
+    }
+
+    // ---- K/V tile copy assignment: 64 rows x 16 units; thread owns unit
+    // (tid & 15) of rows (tid >> 4) + 16 i.
+    const int c_unit = tid & 15, c_row0 = tid >> 4;
+    unsigned k_lds[4], v_lds[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = c_row0 + 16 * i;
+        k_lds[i] = r * 256 + ((c_unit ^ (r & 15)) << 4);
+        v_lds[i] = TILE_BYTES + r * 256 + ((c_unit ^ ((r & 3) << 2)) << 4);
+    }
+    u32x4 rk[4], rv[4];
+    auto load_kv = [&](int kv0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = kv0 + c_row0 + 16 * i;
+            const bool ok = r < s;
+            const unsigned base = (unsigned)((int64_t)r * ld + c_unit * 8) * 2u;
+            rk[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, ok ? base + kcol * 2u : OOB, 0, 0);
+            rv[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, ok ? base + vcol * 2u : OOB, 0, 0);
+        }
+    };
+    auto store_kv = [&](int stage) {
+        char* b = lds + stage * STAGE_BYTES;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            *(u32x4*)(b + k_lds[i]) = rk[i];
+            *(u32x4*)(b + v_lds[i]) = rv[i];
+        }
+    };
+
+    // K operand reads (A of S^T = K·Q^T): lane reads key row (32t + l32),
+    // 16-byte unit (2kk + hi), swizzled by (row & 15) = (lane & 15).
+    unsigned k_rd[8];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) k_rd[kk] = l32 * 256 + (((2 * kk + hi) ^ (lane & 15)) << 4);
+    // V^T operand via transpose reads: 16-lane group G reads 4 key rows x 16
+    // dims; lane gi addresses row (gi >> 2), dims 4*(gi & 3)..+3.
+    const int G = lane >> 4, gi = lane & 15;
+    unsigned v_rd[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+        const int row = 4 * (G >> 1) + (gi >> 2);
+        const int col = 32 * dt + 16 * (G & 1) + 4 * (gi & 3);
+        v_rd[dt] = TILE_BYTES + row * 256 + (((col >> 3) ^ ((row & 3) << 2)) << 4) + (col & 7) * 2;
+    }
+
+    f32x16 oacc[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.0f;
+    float m_run = -INFINITY, l_run = 0.0f;
+
+    const int kv_end = causal ? min(s, q0 + BQ) : s;
+    const int n_kv = (kv_end + BKV - 1) / BKV;
+    const int qw_lo = q0 + 32 * w, qw_hi = qw_lo + 31;   // this wave's queries
+    const int my_q = qw_lo + l32;
+
+    load_kv(0);
+    store_kv(0);
+    __syncthreads();
+
+    for (int kb = 0; kb < n_kv; ++kb) {
+        const int cur = kb & 1;
+        const bool has_next = kb + 1 < n_kv;
+        const int kv0 = kb * BKV;
+        if (has_next) load_kv(kv0 + BKV);
+        const char* base = lds + cur * STAGE_BYTES;
+        const bool active = !causal || kv0 <= qw_hi;
+        if (active) {
+            f32x16 sacc[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sacc[t][r] = 0.0f;
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) {
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const bf16x8 kf = *(const bf16x8*)(base + k_rd[kk] + t * 32 * 256);
+                    sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sacc[t], 0, 0, 0);
+                }
+            }
+            // scale; mask where the tile reaches past the diagonal or the end
+            const bool need_mask = (causal && kv0 + BKV - 1 > qw_lo) || (kv0 + BKV > s);
+            float mloc = -INFINITY;
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float v = sacc[t][r] * scale_log2;
+                    if (need_mask) {
+                        const int key = kv0 + 32 * t + 8 * (r >> 2) + 4 * hi + (r & 3);
+                        if (key >= s || (causal && key > my_q)) v = -INFINITY;
+                    }
+                    sacc[t][r] = v;
+                    mloc = fmaxf(mloc, v);
+                }
+            mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+            const float m_new = fmaxf(m_run, mloc);
+            const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+            const float alpha = exp2f(m_run - m_use);
+            m_run = m_new;
+            float lsum = 0.0f;
+            bf16x8 pk[2][2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    // the normaliser sums the rounded weights the MFMA applies
+                    const __bf16 pb = (__bf16)exp2f(sacc[t][r] - m_use);
+                    lsum += (float)pb;
+                    pk[t][r >> 3][r & 7] = pb;
+                }
+            l_run = l_run * alpha + lsum;
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+            // O^T += V^T · P^T over the 4 k-steps of 16 keys
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    const int koff = (32 * t + 16 * half) * 256;
+#pragma unroll
+                    for (int dt = 0; dt < 4; ++dt) {
+                        const char* p = base + v_rd[dt] + koff;
+                        bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, p));
+                        bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, p + 8 * 256));
+                        const bf16x8 vf = __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+                        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pk[t][half], oacc[dt], 0, 0, 0);
+                    }
+                }
+        }
+        if (has_next) store_kv(cur ^ 1);
+        __syncthreads();
+    }
+
+    // ---- normalise and write: lane holds query l32, dims
+    // 32dt + 8(r>>2) + 4hi + (r&3).  Stage the wave's 32x128 block in LDS.
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    char* stage = lds + w * (32 * 256);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+            bf16x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = (__bf16)(oacc[dt][4 * rq + e] * inv);
+            const int d0 = 32 * dt + 8 * rq + 4 * hi;
+            *(bf16x4*)(stage + l32 * 256 + (((d0 >> 3) ^ (l32 & 15)) << 4) + (d0 & 7) * 2) = v;
+        }
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int idx = i * 64 + lane;
+        const int row = idx >> 4, unit = idx & 15;
+        const int q = qw_lo + row;
+        const u32x4 v = *(const u32x4*)(stage + row * 256 + ((unit ^ (row & 15)) << 4));
+        if (q < s) *(u32x4*)(O + ((int64_t)beta * s + q) * ldo + head * D + unit * 8) = v;
+    }
+}
+
+}  // namespace
+
+hipError_t attention_fwd(const void* qkv, int64_t ld_qkv, void* O,
+                         int64_t b, int64_t s, int64_t H_l, bool causal, hipStream_t stream)
+{
+    const int nqb = (int)((s + BQ - 1) / BQ);
+    const int n_bh = (int)(b * H_l);
+    const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
+    hipLaunchKernelGGL(attn_fwd_kernel, dim3(nqb * n_bh), dim3(256), 0, stream,
+                       (const __bf16*)qkv, ld_qkv, (__bf16*)O, H_l * D, (int)s, (int)H_l,
+                       nqb, n_bh, causal ? 1 : 0, scale_log2);
+    return hipGetLastError();
+}
+
+}  // namespace tpk

@@ -1,0 +1,308 @@
+// extern "C" entry points of libtp.so (declared and documented in tp.h).
+//
+// Every entry point validates all of its arguments before enqueueing any work
+// and returns a tp_status; the kernels themselves live in gemm_bf16.hip,
+// gemm_f32.hip, attention.hip and norm_sum.hip.
+#include "tp.h"
+#include "tp_kernels.h"
+
+#include <stdint.h>
+
+#define TP_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr int64_t kAlign = 256;            // workspace sub-buffer alignment
+constexpr int64_t kHeadDim = 128;          // the attention kernel's head tile
+constexpr int64_t kMaxLnWidth = 16384;     // LayerNorm keeps one row in LDS
+constexpr int64_t kI32 = 0x7fffffffLL;
+
+inline int64_t align_up(int64_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool is_dtype(int t) { return t == TP_F32 || t == TP_BF16; }
+inline int64_t esize(int t) { return t == TP_BF16 ? 2 : 4; }
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+inline tp_status launched(hipError_t e) { return e == hipSuccess ? TP_OK : TP_ERR_LAUNCH; }
+
+// The bf16 GEMM addresses a 256-row tile of an operand with 32-bit byte
+// offsets and uses 32-bit tile counters.
+bool gemm_bf16_fits(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb) {
+    return M <= kI32 && N <= kI32 && K <= kI32 && lda * 2 * 256 < kI32 && ldb * 2 * 64 < kI32 &&
+           ((M + 255) / 256) * ((N + 255) / 256) <= kI32;
+}
+
+tp_status check_linear(const void* X, int64_t ldx, const void* W, int64_t ldw, const void* bias,
+                       const void* C, int64_t ldc, int64_t M, int64_t N, int64_t K, int in,
+                       int out, int epi) {
+    if (!X || !W || !C) return TP_ERR_NULL;
+    if (!is_dtype(in) || !is_dtype(out) || (epi != TP_EPI_NONE && epi != TP_EPI_GELU))
+        return TP_ERR_DTYPE;
+    if (M <= 0 || N <= 0 || K <= 0 || ldx < K || ldw < N || ldc < N) return TP_ERR_SHAPE;
+    if (!aligned16(X) || !aligned16(W) || !aligned16(C) || (bias && !aligned16(bias)))
+        return TP_ERR_ALIGN;
+    if (in == TP_BF16) {
+        if (K % 8 || N % 8 || ldx % 8 || ldw % 8 || !gemm_bf16_fits(M, N, K, ldx, ldw))
+            return TP_ERR_SHAPE;
+    } else if (M > kI32 || N > kI32 || K > kI32) {
+        return TP_ERR_SHAPE;
+    }
+    return TP_OK;
+}
+
+hipError_t run_linear(const void* X, int64_t ldx, const void* W, int64_t ldw, const void* bias,
+                      void* C, int64_t ldc, int64_t M, int64_t N, int64_t K, int in, int out,
+                      bool gelu, hipStream_t st) {
+    if (in == TP_BF16)
+        return tpk::gemm_bf16(X, ldx, W, ldw, (const float*)bias, C, ldc, M, N, K,
+                              out == TP_BF16, gelu, st);
+    return tpk::gemm_f32((const float*)X, ldx, (const float*)W, ldw, (const float*)bias, C, ldc,
+                         M, N, K, out == TP_BF16, gelu, st);
+}
+
+// ---- MLP shard ------------------------------------------------------------
+int64_t mlp_ws(int64_t M, int64_t f, int in) { return align_up(M * f * esize(in)); }
+
+tp_status check_mlp(const void* X, const void* A_i, const void* a_i, const void* B_i,
+                    const void* Z_i, int64_t M, int64_t h, int64_t f, int in, int out) {
+    if (!X || !A_i || !B_i || !Z_i) return TP_ERR_NULL;
+    if (!is_dtype(in) || !is_dtype(out)) return TP_ERR_DTYPE;
+    if (M <= 0 || h <= 0 || f <= 0) return TP_ERR_SHAPE;
+    if (!aligned16(X) || !aligned16(A_i) || !aligned16(B_i) || !aligned16(Z_i) ||
+        (a_i && !aligned16(a_i)))
+        return TP_ERR_ALIGN;
+    if (in == TP_BF16 && (h % 8 || f % 8 || !gemm_bf16_fits(M, f, h, h, f) ||
+                          !gemm_bf16_fits(M, h, f, f, h)))
+        return TP_ERR_SHAPE;
+    if (in == TP_F32 && (M > kI32 || h > kI32 || f > kI32)) return TP_ERR_SHAPE;
+    return TP_OK;
+}
+
+hipError_t run_mlp(const void* X, const void* A_i, const void* a_i, const void* B_i, void* Z_i,
+                   void* ws, int64_t M, int64_t h, int64_t f, int in, int out, hipStream_t st) {
+    // Y'_i = GeLU(X·A_i + a_i), kept in the input precision (column-parallel, §2.1)
+    hipError_t e = run_linear(X, h, A_i, f, a_i, ws, f, M, f, h, in, in, true, st);
+    if (e != hipSuccess) return e;
+    // Z_i = Y'_i·B_i, the rank's partial sum (row-parallel, §2.1)
+    return run_linear(ws, f, B_i, h, nullptr, Z_i, h, M, h, f, in, out, false, st);
+}
+
+// ---- attention shard ------------------------------------------------------
+struct AttnWs { int64_t qkv, o, total; };
+AttnWs attn_ws(int64_t b, int64_t s, int64_t H_l, int64_t d) {
+    const int64_t M = b * s;
+    AttnWs w;
+    w.qkv = 0;
+    w.o = align_up(M * 3 * H_l * d * 2);
+    w.total = w.o + align_up(M * H_l * d * 2);
+    return w;
+}
+
+tp_status check_attn_shape(int64_t b, int64_t s, int64_t h, int64_t H_l, int64_t d) {
+    if (b <= 0 || s <= 0 || h <= 0 || H_l <= 0 || d <= 0) return TP_ERR_SHAPE;
+    if (d != kHeadDim || h % 8) return TP_ERR_SHAPE;
+    const int64_t M = b * s, n3 = 3 * H_l * d;
+    if (!gemm_bf16_fits(M, n3, h, h, n3) || !gemm_bf16_fits(M, h, H_l * d, H_l * d, h))
+        return TP_ERR_SHAPE;
+    // the attention kernel addresses one sequence of qkv with 32-bit offsets
+    if (s * n3 * 2 >= kI32 || ((s + 127) / 128) * b * H_l > kI32) return TP_ERR_SHAPE;
+    return TP_OK;
+}
+
+hipError_t run_attn(const void* X, const void* Wqkv, const void* Wo, void* Z, void* ws,
+                    int64_t b, int64_t s, int64_t h, int64_t H_l, int64_t d, bool causal, int out,
+                    hipStream_t st) {
+    const int64_t M = b * s, n3 = 3 * H_l * d;
+    const AttnWs w = attn_ws(b, s, H_l, d);
+    char* qkv = (char*)ws + w.qkv;
+    char* O = (char*)ws + w.o;
+    // [Q|K|V] = X·W_qkv_i for the local heads (column-parallel, §3.2)
+    hipError_t e = tpk::gemm_bf16(X, h, Wqkv, n3, nullptr, qkv, n3, M, n3, h, true, false, st);
+    if (e != hipSuccess) return e;
+    e = tpk::attention_fwd(qkv, n3, O, b, s, H_l, causal, st);
+    if (e != hipSuccess) return e;
+    // Z_i = O_i·W_o_i (row-parallel partial, §3.2)
+    return tpk::gemm_bf16(O, H_l * d, Wo, h, nullptr, Z, h, M, h, H_l * d, out == TP_BF16, false, st);
+}
+
+// ---- block ----------------------------------------------------------------
+struct BlockWs { int64_t xn, parts, x1, scratch, total; };
+BlockWs block_ws(int64_t b, int64_t s, int64_t h, int64_t H, int64_t d, int64_t F, int P) {
+    const int64_t M = b * s;
+    BlockWs w;
+    w.xn = 0;
+    w.parts = align_up(M * h * 2);
+    w.x1 = w.parts + align_up((int64_t)P * M * h * 4);
+    w.scratch = w.x1 + align_up(M * h * 4);
+    const int64_t a = attn_ws(b, s, H / P, d).total;
+    const int64_t m = mlp_ws(M, F / P, TP_BF16);
+    w.total = w.scratch + (a > m ? a : m);
+    return w;
+}
+
+}  // namespace
+
+// ===========================================================================
+TP_EXPORT const char* tp_status_string(int status) {
+    switch (status) {
+        case TP_OK: return "ok";
+        case TP_ERR_NULL: return "a required pointer is NULL";
+        case TP_ERR_SHAPE: return "unsupported or inconsistent shape";
+        case TP_ERR_DTYPE: return "unsupported dtype or epilogue code";
+        case TP_ERR_ALIGN: return "pointer not 16-byte aligned";
+        case TP_ERR_WORKSPACE: return "workspace missing or too small";
+        case TP_ERR_LAUNCH: return "kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+TP_EXPORT int tp_abi_version(void) { return 1; }
+
+TP_EXPORT tp_status tp_linear(const void* X, int64_t ldx, const void* W, int64_t ldw,
+                              const void* bias, void* C, int64_t ldc, int64_t M, int64_t N,
+                              int64_t K, int in, int out, int epilogue, void* stream) {
+    const tp_status s = check_linear(X, ldx, W, ldw, bias, C, ldc, M, N, K, in, out, epilogue);
+    if (s != TP_OK) return s;
+    return launched(run_linear(X, ldx, W, ldw, bias, C, ldc, M, N, K, in, out,
+                               epilogue == TP_EPI_GELU, as_stream(stream)));
+}
+
+TP_EXPORT size_t tp_mlp_shard_workspace(int64_t M, int64_t f, int in) {
+    if (M <= 0 || f <= 0 || !is_dtype(in)) return 0;
+    return (size_t)mlp_ws(M, f, in);
+}
+
+TP_EXPORT tp_status tp_mlp_shard(const void* X, const void* A_i, const void* a_i,
+                                 const void* B_i, void* Z_i, void* ws, size_t ws_bytes,
+                                 int64_t M, int64_t h, int64_t f, int in, int out, void* stream) {
+    tp_status s = check_mlp(X, A_i, a_i, B_i, Z_i, M, h, f, in, out);
+    if (s != TP_OK) return s;
+    if (!ws || ws_bytes < (size_t)mlp_ws(M, f, in)) return TP_ERR_WORKSPACE;
+    if (!aligned16(ws)) return TP_ERR_ALIGN;
+    return launched(run_mlp(X, A_i, a_i, B_i, Z_i, ws, M, h, f, in, out, as_stream(stream)));
+}
+
+TP_EXPORT size_t tp_attn_shard_workspace(int64_t b, int64_t s, int64_t H_l, int64_t d) {
+    if (b <= 0 || s <= 0 || H_l <= 0 || d <= 0) return 0;
+    return (size_t)attn_ws(b, s, H_l, d).total;
+}
+
+TP_EXPORT tp_status tp_attn_shard(const void* X, const void* W_qkv_i, const void* W_o_i,
+                                  void* Z_i, void* ws, size_t ws_bytes, int64_t b, int64_t s,
+                                  int64_t h, int64_t H_l, int64_t d, int causal, int out,
+                                  void* stream) {
+    if (!X || !W_qkv_i || !W_o_i || !Z_i) return TP_ERR_NULL;
+    if (!is_dtype(out)) return TP_ERR_DTYPE;
+    tp_status st = check_attn_shape(b, s, h, H_l, d);
+    if (st != TP_OK) return st;
+    if (!aligned16(X) || !aligned16(W_qkv_i) || !aligned16(W_o_i) || !aligned16(Z_i))
+        return TP_ERR_ALIGN;
+    if (!ws || ws_bytes < (size_t)attn_ws(b, s, H_l, d).total) return TP_ERR_WORKSPACE;
+    if (!aligned16(ws)) return TP_ERR_ALIGN;
+    return launched(run_attn(X, W_qkv_i, W_o_i, Z_i, ws, b, s, h, H_l, d, causal != 0, out,
+                             as_stream(stream)));
+}
+
+TP_EXPORT tp_status tp_attention_core(const void* qkv, int64_t ld_qkv, void* O, int64_t b,
+                                      int64_t s, int64_t H_l, int64_t d, int causal,
+                                      void* stream) {
+    if (!qkv || !O) return TP_ERR_NULL;
+    if (b <= 0 || s <= 0 || H_l <= 0 || d != kHeadDim || ld_qkv < 3 * H_l * d || ld_qkv % 8)
+        return TP_ERR_SHAPE;
+    if (s * ld_qkv * 2 >= kI32 || ((s + 127) / 128) * b * H_l > kI32) return TP_ERR_SHAPE;
+    if (!aligned16(qkv) || !aligned16(O)) return TP_ERR_ALIGN;
+    return launched(tpk::attention_fwd(qkv, ld_qkv, O, b, s, H_l, causal != 0, as_stream(stream)));
+}
+
+TP_EXPORT tp_status tp_layernorm(const void* x, int in, void* y, const void* gamma,
+                                 const void* beta, float eps, int64_t M, int64_t h,
+                                 void* stream) {
+    if (!x || !y) return TP_ERR_NULL;
+    if (!is_dtype(in)) return TP_ERR_DTYPE;
+    if (M <= 0 || h <= 0 || h % 8 || h > kMaxLnWidth || M > kI32 || !(eps > 0.0f))
+        return TP_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(y) || (gamma && !aligned16(gamma)) || (beta && !aligned16(beta)))
+        return TP_ERR_ALIGN;
+    return launched(tpk::layernorm(x, in == TP_BF16, y, (const float*)gamma, (const float*)beta,
+                                   eps, M, h, as_stream(stream)));
+}
+
+TP_EXPORT tp_status tp_partial_sum(void* Z, int out, const void* partials, int part, int P,
+                                   int64_t M, int64_t h, const void* bias, const void* residual,
+                                   int res, void* stream) {
+    if (!Z || !partials) return TP_ERR_NULL;
+    if (!is_dtype(out) || !is_dtype(part) || (residual && !is_dtype(res))) return TP_ERR_DTYPE;
+    if (P <= 0 || M <= 0 || h <= 0 || h % 4 || h > kI32) return TP_ERR_SHAPE;
+    if (!aligned16(Z) || !aligned16(partials) || (bias && !aligned16(bias)) ||
+        (residual && !aligned16(residual)))
+        return TP_ERR_ALIGN;
+    return launched(tpk::partial_sum(Z, out == TP_BF16, partials, part == TP_BF16, P, M, h,
+                                     (const float*)bias, residual, residual && res == TP_BF16,
+                                     as_stream(stream)));
+}
+
+TP_EXPORT size_t tp_block_shard_workspace(int64_t b, int64_t s, int64_t h, int64_t H, int64_t d,
+                                          int64_t F, int P) {
+    if (b <= 0 || s <= 0 || h <= 0 || H <= 0 || d <= 0 || F <= 0 || P <= 0 || H % P || F % P)
+        return 0;
+    return (size_t)block_ws(b, s, h, H, d, F, P).total;
+}
+
+TP_EXPORT tp_status tp_block_shard(const void* x, void* out, int out_dtype, void* x1,
+                                   const void* ln1_g, const void* ln1_b, const void* ln2_g,
+                                   const void* ln2_b, float eps, const void* const* W_qkv,
+                                   const void* const* W_o, const void* const* A,
+                                   const void* const* B, int P, void* ws, size_t ws_bytes,
+                                   int64_t b, int64_t s, int64_t h, int64_t H, int64_t d,
+                                   int64_t F, void* stream) {
+    if (!x || !out || !W_qkv || !W_o || !A || !B) return TP_ERR_NULL;
+    if (!is_dtype(out_dtype)) return TP_ERR_DTYPE;
+    if (P <= 0 || H <= 0 || F <= 0 || H % P || F % P || h != H * d || !(eps > 0.0f))
+        return TP_ERR_SHAPE;
+    const int64_t M = b * s, Hl = H / P, f = F / P;
+    tp_status st = check_attn_shape(b, s, h, Hl, d);
+    if (st != TP_OK) return st;
+    if (f % 8 || h > kMaxLnWidth || !gemm_bf16_fits(M, f, h, h, f) || !gemm_bf16_fits(M, h, f, f, h))
+        return TP_ERR_SHAPE;
+    for (int r = 0; r < P; ++r)
+        if (!W_qkv[r] || !W_o[r] || !A[r] || !B[r]) return TP_ERR_NULL;
+    const void* ptrs[] = {x, out, x1, ln1_g, ln1_b, ln2_g, ln2_b};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return TP_ERR_ALIGN;
+    for (int r = 0; r < P; ++r)
+        if (!aligned16(W_qkv[r]) || !aligned16(W_o[r]) || !aligned16(A[r]) || !aligned16(B[r]))
+            return TP_ERR_ALIGN;
+    const BlockWs w = block_ws(b, s, h, H, d, F, P);
+    if (!ws || ws_bytes < (size_t)w.total) return TP_ERR_WORKSPACE;
+    if (!aligned16(ws)) return TP_ERR_ALIGN;
+
+    const hipStream_t st_ = as_stream(stream);
+    char* base = (char*)ws;
+    void* xn = base + w.xn;
+    float* parts = (float*)(base + w.parts);
+    float* x1buf = x1 ? (float*)x1 : (float*)(base + w.x1);
+    void* scratch = base + w.scratch;
+    const int64_t n = M * h;
+    hipError_t e;
+
+    // x1 = x + sum_r Attn_r(LN1(x))
+    if ((e = tpk::layernorm(x, true, xn, (const float*)ln1_g, (const float*)ln1_b, eps, M, h, st_)))
+        return TP_ERR_LAUNCH;
+    for (int r = 0; r < P; ++r)
+        if ((e = run_attn(xn, W_qkv[r], W_o[r], parts + r * n, scratch, b, s, h, Hl, d, true,
+                          TP_F32, st_)))
+            return TP_ERR_LAUNCH;
+    if ((e = tpk::partial_sum(x1buf, false, parts, false, P, M, h, nullptr, x, true, st_)))
+        return TP_ERR_LAUNCH;
+    // out = x1 + sum_r MLP_r(LN2(x1))
+    if ((e = tpk::layernorm(x1buf, false, xn, (const float*)ln2_g, (const float*)ln2_b, eps, M, h,
+                            st_)))
+        return TP_ERR_LAUNCH;
+    for (int r = 0; r < P; ++r)
+        if ((e = run_mlp(xn, A[r], nullptr, B[r], parts + r * n, scratch, M, h, f, TP_BF16, TP_F32,
+                         st_)))
+            return TP_ERR_LAUNCH;
+    if ((e = tpk::partial_sum(out, out_dtype == TP_BF16, parts, false, P, M, h, nullptr, x1buf,
+                              false, st_)))
+        return TP_ERR_LAUNCH;
+    return TP_OK;
+}

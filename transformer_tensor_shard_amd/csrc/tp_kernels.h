@@ -1,0 +1,38 @@
+// Internal launcher declarations shared by the HIP translation units of
+// libtp.so.  Not part of the public ABI (include/tp.h is).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tpk {
+
+// C[M,N] = epi(A[M,K]·B[K,N] + bias) on bf16 inputs with the MFMA kernel.
+// Shapes and alignment are validated by the caller (tp_abi.cpp).
+hipError_t gemm_bf16(const void* A, int64_t lda, const void* B, int64_t ldb,
+                     const float* bias, void* C, int64_t ldc,
+                     int64_t M, int64_t N, int64_t K, bool out_bf16, bool gelu,
+                     hipStream_t stream);
+
+// Same contract on f32 inputs (plain FMA kernel, used by the f32 path).
+hipError_t gemm_f32(const float* A, int64_t lda, const float* B, int64_t ldb,
+                    const float* bias, void* C, int64_t ldc,
+                    int64_t M, int64_t N, int64_t K, bool out_bf16, bool gelu,
+                    hipStream_t stream);
+
+// Causal / full softmax(Q K^T / sqrt(d)) V for every (sequence, local head);
+// d == 128.  qkv is [b*s, ld_qkv] bf16, O is [b*s, H_l*128] bf16.
+hipError_t attention_fwd(const void* qkv, int64_t ld_qkv, void* O,
+                         int64_t b, int64_t s, int64_t H_l, bool causal,
+                         hipStream_t stream);
+
+// y = LayerNorm(x) rows of length h, y in bf16.
+hipError_t layernorm(const void* x, bool x_bf16, void* y, const float* gamma,
+                     const float* beta, float eps, int64_t M, int64_t h,
+                     hipStream_t stream);
+
+// Z = sum_r parts[r] (+bias[col]) (+residual).
+hipError_t partial_sum(void* Z, bool out_bf16, const void* parts, bool parts_bf16, int P,
+                       int64_t M, int64_t h, const float* bias,
+                       const void* residual, bool res_bf16, hipStream_t stream);
+
+}  // namespace tpk
