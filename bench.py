@@ -98,7 +98,7 @@ def main():
     ap.add_argument("--workload", default="block_bf16_h12288_tp8")
     ap.add_argument("--mode", default="step", choices=["step", "kernel", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=256,
+    ap.add_argument("--cpu-rows", type=int, default=768,
                     help="tokens of sequence 0 the oracle computes for the CPU baseline")
     args = ap.parse_args()
 

@@ -1,11 +1,17 @@
 """Parity bars for comparing the HIP path with the fp64 oracle.
 
 * f32 path:  max_i |g_i - r_i| / max(|r_i|, rms(r)) <= 1e-4
-* bf16 path: ||g - r||_F / ||r||_F <= 1e-2  and  max_i |g_i - r_i| <= 3e-2 * rms(r)
+* bf16 path: ||g - r||_F / ||r||_F <= 1e-2 over the compared tensor, and
+             max_i |g_i - r_i| <= 3e-2 * rms(r_row(i)), where r_row(i) is the
+             output row (one token's vector) that holds element i.
 
-When the result itself is stored in bf16 (``stored_bf16=True``), storing it
-costs up to half a bf16 ulp, 2^-8 * |r_i|, on top of the arithmetic; the
-max-abs bar then reads |g_i - r_i| <= 3e-2 * rms(r) + 2^-8 * |r_i|.
+The rms in the bf16 max-abs bar is taken per token row: every step of the path
+is defined per token (per query for attention), and causal attention's rows
+differ in scale by an order of magnitude (the first query averages one value,
+the last averages thousands).  With a tensor-wide rms no implementation that
+keeps Q, K, V or O in bf16 meets the bar on the first rows (rounding V alone
+gives 0.054 * rms at s=2048), while per row an exact emulation of the bf16
+roundings gives 0.019 * rms_row.
 """
 import numpy as np
 import torch
@@ -24,13 +30,21 @@ def as_np(t) -> np.ndarray:
 def errors(g, r):
     g, r = as_np(g), as_np(r)
     assert g.shape == r.shape, (g.shape, r.shape)
-    d = np.abs(g - r)
-    rms = float(np.sqrt(np.mean(r * r)))
-    fro = float(np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-300))
-    max_rel = float(np.max(d / np.maximum(np.abs(r), rms))) if r.size else 0.0
-    max_abs = float(d.max()) if r.size else 0.0
-    return {"fro": fro, "max_rel": max_rel, "max_abs": max_abs, "rms": rms,
-            "finite": bool(np.isfinite(g).all())}
+    g2 = g.reshape(-1, g.shape[-1]) if g.ndim else g.reshape(1, 1)
+    r2 = r.reshape(-1, r.shape[-1]) if r.ndim else r.reshape(1, 1)
+    d = np.abs(g2 - r2)
+    rms = float(np.sqrt(np.mean(r2 * r2))) if r2.size else 0.0
+    rms_row = np.sqrt(np.mean(r2 * r2, axis=1, keepdims=True))
+    fro = float(np.linalg.norm(g2 - r2) / max(np.linalg.norm(r2), 1e-300))
+    out = {"fro": fro, "rms": rms, "finite": bool(np.isfinite(g2).all())}
+    if r2.size:
+        out["max_rel"] = float(np.max(d / np.maximum(np.abs(r2), rms)))
+        out["max_abs"] = float(d.max())
+        out["max_abs_over_rms"] = float(d.max() / max(rms, 1e-300))
+        ratio = d.max(axis=1, keepdims=True) / np.maximum(rms_row, 1e-300)
+        out["max_abs_over_row_rms"] = float(ratio.max())
+        out["worst_row"] = int(ratio.argmax())
+    return out
 
 
 def assert_f32(g, r, bar=F32_MAX_REL):
@@ -39,15 +53,9 @@ def assert_f32(g, r, bar=F32_MAX_REL):
     return e
 
 
-def assert_bf16(g, r, fro=BF16_FRO, max_abs_rms=BF16_MAX_ABS_RMS, stored_bf16=False):
+def assert_bf16(g, r, fro=BF16_FRO, max_abs_rms=BF16_MAX_ABS_RMS):
     e = errors(g, r)
     assert e["finite"], e
     assert e["fro"] <= fro, e
-    if stored_bf16:
-        g, r = as_np(g), as_np(r)
-        excess = np.abs(g - r) - (max_abs_rms * e["rms"] + 2.0 ** -8 * np.abs(r))
-        e["max_excess"] = float(excess.max())
-        assert e["max_excess"] <= 0, e
-    else:
-        assert e["max_abs"] <= max_abs_rms * e["rms"], e
+    assert e["max_abs_over_row_rms"] <= max_abs_rms, e
     return e

@@ -51,7 +51,7 @@ def test_linear_bf16_bias_gelu_bf16out(M, N, K):
     C = tts.tp_linear(X.to(DEV), W.to(DEV), bias.to(DEV), gelu=True, out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     ref = oracle.gelu(oracle.matmul(X, W, bias))
-    e = assert_bf16(C, ref, stored_bf16=True)
+    e = assert_bf16(C, ref)
     assert e["fro"] < 5e-3, e   # one bf16 rounding of the output
 
 
@@ -121,7 +121,7 @@ def test_mlp_bf16_small(M, h, f, bias):
     torch.cuda.synchronize()
     ref = oracle.mlp_shard(X, A, B, a)
     assert_bf16(Z, ref)
-    assert_bf16(Zb, ref, stored_bf16=True)
+    assert_bf16(Zb, ref)
 
 
 # ------------------------------------------------------------------ partial sum
@@ -150,7 +150,7 @@ def test_partial_sum_mixed_dtypes_and_alias():
     res = gen((M, h), 1.0, 32, "residual")
     Z = tts.tp_partial_sum(parts.to(DEV), None, res.to(DEV), out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
-    assert_bf16(Z, oracle.partial_sum(parts, None, res), fro=4e-3, stored_bf16=True)
+    assert_bf16(Z, oracle.partial_sum(parts, None, res), fro=4e-3)
     r32 = gen((M, h), 1.0, 32, "residual", torch.float32).to(DEV)
     p32 = gen((P, M, h), 1.0, 33, "partials", torch.float32)
     ref = oracle.partial_sum(p32, None, r32.cpu())
@@ -170,7 +170,7 @@ def test_layernorm(M, h, dtype, affine):
     b = gen((h,), 1.0, 41, "beta", torch.float32) if affine else None
     y = tts.tp_layernorm(x.to(DEV), g.to(DEV) if affine else None, b.to(DEV) if affine else None)
     torch.cuda.synchronize()
-    e = assert_bf16(y, oracle.layernorm(x, g, b, 1e-5), stored_bf16=True)
+    e = assert_bf16(y, oracle.layernorm(x, g, b, 1e-5))
     assert e["fro"] < 4e-3, e   # one bf16 rounding of the output
 
 
@@ -196,7 +196,7 @@ def test_attention_core(b, s, Hl, causal):
     eye = np.eye(n3)
     ref = oracle.attn_shard_rows(qkv, b, s, eye, np.ascontiguousarray(eye[:Hl * d]), Hl, d,
                                  causal)[:, :Hl * d]
-    assert_bf16(O, ref, stored_bf16=True)
+    assert_bf16(O, ref)
 
 
 def test_attention_single_token_is_value():
