@@ -12,9 +12,12 @@
 //    (256 f32 accumulators per lane, held in the unified VGPR/AGPR file);
 //  * K advances in 64-wide steps; the A and B tiles of a step (32 KiB each)
 //    are staged in LDS, double-buffered (128 KiB of the 160 KiB per CU), with
-//    the next step's global loads in flight while the MFMAs of this one run;
-//  * global loads are 16-byte buffer loads whose out-of-range lanes return 0
-//    (ragged M, N and K tails need no branches in the loop);
+//    the next step's loads in flight while the MFMAs of this one run;
+//  * global -> LDS traffic uses the gfx950 direct-to-LDS 16-byte buffer loads
+//    (no staging registers, no LDS write instructions); lanes past M, N or K
+//    are pushed out of the buffer's range, for which the load writes zeros;
+//  * the 16-wide k-step fragments are double-buffered in registers so LDS
+//    reads for the next k-step overlap the MFMAs of this one;
 //  * the A operand (K contiguous) is read with 16-byte LDS reads; the B
 //    operand (N contiguous) is read with the gfx950 LDS transpose read
 //    (ds_read_b64_tr_b16), which hands each lane 4 consecutive K values of
@@ -50,6 +53,39 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
                                              0x7ffffff0, 0x00020000);
 }
 
+// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100;
+
+// One k-step: 16 MFMAs with the next k-step's 12 LDS reads (4 A, 8 B) issued
+// two at a time between the first six, so they land long before use.
+__device__ __forceinline__ void sched_kstep() {
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 10, 0);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// The k-step after the barrier also issues the 16 direct-to-LDS loads of the
+// tile after next.
+__device__ __forceinline__ void sched_kstep_dma() {
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, 2, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 6, 0);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 __device__ __forceinline__ float gelu_erf(float y) {
     return 0.5f * y * (1.0f + erff(y * 0.70710678118654752f));
 }
@@ -77,7 +113,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
     const float* __restrict__ bias, void* __restrict__ C, int64_t ldc,
     int M, int N, int K, int tiles_m, int tiles_n)
 {
-    __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE_BYTES];
+    // Two stages as two separate LDS objects: every access below names its
+    // stage statically, which lets the compiler see that reads of one stage
+    // do not depend on the direct-to-LDS loads still landing in the other.
+    __shared__ __attribute__((aligned(1024))) char lds0[STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char lds1[STAGE_BYTES];
 
     int tm, tn;
     tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
@@ -87,53 +127,54 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
     const int lane = tid & 63, wid = tid >> 6;
     const int wm = wid >> 1, wn = wid & 1;
 
-    // ---- global -> LDS copy assignment -------------------------------------
-    // A tile: 256 rows x 8 units of 16 B; thread owns unit (tid & 7) of rows
-    // (tid >> 3) + 32 i.  B tile: 64 rows x 32 units; thread owns unit
-    // (tid & 31) of rows (tid >> 5) + 8 i.
-    const int a_unit = tid & 7, a_row0 = tid >> 3;
-    const int b_unit = tid & 31, b_row0 = tid >> 5;
-    unsigned a_voff[8], b_voff[8];
-    bool a_row_ok[8];
-    unsigned a_lds[8], b_lds[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int r = a_row0 + 32 * i;
-        a_row_ok[i] = (m0 + r) < M;
-        a_voff[i] = (unsigned)(r * lda + a_unit * 8) * 2u;
-        a_lds[i] = r * 128 + ((a_unit ^ ((r >> 1) & 7)) << 4);
-        const int kr = b_row0 + 8 * i;
-        b_voff[i] = (unsigned)(kr * ldb + b_unit * 8) * 2u;
-        b_lds[i] = A_BYTES + kr * 512 + ((b_unit ^ ((kr & 3) << 2)) << 4);
-    }
-    const bool b_col_ok = (n0 + b_unit * 8) < N;
-
     const __bf16* a_tile = A + (int64_t)m0 * lda;
     const __bf16* b_tile = B + n0;
 
-    u32x4 ra[8], rb[8];
-    auto load_tiles = [&](int k0) {
+    // ---- global -> LDS: direct (DMA) 16-byte buffer loads ---------------------
+    // A buffer_load_dwordx4 ... lds instruction writes 64 lanes x 16 B = 1 KiB
+    // contiguously in LDS (lane l at M0 + 16 l), so the swizzled LDS layout is
+    // produced by choosing which global unit each lane fetches.  Wave w fills
+    // bytes [8 KiB w, 8 KiB w + 8 KiB) of each tile with 8 instructions:
+    //   A: instruction j, lane l -> LDS row 64w + 8j + l/8, physical unit l%8
+    //   B: instruction j, lane l -> LDS row 16w + 2j + l/32, physical unit l%32
+    // and the logical unit is the physical one XOR the row's swizzle.
+    unsigned a_off[8], b_off[8];
+    int a_kcol[8], b_krow[8];
+    bool a_row_ok[8], b_col_ok[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int r = 64 * wid + 8 * j + (lane >> 3);
+        const int u = (lane & 7) ^ ((r >> 1) & 7);
+        a_row_ok[j] = (m0 + r) < M;
+        a_kcol[j] = u * 8;
+        a_off[j] = (unsigned)(r * lda + u * 8) * 2u;
+        const int kr = 16 * wid + 2 * j + (lane >> 5);
+        const int ub = (lane & 31) ^ ((kr & 3) << 2);
+        b_col_ok[j] = (n0 + ub * 8) < N;
+        b_krow[j] = kr;
+        b_off[j] = (unsigned)(kr * ldb + ub * 8) * 2u;
+    }
+    // Lanes past M, N or K fetch nothing and the DMA writes zeros for them, so
+    // ragged tails (and a tile index past the last one) need no branch.
+    auto dma_tile = [&](int k0, char* stage) {
         const __amdgpu_buffer_rsrc_t ar = make_rsrc(a_tile + k0);
         const __amdgpu_buffer_rsrc_t br = make_rsrc(b_tile + (int64_t)k0 * ldb);
-        const bool a_k_ok = (k0 + a_unit * 8) < K;
+        char* sa = stage + wid * 8192;
+        char* sb = stage + A_BYTES + wid * 8192;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const unsigned off = (a_row_ok[i] && a_k_ok) ? a_voff[i] : OOB;
-            ra[i] = __builtin_amdgcn_raw_buffer_load_b128(ar, off, 0, 0);
+        for (int j = 0; j < 8; ++j) {
+            const bool ok = a_row_ok[j] && (k0 + a_kcol[j]) < K;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, LDS_PTR(void, sa + j * 1024), 16,
+                                                     ok ? a_off[j] : OOB, 0, 0, 0);
         }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const bool ok = b_col_ok && (k0 + b_row0 + 8 * i) < K;
-            rb[i] = __builtin_amdgcn_raw_buffer_load_b128(br, ok ? b_voff[i] : OOB, 0, 0);
+        for (int j = 0; j < 8; ++j) {
+            const bool ok = b_col_ok[j] && (k0 + b_krow[j]) < K;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(br, LDS_PTR(void, sb + j * 1024), 16,
+                                                     ok ? b_off[j] : OOB, 0, 0, 0);
         }
     };
-    auto store_tiles = [&](int stage) {
-        char* base = lds + stage * STAGE_BYTES;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) *(u32x4*)(base + a_lds[i]) = ra[i];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) *(u32x4*)(base + b_lds[i]) = rb[i];
-    };
+    const int nk = (K + BK - 1) / BK;
 
     // ---- LDS -> register operand addresses ----------------------------------
     // A operand of MFMA 32x32x16: lane holds row (lane & 31), K values
@@ -149,13 +190,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
     // and receives column i, rows 0..3.  Groups 0/1 cover N columns 0-15 /
     // 16-31 of K rows 0-7, groups 2/3 the same columns of K rows 8-15.
     const int g = lane >> 4, gi = lane & 15;
-    const int b_krow = (g >> 1) * 8 + (gi >> 2);       // + 16*kk + 4*half
+    const int b_row = (g >> 1) * 8 + (gi >> 2);       // + 16*kk + 4*half
     unsigned b_rd[4];
 #pragma unroll
     for (int nj = 0; nj < 4; ++nj) {
         const int col = wn * 128 + nj * 32 + (g & 1) * 16 + 4 * (gi & 3);
         const int unit = col >> 3;
-        b_rd[nj] = A_BYTES + b_krow * 512 + ((unit ^ ((b_krow & 3) << 2)) << 4) + (col & 7) * 2;
+        b_rd[nj] = A_BYTES + b_row * 512 + ((unit ^ ((b_row & 3) << 2)) << 4) + (col & 7) * 2;
     }
 
     f32x16 acc[4][4];
@@ -166,39 +207,66 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    const int nk = (K + BK - 1) / BK;
-    load_tiles(0);
-    store_tiles(0);
-    __syncthreads();
-
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        const bool has_next = (kt + 1) < nk;
-        if (has_next) load_tiles((kt + 1) * BK);
-        const char* base = lds + cur * STAGE_BYTES;
+    bf16x8 fa[2][4], fb[2][4];
+    auto load_frags = [&](bf16x8 (&a)[4], bf16x8 (&b)[4], const char* base, int kk) {
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            bf16x8 af[4], bfr[4];
+        for (int mi = 0; mi < 4; ++mi) a[mi] = *(const bf16x8*)(base + a_rd[kk] + mi * 32 * 128);
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
-                af[mi] = *(const bf16x8*)(base + a_rd[kk] + mi * 32 * 128);
-#pragma unroll
-            for (int nj = 0; nj < 4; ++nj) {
-                const char* p = base + b_rd[nj] + kk * 16 * 512;
-                bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, p));
-                bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, p + 4 * 512));
-                bfr[nj] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            }
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-                for (int nj = 0; nj < 4; ++nj)
-                    acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[nj],
-                                                                          acc[mi][nj], 0, 0, 0);
+        for (int nj = 0; nj < 4; ++nj) {
+            const char* p = base + b_rd[nj] + kk * 16 * 512;
+            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, p));
+            const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, p + 4 * 512));
+            b[nj] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
-        if (has_next) store_tiles(cur ^ 1);
-        __syncthreads();
+    };
+    auto mfmas = [&](const bf16x8 (&a)[4], const bf16x8 (&b)[4]) {
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+            for (int nj = 0; nj < 4; ++nj)
+                acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[nj], acc[mi][nj], 0, 0, 0);
+    };
+
+    // ---- main loop: tile kt+1 is in flight into the other stage while tile kt
+    // is multiplied; k-step fragments are double-buffered in registers; the
+    // barrier that publishes tile kt+1 sits before the last k-step so that the
+    // next tile's first fragments (and tile kt+2's loads) issue under the last
+    // 16 MFMAs.  Scheduling groups pin the interleave: each k-step issues the
+    // next k-step's 12 LDS reads between its first MFMAs.
+    dma_tile(0, lds0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's DMA has landed
+    __syncthreads();
+    dma_tile(BK, lds1);
+    load_frags(fa[0], fb[0], lds0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    // one K tile: three k-steps on `cur`, publish `nxt`, refill `cur` with the
+    // tile after next, last k-step while the next tile's first fragments load
+    auto tile = [&](const char* cur_c, char* cur, const char* nxt, int k_next2) {
+        load_frags(fa[1], fb[1], cur_c, 1);
+        mfmas(fa[0], fb[0]);
+        sched_kstep();
+        load_frags(fa[0], fb[0], cur_c, 2);
+        mfmas(fa[1], fb[1]);
+        sched_kstep();
+        load_frags(fa[1], fb[1], cur_c, 3);
+        mfmas(fa[0], fb[0]);
+        sched_kstep();
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();                            // next tile visible; `cur` free
+        dma_tile(k_next2, cur);                     // all lanes masked past the last tile
+        load_frags(fa[0], fb[0], nxt, 0);
+        mfmas(fa[1], fb[1]);
+        sched_kstep_dma();
+    };
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+        tile(lds0, lds0, lds1, (kt + 2) * BK);
+        tile(lds1, lds1, lds0, (kt + 3) * BK);
     }
+    if (kt < nk) tile(lds0, lds0, lds1, (kt + 2) * BK);
+    // the (masked, zero-writing) loads issued for the tiles past the end must
+    // land before this workgroup's LDS is released
+    __builtin_amdgcn_s_waitcnt(0x0F70);
 
     // ---- epilogue: lane holds column (lane & 31) and rows
     // 8*(r >> 2) + 4*(lane >> 5) + (r & 3) of each 32x32 block.
