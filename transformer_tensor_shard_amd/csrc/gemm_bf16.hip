@@ -3,32 +3,43 @@
 // Computes C[M,N] = epi(A[M,K]·B[K,N] + bias[N]) for row-major A (the
 // activations X, K contiguous) and row-major B (a weight in the [in, out]
 // layout of the Megatron explainer's Y = X @ W, N contiguous).  This is the
-// product behind the column-parallel layer (epilogue: + bias, exact-erf GeLU,
-// store bf16: "图解Transformer并行计算" §2.1, Y'_i = GeLU(X·A_i)) and the
+// product behind the column-parallel layer (epilogue: + bias, GeLU, store
+// bf16: "图解Transformer并行计算" §2.1, Y'_i = GeLU(X·A_i)) and the
 // row-parallel layer (epilogue: store the f32 partial, §2.1 Z_i = Y'_i·B_i).
 //
-// Design (one 256x256 output tile per workgroup, 4 waves of 64 lanes):
-//  * each wave owns a 128x128 sub-tile = 4x4 MFMA 32x32x16 bf16 blocks
-//    (256 f32 accumulators per lane, held in the unified VGPR/AGPR file);
+// Design: one 256x256 output tile per workgroup of 8 waves (two per SIMD).
+//  * wave w owns a 128x64 sub-tile: rows 128*((w&3)>>1), columns
+//    128*(w&1) + 64*(w>>2); that is 4x2 MFMA 32x32x16 bf16 blocks with 128
+//    f32 accumulators per lane.  The two waves on a SIMD (w and w+4) take the
+//    two 64-column halves of one 128x128 quadrant, so while one of them waits
+//    on memory the other keeps the SIMD's matrix core busy;
 //  * K advances in 64-wide steps; the A and B tiles of a step (32 KiB each)
-//    are staged in LDS, double-buffered (128 KiB of the 160 KiB per CU), with
-//    the next step's loads in flight while the MFMAs of this one run;
+//    are staged in LDS, double-buffered (128 KiB of the 160 KiB per CU);
 //  * global -> LDS traffic uses the gfx950 direct-to-LDS 16-byte buffer loads
-//    (no staging registers, no LDS write instructions); lanes past M, N or K
-//    are pushed out of the buffer's range, for which the load writes zeros;
-//  * the 16-wide k-step fragments are double-buffered in registers so LDS
-//    reads for the next k-step overlap the MFMAs of this one;
+//    (no staging registers, no LDS write instructions).  Per-lane offsets are
+//    loop-invariant and only the scalar base of the buffer resource moves per
+//    K step, so issuing a tile's loads costs no vector-ALU work; lanes whose
+//    row (A) or column group (B) lies past M or N get an offset beyond the
+//    buffer's range, for which the load writes zeros;
+//  * k-step fragments are double-buffered in registers so the LDS reads of
+//    the next k-step overlap the MFMAs of this one;
 //  * the A operand (K contiguous) is read with 16-byte LDS reads; the B
-//    operand (N contiguous) is read with the gfx950 LDS transpose read
-//    (ds_read_b64_tr_b16), which hands each lane 4 consecutive K values of
-//    one N column -- the layout the MFMA B operand wants -- so B is never
+//    operand (N contiguous) with the gfx950 LDS transpose read
+//    (ds_read_b64_tr_b16), which hands each lane 4 consecutive K values of one
+//    N column -- the layout the MFMA B operand wants -- so B is never
 //    transposed in memory;
-//  * both LDS tiles are XOR-swizzled in 16-byte units so that the writes, the
-//    16-byte A reads and the transpose B reads each touch all 64 LDS banks
-//    without conflicts;
+//  * both LDS tiles are XOR-swizzled in 16-byte units so that the DMA writes,
+//    the 16-byte A reads and the transpose B reads are free of bank conflicts;
 //  * tiles are renumbered so that consecutive tiles land on the same XCD
 //    (workgroups are dealt round-robin to the 8 XCDs, each with its own L2)
-//    and walk the output in groups of 8 tile-rows.
+//    and walk the output in groups of 4 tile-rows;
+//  * epilogue: the tile is staged through the (then idle) LDS and written with
+//    16-byte row-contiguous stores: one pass for a bf16 tile, two for f32.
+//
+// Measured on MI355X the kernel is bound by the chip's power limit rather than
+// by any one unit: sustained MFMA issue alone pulls the shader clock from 2.4
+// to about 1.6-1.8 GHz, and every byte moved (HBM, L2, LDS) competes for the
+// same budget.
 #include "tp_kernels.h"
 
 namespace tpk {
@@ -37,57 +48,51 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
-constexpr int BM = 256, BN = 256, BK = 64, NTHREADS = 256;
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int NWAVES = 8, NTHREADS = NWAVES * 64;
 constexpr int A_BYTES = BM * BK * 2;          // 32 KiB
 constexpr int B_BYTES = BK * BN * 2;          // 32 KiB
 constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-constexpr int GROUP_M = 8;
+constexpr int GROUP_M = 4;
 constexpr unsigned OOB = 0x80000000u;         // any offset >= num_records reads 0
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
-    // raw buffer, stride 0, num_records just below 2 GiB; word3 = gfx9 format
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
-                                             0x7ffffff0, 0x00020000);
-}
+constexpr int NJ = 2;                         // 32-column MFMA blocks per wave
+constexpr int LOADS = 4;                      // A (and B) loads per wave per K tile
 
 // Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
 constexpr int SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100;
 
-// One k-step: 16 MFMAs with the next k-step's 12 LDS reads (4 A, 8 B) issued
-// two at a time between the first six, so they land long before use.
+// One k-step of a wave: 8 MFMAs with the next k-step's 8 LDS reads issued
+// one after each of the first 8 MFMAs, and V direct-to-LDS loads spread
+// evenly between them.
+template <int V, int I>
+__device__ __forceinline__ void sched_step() {
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+    constexpr int nv = ((I + 1) * V) / 8 - (I * V) / 8;
+    if constexpr (nv > 0) __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, nv, 0);
+    if constexpr (I + 1 < 8) sched_step<V, I + 1>();
+}
+template <int V>
 __device__ __forceinline__ void sched_kstep() {
-#pragma unroll
-    for (int i = 0; i < 6; ++i) {
-        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 10, 0);
+    sched_step<V, 0>();
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// The k-step after the barrier also issues the 16 direct-to-LDS loads of the
-// tile after next.
-__device__ __forceinline__ void sched_kstep_dma() {
-#pragma unroll
-    for (int i = 0; i < 6; ++i) {
-        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, 2, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 6, 0);
-    __builtin_amdgcn_sched_barrier(0);
-}
-
-__device__ __forceinline__ float gelu_erf(float y) {
-    return 0.5f * y * (1.0f + erff(y * 0.70710678118654752f));
+// GeLU(x) = x·Φ(x), Φ(x) = 1 - erfc(x/√2)/2 for x >= 0 and erfc(|x|/√2)/2
+// below, with erfc from Abramowitz & Stegun, Handbook of Mathematical
+// Functions, eq. 7.1.26 (|error| <= 1.5e-7).  Branch-free; in f32 the result
+// is within 4.3e-7 of the exact-erf GeLU over the whole real line, the same
+// bound as x/2·(1 + erff(x/√2)) evaluated in f32.
+__device__ __forceinline__ float gelu(float x) {
+    const float t = fabsf(x) * 0.70710678118654752f;
+    const float u = __builtin_amdgcn_rcpf(1.0f + 0.3275911f * t);
+    const float p = u * (0.254829592f + u * (-0.284496736f + u * (1.421413741f +
+                    u * (-1.453152027f + u * 1.061405429f))));
+    const float h = 0.5f * p * __builtin_amdgcn_exp2f(-1.44269504088896341f * t * t);
+    return x * (x >= 0.0f ? 1.0f - h : h);
 }
 
 // Map a linear workgroup id to (tile_m, tile_n): first make the ids of one XCD
@@ -107,7 +112,7 @@ __device__ __forceinline__ void tile_coords(int pid, int tiles_m, int tiles_n, i
     tn = in_group / gsize;
 }
 
-template <bool OUT_BF16, bool GELU>
+template <bool OUT_BF16, bool GELU, bool CHECK_K>
 __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
     const __bf16* __restrict__ A, int64_t lda, const __bf16* __restrict__ B, int64_t ldb,
     const float* __restrict__ bias, void* __restrict__ C, int64_t ldc,
@@ -124,8 +129,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
     const int m0 = tm * BM, n0 = tn * BN;
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wid = tid >> 6;
-    const int wm = wid >> 1, wn = wid & 1;
+    const int lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+    const int wm = (wid & 3) >> 1, wn = wid & 1, wh = wid >> 2;
 
     const __bf16* a_tile = A + (int64_t)m0 * lda;
     const __bf16* b_tile = B + n0;
@@ -134,45 +140,42 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
     // A buffer_load_dwordx4 ... lds instruction writes 64 lanes x 16 B = 1 KiB
     // contiguously in LDS (lane l at M0 + 16 l), so the swizzled LDS layout is
     // produced by choosing which global unit each lane fetches.  Wave w fills
-    // bytes [8 KiB w, 8 KiB w + 8 KiB) of each tile with 8 instructions:
-    //   A: instruction j, lane l -> LDS row 64w + 8j + l/8, physical unit l%8
-    //   B: instruction j, lane l -> LDS row 16w + 2j + l/32, physical unit l%32
+    // 4 KiB of each operand tile with 4 instructions each:
+    //   A: instruction j, lane l -> row 32w + 8j + l/8 (128 B rows), physical unit l%8
+    //   B: instruction j, lane l -> K row 8w + 2j + l/32 (512 B rows), physical unit l%32
     // and the logical unit is the physical one XOR the row's swizzle.
-    unsigned a_off[8], b_off[8];
-    int a_kcol[8], b_krow[8];
-    bool a_row_ok[8], b_col_ok[8];
+    unsigned a_off[LOADS], b_off[LOADS];
+    int a_kcol[LOADS], b_krow[LOADS];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int r = 64 * wid + 8 * j + (lane >> 3);
+    for (int j = 0; j < LOADS; ++j) {
+        const int r = 32 * wid + 8 * j + (lane >> 3);
         const int u = (lane & 7) ^ ((r >> 1) & 7);
-        a_row_ok[j] = (m0 + r) < M;
         a_kcol[j] = u * 8;
-        a_off[j] = (unsigned)(r * lda + u * 8) * 2u;
-        const int kr = 16 * wid + 2 * j + (lane >> 5);
+        a_off[j] = (m0 + r) < M ? (unsigned)(r * lda + u * 8) * 2u : OOB;
+        const int kr = 8 * wid + 2 * j + (lane >> 5);
         const int ub = (lane & 31) ^ ((kr & 3) << 2);
-        b_col_ok[j] = (n0 + ub * 8) < N;
         b_krow[j] = kr;
-        b_off[j] = (unsigned)(kr * ldb + ub * 8) * 2u;
+        b_off[j] = (n0 + ub * 8) < N ? (unsigned)(kr * ldb + ub * 8) * 2u : OOB;
     }
-    // Lanes past M, N or K fetch nothing and the DMA writes zeros for them, so
-    // ragged tails (and a tile index past the last one) need no branch.
     auto dma_tile = [&](int k0, char* stage) {
-        const __amdgpu_buffer_rsrc_t ar = make_rsrc(a_tile + k0);
-        const __amdgpu_buffer_rsrc_t br = make_rsrc(b_tile + (int64_t)k0 * ldb);
-        char* sa = stage + wid * 8192;
-        char* sb = stage + A_BYTES + wid * 8192;
+        // a tile past the last one gets an empty range: all loads write zeros
+        const int nrec = k0 < K ? 0x7ffffff0 : 0;
+        const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<__bf16*>(a_tile + k0), (short)0, nrec, 0x00020000);
+        const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<__bf16*>(b_tile + (int64_t)k0 * ldb), (short)0, nrec, 0x00020000);
+        char* sa = stage + wid * 4096;
+        char* sb = stage + A_BYTES + wid * 4096;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const bool ok = a_row_ok[j] && (k0 + a_kcol[j]) < K;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, LDS_PTR(void, sa + j * 1024), 16,
-                                                     ok ? a_off[j] : OOB, 0, 0, 0);
-        }
+        for (int j = 0; j < LOADS; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                ar, LDS_PTR(void, sa + j * 1024), 16,
+                (!CHECK_K || (k0 + a_kcol[j]) < K) ? a_off[j] : OOB, 0, 0, 0);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const bool ok = b_col_ok[j] && (k0 + b_krow[j]) < K;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(br, LDS_PTR(void, sb + j * 1024), 16,
-                                                     ok ? b_off[j] : OOB, 0, 0, 0);
-        }
+        for (int j = 0; j < LOADS; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                br, LDS_PTR(void, sb + j * 1024), 16,
+                (!CHECK_K || (k0 + b_krow[j]) < K) ? b_off[j] : OOB, 0, 0, 0);
     };
     const int nk = (K + BK - 1) / BK;
 
@@ -191,72 +194,68 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
     // 16-31 of K rows 0-7, groups 2/3 the same columns of K rows 8-15.
     const int g = lane >> 4, gi = lane & 15;
     const int b_row = (g >> 1) * 8 + (gi >> 2);       // + 16*kk + 4*half
-    unsigned b_rd[4];
+    unsigned b_rd[NJ];
 #pragma unroll
-    for (int nj = 0; nj < 4; ++nj) {
-        const int col = wn * 128 + nj * 32 + (g & 1) * 16 + 4 * (gi & 3);
+    for (int nj = 0; nj < NJ; ++nj) {
+        const int col = wn * 128 + wh * 64 + nj * 32 + (g & 1) * 16 + 4 * (gi & 3);
         const int unit = col >> 3;
         b_rd[nj] = A_BYTES + b_row * 512 + ((unit ^ ((b_row & 3) << 2)) << 4) + (col & 7) * 2;
     }
 
-    f32x16 acc[4][4];
+    f32x16 acc[4][NJ];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NJ; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    bf16x8 fa[2][4], fb[2][4];
-    auto load_frags = [&](bf16x8 (&a)[4], bf16x8 (&b)[4], const char* base, int kk) {
+    bf16x8 fa[2][4], fb[2][NJ];
+    auto load_frags = [&](bf16x8 (&a)[4], bf16x8 (&b)[NJ], const char* base, int kk) {
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) a[mi] = *(const bf16x8*)(base + a_rd[kk] + mi * 32 * 128);
 #pragma unroll
-        for (int nj = 0; nj < 4; ++nj) {
+        for (int nj = 0; nj < NJ; ++nj) {
             const char* p = base + b_rd[nj] + kk * 16 * 512;
             const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, p));
             const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, p + 4 * 512));
             b[nj] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
     };
-    auto mfmas = [&](const bf16x8 (&a)[4], const bf16x8 (&b)[4]) {
+    auto mfmas = [&](const bf16x8 (&a)[4], const bf16x8 (&b)[NJ]) {
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-            for (int nj = 0; nj < 4; ++nj)
+            for (int nj = 0; nj < NJ; ++nj)
                 acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[nj], acc[mi][nj], 0, 0, 0);
     };
 
     // ---- main loop: tile kt+1 is in flight into the other stage while tile kt
-    // is multiplied; k-step fragments are double-buffered in registers; the
-    // barrier that publishes tile kt+1 sits before the last k-step so that the
-    // next tile's first fragments (and tile kt+2's loads) issue under the last
-    // 16 MFMAs.  Scheduling groups pin the interleave: each k-step issues the
-    // next k-step's 12 LDS reads between its first MFMAs.
+    // is multiplied; the barrier that publishes tile kt+1 sits before the last
+    // k-step so that the next tile's first fragments (and tile kt+2's loads)
+    // issue under the last MFMAs.
     dma_tile(0, lds0);
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's DMA has landed
     __syncthreads();
     dma_tile(BK, lds1);
     load_frags(fa[0], fb[0], lds0, 0);
     __builtin_amdgcn_sched_barrier(0);
-    // one K tile: three k-steps on `cur`, publish `nxt`, refill `cur` with the
-    // tile after next, last k-step while the next tile's first fragments load
     auto tile = [&](const char* cur_c, char* cur, const char* nxt, int k_next2) {
         load_frags(fa[1], fb[1], cur_c, 1);
         mfmas(fa[0], fb[0]);
-        sched_kstep();
+        sched_kstep<0>();
         load_frags(fa[0], fb[0], cur_c, 2);
         mfmas(fa[1], fb[1]);
-        sched_kstep();
+        sched_kstep<0>();
         load_frags(fa[1], fb[1], cur_c, 3);
         mfmas(fa[0], fb[0]);
-        sched_kstep();
+        sched_kstep<0>();
         __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();                            // next tile visible; `cur` free
-        dma_tile(k_next2, cur);                     // all lanes masked past the last tile
+        dma_tile(k_next2, cur);                     // empty range past the last tile
         load_frags(fa[0], fb[0], nxt, 0);
         mfmas(fa[1], fb[1]);
-        sched_kstep_dma();
+        sched_kstep<2 * LOADS>();
     };
     int kt = 0;
     for (; kt + 1 < nk; kt += 2) {
@@ -264,32 +263,82 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
         tile(lds1, lds1, lds0, (kt + 3) * BK);
     }
     if (kt < nk) tile(lds0, lds0, lds1, (kt + 2) * BK);
-    // the (masked, zero-writing) loads issued for the tiles past the end must
-    // land before this workgroup's LDS is released
+    // the loads issued for the tiles past the end must land (they write zeros)
+    // before the stages are reused below
     __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
 
-    // ---- epilogue: lane holds column (lane & 31) and rows
-    // 8*(r >> 2) + 4*(lane >> 5) + (r & 3) of each 32x32 block.
-    const int row_base = m0 + wm * 128 + 4 * (lane >> 5);
-    const int col_base = n0 + wn * 128 + (lane & 31);
+    // ---- epilogue ------------------------------------------------------------
+    // Lane holds column (lane & 31) and rows 8*(r >> 2) + 4*(lane >> 5) + (r & 3)
+    // of each 32x32 block.  The tile is staged in LDS row-major with 16-byte
+    // units XOR-swizzled by bit 2 of the row (rows r and r+4, which one store
+    // instruction writes, then fall in different banks) and written back with
+    // one 16-byte store per lane per row segment.
+    const int lcol = wn * 128 + wh * 64 + (lane & 31);        // + 32*nj
+    float bv[NJ];
 #pragma unroll
-    for (int nj = 0; nj < 4; ++nj) {
-        const int col = col_base + nj * 32;
-        if (col >= N) continue;
-        const float bv = bias ? bias[col] : 0.0f;
+    for (int nj = 0; nj < NJ; ++nj)
+        bv[nj] = (bias && n0 + lcol + 32 * nj < N) ? bias[n0 + lcol + 32 * nj] : 0.0f;
+    auto value = [&](int mi, int nj, int r) {
+        const float v = acc[mi][nj][r] + bv[nj];
+        return GELU ? gelu(v) : v;
+    };
+    if constexpr (OUT_BF16) {
+        // rows 0-127 in lds0, 128-255 in lds1, each [128][512 B]
+        char* half = wm ? lds1 : lds0;
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
+        for (int nj = 0; nj < NJ; ++nj) {
+            const int lc = lcol + 32 * nj;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = row_base + mi * 32 + 8 * (r >> 2) + (r & 3);
-                if (row >= M) continue;
-                float v = acc[mi][nj][r] + bv;
-                if (GELU) v = gelu_erf(v);
-                if (OUT_BF16)
-                    ((__bf16*)C)[(int64_t)row * ldc + col] = (__bf16)v;
-                else
-                    ((float*)C)[(int64_t)row * ldc + col] = v;
+            for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int lr = mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                    *(__bf16*)(half + lr * 512 + (((lc >> 3) ^ (((lr >> 2) & 1) << 2)) << 4) +
+                               (lc & 7) * 2) = (__bf16)value(mi, nj, r);
+                }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 8192 / NTHREADS; ++i) {
+            const int idx = i * NTHREADS + tid;
+            const int row = idx >> 5, unit = idx & 31, lr = row & 127;
+            const char* src = (row < 128 ? lds0 : lds1) + lr * 512 +
+                              ((unit ^ (((lr >> 2) & 1) << 2)) << 4);
+            const int grow = m0 + row, gcol = n0 + unit * 8;
+            if (grow < M && gcol < N)
+                *(bf16x8*)((__bf16*)C + (int64_t)grow * ldc + gcol) = *(const bf16x8*)src;
+        }
+    } else {
+        // two passes of 64 rows per wave (mi = 2p, 2p+1): staged row q of wave
+        // row-block wm is local row 64*wm + q, [128][1024 B] over lds0 | lds1
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            char* half = wm ? lds1 : lds0;
+#pragma unroll
+            for (int nj = 0; nj < NJ; ++nj) {
+                const int lc = lcol + 32 * nj;
+#pragma unroll
+                for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int q = m2 * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                        *(float*)(half + q * 1024 + (((lc >> 2) ^ (((q >> 2) & 1) << 3)) << 4) +
+                                  (lc & 3) * 4) = value(2 * p + m2, nj, r);
+                    }
             }
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < 8192 / NTHREADS; ++i) {
+                const int idx = i * NTHREADS + tid;
+                const int lrow = idx >> 6, unit = idx & 63, q = lrow & 63;
+                const char* src = (lrow < 64 ? lds0 : lds1) + q * 1024 +
+                                  ((unit ^ (((q >> 2) & 1) << 3)) << 4);
+                const int grow = m0 + (lrow >> 6) * 128 + 64 * p + q, gcol = n0 + unit * 4;
+                if (grow < M && gcol < N)
+                    *(f32x4*)((float*)C + (int64_t)grow * ldc + gcol) = *(const f32x4*)src;
+            }
+            if (p == 0) __syncthreads();
         }
     }
 }
@@ -305,18 +354,14 @@ hipError_t gemm_bf16(const void* A, int64_t lda, const void* B, int64_t ldb,
     const dim3 grid(tiles_m * tiles_n), block(NTHREADS);
     const __bf16* a = (const __bf16*)A;
     const __bf16* b = (const __bf16*)B;
-    if (out_bf16 && gelu)
-        hipLaunchKernelGGL((gemm_bf16_kernel<true, true>), grid, block, 0, stream,
-                           a, lda, b, ldb, bias, C, ldc, (int)M, (int)N, (int)K, tiles_m, tiles_n);
-    else if (out_bf16)
-        hipLaunchKernelGGL((gemm_bf16_kernel<true, false>), grid, block, 0, stream,
-                           a, lda, b, ldb, bias, C, ldc, (int)M, (int)N, (int)K, tiles_m, tiles_n);
-    else if (gelu)
-        hipLaunchKernelGGL((gemm_bf16_kernel<false, true>), grid, block, 0, stream,
-                           a, lda, b, ldb, bias, C, ldc, (int)M, (int)N, (int)K, tiles_m, tiles_n);
-    else
-        hipLaunchKernelGGL((gemm_bf16_kernel<false, false>), grid, block, 0, stream,
-                           a, lda, b, ldb, bias, C, ldc, (int)M, (int)N, (int)K, tiles_m, tiles_n);
+    const bool ck = (K % BK) != 0;
+#define TP_GEMM(OB, GL, CK) hipLaunchKernelGGL((gemm_bf16_kernel<OB, GL, CK>), grid, block, 0, \
+        stream, a, lda, b, ldb, bias, C, ldc, (int)M, (int)N, (int)K, tiles_m, tiles_n)
+    if (out_bf16 && gelu)  { if (ck) TP_GEMM(true, true, true);   else TP_GEMM(true, true, false); }
+    else if (out_bf16)     { if (ck) TP_GEMM(true, false, true);  else TP_GEMM(true, false, false); }
+    else if (gelu)         { if (ck) TP_GEMM(false, true, true);  else TP_GEMM(false, true, false); }
+    else                   { if (ck) TP_GEMM(false, false, true); else TP_GEMM(false, false, false); }
+#undef TP_GEMM
     return hipGetLastError();
 }
 
