@@ -6,14 +6,16 @@ input already resident in HBM.  The default workload is the full pre-LN block
 at the 175B layer shape (h=12288, 96 heads of 128, F=49152, 8 sequences of
 2048 tokens) with all 8 tensor-parallel ranks' shares run in turn on this GPU
 (tp_block_shard: LayerNorm, per-rank QKV projection, causal attention, W_o
-partial, partial sum + residual, LayerNorm, per-rank MLP shard, partial sum +
-residual).  Throughput is matrix TFLOP/s of the whole step (ranks run one
-after another, so this is also the per-shard rate).
+partial, partial sum + residual fused with the second LayerNorm, per-rank MLP
+shard, partial sum + residual; each step one launch over all ranks).
+Throughput is matrix TFLOP/s of the whole step; all ranks' shares run on this
+one GPU, so this is also the per-shard rate.
 
 Besides the one JSON line the run reports, in the same line:
   roofline      the dominant kernel (the column-parallel GEMM with the fused
-                GeLU epilogue, at its in-block shape) timed per launch with
-                HIP events on the stream it runs on, against the bf16 MFMA peak;
+                GeLU epilogue, launched as the step launches it: for the block,
+                one grouped launch over all 8 ranks) timed per launch with HIP
+                events on the stream it runs on, against the bf16 MFMA peak;
   cpu_baseline  the fp64 oracle timed on the host on a bounded sample of the
                 same workload.
 
@@ -90,6 +92,40 @@ def blas_threads():
         return 1
 
 
+def dominant_operands_cpu(w, wl):
+    """Host copies of the dominant kernel's operands: the activations and the
+    weight(s) of the column-parallel product the step spends the most time in."""
+    if w.kind == "block":
+        return wl.block_input(w), [wl.block_rank_weights(w, r)[2] for r in range(w.P)]
+    if w.kind == "mlp":
+        X, A, _ = wl.mlp_inputs(w)
+        return X, [A]
+    X, Wqkv, _ = wl.attn_inputs(w)
+    return X, [Wqkv]
+
+
+def dominant_kernel(w, tts, torch, X, Ws, dev):
+    """(launch, algorithmic FLOPs per launch, name) of the step's dominant
+    kernel, launched exactly as the step launches it: for the block, the
+    column-parallel GEMM with the GeLU epilogue of all P ranks in one grouped
+    launch; for the MLP shard its GeLU GEMM; for the attention shard its QKV
+    projection."""
+    M, K = X.shape
+    N = Ws[0].shape[1]
+    gelu = w.kind != "attn"
+    outs = [torch.empty(M, N, dtype=torch.bfloat16, device=dev) for _ in Ws]
+    if len(Ws) > 1:
+        def launch():
+            tts.tp_linear_batched([X] * len(Ws), Ws, gelu=gelu, outs=outs)
+    else:
+        def launch():
+            tts.tp_linear(X, Ws[0], gelu=gelu, out=outs[0])
+    name = "gemm_bf16_kernel<bf16 out, %s> %s[%dx%d]x[%dx%d]" % (
+        "GeLU" if gelu else "no epilogue",
+        ("grouped over %d ranks, each " % len(Ws)) if len(Ws) > 1 else "", M, K, K, N)
+    return launch, 2 * M * N * K * len(Ws), name
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -129,22 +165,16 @@ def main():
         return
 
     if args.mode == "kernel":
-        # only the dominant kernel's operands: the token activations and rank
-        # 0's column-parallel weight, at the shape the step uses
-        if w.kind == "block":
-            X_cpu = wl.block_input(w)
-            A_cpu = wl.block_rank_weights(w, 0)[2]
-        elif w.kind == "mlp":
-            X_cpu, A_cpu, _ = wl.mlp_inputs(w)
-        else:
-            X_cpu, A_cpu, _ = wl.attn_inputs(w)
-        X_k, A_k = X_cpu.to(dev), A_cpu.to(dev)
-        y_k = torch.empty(X_k.shape[0], A_k.shape[1], dtype=torch.bfloat16, device=dev)
+        # only the dominant kernel's operands, at the shape the step uses
+        X_cpu, W_cpu = dominant_operands_cpu(w, wl)
+        X_k = X_cpu.to(dev)
+        W_k = [t.to(dev) for t in W_cpu]
+        del X_cpu, W_cpu
+        kernel, kern_flops, kern_name = dominant_kernel(w, tts, torch, X_k, W_k, dev)
         for _ in range(args.warmup + args.steps):
-            tts.tp_linear(X_k, A_k, gelu=True, out=y_k)
+            kernel()
         torch.cuda.synchronize()
-        log(f"kernel mode: {args.warmup + args.steps} launches of the GeLU GEMM "
-            f"[{X_k.shape[0]}x{X_k.shape[1]}]x[{A_k.shape[0]}x{A_k.shape[1]}] done")
+        log(f"kernel mode: {args.warmup + args.steps} launches of {kern_name} done")
         return
 
     # ---------------------------------------------------------------- inputs
@@ -165,7 +195,7 @@ def main():
 
         def step():
             tts.tp_block_shard(x, Wqkv, Wo, A, B, w.b, w.s, w.H, w.d, out=out, ws=ws)
-        X_k, A_k = x, A[0]
+        X_k, W_k = x, A
     elif w.kind == "mlp":
         X_cpu, A_cpu, B_cpu = wl.mlp_inputs(w)
         x, A0, B0 = X_cpu.to(dev), A_cpu.to(dev), B_cpu.to(dev)
@@ -175,7 +205,7 @@ def main():
 
         def step():
             tts.tp_mlp_shard(x, A0, B0, out=out, ws=ws)
-        X_k, A_k = x, A0
+        X_k, W_k = x, [A0]
     else:
         X_cpu, Wqkv_cpu, Wo_cpu = wl.attn_inputs(w)
         x, Wqkv0, Wo0 = X_cpu.to(dev), Wqkv_cpu.to(dev), Wo_cpu.to(dev)
@@ -187,16 +217,11 @@ def main():
 
         def step():
             tts.tp_attn_shard(x, Wqkv0, Wo0, w.b, w.s, w.Hl, w.d, True, out=out, ws=ws)
-        X_k, A_k = x, Wqkv0
+        X_k, W_k = x, [Wqkv0]
     torch.cuda.synchronize()
     log(f"inputs ready in {time.time() - t0:.1f} s")
 
-    # dominant kernel: column GEMM + fused GeLU, bf16 out, at [M,h] x [h,f]
-    kf = A_k.shape[1]
-    y_k = torch.empty(M, kf, dtype=torch.bfloat16, device=dev)
-
-    def kernel():
-        tts.tp_linear(X_k, A_k, gelu=True, out=y_k)
+    kernel, kern_flops, kern_name = dominant_kernel(w, tts, torch, X_k, W_k, dev)
 
     # ---------------------------------------------------------------- timing
     log(f"warmup {args.warmup} step(s)")
@@ -219,35 +244,41 @@ def main():
     log(f"{ms:.3f} ms/step, {tflops:.1f} TFLOP/s (wall {wall:.2f} s)")
 
     kern_ms, kern_all = event_time(kernel, max(args.steps, 5), stream)
-    kern_flops = 2 * M * h * kf
     kern_tflops = kern_flops / (kern_ms * 1e-3) / 1e12
     traffic = measured_traffic()
     log(f"dominant kernel: {kern_ms:.3f} ms/launch, {kern_tflops:.1f} TFLOP/s")
 
     components = {}
     if w.kind == "block":
+        P, HD = w.P, w.Hl * w.d
         xn = torch.empty(M, h, dtype=torch.bfloat16, device=dev)
-        part = torch.empty(M, h, dtype=torch.float32, device=dev)
-        parts = torch.empty(w.P, M, h, dtype=torch.float32, device=dev)
-        aws = torch.empty(tts.tp_attn_shard_workspace(w.b, w.s, w.Hl, w.d), dtype=torch.uint8,
-                          device=dev)
-        mws = torch.empty(tts.tp_mlp_shard_workspace(M, f), dtype=torch.uint8, device=dev)
+        x1 = torch.empty(M, h, dtype=torch.float32, device=dev)
+        parts = torch.empty(P, M, h, dtype=torch.float32, device=dev)
+        qkv_all = torch.empty(P * M, 3 * HD, dtype=torch.bfloat16, device=dev)
+        o_all = torch.empty(P * M, HD, dtype=torch.bfloat16, device=dev)
+        y_all = torch.empty(P * M, f, dtype=torch.bfloat16, device=dev)
+        qkv_r = [qkv_all[r * M:(r + 1) * M] for r in range(P)]
+        o_r = [o_all[r * M:(r + 1) * M] for r in range(P)]
+        y_r = [y_all[r * M:(r + 1) * M] for r in range(P)]
         att = w.attn_flops_rank()
-        qkv_buf = torch.empty(M, 3 * w.Hl * w.d, dtype=torch.bfloat16, device=dev)
-        o_buf = torch.empty(M, w.Hl * w.d, dtype=torch.bfloat16, device=dev)
+        # the launches tp_block_shard makes, one by one (all ranks per launch);
+        # every rank's Q|K|V rows follow the previous rank's, so the attention
+        # of all ranks is the attention of P*b sequences
         items = {
             "layernorm": (lambda: tts.tp_layernorm(x, out=xn), None, 2 * M * h * 2),
-            "attn_shard_rank": (lambda: tts.tp_attn_shard(x, Wqkv[0], Wo[0], w.b, w.s, w.Hl,
-                                                          w.d, True, out=part, ws=aws),
-                                att["total"], None),
-            "qkv_gemm": (lambda: tts.tp_linear(x, Wqkv[0], out=qkv_buf), att["qkv"], None),
-            "attention_core": (lambda: tts.tp_attention_core(qkv_buf, w.b, w.s, w.Hl, w.d, True,
-                                                             out=o_buf), att["core"], None),
-            "wo_gemm": (lambda: tts.tp_linear(o_buf, Wo[0], out=part), att["wo"], None),
-            "mlp_shard_rank": (lambda: tts.tp_mlp_shard(xn, A[0], B[0], out=part, ws=mws),
-                               w.mlp_flops_rank(), None),
-            "partial_sum": (lambda: tts.tp_partial_sum(parts, None, x, out=part), None,
-                            (w.P * 4 + 2 + 4) * M * h),
+            "qkv_gemm_all_ranks": (lambda: tts.tp_linear_batched([x] * P, Wqkv, outs=qkv_r),
+                                   P * att["qkv"], None),
+            "attention_core_all_ranks": (lambda: tts.tp_attention_core(
+                qkv_all, P * w.b, w.s, w.Hl, w.d, True, out=o_all), P * att["core"], None),
+            "wo_gemm_all_ranks": (lambda: tts.tp_linear_batched(o_r, Wo, outs=list(parts)),
+                                  P * att["wo"], None),
+            "mlp_gelu_gemm_all_ranks": (lambda: tts.tp_linear_batched([xn] * P, A, gelu=True,
+                                                                      outs=y_r),
+                                        P * w.mlp_flops_rank() // 2, None),
+            "mlp_row_gemm_all_ranks": (lambda: tts.tp_linear_batched(y_r, B, outs=list(parts)),
+                                       P * w.mlp_flops_rank() // 2, None),
+            "partial_sum_residual": (lambda: tts.tp_partial_sum(parts, None, x1, out=x1), None,
+                                     (P * 4 + 4 + 4) * M * h),
         }
         for name, (fn, fl, by) in items.items():
             fn()
@@ -261,6 +292,7 @@ def main():
                 c["pct_hbm"] = round(100 * by / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 1)
             components[name] = c
             log(f"component {name}: {c}")
+        del qkv_all, o_all, y_all, parts
 
     # ---------------------------------------------------------------- oracle
     cpu = None
@@ -286,7 +318,7 @@ def main():
                    "ranks_emulated": w.P if w.all_ranks else 1, "flops_per_step": flops,
                    "parallelism": "tp%d emulated on 1 GPU" % w.P},
         "roofline": {
-            "kernel": "gemm_bf16_kernel<bf16 out, GeLU> [%dx%d]x[%dx%d]" % (M, h, h, kf),
+            "kernel": kern_name,
             "bound": "mfma",
             "achieved": round(kern_tflops, 1),
             "peak": PEAK_BF16_TFLOPS,

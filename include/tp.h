@@ -17,7 +17,8 @@
  *    position t = m % s of sequence m / s.
  *  - Every tensor pointer is a DEVICE pointer (hipMalloc / PyTorch memory)
  *    owned by the caller, 16-byte aligned.  Host pointers are only the arrays
- *    of per-rank device pointers taken by tp_block_shard.
+ *    of per-rank device pointers taken by tp_block_shard and
+ *    tp_linear_batched.
  *  - The library never allocates, frees or synchronises.  All work is
  *    enqueued asynchronously on `stream` (a hipStream_t; NULL = the null
  *    stream); outputs are ready when that stream reaches this point.
@@ -118,11 +119,15 @@ tp_status tp_partial_sum(void* Z, int out, const void* partials, int part, int P
 
 /* ------------------------------------------------------------------------
  * tp_block_shard -- a whole pre-LN Transformer block with all P ranks'
- * shares emulated one after another on this GPU ([PyTorch TP tutorial] 3.3):
+ * shares emulated on this GPU ([PyTorch TP tutorial] 3.3):
  *     x1  = x  + sum_r Attn_r(LN1(x))       (the attention all-reduce)
  *     out = x1 + sum_r MLP_r(LN2(x1))       (the MLP all-reduce)
  * with Attn_r and MLP_r the tp_attn_shard / tp_mlp_shard shares of rank r
  * (H_l = H/P heads, f = F/P columns of A), causal attention, no biases.
+ * Each step runs as one launch over all ranks (the ranks' products have one
+ * shape; each rank still uses only its own slices and writes its own f32
+ * partial), and the sum over ranks is taken in ascending rank order, f32,
+ * then the residual; LN2 is fused into the first sum.
  *   x      [b·s, h] bf16           out  [b·s, h] dtype `out`
  *   x1     [b·s, h] f32 or NULL    (if given, receives the residual stream
  *                                   after attention)
@@ -163,6 +168,20 @@ tp_status tp_linear(const void* X, int64_t ldx, const void* W, int64_t ldw,
                     const void* bias, void* C, int64_t ldc,
                     int64_t M, int64_t N, int64_t K, int in, int out, int epilogue,
                     void* stream);
+
+/* tp_linear_batched -- `count` independent products of one shape in one
+ * launch: C[g] = epi(X[g]·W[g] + bias[g]) for g = 0 .. count-1, each as in
+ * tp_linear.  X, W, C (and bias, which may be NULL as a whole or per entry)
+ * are HOST arrays of `count` device pointers; a pointer may repeat (e.g. the
+ * same X for every rank's column-parallel product).  This is how one GPU runs
+ * the identical per-rank products of several emulated tensor-parallel ranks
+ * ([Megatron explainer] §2.1, §3.2: every rank applies the same operation to
+ * its own slice) without a tail per rank.  bf16 inputs run as one grouped
+ * MFMA launch per 16 products; f32 inputs run one product after another. */
+tp_status tp_linear_batched(const void* const* X, int64_t ldx, const void* const* W,
+                            int64_t ldw, const void* const* bias, void* const* C, int64_t ldc,
+                            int count, int64_t M, int64_t N, int64_t K, int in, int out,
+                            int epilogue, void* stream);
 
 /* tp_attention_core -- per (sequence, local head) softmax(Q·K^T/sqrt d)·V
  * ([Megatron explainer] §3.1) on projections already in memory.

@@ -157,3 +157,20 @@ def test_python_binding_raises_valueerror_on_shape():
         tts._check(_lib.TP_ERR_LAUNCH, "x")
     with pytest.raises(ValueError):
         tts._dev(torch.zeros(2), "cpu tensor")
+
+
+def test_linear_batched_rejects():
+    L = tts.lib()
+    two = (ctypes.c_void_p * 2)(FAKE.value, FAKE.value)
+    hole = (ctypes.c_void_p * 2)(FAKE.value, None)
+    odd = (ctypes.c_void_p * 2)(FAKE.value, FAKE_ODD.value)
+    call = lambda X=two, W=two, C=two, count=2, K=16, epi=0: L.tp_linear_batched(
+        X, K, W, 8, None, C, 8, count, 4, 8, K, _lib.TP_BF16, _lib.TP_F32, epi, None)
+    assert call(count=0) == _lib.TP_ERR_SHAPE
+    assert call(W=hole) == _lib.TP_ERR_NULL
+    assert call(C=hole) == _lib.TP_ERR_NULL
+    assert call(K=12) == _lib.TP_ERR_SHAPE          # bf16 needs K % 8 == 0
+    assert call(epi=5) == _lib.TP_ERR_DTYPE
+    assert call(X=odd) == _lib.TP_ERR_ALIGN
+    assert L.tp_linear_batched(None, 16, two, 8, None, two, 8, 2, 4, 8, 16, 1, 0, 0, None) \
+        == _lib.TP_ERR_NULL

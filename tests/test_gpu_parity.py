@@ -66,6 +66,29 @@ def test_linear_f32(M, N, K):
     assert_f32(C, oracle.gelu(oracle.matmul(X, W, bias)))
 
 
+@pytest.mark.parametrize("count,M,N,K,gelu", [(3, 300, 264, 200, True), (8, 256, 256, 64, False),
+                                              (2, 1, 8, 8, False), (17, 40, 520, 96, True)])
+def test_linear_batched(count, M, N, K, gelu):
+    """Grouped launches: every group g against the oracle's X[g]·W[g] (+bias),
+    including a repeated X, a single-tile shape (fewer tiles than XCDs) and
+    more groups than one launch takes."""
+    banner(f"linear batched count={count} M={M} N={N} K={K} gelu={gelu}")
+    Xs = [gen((M, K), 1.0, 70 + g, "x") for g in range(count)]
+    Xs[-1] = Xs[0]                                  # a shared activation
+    Ws = [gen((K, N), 1 / math.sqrt(K), 70 + g, "A") for g in range(count)]
+    bs = [gen((N,), 0.3, 70 + g, "bias", torch.float32) if g % 2 else None for g in range(count)]
+    outs = tts.tp_linear_batched([X.to(DEV) for X in Xs], [W.to(DEV) for W in Ws],
+                                 [b.to(DEV) if b is not None else None for b in bs], gelu=gelu,
+                                 out_dtype=torch.bfloat16 if gelu else torch.float32)
+    torch.cuda.synchronize()
+    for g in range(count):
+        ref = oracle.matmul(Xs[g], Ws[g], bs[g])
+        if gelu:
+            assert_bf16(outs[g], oracle.gelu(ref))
+        else:
+            assert_f32(outs[g], ref, bar=1e-4)
+
+
 def test_linear_deterministic():
     X = gen((700, 512), 1.0, 14, "x").to(DEV)
     W = gen((512, 640), 1 / math.sqrt(512), 14, "A").to(DEV)
@@ -125,7 +148,7 @@ def test_mlp_bf16_small(M, h, f, bias):
 
 
 # ------------------------------------------------------------------ partial sum
-@pytest.mark.parametrize("P,M,h", [(8, 33, 520), (1, 5, 4), (3, 1000, 64)])
+@pytest.mark.parametrize("P,M,h", [(8, 33, 520), (1, 5, 4), (3, 1000, 64), (2, 3, 16392)])
 def test_partial_sum_f32(P, M, h):
     banner(f"partial sum f32 P={P} M={M} h={h}")
     parts = gen((P, M, h), 1.0, 31, "partials", torch.float32)

@@ -21,7 +21,7 @@ from ._lib import TP_BF16, TP_EPI_GELU, TP_EPI_NONE, TP_F32
 __all__ = [
     "TpError", "tp_abi_version", "tp_mlp_shard", "tp_mlp_shard_workspace", "tp_attn_shard",
     "tp_attn_shard_workspace", "tp_partial_sum", "tp_block_shard", "tp_block_shard_workspace",
-    "tp_linear", "tp_attention_core", "tp_layernorm", "lib",
+    "tp_linear", "tp_linear_batched", "tp_attention_core", "tp_layernorm", "lib",
 ]
 
 
@@ -183,6 +183,31 @@ def tp_linear(X, W, bias=None, *, gelu=False, out=None, out_dtype=torch.float32,
                                TP_EPI_GELU if gelu else TP_EPI_NONE, _stream(stream))
     _check(st, "tp_linear")
     return out
+
+
+def tp_linear_batched(Xs: Sequence, Ws: Sequence, biases=None, *, gelu=False, outs=None,
+                      out_dtype=torch.float32, stream=None):
+    """C[g] = epi(X[g]·W[g] + bias[g]) for every g in one grouped launch."""
+    count = len(Xs)
+    if len(Ws) != count or (outs is not None and len(outs) != count):
+        raise ValueError("Xs, Ws and outs must have the same length")
+    M, K = Xs[0].shape
+    N = Ws[0].shape[1]
+    for X, W in zip(Xs, Ws):
+        if tuple(X.shape) != (M, K) or tuple(W.shape) != (K, N) or X.dtype != Xs[0].dtype:
+            raise ValueError("all products must have the same shape and dtype")
+    if outs is None:
+        outs = [torch.empty(M, N, dtype=out_dtype, device=Xs[0].device) for _ in range(count)]
+    bias_arr = None
+    if biases is not None:
+        bias_arr = (ctypes.c_void_p * count)(
+            *[(_dev(bv, "bias").value if bv is not None else None) for bv in biases])
+    st = _lib.load().tp_linear_batched(
+        _ptr_array(Xs, "X"), K, _ptr_array(Ws, "W"), N, bias_arr, _ptr_array(outs, "out"), N,
+        count, M, N, K, _code(Xs[0].dtype), _code(outs[0].dtype),
+        TP_EPI_GELU if gelu else TP_EPI_NONE, _stream(stream))
+    _check(st, "tp_linear_batched")
+    return outs
 
 
 def tp_attention_core(qkv, b: int, s: int, H_l: int, d: int = 128, causal=True, *, out=None,

@@ -44,6 +44,9 @@ SIGNATURES = {
                               _i64, _vp]),
     "tp_linear": (_int, [_vp, _i64, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _int, _int, _int,
                          _vp]),
+    "tp_linear_batched": (_int, [ctypes.POINTER(_vp), _i64, ctypes.POINTER(_vp), _i64,
+                                 ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i64, _int, _i64, _i64,
+                                 _i64, _int, _int, _int, _vp]),
     "tp_attention_core": (_int, [_vp, _i64, _vp, _i64, _i64, _i64, _i64, _int, _vp]),
     "tp_layernorm": (_int, [_vp, _int, _vp, _vp, _vp, ctypes.c_float, _i64, _i64, _vp]),
 }

@@ -45,16 +45,22 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
 }
 
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
-    const __bf16* __restrict__ qkv, int64_t ld, __bf16* __restrict__ O, int64_t ldo,
-    int s, int Hl, int nqb, int n_bh, int causal, float scale_log2)
+    const __bf16* __restrict__ qkv, int64_t ld, int64_t qkv_rank_stride,
+    __bf16* __restrict__ O, int64_t ldo, int64_t o_rank_stride,
+    int s, int b, int Hl, int nqb, int n_bh, int causal, float scale_log2)
 {
     __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE_BYTES];
 
+    // (query block, rank, sequence, head): the heaviest query blocks of every
+    // (rank, sequence, head) first, so the launch ends on short causal rows
     const int id = blockIdx.x;
-    const int qb = nqb - 1 - id / n_bh;          // heaviest query blocks first
+    const int qb = nqb - 1 - id / n_bh;
     const int bh = id % n_bh;
-    const int beta = bh / Hl, head = bh % Hl;
+    const int rank = bh / (b * Hl), rem = bh % (b * Hl);
+    const int beta = rem / Hl, head = rem % Hl;
     const int q0 = qb * BQ;
+    qkv += rank * qkv_rank_stride;
+    O += rank * o_rank_stride;
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int l32 = lane & 31, hi = lane >> 5;
@@ -243,14 +249,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
 }  // namespace
 
 hipError_t attention_fwd(const void* qkv, int64_t ld_qkv, void* O,
-                         int64_t b, int64_t s, int64_t H_l, bool causal, hipStream_t stream)
+                         int64_t b, int64_t s, int64_t H_l, bool causal, hipStream_t stream,
+                         int ranks, int64_t qkv_rank_stride, int64_t o_rank_stride)
 {
     const int nqb = (int)((s + BQ - 1) / BQ);
-    const int n_bh = (int)(b * H_l);
+    const int n_bh = (int)(ranks * b * H_l);
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
     hipLaunchKernelGGL(attn_fwd_kernel, dim3(nqb * n_bh), dim3(256), 0, stream,
-                       (const __bf16*)qkv, ld_qkv, (__bf16*)O, H_l * D, (int)s, (int)H_l,
-                       nqb, n_bh, causal ? 1 : 0, scale_log2);
+                       (const __bf16*)qkv, ld_qkv, qkv_rank_stride, (__bf16*)O, H_l * D,
+                       o_rank_stride, (int)s, (int)b, (int)H_l, nqb, n_bh, causal ? 1 : 0,
+                       scale_log2);
     return hipGetLastError();
 }
 

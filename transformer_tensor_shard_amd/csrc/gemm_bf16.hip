@@ -95,14 +95,24 @@ __device__ __forceinline__ float gelu(float x) {
     return x * (x >= 0.0f ? 1.0f - h : h);
 }
 
-// Map a linear workgroup id to (tile_m, tile_n): first make the ids of one XCD
-// contiguous, then walk GROUP_M tile-rows at a time.
-__device__ __forceinline__ void tile_coords(int pid, int tiles_m, int tiles_n, int& tm, int& tn) {
+// Map a workgroup to (group g, tile_m, tile_n).  Workgroups are dealt
+// round-robin to the 8 XCDs (XCD = pid % 8), so each XCD executes its ids
+// local = pid / 8 in order.  Every group's tile grid is split into 8
+// contiguous ranges, one per XCD, and an XCD walks its range of group 0, then
+// of group 1, ...: all XCDs work on the same group (the same weight matrix)
+// at the same time and one group's tail overlaps the next group's head.
+// Inside a range, tiles walk the output GROUP_M tile-rows at a time.  Returns
+// false for the few padding workgroups of XCDs with one tile fewer per group.
+__device__ __forceinline__ bool tile_coords(int pid, int groups, int tiles_m, int tiles_n,
+                                            int& g, int& tm, int& tn) {
     const int ntiles = tiles_m * tiles_n;
     const int xcd = pid & 7, local = pid >> 3;
     const int per = ntiles >> 3, rem = ntiles & 7;
-    const int id = (xcd < rem) ? xcd * (per + 1) + local
-                               : rem * (per + 1) + (xcd - rem) * per + local;
+    const int cnt = per + (xcd < rem ? 1 : 0);         // this XCD's tiles per group
+    if (cnt == 0) return false;
+    g = local / cnt;
+    if (g >= groups) return false;
+    const int id = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + local % cnt;
     const int width = GROUP_M * tiles_n;
     const int group = id / width;
     const int first_m = group * GROUP_M;
@@ -110,12 +120,12 @@ __device__ __forceinline__ void tile_coords(int pid, int tiles_m, int tiles_n, i
     const int in_group = id - group * width;
     tm = first_m + in_group % gsize;
     tn = in_group / gsize;
+    return true;
 }
 
 template <bool OUT_BF16, bool GELU, bool CHECK_K>
 __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
-    const __bf16* __restrict__ A, int64_t lda, const __bf16* __restrict__ B, int64_t ldb,
-    const float* __restrict__ bias, void* __restrict__ C, int64_t ldc,
+    GemmBatch batch, int64_t lda, int64_t ldb, int64_t ldc,
     int M, int N, int K, int tiles_m, int tiles_n)
 {
     // Two stages as two separate LDS objects: every access below names its
@@ -124,9 +134,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
     __shared__ __attribute__((aligned(1024))) char lds0[STAGE_BYTES];
     __shared__ __attribute__((aligned(1024))) char lds1[STAGE_BYTES];
 
-    int tm, tn;
-    tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    int grp, tm, tn;
+    if (!tile_coords(blockIdx.x, batch.count, tiles_m, tiles_n, grp, tm, tn)) return;
     const int m0 = tm * BM, n0 = tn * BN;
+    const __bf16* __restrict__ A = batch.A[grp];
+    const __bf16* __restrict__ B = batch.B[grp];
+    const float* __restrict__ bias = batch.bias[grp];
+    void* __restrict__ C = batch.C[grp];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -345,24 +359,36 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
 
 }  // namespace
 
-hipError_t gemm_bf16(const void* A, int64_t lda, const void* B, int64_t ldb,
-                     const float* bias, void* C, int64_t ldc,
-                     int64_t M, int64_t N, int64_t K, bool out_bf16, bool gelu,
-                     hipStream_t stream)
+hipError_t gemm_bf16_batched(const GemmBatch& batch, int64_t lda, int64_t ldb, int64_t ldc,
+                             int64_t M, int64_t N, int64_t K, bool out_bf16, bool gelu,
+                             hipStream_t stream)
 {
     const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
-    const dim3 grid(tiles_m * tiles_n), block(NTHREADS);
-    const __bf16* a = (const __bf16*)A;
-    const __bf16* b = (const __bf16*)B;
+    const int per_xcd = (tiles_m * tiles_n + 7) / 8;
+    const dim3 grid(8 * per_xcd * batch.count), block(NTHREADS);
     const bool ck = (K % BK) != 0;
 #define TP_GEMM(OB, GL, CK) hipLaunchKernelGGL((gemm_bf16_kernel<OB, GL, CK>), grid, block, 0, \
-        stream, a, lda, b, ldb, bias, C, ldc, (int)M, (int)N, (int)K, tiles_m, tiles_n)
+        stream, batch, lda, ldb, ldc, (int)M, (int)N, (int)K, tiles_m, tiles_n)
     if (out_bf16 && gelu)  { if (ck) TP_GEMM(true, true, true);   else TP_GEMM(true, true, false); }
     else if (out_bf16)     { if (ck) TP_GEMM(true, false, true);  else TP_GEMM(true, false, false); }
     else if (gelu)         { if (ck) TP_GEMM(false, true, true);  else TP_GEMM(false, true, false); }
     else                   { if (ck) TP_GEMM(false, false, true); else TP_GEMM(false, false, false); }
 #undef TP_GEMM
     return hipGetLastError();
+}
+
+hipError_t gemm_bf16(const void* A, int64_t lda, const void* B, int64_t ldb,
+                     const float* bias, void* C, int64_t ldc,
+                     int64_t M, int64_t N, int64_t K, bool out_bf16, bool gelu,
+                     hipStream_t stream)
+{
+    GemmBatch b = {};
+    b.A[0] = (const __bf16*)A;
+    b.B[0] = (const __bf16*)B;
+    b.bias[0] = bias;
+    b.C[0] = C;
+    b.count = 1;
+    return gemm_bf16_batched(b, lda, ldb, ldc, M, N, K, out_bf16, gelu, stream);
 }
 
 }  // namespace tpk

@@ -9,6 +9,12 @@
 //   §1.1 / §2.1: Z = Z1 + Z2 + ...): a grid-stride streaming kernel, 16-byte
 //   loads of every rank's partial, f32 sum in ascending rank order, optional
 //   bias and residual, one 16-byte (f32) or 8-byte (bf16) store per 4 outputs.
+// * Row partial sum (the same sum, one 256-thread workgroup per row of length
+//   h <= 16384, the row held in registers as 16-byte vectors, every rank's
+//   row segment loaded before any add so each thread has a rank's loads in
+//   flight at once), optionally followed by the next sub-layer's LayerNorm of
+//   the summed row: x1 = residual + sum_r Z_r and LN(x1) in one pass over HBM,
+//   the pre-LN block's "x + attention(norm1(x))" feeding "norm2".
 #include "tp_kernels.h"
 
 namespace tpk {
@@ -119,6 +125,90 @@ __global__ __launch_bounds__(256) void partial_sum_kernel(
     }
 }
 
+// RES: 0 none, 1 f32, 2 bf16.  The summation order is the one of
+// partial_sum_kernel (ranks ascending, then bias, then residual), so both give
+// bit-identical sums.
+template <bool PART_BF16, int RES, bool OUT_BF16, bool LN>
+__global__ __launch_bounds__(256) void row_sum_kernel(
+    void* __restrict__ Z, const void* __restrict__ parts, int P, int64_t n4, int h,
+    const float* __restrict__ bias, const void* __restrict__ res,
+    __bf16* __restrict__ y, const float* __restrict__ gamma, const float* __restrict__ beta,
+    float eps)
+{
+    constexpr int MAXV = 16;                      // 16 x 256 x 4 = 16384 columns
+    __shared__ float red[4];
+    const int64_t row4 = (int64_t)blockIdx.x * (h / 4);
+    const int nv = h / 4;
+    f32x4 acc[MAXV];
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int r = 0; r < P; ++r) {
+        f32x4 t[MAXV];
+#pragma unroll
+        for (int i = 0; i < MAXV; ++i) {
+            const int c = threadIdx.x + 256 * i;
+            if (c < nv) {
+                const int64_t k = r * n4 + row4 + c;
+                if (PART_BF16) {
+                    const bf16x4 b = ((const bf16x4*)parts)[k];
+                    t[i] = f32x4{(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
+                } else {
+                    t[i] = __builtin_nontemporal_load((const f32x4*)parts + k);
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < MAXV; ++i)
+            if (threadIdx.x + 256 * i < nv) acc[i] += t[i];
+    }
+    float sum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+        const int c = threadIdx.x + 256 * i;
+        if (c >= nv) continue;
+        if (bias) acc[i] += *(const f32x4*)(bias + 4 * c);
+        if (RES == 1) acc[i] += ((const f32x4*)res)[row4 + c];
+        if (RES == 2) {
+            const bf16x4 b = ((const bf16x4*)res)[row4 + c];
+            acc[i] += f32x4{(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
+        }
+        if (OUT_BF16) {
+            bf16x4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = (__bf16)acc[i][e];
+            ((bf16x4*)Z)[row4 + c] = o;
+        } else {
+            ((f32x4*)Z)[row4 + c] = acc[i];
+        }
+        if (LN) sum += (acc[i][0] + acc[i][1]) + (acc[i][2] + acc[i][3]);
+    }
+    if (!LN) return;
+    // LayerNorm of the summed row (f32 statistics, population variance,
+    // two exact passes over the registers)
+    const float mean = block_sum(sum, red) / (float)h;
+    float q = 0.0f;
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i)
+        if (threadIdx.x + 256 * i < nv)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { const float d = acc[i][e] - mean; q += d * d; }
+    const float inv = rsqrtf(block_sum(q, red) / (float)h + eps);
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+        const int c = threadIdx.x + 256 * i;
+        if (c >= nv) continue;
+        bf16x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float v = (acc[i][e] - mean) * inv;
+            if (gamma) v *= gamma[4 * c + e];
+            if (beta) v += beta[4 * c + e];
+            o[e] = (__bf16)v;
+        }
+        ((bf16x4*)y)[row4 + c] = o;
+    }
+}
+
 template <bool PB, bool RB, bool OB>
 void launch_ps(void* Z, const void* parts, int P, int64_t n4, int h, const float* bias,
                const void* res, hipStream_t stream) {
@@ -158,6 +248,31 @@ hipError_t partial_sum(void* Z, bool out_bf16, const void* parts, bool parts_bf1
         else          { if (out_bf16) TP_PS(false, false, true); else TP_PS(false, false, false); }
     }
 #undef TP_PS
+    return hipGetLastError();
+}
+
+hipError_t row_sum(void* Z, bool out_bf16, const void* parts, bool parts_bf16, int P,
+                   int64_t M, int64_t h, const float* bias, const void* residual, bool res_bf16,
+                   void* ln_out, const float* gamma, const float* beta, float eps,
+                   hipStream_t stream)
+{
+    const int64_t n4 = M * h / 4;
+    const int res = residual ? (res_bf16 ? 2 : 1) : 0;
+    const dim3 grid((unsigned)M), block(256);
+    __bf16* y = (__bf16*)ln_out;
+#define TP_RS(PB, R, OB, L) hipLaunchKernelGGL((row_sum_kernel<PB, R, OB, L>), grid, block, 0, \
+        stream, Z, parts, P, n4, (int)h, bias, residual, y, gamma, beta, eps)
+#define TP_RS_RES(PB, OB, L) { if (res == 0) TP_RS(PB, 0, OB, L); \
+        else if (res == 1) TP_RS(PB, 1, OB, L); else TP_RS(PB, 2, OB, L); }
+    if (ln_out) {
+        if (parts_bf16) { if (out_bf16) TP_RS_RES(true, true, true) else TP_RS_RES(true, false, true) }
+        else            { if (out_bf16) TP_RS_RES(false, true, true) else TP_RS_RES(false, false, true) }
+    } else {
+        if (parts_bf16) { if (out_bf16) TP_RS_RES(true, true, false) else TP_RS_RES(true, false, false) }
+        else            { if (out_bf16) TP_RS_RES(false, true, false) else TP_RS_RES(false, false, false) }
+    }
+#undef TP_RS_RES
+#undef TP_RS
     return hipGetLastError();
 }
 

@@ -125,18 +125,46 @@ hipError_t run_attn(const void* X, const void* Wqkv, const void* Wo, void* Z, vo
 }
 
 // ---- block ----------------------------------------------------------------
-struct BlockWs { int64_t xn, parts, x1, scratch, total; };
+// The P emulated ranks' products have identical shapes, so each step of the
+// block runs as one grouped launch over all ranks (each tile still belongs to
+// one rank and uses only that rank's slice); every rank keeps its own
+// projections, attention output, activations and f32 partial in the
+// workspace, sized for HBM rather than folded early.
+struct BlockWs { int64_t xn, parts, x1, qkv, o, y, total; };
 BlockWs block_ws(int64_t b, int64_t s, int64_t h, int64_t H, int64_t d, int64_t F, int P) {
-    const int64_t M = b * s;
+    const int64_t M = b * s, Hl = H / P, f = F / P;
     BlockWs w;
     w.xn = 0;
     w.parts = align_up(M * h * 2);
     w.x1 = w.parts + align_up((int64_t)P * M * h * 4);
-    w.scratch = w.x1 + align_up(M * h * 4);
-    const int64_t a = attn_ws(b, s, H / P, d).total;
-    const int64_t m = mlp_ws(M, F / P, TP_BF16);
-    w.total = w.scratch + (a > m ? a : m);
+    const int64_t scratch = w.x1 + align_up(M * h * 4);
+    // attention scratch (all ranks' Q|K|V and O) and the MLP scratch (all
+    // ranks' GeLU(X·A_r)) are never live at the same time
+    w.qkv = scratch;
+    w.o = w.qkv + align_up((int64_t)P * M * 3 * Hl * d * 2);
+    w.y = scratch;
+    const int64_t attn_end = w.o + align_up((int64_t)P * M * Hl * d * 2);
+    const int64_t mlp_end = w.y + align_up((int64_t)P * M * f * 2);
+    w.total = attn_end > mlp_end ? attn_end : mlp_end;
     return w;
+}
+
+// C[r] = epi(A[r]·B[r]) for ranks r0 .. r0+n-1 in launches of up to kMaxBatch
+template <typename FA, typename FB, typename FC>
+hipError_t grouped(int P, FA a_of, FB b_of, FC c_of, int64_t lda, int64_t ldb, int64_t ldc,
+                   int64_t M, int64_t N, int64_t K, bool out_bf16, bool gelu, hipStream_t st) {
+    for (int r0 = 0; r0 < P; r0 += tpk::kMaxBatch) {
+        tpk::GemmBatch gb = {};
+        gb.count = P - r0 < tpk::kMaxBatch ? P - r0 : tpk::kMaxBatch;
+        for (int i = 0; i < gb.count; ++i) {
+            gb.A[i] = (const __bf16*)a_of(r0 + i);
+            gb.B[i] = (const __bf16*)b_of(r0 + i);
+            gb.C[i] = c_of(r0 + i);
+        }
+        const hipError_t e = tpk::gemm_bf16_batched(gb, lda, ldb, ldc, M, N, K, out_bf16, gelu, st);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace
@@ -164,6 +192,42 @@ TP_EXPORT tp_status tp_linear(const void* X, int64_t ldx, const void* W, int64_t
     if (s != TP_OK) return s;
     return launched(run_linear(X, ldx, W, ldw, bias, C, ldc, M, N, K, in, out,
                                epilogue == TP_EPI_GELU, as_stream(stream)));
+}
+
+TP_EXPORT tp_status tp_linear_batched(const void* const* X, int64_t ldx, const void* const* W,
+                                      int64_t ldw, const void* const* bias, void* const* C,
+                                      int64_t ldc, int count, int64_t M, int64_t N, int64_t K,
+                                      int in, int out, int epilogue, void* stream) {
+    if (!X || !W || !C) return TP_ERR_NULL;
+    if (count <= 0) return TP_ERR_SHAPE;
+    for (int g = 0; g < count; ++g) {
+        const tp_status s = check_linear(X[g], ldx, W[g], ldw, bias ? bias[g] : nullptr, C[g], ldc,
+                                         M, N, K, in, out, epilogue);
+        if (s != TP_OK) return s;
+    }
+    const hipStream_t st = as_stream(stream);
+    const bool gelu = epilogue == TP_EPI_GELU;
+    if (in != TP_BF16) {
+        for (int g = 0; g < count; ++g) {
+            const hipError_t e = run_linear(X[g], ldx, W[g], ldw, bias ? bias[g] : nullptr, C[g],
+                                            ldc, M, N, K, in, out, gelu, st);
+            if (e != hipSuccess) return TP_ERR_LAUNCH;
+        }
+        return TP_OK;
+    }
+    for (int g0 = 0; g0 < count; g0 += tpk::kMaxBatch) {
+        tpk::GemmBatch gb = {};
+        gb.count = count - g0 < tpk::kMaxBatch ? count - g0 : tpk::kMaxBatch;
+        for (int i = 0; i < gb.count; ++i) {
+            gb.A[i] = (const __bf16*)X[g0 + i];
+            gb.B[i] = (const __bf16*)W[g0 + i];
+            gb.bias[i] = bias ? (const float*)bias[g0 + i] : nullptr;
+            gb.C[i] = C[g0 + i];
+        }
+        if (tpk::gemm_bf16_batched(gb, ldx, ldw, ldc, M, N, K, out == TP_BF16, gelu, st))
+            return TP_ERR_LAUNCH;
+    }
+    return TP_OK;
 }
 
 TP_EXPORT size_t tp_mlp_shard_workspace(int64_t M, int64_t f, int in) {
@@ -235,6 +299,10 @@ TP_EXPORT tp_status tp_partial_sum(void* Z, int out, const void* partials, int p
     if (!aligned16(Z) || !aligned16(partials) || (bias && !aligned16(bias)) ||
         (residual && !aligned16(residual)))
         return TP_ERR_ALIGN;
+    if (h <= kMaxLnWidth && M <= kI32)   // one row per workgroup, row in registers
+        return launched(tpk::row_sum(Z, out == TP_BF16, partials, part == TP_BF16, P, M, h,
+                                     (const float*)bias, residual, residual && res == TP_BF16,
+                                     nullptr, nullptr, nullptr, 0.0f, as_stream(stream)));
     return launched(tpk::partial_sum(Z, out == TP_BF16, partials, part == TP_BF16, P, M, h,
                                      (const float*)bias, residual, residual && res == TP_BF16,
                                      as_stream(stream)));
@@ -259,8 +327,9 @@ TP_EXPORT tp_status tp_block_shard(const void* x, void* out, int out_dtype, void
     if (P <= 0 || H <= 0 || F <= 0 || H % P || F % P || h != H * d || !(eps > 0.0f))
         return TP_ERR_SHAPE;
     const int64_t M = b * s, Hl = H / P, f = F / P;
-    tp_status st = check_attn_shape(b, s, h, Hl, d);
-    if (st != TP_OK) return st;
+    tp_status stat = check_attn_shape(b, s, h, Hl, d);
+    if (stat != TP_OK) return stat;
+    if (((s + 127) / 128) * b * H > kI32) return TP_ERR_SHAPE;
     if (f % 8 || h > kMaxLnWidth || !gemm_bf16_fits(M, f, h, h, f) || !gemm_bf16_fits(M, h, f, f, h))
         return TP_ERR_SHAPE;
     for (int r = 0; r < P; ++r)
@@ -275,34 +344,47 @@ TP_EXPORT tp_status tp_block_shard(const void* x, void* out, int out_dtype, void
     if (!ws || ws_bytes < (size_t)w.total) return TP_ERR_WORKSPACE;
     if (!aligned16(ws)) return TP_ERR_ALIGN;
 
-    const hipStream_t st_ = as_stream(stream);
+    const hipStream_t st = as_stream(stream);
     char* base = (char*)ws;
-    void* xn = base + w.xn;
+    __bf16* xn = (__bf16*)(base + w.xn);
     float* parts = (float*)(base + w.parts);
     float* x1buf = x1 ? (float*)x1 : (float*)(base + w.x1);
-    void* scratch = base + w.scratch;
-    const int64_t n = M * h;
-    hipError_t e;
+    char* qkv = base + w.qkv;
+    char* O = base + w.o;
+    char* Y = base + w.y;
+    const int64_t n = M * h, HD = Hl * d;
+    const int64_t qkv_r = M * 3 * HD, o_r = M * HD, y_r = M * f;     // per-rank elements
 
     // x1 = x + sum_r Attn_r(LN1(x))
-    if ((e = tpk::layernorm(x, true, xn, (const float*)ln1_g, (const float*)ln1_b, eps, M, h, st_)))
+    if (tpk::layernorm(x, true, xn, (const float*)ln1_g, (const float*)ln1_b, eps, M, h, st))
         return TP_ERR_LAUNCH;
-    for (int r = 0; r < P; ++r)
-        if ((e = run_attn(xn, W_qkv[r], W_o[r], parts + r * n, scratch, b, s, h, Hl, d, true,
-                          TP_F32, st_)))
-            return TP_ERR_LAUNCH;
-    if ((e = tpk::partial_sum(x1buf, false, parts, false, P, M, h, nullptr, x, true, st_)))
+    // [Q|K|V]_r = LN1(x)·W_qkv_r for every rank (column-parallel, §3.2)
+    if (grouped(P, [&](int) { return (const void*)xn; }, [&](int r) { return W_qkv[r]; },
+                [&](int r) { return (void*)(qkv + r * qkv_r * 2); }, h, 3 * HD, 3 * HD,
+                M, 3 * HD, h, true, false, st))
         return TP_ERR_LAUNCH;
-    // out = x1 + sum_r MLP_r(LN2(x1))
-    if ((e = tpk::layernorm(x1buf, false, xn, (const float*)ln2_g, (const float*)ln2_b, eps, M, h,
-                            st_)))
+    // every rank's heads, causal (§3.1), one launch
+    if (tpk::attention_fwd(qkv, 3 * HD, O, b, s, Hl, true, st, P, qkv_r, o_r))
         return TP_ERR_LAUNCH;
-    for (int r = 0; r < P; ++r)
-        if ((e = run_mlp(xn, A[r], nullptr, B[r], parts + r * n, scratch, M, h, f, TP_BF16, TP_F32,
-                         st_)))
-            return TP_ERR_LAUNCH;
-    if ((e = tpk::partial_sum(out, out_dtype == TP_BF16, parts, false, P, M, h, nullptr, x1buf,
-                              false, st_)))
+    // Z_r = O_r·W_o_r, f32 partials (row-parallel, §3.2)
+    if (grouped(P, [&](int r) { return (const void*)(O + r * o_r * 2); },
+                [&](int r) { return W_o[r]; }, [&](int r) { return (void*)(parts + r * n); },
+                HD, h, h, M, h, HD, false, false, st))
+        return TP_ERR_LAUNCH;
+    // the all-reduce's sum + residual, fused with LN2 of the summed rows
+    if (tpk::row_sum(x1buf, false, parts, false, P, M, h, nullptr, x, true, xn,
+                     (const float*)ln2_g, (const float*)ln2_b, eps, st))
+        return TP_ERR_LAUNCH;
+    // out = x1 + sum_r MLP_r(LN2(x1)): Y'_r = GeLU(LN2(x1)·A_r), Z_r = Y'_r·B_r (§2.1)
+    if (grouped(P, [&](int) { return (const void*)xn; }, [&](int r) { return A[r]; },
+                [&](int r) { return (void*)(Y + r * y_r * 2); }, h, f, f, M, f, h, true, true, st))
+        return TP_ERR_LAUNCH;
+    if (grouped(P, [&](int r) { return (const void*)(Y + r * y_r * 2); },
+                [&](int r) { return B[r]; }, [&](int r) { return (void*)(parts + r * n); },
+                f, h, h, M, h, f, false, false, st))
+        return TP_ERR_LAUNCH;
+    if (tpk::row_sum(out, out_dtype == TP_BF16, parts, false, P, M, h, nullptr, x1buf, false,
+                     nullptr, nullptr, nullptr, 0.0f, st))
         return TP_ERR_LAUNCH;
     return TP_OK;
 }

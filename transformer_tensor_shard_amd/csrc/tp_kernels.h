@@ -6,6 +6,21 @@
 
 namespace tpk {
 
+// Up to kMaxBatch independent GEMMs of one shape, launched together: group g
+// computes C[g] = epi(A[g]·B[g] + bias[g]).  Used for the emulated ranks of a
+// block, whose per-rank products have identical shapes.
+constexpr int kMaxBatch = 16;
+struct GemmBatch {
+    const __bf16* A[kMaxBatch];
+    const __bf16* B[kMaxBatch];
+    const float* bias[kMaxBatch];
+    void* C[kMaxBatch];
+    int count;
+};
+hipError_t gemm_bf16_batched(const GemmBatch& batch, int64_t lda, int64_t ldb, int64_t ldc,
+                             int64_t M, int64_t N, int64_t K, bool out_bf16, bool gelu,
+                             hipStream_t stream);
+
 // C[M,N] = epi(A[M,K]·B[K,N] + bias) on bf16 inputs with the MFMA kernel.
 // Shapes and alignment are validated by the caller (tp_abi.cpp).
 hipError_t gemm_bf16(const void* A, int64_t lda, const void* B, int64_t ldb,
@@ -19,11 +34,13 @@ hipError_t gemm_f32(const float* A, int64_t lda, const float* B, int64_t ldb,
                     int64_t M, int64_t N, int64_t K, bool out_bf16, bool gelu,
                     hipStream_t stream);
 
-// Causal / full softmax(Q K^T / sqrt(d)) V for every (sequence, local head);
-// d == 128.  qkv is [b*s, ld_qkv] bf16, O is [b*s, H_l*128] bf16.
+// Causal / full softmax(Q K^T / sqrt(d)) V for every (rank, sequence, local
+// head); d == 128.  Rank r's qkv is [b*s, ld_qkv] bf16 at qkv + r*qkv_rank_stride,
+// its O is [b*s, H_l*128] bf16 at O + r*o_rank_stride (strides in elements).
 hipError_t attention_fwd(const void* qkv, int64_t ld_qkv, void* O,
                          int64_t b, int64_t s, int64_t H_l, bool causal,
-                         hipStream_t stream);
+                         hipStream_t stream, int ranks = 1, int64_t qkv_rank_stride = 0,
+                         int64_t o_rank_stride = 0);
 
 // y = LayerNorm(x) rows of length h, y in bf16.
 hipError_t layernorm(const void* x, bool x_bf16, void* y, const float* gamma,
@@ -34,5 +51,12 @@ hipError_t layernorm(const void* x, bool x_bf16, void* y, const float* gamma,
 hipError_t partial_sum(void* Z, bool out_bf16, const void* parts, bool parts_bf16, int P,
                        int64_t M, int64_t h, const float* bias,
                        const void* residual, bool res_bf16, hipStream_t stream);
+
+// The same sum computed one row per workgroup (h % 4 == 0, h <= 16384); if
+// ln_out is not NULL, also ln_out = LayerNorm(Z row) in bf16.
+hipError_t row_sum(void* Z, bool out_bf16, const void* parts, bool parts_bf16, int P,
+                   int64_t M, int64_t h, const float* bias, const void* residual, bool res_bf16,
+                   void* ln_out, const float* gamma, const float* beta, float eps,
+                   hipStream_t stream);
 
 }  // namespace tpk
