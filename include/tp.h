@@ -196,7 +196,7 @@ tp_status tp_attention_core(const void* qkv, int64_t ld_qkv, void* O,
 /* tp_layernorm -- y = (x - mean)/sqrt(var + eps)·gamma + beta over each row of
  * x [M,h] (population variance, f32 statistics), the block's nn.LayerNorm(h)
  * ([PyTorch TP tutorial] 3.3).  x in TP_F32 or TP_BF16; y is bf16 [M,h];
- * gamma/beta f32 [h] or NULL.  Needs h % 8 == 0. */
+ * gamma/beta f32 [h] or NULL.  Needs h % 8 == 0 and h <= 32768. */
 tp_status tp_layernorm(const void* x, int in, void* y, const void* gamma,
                        const void* beta, float eps, int64_t M, int64_t h, void* stream);
 

@@ -185,7 +185,8 @@ def test_partial_sum_mixed_dtypes_and_alias():
 # ------------------------------------------------------------------ LayerNorm
 @pytest.mark.parametrize("M,h,dtype,affine", [(64, 4096, torch.bfloat16, False),
                                               (37, 520, torch.float32, True),
-                                              (3, 12288, torch.float32, False)])
+                                              (3, 12288, torch.float32, False),
+                                              (5, 20000, torch.bfloat16, True)])
 def test_layernorm(M, h, dtype, affine):
     banner(f"layernorm M={M} h={h} {dtype} affine={affine}")
     x = gen((M, h), 2.0, 41, "x", dtype) + 0.5

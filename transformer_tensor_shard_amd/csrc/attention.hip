@@ -4,8 +4,9 @@
 // each rank runs whole heads locally, §3.2).
 //
 // Design (flash-style, scores never reach HBM):
-//  * one workgroup = 4 waves = 128 queries of one (sequence, head); grid order
-//    puts the longest causal rows first so the tail of the launch is short;
+//  * one workgroup = NW waves = 32*NW queries of one (sequence, head); all query
+//    blocks of a head run on one XCD side by side (their K/V is read from that
+//    XCD's L2), longest causal rows first so the tail of the launch is short;
 //  * keys/values stream through LDS in 64-key tiles, double-buffered, the next
 //    tile's global loads in flight during this tile's MFMAs;
 //  * each wave owns 32 queries and computes S^T = K·Q^T with MFMA 32x32x16
@@ -16,7 +17,9 @@
 //    the B operand of O^T += V^T·P^T (the row sum is taken over the same
 //    rounded values, so the weights applied to V sum exactly to one); the V^T operand comes from the
 //    row-major V tile via the gfx950 LDS transpose read (ds_read_b64_tr_b16);
-//  * exp uses exp2 with log2(e)/sqrt(d) folded into the score scale;
+//  * exp is the hardware exp2 with log2(e)/sqrt(d) folded into one FMA per
+//    score; the mask is applied only on tiles that reach the diagonal or the
+//    end, and the accumulator is rescaled only when a running max moved;
 //  * LDS tiles are XOR-swizzled in 16-byte units (64 banks, conflict-free for
 //    the 16-byte K reads and the transpose V reads);
 //  * the output block is staged through LDS and written with 16-byte stores.
@@ -32,9 +35,14 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
-constexpr int D = 128, BQ = 128, BKV = 64;
+#ifndef ATTN_WAVES
+#define ATTN_WAVES 4
+#endif
+constexpr int NW = ATTN_WAVES, NT = 64 * NW;   // waves and threads per workgroup
+constexpr int D = 128, BQ = 32 * NW, BKV = 64;
 constexpr int TILE_BYTES = BKV * D * 2;      // 16 KiB (64 rows x 256 B)
 constexpr int STAGE_BYTES = 2 * TILE_BYTES;  // K tile + V tile
 constexpr unsigned OOB = 0x80000000u;
@@ -44,18 +52,23 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
                                              0x7ffffff0, 0x00020000);
 }
 
-__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
+__global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(
     const __bf16* __restrict__ qkv, int64_t ld, int64_t qkv_rank_stride,
     __bf16* __restrict__ O, int64_t ldo, int64_t o_rank_stride,
     int s, int b, int Hl, int nqb, int n_bh, int causal, float scale_log2)
 {
     __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE_BYTES];
 
-    // (query block, rank, sequence, head): the heaviest query blocks of every
-    // (rank, sequence, head) first, so the launch ends on short causal rows
+    // Workgroups are dealt round-robin to the 8 XCDs.  All query blocks of one
+    // (rank, sequence, head) go to the same XCD back to back, heaviest causal
+    // block first, so they read that head's K/V from the XCD's L2 while the
+    // blocks run side by side; the (rank, sequence, head) pairs are dealt to
+    // the XCDs in turn.
     const int id = blockIdx.x;
-    const int qb = nqb - 1 - id / n_bh;
-    const int bh = id % n_bh;
+    const int xcd = id & 7, local = id >> 3;
+    const int bh = (local / nqb) * 8 + xcd;
+    if (bh >= n_bh) return;
+    const int qb = nqb - 1 - local % nqb;
     const int rank = bh / (b * Hl), rem = bh % (b * Hl);
     const int beta = rem / Hl, head = rem % Hl;
     const int q0 = qb * BQ;
@@ -81,20 +94,21 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     }
 
     // ---- K/V tile copy assignment: 64 rows x 16 units; thread owns unit
-    // (tid & 15) of rows (tid >> 4) + 16 i.
+    // (tid & 15) of rows (tid >> 4) + (NT/16) i.
+    constexpr int CP = 1024 / NT;            // 16-byte units per thread per tile
     const int c_unit = tid & 15, c_row0 = tid >> 4;
-    unsigned k_lds[4], v_lds[4];
+    unsigned k_lds[CP], v_lds[CP];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = c_row0 + 16 * i;
+    for (int i = 0; i < CP; ++i) {
+        const int r = c_row0 + (NT / 16) * i;
         k_lds[i] = r * 256 + ((c_unit ^ (r & 15)) << 4);
         v_lds[i] = TILE_BYTES + r * 256 + ((c_unit ^ ((r & 3) << 2)) << 4);
     }
-    u32x4 rk[4], rv[4];
+    u32x4 rk[CP], rv[CP];
     auto load_kv = [&](int kv0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = kv0 + c_row0 + 16 * i;
+        for (int i = 0; i < CP; ++i) {
+            const int r = kv0 + c_row0 + (NT / 16) * i;
             const bool ok = r < s;
             const unsigned base = (unsigned)((int64_t)r * ld + c_unit * 8) * 2u;
             rk[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, ok ? base + kcol * 2u : OOB, 0, 0);
@@ -104,7 +118,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     auto store_kv = [&](int stage) {
         char* b = lds + stage * STAGE_BYTES;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < CP; ++i) {
             *(u32x4*)(b + k_lds[i]) = rk[i];
             *(u32x4*)(b + v_lds[i]) = rv[i];
         }
@@ -163,42 +177,54 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
                     sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sacc[t], 0, 0, 0);
                 }
             }
-            // scale; mask where the tile reaches past the diagonal or the end
-            const bool need_mask = (causal && kv0 + BKV - 1 > qw_lo) || (kv0 + BKV > s);
+            // mask keys past the diagonal or the end (only tiles that reach
+            // them); the raw score -inf gives weight exactly 0 below
+            if ((causal && kv0 + BKV - 1 > qw_lo) || kv0 + BKV > s) {
+                const int lim = causal ? min(my_q, s - 1) : s - 1;
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = kv0 + 32 * t + 8 * (r >> 2) + 4 * hi + (r & 3);
+                        sacc[t][r] = key > lim ? -INFINITY : sacc[t][r];
+                    }
+            }
+            // online softmax in the log2 domain: the scale log2(e)/sqrt(d) > 0
+            // commutes with max, so p = 2^(s*scale - m) is one FMA and one exp
             float mloc = -INFINITY;
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float v = sacc[t][r] * scale_log2;
-                    if (need_mask) {
-                        const int key = kv0 + 32 * t + 8 * (r >> 2) + 4 * hi + (r & 3);
-                        if (key >= s || (causal && key > my_q)) v = -INFINITY;
-                    }
-                    sacc[t][r] = v;
-                    mloc = fmaxf(mloc, v);
-                }
-            mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+                for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sacc[t][r]);
+            mloc = fmaxf(mloc, __shfl_xor(mloc, 32)) * scale_log2;
             const float m_new = fmaxf(m_run, mloc);
             const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-            const float alpha = exp2f(m_run - m_use);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
             m_run = m_new;
+            // probabilities rounded to bf16 (the MFMA operand); the normaliser
+            // sums the same rounded weights, two at a time with a bf16 dot
             float lsum = 0.0f;
             bf16x8 pk[2][2];
+            const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    // the normaliser sums the rounded weights the MFMA applies
-                    const __bf16 pb = (__bf16)exp2f(sacc[t][r] - m_use);
-                    lsum += (float)pb;
-                    pk[t][r >> 3][r & 7] = pb;
+                for (int r = 0; r < 16; r += 2) {
+                    bf16x2 pb;
+                    pb[0] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[t][r], scale_log2, -m_use));
+                    pb[1] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[t][r + 1], scale_log2, -m_use));
+                    lsum = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, lsum, false);
+                    pk[t][r >> 3][r & 7] = pb[0];
+                    pk[t][r >> 3][(r & 7) + 1] = pb[1];
                 }
             l_run = l_run * alpha + lsum;
+            // rescale the accumulator only when some lane's running max moved
+            if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
-            for (int dt = 0; dt < 4; ++dt)
+                for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+                    for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+            }
             // O^T += V^T · P^T over the 4 k-steps of 16 keys
 #pragma unroll
             for (int t = 0; t < 2; ++t)
@@ -255,7 +281,8 @@ hipError_t attention_fwd(const void* qkv, int64_t ld_qkv, void* O,
     const int nqb = (int)((s + BQ - 1) / BQ);
     const int n_bh = (int)(ranks * b * H_l);
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
-    hipLaunchKernelGGL(attn_fwd_kernel, dim3(nqb * n_bh), dim3(256), 0, stream,
+    const int groups_per_xcd = (n_bh + 7) / 8;
+    hipLaunchKernelGGL(attn_fwd_kernel, dim3(8 * groups_per_xcd * nqb), dim3(NT), 0, stream,
                        (const __bf16*)qkv, ld_qkv, qkv_rank_stride, (__bf16*)O, H_l * D,
                        o_rank_stride, (int)s, (int)b, (int)H_l, nqb, n_bh, causal ? 1 : 0,
                        scale_log2);

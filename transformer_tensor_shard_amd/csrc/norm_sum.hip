@@ -1,8 +1,9 @@
 // HBM-bound steps of the path: LayerNorm and the partial sum.
 //
 // * LayerNorm (the pre-LN block's nn.LayerNorm(h), PyTorch tensor-parallel
-//   tutorial section 3.3): one 256-thread workgroup per row; the row is read
-//   once from HBM with 16-byte loads into LDS as f32, the mean and the
+//   tutorial section 3.3): rows up to 16384 wide run through the row-sum
+//   kernel below (row in registers); wider rows use one 256-thread workgroup
+//   per row; the row is read once from HBM with 16-byte loads into LDS as f32, the mean and the
 //   population variance are two exact passes over LDS (no E[x^2]-E[x]^2
 //   cancellation), and the bf16 result is written with 16-byte stores.
 // * Partial sum (the all-reduce's arithmetic on one GPU, "图解Transformer并行计算"
@@ -172,12 +173,12 @@ __global__ __launch_bounds__(256) void row_sum_kernel(
             const bf16x4 b = ((const bf16x4*)res)[row4 + c];
             acc[i] += f32x4{(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
         }
-        if (OUT_BF16) {
+        if (Z && OUT_BF16) {
             bf16x4 o;
 #pragma unroll
             for (int e = 0; e < 4; ++e) o[e] = (__bf16)acc[i][e];
             ((bf16x4*)Z)[row4 + c] = o;
-        } else {
+        } else if (Z) {
             ((f32x4*)Z)[row4 + c] = acc[i];
         }
         if (LN) sum += (acc[i][0] + acc[i][1]) + (acc[i][2] + acc[i][3]);
@@ -223,6 +224,11 @@ void launch_ps(void* Z, const void* parts, int P, int64_t n4, int h, const float
 hipError_t layernorm(const void* x, bool x_bf16, void* y, const float* gamma,
                      const float* beta, float eps, int64_t M, int64_t h, hipStream_t stream)
 {
+    // rows that fit the registers of one workgroup: the row-sum kernel with no
+    // partials, x as the "residual" and only the normalised row written
+    if (h % 4 == 0 && h <= 16384)
+        return row_sum(nullptr, false, nullptr, false, 0, M, h, nullptr, x, x_bf16, y, gamma,
+                       beta, eps, stream);
     const size_t lds = (size_t)h * sizeof(float);
     if (x_bf16)
         hipLaunchKernelGGL((layernorm_kernel<true>), dim3((unsigned)M), dim3(256), lds, stream,

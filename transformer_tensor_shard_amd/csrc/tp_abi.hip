@@ -14,7 +14,8 @@ namespace {
 
 constexpr int64_t kAlign = 256;            // workspace sub-buffer alignment
 constexpr int64_t kHeadDim = 128;          // the attention kernel's head tile
-constexpr int64_t kMaxLnWidth = 16384;     // LayerNorm keeps one row in LDS
+constexpr int64_t kMaxLnWidth = 16384;     // the block's row kernels keep a row in registers
+constexpr int64_t kMaxLnWidthWide = 32768; // tp_layernorm's wide-row kernel keeps it in LDS
 constexpr int64_t kI32 = 0x7fffffffLL;
 
 inline int64_t align_up(int64_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -104,7 +105,7 @@ tp_status check_attn_shape(int64_t b, int64_t s, int64_t h, int64_t H_l, int64_t
     if (!gemm_bf16_fits(M, n3, h, h, n3) || !gemm_bf16_fits(M, h, H_l * d, H_l * d, h))
         return TP_ERR_SHAPE;
     // the attention kernel addresses one sequence of qkv with 32-bit offsets
-    if (s * n3 * 2 >= kI32 || ((s + 127) / 128) * b * H_l > kI32) return TP_ERR_SHAPE;
+    if (s * n3 * 2 >= kI32 || ((s + 127) / 128) * (b * H_l + 7) > kI32) return TP_ERR_SHAPE;
     return TP_OK;
 }
 
@@ -272,7 +273,7 @@ TP_EXPORT tp_status tp_attention_core(const void* qkv, int64_t ld_qkv, void* O, 
     if (!qkv || !O) return TP_ERR_NULL;
     if (b <= 0 || s <= 0 || H_l <= 0 || d != kHeadDim || ld_qkv < 3 * H_l * d || ld_qkv % 8)
         return TP_ERR_SHAPE;
-    if (s * ld_qkv * 2 >= kI32 || ((s + 127) / 128) * b * H_l > kI32) return TP_ERR_SHAPE;
+    if (s * ld_qkv * 2 >= kI32 || ((s + 127) / 128) * (b * H_l + 7) > kI32) return TP_ERR_SHAPE;
     if (!aligned16(qkv) || !aligned16(O)) return TP_ERR_ALIGN;
     return launched(tpk::attention_fwd(qkv, ld_qkv, O, b, s, H_l, causal != 0, as_stream(stream)));
 }
@@ -282,7 +283,7 @@ TP_EXPORT tp_status tp_layernorm(const void* x, int in, void* y, const void* gam
                                  void* stream) {
     if (!x || !y) return TP_ERR_NULL;
     if (!is_dtype(in)) return TP_ERR_DTYPE;
-    if (M <= 0 || h <= 0 || h % 8 || h > kMaxLnWidth || M > kI32 || !(eps > 0.0f))
+    if (M <= 0 || h <= 0 || h % 8 || h > kMaxLnWidthWide || M > kI32 || !(eps > 0.0f))
         return TP_ERR_SHAPE;
     if (!aligned16(x) || !aligned16(y) || (gamma && !aligned16(gamma)) || (beta && !aligned16(beta)))
         return TP_ERR_ALIGN;
@@ -329,7 +330,7 @@ TP_EXPORT tp_status tp_block_shard(const void* x, void* out, int out_dtype, void
     const int64_t M = b * s, Hl = H / P, f = F / P;
     tp_status stat = check_attn_shape(b, s, h, Hl, d);
     if (stat != TP_OK) return stat;
-    if (((s + 127) / 128) * b * H > kI32) return TP_ERR_SHAPE;
+    if (((s + 127) / 128) * (b * H + 7) > kI32) return TP_ERR_SHAPE;
     if (f % 8 || h > kMaxLnWidth || !gemm_bf16_fits(M, f, h, h, f) || !gemm_bf16_fits(M, h, f, f, h))
         return TP_ERR_SHAPE;
     for (int r = 0; r < P; ++r)
