@@ -17,7 +17,10 @@ Besides the one JSON line the run reports, in the same line:
                 one grouped launch over all 8 ranks) timed per launch with HIP
                 events on the stream it runs on, against the bf16 MFMA peak;
   cpu_baseline  the fp64 oracle timed on the host on a bounded sample of the
-                same workload.
+                same workload;
+  calibration   the throughput of a register-only MFMA loop on this GPU (the
+                matrix cores' ceiling under the current clock and power
+                limits) and of the vendor GEMM at the dominant kernel's shape.
 
 Modes for profiler runs: --mode kernel launches only the dominant kernel,
 --mode copy only a plain device copy of a known size (counter calibration).
@@ -52,17 +55,17 @@ def kernel_source_hash() -> str:
     return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
 
 
-def measured_traffic():
+def measured_traffic(path=TRAFFIC_FILE, source_hash=None):
     """HBM bytes per launch of the dominant kernel from the committed counter
     summary, or None when it is missing or was taken on another kernel source."""
-    if not os.path.exists(TRAFFIC_FILE):
+    if not os.path.exists(path):
         return None
     kv = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("gemm_bf16.hip sha256[:16]") != kernel_source_hash():
+    if kv.get("gemm_bf16_hip_sha256_16") != (source_hash or kernel_source_hash()):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -90,6 +93,32 @@ def blas_threads():
         return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         return 1
+
+
+def calibration(tts, torch, X, W, stream):
+    """Two reference points measured on this GPU in this run, for reading the
+    roofline fraction: the throughput of a register-only MFMA loop (the
+    matrix cores' ceiling under the current clock and power limits), and the
+    vendor GEMM (torch.mm, i.e. hipBLASLt) at the dominant kernel's per-rank
+    shape."""
+    out = torch.empty(256 * 512, dtype=torch.float32, device=X.device)
+    for _ in range(3):
+        tts.tp_probe_mfma(256, 200, out=out)
+    probe_flops = 256 * 8 * 32 * 200 * 16384
+    ms, _ = event_time(lambda: tts.tp_probe_mfma(256, 200, out=out), 5, stream)
+    Y = torch.empty(X.shape[0], W.shape[1], dtype=torch.bfloat16, device=X.device)
+    for _ in range(2):
+        torch.mm(X, W, out=Y)
+    ms_mm, _ = event_time(lambda: torch.mm(X, W, out=Y), 5, stream)
+    mm_flops = 2 * X.shape[0] * X.shape[1] * W.shape[1]
+    return {
+        "mfma_only": {"tflops": round(probe_flops / (ms * 1e-3) / 1e12, 1),
+                      "frac_of_peak": round(probe_flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                      "kernel": "tp_probe_mfma: register-only MFMA 16x16x32 bf16, 2 waves/SIMD"},
+        "vendor_gemm": {"tflops": round(mm_flops / (ms_mm * 1e-3) / 1e12, 1),
+                        "kernel": "torch.mm bf16 [%dx%d]x[%dx%d] (hipBLASLt)" % (
+                            X.shape[0], X.shape[1], W.shape[0], W.shape[1])},
+    }
 
 
 def dominant_operands_cpu(w, wl):
@@ -247,6 +276,8 @@ def main():
     kern_tflops = kern_flops / (kern_ms * 1e-3) / 1e12
     traffic = measured_traffic()
     log(f"dominant kernel: {kern_ms:.3f} ms/launch, {kern_tflops:.1f} TFLOP/s")
+    calib = calibration(tts, torch, X_k, W_k[0], stream)
+    log(f"calibration: {calib}")
 
     components = {}
     if w.kind == "block":
@@ -326,10 +357,12 @@ def main():
             "frac": round(kern_tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
             "algorithmic_flops_per_launch": kern_flops,
+            "frac_of_mfma_only": round(kern_tflops / calib["mfma_only"]["tflops"], 4),
             "avg_launch_ms": round(kern_ms, 4),
             "launches_timed": len(kern_all),
         },
         "cpu_baseline": cpu,
+        "calibration": calib,
         "components": components,
     }
     print(json.dumps(result), flush=True)

@@ -200,6 +200,21 @@ tp_status tp_attention_core(const void* qkv, int64_t ld_qkv, void* O,
 tp_status tp_layernorm(const void* x, int in, void* y, const void* gamma,
                        const void* beta, float eps, int64_t M, int64_t h, void* stream);
 
+/* ========================================================================
+ * Measurement support (not part of the method).
+ * ====================================================================== */
+
+/* tp_probe_mfma -- a register-only loop of MFMA 16x16x32 bf16 instructions:
+ * `blocks` workgroups of 8 waves (two per SIMD), each wave issuing
+ * 32 * iters independent MFMAs on values held in registers; nothing is loaded
+ * from memory.  Each MFMA is 2*16*16*32 = 16384 FLOP, so a launch does
+ * blocks * 8 * 32 * iters * 16384 FLOP.  Timed by the caller, it gives the
+ * matrix-core throughput the GPU sustains under its current clock and power
+ * limits -- the practical ceiling for any MFMA-bound kernel.
+ *   out  device f32 buffer of blocks * 512 elements (receives the sums that
+ *        keep the loop from being removed; the values mean nothing). */
+tp_status tp_probe_mfma(float* out, int blocks, int iters, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,0 +1,31 @@
+"""Host-side logic of bench.py (no GPU): the counter-summary parser that
+fills roofline.traffic, and the refusal of more than one GPU."""
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_traffic_parser(tmp_path):
+    f = tmp_path / "t.txt"
+    f.write_text("# comment: with a colon\ngemm_bf16_hip_sha256_16: abc123\n"
+                 "hbm_bytes_per_launch: 12345\n")
+    assert bench.measured_traffic(str(f), "abc123") == 12345.0
+    assert bench.measured_traffic(str(f), "other") is None      # stale: kernel changed
+    assert bench.measured_traffic(str(tmp_path / "missing.txt"), "abc123") is None
+
+
+def test_committed_traffic_file_parses():
+    # the committed summary names the kernel source it was taken on
+    kv = dict(l.split(":", 1) for l in open(bench.TRAFFIC_FILE) if ":" in l and not l.startswith("#"))
+    h = kv["gemm_bf16_hip_sha256_16"].strip()
+    assert bench.measured_traffic(bench.TRAFFIC_FILE, h) > 0
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True)
+    assert r.returncode == 2 and "single" in r.stderr

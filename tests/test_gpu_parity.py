@@ -291,3 +291,13 @@ def test_block_small_all_ranks():
     # the residual dominates out: check the block's own contributions too
     assert_bf16(x1.cpu().double() - oracle.f64(x), x1_ref - oracle.f64(x))
     assert_bf16(out.cpu().double() - x1.cpu().double(), out_ref - x1_ref)
+
+
+def test_probe_mfma_runs():
+    """Measurement support: the register-only MFMA loop launches and returns
+    finite sums (its values carry no meaning)."""
+    out = torch.empty(4 * 512, device=DEV)
+    flops = tts.tp_probe_mfma(4, 3, out=out)
+    torch.cuda.synchronize()
+    assert flops == 4 * 8 * 32 * 3 * 16384
+    assert torch.isfinite(out).all()

@@ -21,7 +21,8 @@ from ._lib import TP_BF16, TP_EPI_GELU, TP_EPI_NONE, TP_F32
 __all__ = [
     "TpError", "tp_abi_version", "tp_mlp_shard", "tp_mlp_shard_workspace", "tp_attn_shard",
     "tp_attn_shard_workspace", "tp_partial_sum", "tp_block_shard", "tp_block_shard_workspace",
-    "tp_linear", "tp_linear_batched", "tp_attention_core", "tp_layernorm", "lib",
+    "tp_linear", "tp_linear_batched", "tp_attention_core", "tp_layernorm", "tp_probe_mfma",
+    "lib",
 ]
 
 
@@ -231,3 +232,13 @@ def tp_layernorm(x, gamma=None, beta=None, eps=1e-5, *, out=None, stream=None):
                                   _stream(stream))
     _check(st, "tp_layernorm")
     return out
+
+
+# ------------------------------------------------------------------ measurement support
+def tp_probe_mfma(blocks: int = 256, iters: int = 2000, *, out=None, stream=None) -> int:
+    """Launch the register-only MFMA loop; returns the FLOPs of the launch."""
+    if out is None:
+        out = torch.empty(blocks * 512, dtype=torch.float32, device="cuda")
+    st = _lib.load().tp_probe_mfma(_dev(out, "out"), int(blocks), int(iters), _stream(stream))
+    _check(st, "tp_probe_mfma")
+    return blocks * 8 * 32 * iters * 16384

@@ -49,6 +49,7 @@ SIGNATURES = {
                                  _i64, _int, _int, _int, _vp]),
     "tp_attention_core": (_int, [_vp, _i64, _vp, _i64, _i64, _i64, _i64, _int, _vp]),
     "tp_layernorm": (_int, [_vp, _int, _vp, _vp, _vp, ctypes.c_float, _i64, _i64, _vp]),
+    "tp_probe_mfma": (_int, [_vp, _int, _int, _vp]),
 }
 
 _lib = None

@@ -389,3 +389,10 @@ TP_EXPORT tp_status tp_block_shard(const void* x, void* out, int out_dtype, void
         return TP_ERR_LAUNCH;
     return TP_OK;
 }
+
+TP_EXPORT tp_status tp_probe_mfma(float* out, int blocks, int iters, void* stream) {
+    if (!out) return TP_ERR_NULL;
+    if (blocks <= 0 || iters <= 0) return TP_ERR_SHAPE;
+    if (!aligned16(out)) return TP_ERR_ALIGN;
+    return launched(tpk::mfma_probe(out, blocks, iters, as_stream(stream)));
+}

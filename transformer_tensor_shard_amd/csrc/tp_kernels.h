@@ -59,4 +59,8 @@ hipError_t row_sum(void* Z, bool out_bf16, const void* parts, bool parts_bf16, i
                    void* ln_out, const float* gamma, const float* beta, float eps,
                    hipStream_t stream);
 
+// Register-only MFMA 16x16x32 bf16 loop: `blocks` workgroups of 8 waves, each
+// wave issuing 32 * iters MFMAs; out receives blocks * 512 floats.
+hipError_t mfma_probe(float* out, int blocks, int iters, hipStream_t stream);
+
 }  // namespace tpk
