@@ -89,6 +89,27 @@ def test_linear_batched(count, M, N, K, gelu):
             assert_f32(outs[g], ref, bar=1e-4)
 
 
+@pytest.mark.parametrize("count,M,N,K,gelu", [(3, 2048, 264, 200, True), (5, 4096, 520, 328, False),
+                                              (18, 2048, 256, 64, True)])
+def test_linear_batched_shared_x(count, M, N, K, gelu):
+    """Every group shares X (the column-parallel products of all ranks), with
+    whole tile-row bands per XCD: the band tile order, including ragged N and
+    K and more groups than one launch takes."""
+    banner(f"linear batched shared X count={count} M={M} N={N} K={K} gelu={gelu}")
+    X = gen((M, K), 1.0, 80, "x")
+    Ws = [gen((K, N), 1 / math.sqrt(K), 80 + g, "A") for g in range(count)]
+    Xd = X.to(DEV)
+    outs = tts.tp_linear_batched([Xd] * count, [W.to(DEV) for W in Ws], gelu=gelu,
+                                 out_dtype=torch.bfloat16 if gelu else torch.float32)
+    torch.cuda.synchronize()
+    for g in range(count):
+        ref = oracle.matmul(X, Ws[g])
+        if gelu:
+            assert_bf16(outs[g], oracle.gelu(ref))
+        else:
+            assert_f32(outs[g], ref, bar=1e-4)
+
+
 def test_linear_deterministic():
     X = gen((700, 512), 1.0, 14, "x").to(DEV)
     W = gen((512, 640), 1 / math.sqrt(512), 14, "A").to(DEV)

@@ -36,7 +36,8 @@
 //    the 16-byte A reads and the transpose B reads are free of bank conflicts;
 //  * tiles are renumbered so that consecutive tiles land on the same XCD
 //    (workgroups are dealt round-robin to the 8 XCDs, each with its own L2)
-//    and walk the output in groups of 4 tile-rows;
+//    and walk the output in groups of 4 tile-rows; a grouped launch whose
+//    groups share the activations walks row bands across all groups;
 //  * epilogue: the tile is staged through the (then idle) LDS and written with
 //    16-byte row-contiguous stores: one pass for a bf16 tile, two for f32.
 //
@@ -135,6 +136,30 @@ __device__ __forceinline__ bool tile_coords(int pid, int groups, int tiles_m, in
     return true;
 }
 
+// The order used when every group shares its A operand (the activations X
+// of the column-parallel products of all ranks): XCD x owns tile-rows
+// [x*band, (x+1)*band) of every group and walks them GROUP_M rows at a time;
+// for each such row block it visits all groups' column tiles before moving
+// on, so the row block of the shared X stays resident in the last-level
+// cache while the groups' weights stream past.  Needs tiles_m % 8 == 0.
+__device__ __forceinline__ bool tile_coords_band(int pid, int groups, int tiles_m, int tiles_n,
+                                                 int& g, int& tm, int& tn) {
+    const int xcd = pid & 7, local = pid >> 3;
+    const int band = tiles_m >> 3;
+    const int per_block = GROUP_M * tiles_n;           // one row block of one group
+    const int rb = local / (groups * per_block);
+    const int rest = local - rb * (groups * per_block);
+    g = rest / per_block;
+    const int in_block = rest - g * per_block;
+    const int first = rb * GROUP_M;
+    if (first >= band) return false;
+    const int gsize = min(band - first, GROUP_M);
+    if (in_block >= gsize * tiles_n) return false;
+    tm = xcd * band + first + in_block % gsize;
+    tn = in_block / gsize;
+    return true;
+}
+
 template <bool OUT_BF16, bool GELU, bool CHECK_K>
 __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
     GemmBatch batch, int64_t lda, int64_t ldb, int64_t ldc,
@@ -147,7 +172,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
     __shared__ __attribute__((aligned(1024))) char lds1[STAGE_BYTES];
 
     int grp, tm, tn;
-    if (!tile_coords(blockIdx.x, batch.count, tiles_m, tiles_n, grp, tm, tn)) return;
+    if (batch.band ? !tile_coords_band(blockIdx.x, batch.count, tiles_m, tiles_n, grp, tm, tn)
+                   : !tile_coords(blockIdx.x, batch.count, tiles_m, tiles_n, grp, tm, tn))
+        return;
     const int m0 = tm * BM, n0 = tn * BN;
     const __bf16* __restrict__ A = batch.A[grp];
     const __bf16* __restrict__ B = batch.B[grp];
@@ -366,11 +393,16 @@ hipError_t gemm_bf16_batched(const GemmBatch& batch, int64_t lda, int64_t ldb, i
                              hipStream_t stream)
 {
     const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
-    const int per_xcd = (tiles_m * tiles_n + 7) / 8;
-    const dim3 grid(8 * per_xcd * batch.count), block(NTHREADS);
+    GemmBatch b = batch;
+    bool shared_a = b.count > 1;
+    for (int i = 1; i < b.count; ++i) shared_a = shared_a && b.A[i] == b.A[0];
+    b.band = (shared_a && tiles_m % 8 == 0) ? 1 : 0;
+    const int per_xcd = b.band ? ((tiles_m / 8 + GROUP_M - 1) / GROUP_M) * GROUP_M * tiles_n
+                               : (tiles_m * tiles_n + 7) / 8;
+    const dim3 grid(8 * per_xcd * b.count), block(NTHREADS);
     const bool ck = (K % BK) != 0;
 #define TP_GEMM(OB, GL, CK) hipLaunchKernelGGL((gemm_bf16_kernel<OB, GL, CK>), grid, block, 0, \
-        stream, batch, lda, ldb, ldc, (int)M, (int)N, (int)K, tiles_m, tiles_n)
+        stream, b, lda, ldb, ldc, (int)M, (int)N, (int)K, tiles_m, tiles_n)
     if (out_bf16 && gelu)  { if (ck) TP_GEMM(true, true, true);   else TP_GEMM(true, true, false); }
     else if (out_bf16)     { if (ck) TP_GEMM(true, false, true);  else TP_GEMM(true, false, false); }
     else if (gelu)         { if (ck) TP_GEMM(false, true, true);  else TP_GEMM(false, true, false); }

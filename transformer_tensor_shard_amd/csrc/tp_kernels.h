@@ -16,6 +16,7 @@ struct GemmBatch {
     const float* bias[kMaxBatch];
     void* C[kMaxBatch];
     int count;
+    int band;       // set by the launcher: tile order for groups sharing A
 };
 hipError_t gemm_bf16_batched(const GemmBatch& batch, int64_t lda, int64_t ldb, int64_t ldc,
                              int64_t M, int64_t N, int64_t K, bool out_bf16, bool gelu,
