@@ -46,6 +46,9 @@ def _load():
     lib.orc_gelu.argtypes = [ctypes.c_double]
     lib.orc_gelu.restype = ctypes.c_double
     lib.orc_gelu_inplace.argtypes = [_dp, _i64]
+    lib.orc_gelu_grad.argtypes = [ctypes.c_double]
+    lib.orc_gelu_grad.restype = ctypes.c_double
+    lib.orc_gelu_grad_inplace.argtypes = [_dp, _i64]
     lib.orc_layernorm.argtypes = [_dp, _dp, _dp, ctypes.c_double, _dp, _i64, _i64]
     lib.orc_attention_rows.argtypes = [_dp, _dp, _dp, ctypes.POINTER(_i64), _i64, _i64, _i64,
                                        _i64, ctypes.c_int, _dp]
@@ -133,6 +136,39 @@ def mlp_shard(X, A_i, B_i, a_i=None) -> np.ndarray:
     f = A_i.shape[1]
     assert A_i.shape == (h, f) and B_i.shape == (f, h)
     return matmul(gelu(matmul(X, A_i, a_i)), B_i)
+
+
+def gelu_grad(x) -> np.ndarray:
+    """Derivative of the exact-erf GeLU, elementwise: Phi(x) + x·phi(x)."""
+    y = np.array(f64(x), dtype=np.float64, copy=True, order="C")
+    _load().orc_gelu_grad_inplace(_p(y), y.size)
+    return y
+
+
+def mlp_shard_backward(X, A_i, B_i, dZ, a_i=None):
+    """Gradients of one rank's MLP share Z_i = GeLU(X·A_i + a_i)·B_i.
+
+    In the Megatron split ("图解Transformer并行计算" §2.2) the forward
+    all-reduce of the Z_i (operator g) is the identity in the backward pass:
+    every rank receives the same upstream gradient dZ of the summed output.
+    Conversely the identity copy of X into every rank (operator f) becomes an
+    all-reduce in the backward pass: the rank returns a partial dX_i, and
+    dX = sum_r dX_r.  By the chain rule, with Y = X·A_i + a_i, Y' = GeLU(Y):
+        dB_i = Y'^T·dZ                     [f, h]
+        dY'  = dZ·B_i^T                    [M, f]
+        dY   = dY' ⊙ GeLU'(Y)             (local, like the forward GeLU)
+        dA_i = X^T·dY,   da_i = sum over rows of dY
+        dX_i = dY·A_i^T                    [M, h], a partial of dX.
+    Returns (dX_i, dA_i, dB_i, da_i); da_i is None without a bias."""
+    X, A_i, B_i, dZ = f64(X), f64(A_i), f64(B_i), f64(dZ)
+    Y = matmul(X, A_i, a_i)
+    Yp = gelu(Y)
+    dB = matmul(Yp.T.copy(), dZ)
+    dY = matmul(dZ, B_i.T.copy()) * gelu_grad(Y)
+    dA = matmul(X.T.copy(), dY)
+    da = dY.sum(axis=0) if a_i is not None else None
+    dX = matmul(dY, A_i.T.copy())
+    return dX, dA, dB, da
 
 
 def attention_rows(Q, K, V, tpos, Hl: int, d: int, causal: bool) -> np.ndarray:

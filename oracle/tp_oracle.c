@@ -46,6 +46,24 @@ EXPORT void orc_gelu_inplace(double* y, int64_t n)
     for (int64_t i = 0; i < n; ++i) y[i] = orc_gelu(y[i]);
 }
 
+/* Derivative of the exact GeLU, by the product rule on x·Phi(x):
+ *   d/dx GeLU(x) = Phi(x) + x·phi(x),  phi(x) = exp(-x^2/2)/sqrt(2 pi),
+ * the standard normal density (Phi' = phi).  Needed by the backward pass of
+ * the MLP share: the gradient of Y'_i = GeLU(Y_i) is taken locally on each
+ * rank, exactly as the forward GeLU is ([Megatron explainer] §2.2). */
+EXPORT double orc_gelu_grad(double x)
+{
+    const double Phi = 0.5 * (1.0 + erf(x / sqrt(2.0)));
+    const double phi = exp(-0.5 * x * x) / sqrt(2.0 * acos(-1.0));
+    return Phi + x * phi;
+}
+
+EXPORT void orc_gelu_grad_inplace(double* y, int64_t n)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) y[i] = orc_gelu_grad(y[i]);
+}
+
 /* LayerNorm over the last dimension (the tutorial block's nn.LayerNorm(h)):
  *   mu = (1/h) sum_c x_c,  var = (1/h) sum_c (x_c - mu)^2  (population form),
  *   y_c = (x_c - mu) / sqrt(var + eps) · gamma_c + beta_c.

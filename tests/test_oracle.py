@@ -411,3 +411,80 @@ def test_block_ranks_sum_to_unsharded_block():
     rows = [9, 0, 6]
     x1c, outc = oracle.block_rows(x, b, s, *shard, H, d, rows=rows)
     assert rel(outc, outb[rows]) < 1e-14 and rel(x1c, x1b[rows]) < 1e-14
+
+
+# ------------------------------------------------------------------ backward of the MLP share
+def test_gelu_grad_closed_forms():
+    """GeLU'(x) = Phi(x) + x·phi(x): GeLU'(0) = 1/2; GeLU(x) - GeLU(-x) = x
+    gives GeLU'(x) + GeLU'(-x) = 1; the slope tends to 1 and 0 at the ends;
+    and it is the central difference of the oracle's own GeLU."""
+    x = np.linspace(-6, 6, 241)
+    g = oracle.gelu_grad(x)
+    assert abs(oracle.gelu_grad(np.array([0.0]))[0] - 0.5) < 1e-15
+    assert np.abs(g + oracle.gelu_grad(-x) - 1.0).max() < 1e-14
+    assert abs(oracle.gelu_grad(np.array([12.0]))[0] - 1.0) < 1e-12
+    assert abs(oracle.gelu_grad(np.array([-12.0]))[0]) < 1e-12
+    eps = 1e-6
+    fd = (oracle.gelu(x + eps) - oracle.gelu(x - eps)) / (2 * eps)
+    assert np.abs(fd - g).max() < 1e-8
+
+
+def test_mlp_backward_matches_autograd():
+    """Library check: torch autograd in float64 on the unsharded formula."""
+    rng = np.random.default_rng(5)
+    X, A, B = rng.normal(size=(7, 10)), rng.normal(size=(10, 6)) / 3, rng.normal(size=(6, 10)) / 3
+    a, dZ = rng.normal(size=6), rng.normal(size=(7, 10))
+    dX, dA, dB, da = oracle.mlp_shard_backward(X, A, B, dZ, a)
+    t = [torch.tensor(v, requires_grad=True) for v in (X, A, B, a)]
+    Z = torch.nn.functional.gelu(t[0] @ t[1] + t[3]) @ t[2]
+    Z.backward(torch.tensor(dZ))
+    for mine, ref in zip((dX, dA, dB, da), t):
+        assert np.abs(mine - ref.grad.numpy()).max() < 1e-12
+
+
+def test_mlp_backward_finite_differences():
+    """Brute force: <grad, V> equals the central difference of <dZ, Z> along
+    V for each input (X, A, B), on a tiny shard."""
+    rng = np.random.default_rng(6)
+    X, A, B = rng.normal(size=(3, 5)), rng.normal(size=(5, 4)) / 2, rng.normal(size=(4, 5)) / 2
+    dZ = rng.normal(size=(3, 5))
+    grads = oracle.mlp_shard_backward(X, A, B, dZ)
+    loss = lambda X, A, B: float((dZ * oracle.mlp_shard(X, A, B)).sum())
+    eps = 1e-6
+    for k, g in enumerate(grads[:3]):
+        V = rng.normal(size=g.shape)
+        args = [X, A, B]
+        plus = [v + eps * V if i == k else v for i, v in enumerate(args)]
+        minus = [v - eps * V if i == k else v for i, v in enumerate(args)]
+        fd = (loss(*plus) - loss(*minus)) / (2 * eps)
+        assert abs(fd - float((g * V).sum())) < 1e-7 * max(1.0, abs(fd))
+
+
+@pytest.mark.parametrize("P", [2, 4])
+def test_mlp_backward_ranks_sum_to_unsharded(P):
+    """§2.2's backward: each rank gets the same dZ; the rank partials dX_r sum
+    to the unsharded dX (the backward all-reduce), the dA_r are the column
+    blocks of the unsharded dA and the dB_r its row blocks."""
+    rng = np.random.default_rng(7 + P)
+    M, h, F = 9, 12, 8 * P
+    X, A, B = rng.normal(size=(M, h)), rng.normal(size=(h, F)) / 4, rng.normal(size=(F, h)) / 4
+    dZ = rng.normal(size=(M, h))
+    dX, dA, dB, _ = oracle.mlp_shard_backward(X, A, B, dZ)
+    f = F // P
+    parts = [oracle.mlp_shard_backward(X, A[:, r * f:(r + 1) * f], B[r * f:(r + 1) * f], dZ)
+             for r in range(P)]
+    assert np.abs(sum(p[0] for p in parts) - dX).max() < 1e-12
+    assert np.abs(np.concatenate([p[1] for p in parts], axis=1) - dA).max() < 1e-12
+    assert np.abs(np.concatenate([p[2] for p in parts], axis=0) - dB).max() < 1e-12
+
+
+def test_mlp_backward_needs_the_gelu_derivative():
+    """Negative control: skipping the GeLU derivative (or using GeLU itself)
+    in place of GeLU' changes dA, so the chain-rule factor is pinned."""
+    rng = np.random.default_rng(9)
+    X, A, B, dZ = rng.normal(size=(6, 8)), rng.normal(size=(8, 5)), rng.normal(size=(5, 8)), \
+        rng.normal(size=(6, 8))
+    _, dA, _, _ = oracle.mlp_shard_backward(X, A, B, dZ)
+    dYp = oracle.matmul(dZ, B.T.copy())
+    wrong = oracle.matmul(X.T.copy(), dYp)                           # no GeLU' factor
+    assert np.abs(wrong - dA).max() > 1e-3
