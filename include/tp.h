@@ -81,6 +81,41 @@ tp_status tp_mlp_shard(const void* X, const void* A_i, const void* a_i, const vo
                        int64_t M, int64_t h, int64_t f, int in, int out, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Training: the MLP share's forward keeping its activations, and its
+ * backward.  [Megatron explainer] §2.2: the backward mirrors the forward;
+ * every rank receives the same dZ = ∂L/∂Z, computes the gradients of its own
+ * A_i, B_i by the chain rule through Z_i = GeLU(X·A_i + a_i)·B_i, and forms a
+ * local input gradient dX_i whose sum over ranks, one all-reduce, is ∂L/∂X
+ * (tp_partial_sum stands in for that all-reduce):
+ *     dY'_i = dZ·B_i^T,   dY_i = dY'_i ⊙ GeLU'(Y_i),
+ *     dB_i = Y'_i^T·dZ,   dA_i = X^T·dY_i,   da_i = Σ_rows dY_i,
+ *     dX_i = dY_i·A_i^T   (dX = Σ_i dX_i).
+ * bf16 operands only (the MFMA path), h % 8 == 0 and f % 8 == 0.
+ *
+ * tp_mlp_shard_train_fwd -- Z_i as tp_mlp_shard, also storing
+ *   Y_i  [M,f] bf16: the pre-activation X·A_i + a_i,
+ *   Yp_i [M,f] bf16: GeLU(Y_i) (the second GEMM's input),
+ * which tp_mlp_shard_backward takes back.  Z_i in dtype `out`. */
+tp_status tp_mlp_shard_train_fwd(const void* X, const void* A_i, const void* a_i,
+                                 const void* B_i, void* Z_i, void* Y_i, void* Yp_i,
+                                 int64_t M, int64_t h, int64_t f, int out, void* stream);
+
+/* tp_mlp_shard_backward -- the gradients above from the saved Y_i, Yp_i.
+ *   X [M,h], A_i [h,f], B_i [f,h], Y_i, Yp_i [M,f], dZ [M,h]: bf16 inputs
+ *   dX_i [M,h] in dtype `dx_dtype` (TP_F32 or TP_BF16): this rank's partial
+ *   dA_i [h,f], dB_i [f,h]: f32;  da_i [f] f32, or NULL to skip it
+ *   ws >= tp_mlp_shard_backward_workspace(M, f) bytes (dY_i in bf16 and the
+ *        bias gradient's per-chunk partial sums).
+ * The bias gradient is summed in a fixed order: results are bitwise
+ * reproducible from run to run. */
+size_t tp_mlp_shard_backward_workspace(int64_t M, int64_t f);
+tp_status tp_mlp_shard_backward(const void* X, const void* A_i, const void* B_i,
+                                const void* Y_i, const void* Yp_i, const void* dZ,
+                                void* dX_i, void* dA_i, void* dB_i, void* da_i, void* ws,
+                                size_t ws_bytes, int64_t M, int64_t h, int64_t f,
+                                int dx_dtype, void* stream);
+
+/* ------------------------------------------------------------------------
  * tp_attn_shard -- one rank's attention share.  [Megatron explainer] §3.1,
  * §3.2: the Q, K and V projections are split by columns so that this rank
  * owns H_l whole heads, each head computes softmax(Q·K^T/sqrt d)·V locally,
@@ -152,10 +187,14 @@ tp_status tp_block_shard(const void* x, void* out, int out_dtype, void* x1,
  * that each can be checked on its own.
  * ====================================================================== */
 
-/* Epilogues of tp_linear. */
+/* Epilogues of tp_linear (NONE, GELU) and tp_matmul (all four). */
 typedef enum tp_epilogue {
-    TP_EPI_NONE = 0,  /* C = X·W (+bias)                                    */
-    TP_EPI_GELU = 1   /* C = GeLU(X·W + bias), exact erf form (§2.1's GeLU) */
+    TP_EPI_NONE = 0,     /* C = X·W (+bias)                                    */
+    TP_EPI_GELU = 1,     /* C = GeLU(X·W + bias), exact erf form (§2.1's GeLU) */
+    TP_EPI_GELU_BWD = 2, /* C = (X·W + bias) ⊙ GeLU'(aux): the chain rule
+                            through the GeLU, aux = the saved pre-activation   */
+    TP_EPI_GELU_SAVE = 3 /* C = GeLU(X·W + bias) and aux = X·W + bias, both bf16:
+                            the training forward keeps what the backward needs */
 } tp_epilogue;
 
 /* tp_linear -- C[M,N] = epi(X[M,K]·W[K,N] + bias[N]) with an f32 accumulator.
@@ -182,6 +221,29 @@ tp_status tp_linear_batched(const void* const* X, int64_t ldx, const void* const
                             int64_t ldw, const void* const* bias, void* const* C, int64_t ldc,
                             int count, int64_t M, int64_t N, int64_t K, int in, int out,
                             int epilogue, void* stream);
+
+/* tp_matmul -- C[M,N] = epi(op(A)·op(B) + bias[N]) on bf16 operands with an
+ * f32 accumulator, where op(A) = A [M,K] (trans_a = 0) or A^T for A stored
+ * [K,M] (trans_a = 1), and op(B) = B [K,N] (trans_b = 0) or B^T for B stored
+ * [N,K] (trans_b = 1).  The backward of the column- and row-parallel layers
+ * ([Megatron explainer] §2.2) needs both transposed forms: the input gradient
+ * dY·W^T (trans_b) and the weight gradient X^T·dY (trans_a).  No operand is
+ * transposed in memory.  Row-major storage, leading dimensions in elements.
+ * Supported (trans_a, trans_b, epilogue):
+ *     (0,0) NONE, GELU (out f32 or bf16), GELU_SAVE (out bf16);
+ *     (0,1) NONE, GELU_BWD (out f32 or bf16);
+ *     (1,0) NONE (out f32 or bf16);
+ * anything else is TP_ERR_DTYPE.
+ *   aux  [M,N] bf16 with leading dimension ldaux: read by GELU_BWD, written by
+ *        GELU_SAVE, ignored (may be NULL) otherwise.
+ *   bias f32 [N] or NULL.
+ * The contiguous dimension of every operand and of C must be a multiple of 8
+ * (K for a K-contiguous operand, M or N otherwise) and so must every leading
+ * dimension. */
+tp_status tp_matmul(const void* A, int64_t lda, int trans_a, const void* B, int64_t ldb,
+                    int trans_b, const void* bias, void* C, int64_t ldc, void* aux,
+                    int64_t ldaux, int64_t M, int64_t N, int64_t K, int out, int epilogue,
+                    void* stream);
 
 /* tp_attention_core -- per (sequence, local head) softmax(Q·K^T/sqrt d)·V
  * ([Megatron explainer] §3.1) on projections already in memory.

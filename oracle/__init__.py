@@ -148,12 +148,11 @@ def gelu_grad(x) -> np.ndarray:
 def mlp_shard_backward(X, A_i, B_i, dZ, a_i=None):
     """Gradients of one rank's MLP share Z_i = GeLU(X·A_i + a_i)·B_i.
 
-    In the Megatron split ("图解Transformer并行计算" §2.2) the forward
-    all-reduce of the Z_i (operator g) is the identity in the backward pass:
-    every rank receives the same upstream gradient dZ of the summed output.
-    Conversely the identity copy of X into every rank (operator f) becomes an
-    all-reduce in the backward pass: the rank returns a partial dX_i, and
-    dX = sum_r dX_r.  By the chain rule, with Y = X·A_i + a_i, Y' = GeLU(Y):
+    "图解Transformer并行计算" §2.2: the backward mirrors the forward.  Every
+    rank receives the same upstream gradient dZ of the summed output, computes
+    the gradients of its own A_i and B_i, and forms a local input gradient
+    dX_i; one all-reduce sums them, dX = sum_r dX_r.  By the chain rule, with
+    Y = X·A_i + a_i, Y' = GeLU(Y):
         dB_i = Y'^T·dZ                     [f, h]
         dY'  = dZ·B_i^T                    [M, f]
         dY   = dY' ⊙ GeLU'(Y)             (local, like the forward GeLU)

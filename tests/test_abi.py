@@ -174,3 +174,90 @@ def test_linear_batched_rejects():
     assert call(X=odd) == _lib.TP_ERR_ALIGN
     assert L.tp_linear_batched(None, 16, two, 8, None, two, 8, 2, 4, 8, 16, 1, 0, 0, None) \
         == _lib.TP_ERR_NULL
+
+
+def matmul(**kw):
+    a = dict(A=FAKE, lda=64, ta=0, B=FAKE, ldb=64, tb=0, bias=None, C=FAKE, ldc=64, aux=None,
+             ldaux=0, M=32, N=64, K=64, o=_lib.TP_F32, epi=_lib.TP_EPI_NONE)
+    a.update(kw)
+    return tts.lib().tp_matmul(a["A"], a["lda"], a["ta"], a["B"], a["ldb"], a["tb"], a["bias"],
+                               a["C"], a["ldc"], a["aux"], a["ldaux"], a["M"], a["N"], a["K"],
+                               a["o"], a["epi"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(A=None), _lib.TP_ERR_NULL),
+    (dict(C=None), _lib.TP_ERR_NULL),
+    (dict(ta=1, tb=1), _lib.TP_ERR_DTYPE),                 # A^T·B^T has no kernel
+    (dict(ta=2), _lib.TP_ERR_DTYPE),
+    (dict(ta=1, epi=_lib.TP_EPI_GELU), _lib.TP_ERR_DTYPE),  # TN takes no epilogue
+    (dict(epi=_lib.TP_EPI_GELU_BWD), _lib.TP_ERR_DTYPE),    # GeLU backward is NT only
+    (dict(epi=_lib.TP_EPI_GELU_SAVE, aux=FAKE, ldaux=64), _lib.TP_ERR_DTYPE),  # needs bf16 out
+    (dict(tb=1, epi=_lib.TP_EPI_GELU_BWD), _lib.TP_ERR_NULL),  # aux missing
+    (dict(o=5), _lib.TP_ERR_DTYPE),
+    (dict(M=0), _lib.TP_ERR_SHAPE),
+    (dict(K=60, lda=64), _lib.TP_ERR_SHAPE),               # NN: K is A's contiguous dim
+    (dict(ta=1, lda=32, M=28, K=60), _lib.TP_ERR_SHAPE),   # TN: M is A's contiguous dim
+    (dict(tb=1, ldb=64, N=60), _lib.TP_ERR_SHAPE),         # C's rows must be 16-byte multiples
+    (dict(ldc=60), _lib.TP_ERR_SHAPE),
+    (dict(lda=32), _lib.TP_ERR_SHAPE),                     # lda < K
+    (dict(tb=1, ldb=32), _lib.TP_ERR_SHAPE),               # B^T stored [N,K]: ldb < K
+    (dict(ta=1, lda=16), _lib.TP_ERR_SHAPE),               # A^T stored [K,M]: lda < M
+    (dict(lda=1 << 23), _lib.TP_ERR_SHAPE),                # 256 rows past 32-bit offsets
+    (dict(B=FAKE_ODD), _lib.TP_ERR_ALIGN),
+    (dict(tb=1, epi=_lib.TP_EPI_GELU_BWD, aux=FAKE_ODD, ldaux=64), _lib.TP_ERR_ALIGN),
+])
+def test_matmul_rejects(kw, status):
+    assert matmul(**kw) == status
+
+
+def test_matmul_accepts_the_documented_forms_on_cpu_arguments():
+    """Every supported (trans_a, trans_b, epilogue) passes validation: with a
+    NULL A it must fail on the pointer, not on the form."""
+    for ta, tb, epi, o in [(0, 0, 0, 0), (0, 0, 1, 1), (0, 0, 3, 1), (0, 1, 0, 0), (0, 1, 2, 1),
+                           (1, 0, 0, 0), (1, 0, 0, 1)]:
+        assert matmul(A=None, ta=ta, tb=tb, epi=epi, o=o, aux=FAKE, ldaux=64) == _lib.TP_ERR_NULL
+
+
+def mlp_bwd(**kw):
+    a = dict(X=FAKE, A=FAKE, B=FAKE, Y=FAKE, Yp=FAKE, dZ=FAKE, dX=FAKE, dA=FAKE, dB=FAKE,
+             da=FAKE, ws=FAKE, wsb=BIG, M=300, h=64, f=32, o=_lib.TP_F32)
+    a.update(kw)
+    return tts.lib().tp_mlp_shard_backward(a["X"], a["A"], a["B"], a["Y"], a["Yp"], a["dZ"],
+                                           a["dX"], a["dA"], a["dB"], a["da"], a["ws"], a["wsb"],
+                                           a["M"], a["h"], a["f"], a["o"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Y=None), _lib.TP_ERR_NULL),
+    (dict(dB=None), _lib.TP_ERR_NULL),
+    (dict(o=4), _lib.TP_ERR_DTYPE),
+    (dict(M=0), _lib.TP_ERR_SHAPE),
+    (dict(h=60), _lib.TP_ERR_SHAPE),
+    (dict(f=12), _lib.TP_ERR_SHAPE),
+    (dict(M=65536 * 256 + 1), _lib.TP_ERR_SHAPE),   # more bias-sum chunks than a grid column
+    (dict(ws=None), _lib.TP_ERR_WORKSPACE),
+    (dict(wsb=300 * 32 * 2), _lib.TP_ERR_WORKSPACE),  # dY fits, the bias partials do not
+    (dict(dA=FAKE_ODD), _lib.TP_ERR_ALIGN),
+    (dict(da=FAKE_ODD), _lib.TP_ERR_ALIGN),
+])
+def test_mlp_backward_rejects(kw, status):
+    assert mlp_bwd(**kw) == status
+
+
+def test_mlp_backward_workspace_size():
+    L = tts.lib()
+    # dY: 300*32*2 = 19200 bytes (a multiple of 256); partials: 2 chunks * 32 * 4 -> 256
+    assert L.tp_mlp_shard_backward_workspace(300, 32) == 19200 + 256
+    assert L.tp_mlp_shard_backward_workspace(0, 32) == 0
+
+
+def test_mlp_train_fwd_rejects():
+    L = tts.lib()
+    call = lambda Y=FAKE, Yp=FAKE, h=64, o=_lib.TP_F32: L.tp_mlp_shard_train_fwd(
+        FAKE, FAKE, None, FAKE, FAKE, Y, Yp, 100, h, 32, o, None)
+    assert call(Y=None) == _lib.TP_ERR_NULL
+    assert call(Yp=None) == _lib.TP_ERR_NULL
+    assert call(h=20) == _lib.TP_ERR_SHAPE
+    assert call(o=9) == _lib.TP_ERR_DTYPE
+    assert call(Yp=FAKE_ODD) == _lib.TP_ERR_ALIGN

@@ -16,13 +16,14 @@ from typing import Optional, Sequence
 import torch
 
 from . import _lib
-from ._lib import TP_BF16, TP_EPI_GELU, TP_EPI_NONE, TP_F32
+from ._lib import TP_BF16, TP_EPI_GELU, TP_EPI_GELU_BWD, TP_EPI_GELU_SAVE, TP_EPI_NONE, TP_F32
 
 __all__ = [
     "TpError", "tp_abi_version", "tp_mlp_shard", "tp_mlp_shard_workspace", "tp_attn_shard",
     "tp_attn_shard_workspace", "tp_partial_sum", "tp_block_shard", "tp_block_shard_workspace",
     "tp_linear", "tp_linear_batched", "tp_attention_core", "tp_layernorm", "tp_probe_mfma",
-    "lib",
+    "tp_matmul", "tp_mlp_shard_train_fwd", "tp_mlp_shard_backward",
+    "tp_mlp_shard_backward_workspace", "lib",
 ]
 
 
@@ -102,6 +103,55 @@ def tp_mlp_shard(X, A_i, B_i, a_i=None, *, out=None, out_dtype=torch.float32, ws
                                   M, h, f, _code(X.dtype), _code(out.dtype), _stream(stream))
     _check(st, "tp_mlp_shard")
     return out
+
+
+def tp_mlp_shard_train_fwd(X, A_i, B_i, a_i=None, *, out=None, out_dtype=torch.float32,
+                           Y_out=None, Yp_out=None, stream=None):
+    """Z_i as tp_mlp_shard, also returning the saved activations:
+    (Z_i [M,h], Y_i = X·A_i + a_i [M,f] bf16, Yp_i = GeLU(Y_i) [M,f] bf16)."""
+    M, h = X.shape
+    f = A_i.shape[1]
+    if out is None:
+        out = torch.empty(M, h, dtype=out_dtype, device=X.device)
+    if Y_out is None:
+        Y_out = torch.empty(M, f, dtype=torch.bfloat16, device=X.device)
+    if Yp_out is None:
+        Yp_out = torch.empty(M, f, dtype=torch.bfloat16, device=X.device)
+    st = _lib.load().tp_mlp_shard_train_fwd(
+        _dev(X, "X"), _dev(A_i, "A_i"), _dev(a_i, "a_i"), _dev(B_i, "B_i"), _dev(out, "out"),
+        _dev(Y_out, "Y_out"), _dev(Yp_out, "Yp_out"), M, h, f, _code(out.dtype), _stream(stream))
+    _check(st, "tp_mlp_shard_train_fwd")
+    return out, Y_out, Yp_out
+
+
+def tp_mlp_shard_backward_workspace(M: int, f: int) -> int:
+    return int(_lib.load().tp_mlp_shard_backward_workspace(M, f))
+
+
+def tp_mlp_shard_backward(X, A_i, B_i, Y_i, Yp_i, dZ, *, bias_grad=True, dx_dtype=torch.float32,
+                          dX_out=None, dA_out=None, dB_out=None, da_out=None, ws=None,
+                          stream=None):
+    """One rank's MLP gradients from the saved activations: returns
+    (dX_i [M,h] partial, dA_i [h,f] f32, dB_i [f,h] f32, da_i [f] f32 or None)."""
+    M, h = X.shape
+    f = A_i.shape[1]
+    dev = X.device
+    if dX_out is None:
+        dX_out = torch.empty(M, h, dtype=dx_dtype, device=dev)
+    if dA_out is None:
+        dA_out = torch.empty(h, f, dtype=torch.float32, device=dev)
+    if dB_out is None:
+        dB_out = torch.empty(f, h, dtype=torch.float32, device=dev)
+    if bias_grad and da_out is None:
+        da_out = torch.empty(f, dtype=torch.float32, device=dev)
+    ws = _ws(ws, tp_mlp_shard_backward_workspace(M, f), dev)
+    st = _lib.load().tp_mlp_shard_backward(
+        _dev(X, "X"), _dev(A_i, "A_i"), _dev(B_i, "B_i"), _dev(Y_i, "Y_i"), _dev(Yp_i, "Yp_i"),
+        _dev(dZ, "dZ"), _dev(dX_out, "dX_out"), _dev(dA_out, "dA_out"), _dev(dB_out, "dB_out"),
+        _dev(da_out if bias_grad else None, "da_out"), _dev(ws, "ws"), _bytes(ws), M, h, f,
+        _code(dX_out.dtype), _stream(stream))
+    _check(st, "tp_mlp_shard_backward")
+    return dX_out, dA_out, dB_out, (da_out if bias_grad else None)
 
 
 # ------------------------------------------------------------------ attention
@@ -209,6 +259,33 @@ def tp_linear_batched(Xs: Sequence, Ws: Sequence, biases=None, *, gelu=False, ou
         TP_EPI_GELU if gelu else TP_EPI_NONE, _stream(stream))
     _check(st, "tp_linear_batched")
     return outs
+
+
+_EPILOGUES = {"none": TP_EPI_NONE, "gelu": TP_EPI_GELU, "gelu_bwd": TP_EPI_GELU_BWD,
+              "gelu_save": TP_EPI_GELU_SAVE}
+
+
+def tp_matmul(A, B, bias=None, *, trans_a=False, trans_b=False, epilogue="none", aux=None,
+              out=None, out_dtype=torch.float32, stream=None):
+    """C = epi(op(A)·op(B) + bias) on bf16 operands: op(A) = A.T when trans_a
+    (A stored [K,M]), op(B) = B.T when trans_b (B stored [N,K]).  epilogue:
+    "none", "gelu", "gelu_bwd" (C ⊙ GeLU'(aux)) or "gelu_save" (aux receives
+    the pre-activation).  Returns C [M,N]."""
+    M, K = (A.shape[1], A.shape[0]) if trans_a else (A.shape[0], A.shape[1])
+    N = B.shape[0] if trans_b else B.shape[1]
+    if (B.shape[1] if trans_b else B.shape[0]) != K:
+        raise ValueError(f"inner dimensions differ: {tuple(A.shape)} and {tuple(B.shape)}")
+    if out is None:
+        out = torch.empty(M, N, dtype=out_dtype, device=A.device)
+    if epilogue == "gelu_save" and aux is None:
+        aux = torch.empty(M, N, dtype=torch.bfloat16, device=A.device)
+    st = _lib.load().tp_matmul(
+        _dev(A, "A"), A.shape[1], int(bool(trans_a)), _dev(B, "B"), B.shape[1],
+        int(bool(trans_b)), _dev(bias, "bias"), _dev(out, "out"), out.shape[1], _dev(aux, "aux"),
+        aux.shape[1] if aux is not None else 0, M, N, K, _code(out.dtype), _EPILOGUES[epilogue],
+        _stream(stream))
+    _check(st, "tp_matmul")
+    return (out, aux) if epilogue == "gelu_save" else out
 
 
 def tp_attention_core(qkv, b: int, s: int, H_l: int, d: int = 128, causal=True, *, out=None,

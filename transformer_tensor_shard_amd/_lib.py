@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtp.so")
 
 TP_OK, TP_ERR_NULL, TP_ERR_SHAPE, TP_ERR_DTYPE, TP_ERR_ALIGN, TP_ERR_WORKSPACE, TP_ERR_LAUNCH = range(7)
 TP_F32, TP_BF16 = 0, 1
-TP_EPI_NONE, TP_EPI_GELU = 0, 1
+TP_EPI_NONE, TP_EPI_GELU, TP_EPI_GELU_BWD, TP_EPI_GELU_SAVE = 0, 1, 2, 3
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -50,6 +50,13 @@ SIGNATURES = {
     "tp_attention_core": (_int, [_vp, _i64, _vp, _i64, _i64, _i64, _i64, _int, _vp]),
     "tp_layernorm": (_int, [_vp, _int, _vp, _vp, _vp, ctypes.c_float, _i64, _i64, _vp]),
     "tp_probe_mfma": (_int, [_vp, _int, _int, _vp]),
+    "tp_matmul": (_int, [_vp, _i64, _int, _vp, _i64, _int, _vp, _vp, _i64, _vp, _i64, _i64, _i64,
+                         _i64, _int, _int, _vp]),
+    "tp_mlp_shard_train_fwd": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int,
+                                      _vp]),
+    "tp_mlp_shard_backward_workspace": (_sz, [_i64, _i64]),
+    "tp_mlp_shard_backward": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
+                                     _i64, _i64, _i64, _int, _vp]),
 }
 
 _lib = None

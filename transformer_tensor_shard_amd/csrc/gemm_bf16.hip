@@ -1,11 +1,21 @@
 // bf16 x bf16 -> f32-accumulate GEMM for gfx950 (CDNA4) with fused epilogues.
 //
-// Computes C[M,N] = epi(A[M,K]·B[K,N] + bias[N]) for row-major A (the
-// activations X, K contiguous) and row-major B (a weight in the [in, out]
-// layout of the Megatron explainer's Y = X @ W, N contiguous).  This is the
-// product behind the column-parallel layer (epilogue: + bias, GeLU, store
-// bf16: "图解Transformer并行计算" §2.1, Y'_i = GeLU(X·A_i)) and the
-// row-parallel layer (epilogue: store the f32 partial, §2.1 Z_i = Y'_i·B_i).
+// Computes C[M,N] = epi(op(A)·op(B) + bias[N]).  In the forward layout (NN)
+// A [M,K] is row-major with K contiguous (the activations X) and B [K,N] is
+// row-major with N contiguous (a weight in the [in, out] layout of the
+// Megatron explainer's Y = X @ W).  This is the product behind the
+// column-parallel layer (epilogue: + bias, GeLU, store bf16:
+// "图解Transformer并行计算" §2.1, Y'_i = GeLU(X·A_i)) and the row-parallel
+// layer (epilogue: store the f32 partial, §2.1 Z_i = Y'_i·B_i).  The backward
+// of the MLP share (§2.2) also needs B stored [N,K] (NT: dY' = dZ·B_i^T,
+// dX_i = dY·A_i^T) and A stored [K,M] (TN: dB_i = Y'^T·dZ, dA_i = X^T·dY).
+// An operand tile is staged either K-contiguous (read with 16-byte LDS reads)
+// or M/N-contiguous (read with the LDS transpose read), whichever its memory
+// layout is; nothing is transposed in memory.
+//
+// Epilogues: none; + bias and GeLU; GeLU backward (C = (A·B)·GeLU'(Y) with the
+// saved pre-activation Y read as `aux`); and the training forward's dual store
+// (C = GeLU(A·B + bias) and aux = A·B + bias, both bf16).
 //
 // Design: one 256x256 output tile per workgroup of 8 waves (two per SIMD).
 //  * wave w owns a 128x64 sub-tile: rows 128*((w&3)>>1), columns
@@ -69,28 +79,23 @@ constexpr int LOADS = 4;                      // A (and B) loads per wave per K 
 // Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
 constexpr int SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100;
 
-// One k-step of a wave: 8 MFMAs with the next k-step's 8 LDS reads issued
-// one after each of the first 8 MFMAs, and V direct-to-LDS loads spread
-// evenly between them.
-#ifndef DSP
-#define DSP 1
-#endif
 // One 32-wide k-step of a wave: 32 MFMAs (A block mi = I/4 against the 4 B
-// blocks); the next k-step's 8 B reads go out after the first 8 MFMAs and
-// each A block's reload right after its last MFMA; V direct-to-LDS loads are
-// spread one per 32/V MFMAs.
-template <int V, int I>
+// blocks); the next k-step's B reads (DB LDS instructions per block) go out
+// over the first 8 MFMAs and each A block's reload (DA instructions) right
+// after its last MFMA; V direct-to-LDS loads are spread one per 32/V MFMAs.
+template <int V, int DA, int DB, int I>
 __device__ __forceinline__ void sched_step() {
     __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-    constexpr int nds = (I < 8 ? 1 : 0) + (I % 4 == 3 ? 1 : 0);
+    constexpr int nb = I < 8 ? ((I + 1) * 4 * DB) / 8 - (I * 4 * DB) / 8 : 0;
+    constexpr int nds = nb + (I % 4 == 3 ? DA : 0);
     if constexpr (nds > 0) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, nds, 0);
     constexpr int nv = ((I + 1) * V) / 32 - (I * V) / 32;
     if constexpr (nv > 0) __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, nv, 0);
-    if constexpr (I + 1 < 32) sched_step<V, I + 1>();
+    if constexpr (I + 1 < 32) sched_step<V, DA, DB, I + 1>();
 }
-template <int V>
+template <int V, int DA, int DB>
 __device__ __forceinline__ void sched_kstep() {
-    sched_step<V, 0>();
+    sched_step<V, DA, DB, 0>();
     __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -106,6 +111,18 @@ __device__ __forceinline__ float gelu(float x) {
                     u * (-1.453152027f + u * 1.061405429f))));
     const float h = 0.5f * p * __builtin_amdgcn_exp2f(-1.44269504088896341f * t * t);
     return x * (x >= 0.0f ? 1.0f - h : h);
+}
+
+// GeLU'(x) = Phi(x) + x·phi(x), phi the standard normal density; Phi from the
+// same erfc approximation, and phi(x) = exp(-x^2/2)/sqrt(2 pi) shares its exp.
+__device__ __forceinline__ float gelu_grad(float x) {
+    const float t = fabsf(x) * 0.70710678118654752f;
+    const float u = __builtin_amdgcn_rcpf(1.0f + 0.3275911f * t);
+    const float p = u * (0.254829592f + u * (-0.284496736f + u * (1.421413741f +
+                    u * (-1.453152027f + u * 1.061405429f))));
+    const float e = __builtin_amdgcn_exp2f(-1.44269504088896341f * t * t);
+    const float h = 0.5f * p * e;
+    return (x >= 0.0f ? 1.0f - h : h) + x * e * 0.39894228040143268f;
 }
 
 // Map a workgroup to (group g, tile_m, tile_n).  Workgroups are dealt
@@ -160,11 +177,21 @@ __device__ __forceinline__ bool tile_coords_band(int pid, int groups, int tiles_
     return true;
 }
 
-template <bool OUT_BF16, bool GELU, bool CHECK_K>
+// K position, relative to the tile's k0, of the unit that lane fetches with
+// direct-to-LDS load j of a K-contiguous tile (row 32w + 8j + lane/8, logical
+// unit (lane % 8) ^ ((row >> 1) & 7)).  Only the K-tail variant tests it, and
+// recomputes it there rather than holding it in registers.
+__device__ __forceinline__ int kc_kpos(int lane, int j) {
+    return ((lane & 7) ^ ((4 * j + (lane >> 4)) & 7)) * 8;
+}
+
+template <int LAYOUT, int EPI, bool OUT_BF16, bool CHECK_K>
 __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
-    GemmBatch batch, int64_t lda, int64_t ldb, int64_t ldc,
+    GemmBatch batch, int64_t lda, int64_t ldb, int64_t ldc, int64_t ldaux,
     int M, int N, int K, int tiles_m, int tiles_n)
 {
+    constexpr bool A_MC = LAYOUT == GEMM_TN;    // A stored [K,M]: M contiguous
+    constexpr bool B_KC = LAYOUT == GEMM_NT;    // B stored [N,K]: K contiguous
     // Two stages as two separate LDS objects: every access below names its
     // stage statically, which lets the compiler see that reads of one stage
     // do not depend on the direct-to-LDS loads still landing in the other.
@@ -180,79 +207,110 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
     const __bf16* __restrict__ B = batch.B[grp];
     const float* __restrict__ bias = batch.bias[grp];
     void* __restrict__ C = batch.C[grp];
+    __bf16* aux = batch.aux[grp];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int wm = (wid & 3) >> 1, wn = wid & 1, wh = wid >> 2;
 
-    const __bf16* a_tile = A + (int64_t)m0 * lda;
-    const __bf16* b_tile = B + n0;
+    const __bf16* a_tile = A_MC ? A + m0 : A + (int64_t)m0 * lda;
+    const __bf16* b_tile = B_KC ? B + (int64_t)n0 * ldb : B + n0;
 
     // ---- global -> LDS: direct (DMA) 16-byte buffer loads ---------------------
     // A buffer_load_dwordx4 ... lds instruction writes 64 lanes x 16 B = 1 KiB
     // contiguously in LDS (lane l at M0 + 16 l), so the swizzled LDS layout is
     // produced by choosing which global unit each lane fetches.  Wave w fills
-    // 4 KiB of each operand tile with 4 instructions each:
-    //   A: instruction j, lane l -> row 32w + 8j + l/8 (128 B rows), physical unit l%8
-    //   B: instruction j, lane l -> K row 8w + 2j + l/32 (512 B rows), physical unit l%32
-    // and the logical unit is the physical one XOR the row's swizzle.
+    // 4 KiB of each operand tile with 4 instructions, lane l of instruction j:
+    //   K-contiguous tile (256 rows x 64 K, 128 B rows): row 32w + 8j + l/8,
+    //     physical unit l%8, logical unit = physical ^ ((row >> 1) & 7);
+    //   M/N-contiguous tile (64 K rows x 256, 512 B rows): K row 8w + 2j + l/32,
+    //     physical unit l%32, logical unit = physical ^ ((K row & 3) << 2).
+    // The offsets are loop-invariant; a K step only moves the scalar base.
     unsigned a_off[LOADS], b_off[LOADS];
-    int a_kcol[LOADS], b_krow[LOADS];
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
         const int r = 32 * wid + 8 * j + (lane >> 3);
         const int u = (lane & 7) ^ ((r >> 1) & 7);
-        a_kcol[j] = u * 8;
-        a_off[j] = (m0 + r) < M ? (unsigned)(r * lda + u * 8) * 2u : OOB;
         const int kr = 8 * wid + 2 * j + (lane >> 5);
         const int ub = (lane & 31) ^ ((kr & 3) << 2);
-        b_krow[j] = kr;
-        b_off[j] = (n0 + ub * 8) < N ? (unsigned)(kr * ldb + ub * 8) * 2u : OOB;
+        if (A_MC)
+            a_off[j] = (m0 + ub * 8) < M ? (unsigned)(kr * lda + ub * 8) * 2u : OOB;
+        else
+            a_off[j] = (m0 + r) < M ? (unsigned)(r * lda + u * 8) * 2u : OOB;
+        if (B_KC)
+            b_off[j] = (n0 + r) < N ? (unsigned)(r * ldb + u * 8) * 2u : OOB;
+        else
+            b_off[j] = (n0 + ub * 8) < N ? (unsigned)(kr * ldb + ub * 8) * 2u : OOB;
     }
     auto dma_tile = [&](int k0, char* stage) {
-        // a tile past the last one gets an empty range: all loads write zeros
+        // A tile past the last one gets an empty range: all loads write zeros.
+        // In the K-tail variant, an operand stored with K as its row index gets
+        // a range ending at row K, so its rows past K read zeros the same way;
+        // a K-contiguous operand tests each unit's K position instead.
         const int nrec = k0 < K ? 0x7ffffff0 : 0;
+        auto tail = [&](int64_t ld) -> int {      // wave-uniform
+            const int64_t bytes = (int64_t)(K - k0) * ld * 2;
+            return __builtin_amdgcn_readfirstlane(
+                bytes <= 0 ? 0 : (int)(bytes < 0x7ffffff0 ? bytes : 0x7ffffff0));
+        };
         const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<__bf16*>(a_tile + k0), (short)0, nrec, 0x00020000);
+            const_cast<__bf16*>(A_MC ? a_tile + (int64_t)k0 * lda : a_tile + k0), (short)0,
+            (CHECK_K && A_MC) ? tail(lda) : nrec, 0x00020000);
         const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<__bf16*>(b_tile + (int64_t)k0 * ldb), (short)0, nrec, 0x00020000);
+            const_cast<__bf16*>(B_KC ? b_tile + k0 : b_tile + (int64_t)k0 * ldb), (short)0,
+            (CHECK_K && !B_KC) ? tail(ldb) : nrec, 0x00020000);
         char* sa = stage + wid * 4096;
         char* sb = stage + A_BYTES + wid * 4096;
 #pragma unroll
         for (int j = 0; j < LOADS; ++j)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 ar, LDS_PTR(void, sa + j * 1024), 16,
-                (!CHECK_K || (k0 + a_kcol[j]) < K) ? a_off[j] : OOB, 0, 0, 0);
+                (!CHECK_K || A_MC || k0 + kc_kpos(lane, j) < K) ? a_off[j] : OOB, 0, 0, 0);
 #pragma unroll
         for (int j = 0; j < LOADS; ++j)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 br, LDS_PTR(void, sb + j * 1024), 16,
-                (!CHECK_K || (k0 + b_krow[j]) < K) ? b_off[j] : OOB, 0, 0, 0);
+                (!CHECK_K || !B_KC || k0 + kc_kpos(lane, j) < K) ? b_off[j] : OOB, 0, 0, 0);
     };
     const int nk = (K + BK - 1) / BK;
 
     // ---- LDS -> register operand addresses (MFMA 16x16x32) -------------------
-    // A operand: lane holds row (lane & 15), K values 8*(lane >> 4) .. +7 of the
-    // 32-wide k-step.
-    const int a_r = wm * 128 + (lane & 15);
-    const int a_swz = (a_r >> 1) & 7;
-    unsigned a_rd[2];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-        a_rd[kk] = a_r * 128 + (((kk * 4 + (lane >> 4)) ^ a_swz) << 4);
-    // B operand via transpose reads: the 16-lane group g reads K rows 8g..8g+3
-    // (and +4 for the second read) of 16 columns; lane gi addresses row
-    // (gi >> 2), columns 4*(gi & 3)..+3 and receives column gi.
+    // An MFMA operand block: lane holds row/column (lane & 15) of 16 and the K
+    // values 8*(lane >> 4) .. +7 of the 32-wide k-step.
+    //  * from a K-contiguous tile: one 16-byte read of row (lane & 15); the
+    //    row's swizzle does not depend on which 16-row block is read;
+    //  * from an M/N-contiguous tile: two transpose reads; the 16-lane group g
+    //    reads K rows 8g..8g+3 (and +4) of 16 columns, lane gi addressing row
+    //    (gi >> 2), columns 4*(gi & 3)..+3 and receiving column gi.
     const int g = lane >> 4, gi = lane & 15;
-    const int b_row = 8 * g + (gi >> 2);              // + 32*kk (+4 for the second half)
-    unsigned b_rd[NJ];
+    const unsigned kc_rd = (lane & 15) * 128 + (((lane >> 4) ^ (((lane & 15) >> 1) & 7)) << 4);
+    auto mc_rd = [&](int col) -> unsigned {      // col: first column of the block
+        const int row = 8 * g + (gi >> 2);
+        const int c = col + 4 * (gi & 3);
+        return row * 512 + (((c >> 3) ^ ((row & 3) << 2)) << 4) + (c & 7) * 2;
+    };
+    // For an M-contiguous A, block mi's address is block 0's with bits 5-7
+    // XOR-ed by mi (the 16-column blocks differ only in the swizzled unit
+    // bits 1-3).
+    const unsigned a_rd0 = A_MC ? mc_rd(wm * 128) : wm * 128 * 128 + kc_rd;
+    unsigned b_rd[B_KC ? 1 : NJ];
+    if constexpr (B_KC) {
+        b_rd[0] = A_BYTES + (wn * 128 + wh * 64) * 128 + kc_rd;
+    } else {
 #pragma unroll
-    for (int nj = 0; nj < NJ; ++nj) {
-        const int col = wn * 128 + wh * 64 + nj * 16 + 4 * (gi & 3);
-        const int unit = col >> 3;
-        b_rd[nj] = A_BYTES + b_row * 512 + ((unit ^ ((b_row & 3) << 2)) << 4) + (col & 7) * 2;
+        for (int nj = 0; nj < NJ; ++nj) b_rd[nj] = A_BYTES + mc_rd(wn * 128 + wh * 64 + 16 * nj);
     }
+    auto read_kc = [&](const char* base, unsigned addr, int blk, int kk) -> bf16x8 {
+        // 16-byte unit (4kk + lane>>4) of the row: XOR with kk*4 keeps the swizzle
+        return *(const bf16x8*)(base + ((addr + blk * 16 * 128) ^ (kk << 6)));
+    };
+    auto read_mc = [&](const char* base, unsigned addr, int kk) -> bf16x8 {
+        const char* p = base + addr + kk * 32 * 512;
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, p));
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, p + 4 * 512));
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
 
     f32x4 acc[NI][NJ];
 #pragma unroll
@@ -265,15 +323,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
     bf16x8 fa[NI], fb[2][NJ];
     auto load_b = [&](bf16x8 (&b)[NJ], const char* base, int kk) {
 #pragma unroll
-        for (int nj = 0; nj < NJ; ++nj) {
-            const char* p = base + b_rd[nj] + kk * 32 * 512;
-            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, p));
-            const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, p + 4 * 512));
-            b[nj] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        }
+        for (int nj = 0; nj < NJ; ++nj)
+            if constexpr (B_KC) b[nj] = read_kc(base, b_rd[0], nj, kk);
+            else b[nj] = read_mc(base, b_rd[nj], kk);
     };
     auto load_a = [&](int mi, const char* base, int kk) {
-        fa[mi] = *(const bf16x8*)(base + a_rd[kk] + mi * 16 * 128);
+        if constexpr (A_MC) fa[mi] = read_mc(base, a_rd0 ^ (mi << 5), kk);
+        else fa[mi] = read_kc(base, a_rd0, mi, kk);
     };
     // MFMAs of one k-step on fa / bc; the next k-step's operands come from
     // (nbase, nkk): B into bn first, each A block into fa[mi] after its last use
@@ -300,12 +356,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
     // tile sits before the second, whose operand reloads read the next tile
     auto tile = [&](const char* cur_c, char* cur, const char* nxt, int k_next2) {
         kstep(fb[0], fb[1], cur_c, 1);
-        sched_kstep<0>();
+        sched_kstep<0, A_MC ? 2 : 1, B_KC ? 1 : 2>();
         __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();                            // next tile visible; `cur` free
         dma_tile(k_next2, cur);                     // empty range past the last tile
         kstep(fb[1], fb[0], nxt, 0);
-        sched_kstep<2 * LOADS>();
+        sched_kstep<2 * LOADS, A_MC ? 2 : 1, B_KC ? 1 : 2>();
     };
     int kt = 0;
     for (; kt + 1 < nk; kt += 2) {
@@ -327,9 +383,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
         bv[nj] = (bias && n0 + lcol + 16 * nj < N) ? bias[n0 + lcol + 16 * nj] : 0.0f;
     auto value = [&](int mi, int nj, int r) {
         const float v = acc[mi][nj][r] + bv[nj];
-        return GELU ? gelu(v) : v;
+        return EPI == EPI_GELU ? gelu(v) : v;
     };
-    if constexpr (OUT_BF16) {
+    if constexpr (OUT_BF16 && (EPI == EPI_NONE || EPI == EPI_GELU)) {
         char* half = wm ? lds1 : lds0;
 #pragma unroll
         for (int nj = 0; nj < NJ; ++nj) {
@@ -355,6 +411,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
                 *(bf16x8*)((__bf16*)C + (int64_t)grow * ldc + gcol) = *(const bf16x8*)src;
         }
     } else {
+        // f32 staging in two passes of 64 rows per half; the store phase applies
+        // the element-wise epilogues that need a second operand or output
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
             char* half = wm ? lds1 : lds0;
@@ -378,8 +436,32 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
                 const char* src = (lrow < 64 ? lds0 : lds1) + q * 1024 +
                                   ((unit ^ (((q >> 2) & 3) << 2)) << 4);
                 const int grow = m0 + (lrow >> 6) * 128 + 64 * p + q, gcol = n0 + unit * 4;
-                if (grow < M && gcol < N)
-                    *(f32x4*)((float*)C + (int64_t)grow * ldc + gcol) = *(const f32x4*)src;
+                if (grow < M && gcol < N) {
+                    f32x4 v = *(const f32x4*)src;
+                    const int64_t o = (int64_t)grow * ldc + gcol;
+                    if constexpr (EPI == EPI_GELU_BWD) {
+                        const bf16x4 y = *(const bf16x4*)(aux + (int64_t)grow * ldaux + gcol);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) v[e] *= gelu_grad((float)y[e]);
+                    }
+                    if constexpr (EPI == EPI_DUAL) {
+                        bf16x4 y, yp;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            y[e] = (__bf16)v[e];
+                            yp[e] = (__bf16)gelu(v[e]);
+                        }
+                        *(bf16x4*)(aux + (int64_t)grow * ldaux + gcol) = y;
+                        *(bf16x4*)((__bf16*)C + o) = yp;
+                    } else if constexpr (OUT_BF16) {
+                        bf16x4 c;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) c[e] = (__bf16)v[e];
+                        *(bf16x4*)((__bf16*)C + o) = c;
+                    } else {
+                        *(f32x4*)((float*)C + o) = v;
+                    }
+                }
             }
             if (p == 0) __syncthreads();
         }
@@ -388,10 +470,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
 
 }  // namespace
 
-hipError_t gemm_bf16_batched(const GemmBatch& batch, int64_t lda, int64_t ldb, int64_t ldc,
-                             int64_t M, int64_t N, int64_t K, bool out_bf16, bool gelu,
-                             hipStream_t stream)
+hipError_t gemm_bf16_batched(const GemmBatch& batch, int layout, int epi, int64_t lda,
+                             int64_t ldb, int64_t ldc, int64_t ldaux, int64_t M, int64_t N,
+                             int64_t K, bool out_bf16, hipStream_t stream)
 {
+    if (M <= 0 || N <= 0 || batch.count <= 0) return hipSuccess;
     const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
     GemmBatch b = batch;
     bool shared_a = b.count > 1;
@@ -401,14 +484,40 @@ hipError_t gemm_bf16_batched(const GemmBatch& batch, int64_t lda, int64_t ldb, i
                                : (tiles_m * tiles_n + 7) / 8;
     const dim3 grid(8 * per_xcd * b.count), block(NTHREADS);
     const bool ck = (K % BK) != 0;
-#define TP_GEMM(OB, GL, CK) hipLaunchKernelGGL((gemm_bf16_kernel<OB, GL, CK>), grid, block, 0, \
-        stream, b, lda, ldb, ldc, (int)M, (int)N, (int)K, tiles_m, tiles_n)
-    if (out_bf16 && gelu)  { if (ck) TP_GEMM(true, true, true);   else TP_GEMM(true, true, false); }
-    else if (out_bf16)     { if (ck) TP_GEMM(true, false, true);  else TP_GEMM(true, false, false); }
-    else if (gelu)         { if (ck) TP_GEMM(false, true, true);  else TP_GEMM(false, true, false); }
-    else                   { if (ck) TP_GEMM(false, false, true); else TP_GEMM(false, false, false); }
+#define TP_GEMM(L, E, OB)                                                                      \
+    do {                                                                                       \
+        if (ck)                                                                                \
+            hipLaunchKernelGGL((gemm_bf16_kernel<L, E, OB, true>), grid, block, 0, stream, b,  \
+                               lda, ldb, ldc, ldaux, (int)M, (int)N, (int)K, tiles_m, tiles_n); \
+        else                                                                                   \
+            hipLaunchKernelGGL((gemm_bf16_kernel<L, E, OB, false>), grid, block, 0, stream, b, \
+                               lda, ldb, ldc, ldaux, (int)M, (int)N, (int)K, tiles_m, tiles_n); \
+        return hipGetLastError();                                                              \
+    } while (0)
+    switch (layout) {
+    case GEMM_NN:
+        if (epi == EPI_NONE) { if (out_bf16) TP_GEMM(GEMM_NN, EPI_NONE, true); TP_GEMM(GEMM_NN, EPI_NONE, false); }
+        if (epi == EPI_GELU) { if (out_bf16) TP_GEMM(GEMM_NN, EPI_GELU, true); TP_GEMM(GEMM_NN, EPI_GELU, false); }
+        if (epi == EPI_DUAL && out_bf16) TP_GEMM(GEMM_NN, EPI_DUAL, true);
+        break;
+    case GEMM_NT:
+        if (epi == EPI_NONE) { if (out_bf16) TP_GEMM(GEMM_NT, EPI_NONE, true); TP_GEMM(GEMM_NT, EPI_NONE, false); }
+        if (epi == EPI_GELU_BWD) { if (out_bf16) TP_GEMM(GEMM_NT, EPI_GELU_BWD, true); TP_GEMM(GEMM_NT, EPI_GELU_BWD, false); }
+        break;
+    case GEMM_TN:
+        if (epi == EPI_NONE) { if (out_bf16) TP_GEMM(GEMM_TN, EPI_NONE, true); TP_GEMM(GEMM_TN, EPI_NONE, false); }
+        break;
+    }
 #undef TP_GEMM
-    return hipGetLastError();
+    return hipErrorInvalidValue;      // a layout / epilogue pair with no kernel
+}
+
+hipError_t gemm_bf16_batched(const GemmBatch& batch, int64_t lda, int64_t ldb, int64_t ldc,
+                             int64_t M, int64_t N, int64_t K, bool out_bf16, bool gelu,
+                             hipStream_t stream)
+{
+    return gemm_bf16_batched(batch, GEMM_NN, gelu ? EPI_GELU : EPI_NONE, lda, ldb, ldc, 0, M, N,
+                             K, out_bf16, stream);
 }
 
 hipError_t gemm_bf16(const void* A, int64_t lda, const void* B, int64_t ldb,

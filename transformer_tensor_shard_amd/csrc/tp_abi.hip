@@ -42,7 +42,7 @@ tp_status check_linear(const void* X, int64_t ldx, const void* W, int64_t ldw, c
     if (!aligned16(X) || !aligned16(W) || !aligned16(C) || (bias && !aligned16(bias)))
         return TP_ERR_ALIGN;
     if (in == TP_BF16) {
-        if (K % 8 || N % 8 || ldx % 8 || ldw % 8 || !gemm_bf16_fits(M, N, K, ldx, ldw))
+        if (K % 8 || N % 8 || ldx % 8 || ldw % 8 || ldc % 8 || !gemm_bf16_fits(M, N, K, ldx, ldw))
             return TP_ERR_SHAPE;
     } else if (M > kI32 || N > kI32 || K > kI32) {
         return TP_ERR_SHAPE;
@@ -58,6 +58,68 @@ hipError_t run_linear(const void* X, int64_t ldx, const void* W, int64_t ldw, co
                               out == TP_BF16, gelu, st);
     return tpk::gemm_f32((const float*)X, ldx, (const float*)W, ldw, (const float*)bias, C, ldc,
                          M, N, K, out == TP_BF16, gelu, st);
+}
+
+// ---- general bf16 product (tp_matmul) -------------------------------------
+// A K-contiguous operand tile spans 256 rows of the operand, an M/N-contiguous
+// one 64 K rows; the kernel addresses a tile with 32-bit byte offsets.
+bool operand_fits(int64_t ld, bool k_contiguous) {
+    return ld * 2 * (k_contiguous ? 256 : 64) < kI32;
+}
+
+int gemm_epi(int epi) {
+    switch (epi) {
+    case TP_EPI_GELU: return tpk::EPI_GELU;
+    case TP_EPI_GELU_BWD: return tpk::EPI_GELU_BWD;
+    case TP_EPI_GELU_SAVE: return tpk::EPI_DUAL;
+    default: return tpk::EPI_NONE;
+    }
+}
+
+bool matmul_supported(int ta, int tb, int out, int epi) {
+    if (ta == 0 && tb == 0)
+        return epi == TP_EPI_NONE || epi == TP_EPI_GELU || (epi == TP_EPI_GELU_SAVE && out == TP_BF16);
+    if (ta == 0 && tb == 1) return epi == TP_EPI_NONE || epi == TP_EPI_GELU_BWD;
+    if (ta == 1 && tb == 0) return epi == TP_EPI_NONE;
+    return false;
+}
+
+tp_status check_matmul(const void* A, int64_t lda, int ta, const void* B, int64_t ldb, int tb,
+                       const void* bias, const void* C, int64_t ldc, const void* aux,
+                       int64_t ldaux, int64_t M, int64_t N, int64_t K, int out, int epi) {
+    if (!A || !B || !C) return TP_ERR_NULL;
+    if (!is_dtype(out) || !matmul_supported(ta, tb, out, epi)) return TP_ERR_DTYPE;
+    const bool uses_aux = epi == TP_EPI_GELU_BWD || epi == TP_EPI_GELU_SAVE;
+    if (uses_aux && !aux) return TP_ERR_NULL;
+    if (M <= 0 || N <= 0 || K <= 0 || M > kI32 || N > kI32 || K > kI32) return TP_ERR_SHAPE;
+    if (lda < (ta ? M : K) || ldb < (tb ? K : N) || ldc < N || (uses_aux && ldaux < N))
+        return TP_ERR_SHAPE;
+    // every contiguous dimension and leading dimension a multiple of 8
+    if ((ta ? M : K) % 8 || (tb ? K : N) % 8 || N % 8 || lda % 8 || ldb % 8 || ldc % 8 ||
+        (uses_aux && ldaux % 8))
+        return TP_ERR_SHAPE;
+    if (!operand_fits(lda, !ta) || !operand_fits(ldb, tb != 0) ||
+        ((M + 255) / 256) * ((N + 255) / 256) > kI32 / 8)
+        return TP_ERR_SHAPE;
+    if (!aligned16(A) || !aligned16(B) || !aligned16(C) || (bias && !aligned16(bias)) ||
+        (uses_aux && !aligned16(aux)))
+        return TP_ERR_ALIGN;
+    return TP_OK;
+}
+
+hipError_t run_matmul(const void* A, int64_t lda, int ta, const void* B, int64_t ldb, int tb,
+                      const void* bias, void* C, int64_t ldc, void* aux, int64_t ldaux,
+                      int64_t M, int64_t N, int64_t K, int out, int epi, hipStream_t st) {
+    tpk::GemmBatch gb = {};
+    gb.A[0] = (const __bf16*)A;
+    gb.B[0] = (const __bf16*)B;
+    gb.bias[0] = (const float*)bias;
+    gb.C[0] = C;
+    gb.aux[0] = (__bf16*)aux;
+    gb.count = 1;
+    const int layout = ta ? tpk::GEMM_TN : (tb ? tpk::GEMM_NT : tpk::GEMM_NN);
+    return tpk::gemm_bf16_batched(gb, layout, gemm_epi(epi), lda, ldb, ldc, ldaux, M, N, K,
+                                  out == TP_BF16, st);
 }
 
 // ---- MLP shard ------------------------------------------------------------
@@ -244,6 +306,107 @@ TP_EXPORT tp_status tp_mlp_shard(const void* X, const void* A_i, const void* a_i
     if (!ws || ws_bytes < (size_t)mlp_ws(M, f, in)) return TP_ERR_WORKSPACE;
     if (!aligned16(ws)) return TP_ERR_ALIGN;
     return launched(run_mlp(X, A_i, a_i, B_i, Z_i, ws, M, h, f, in, out, as_stream(stream)));
+}
+
+TP_EXPORT tp_status tp_matmul(const void* A, int64_t lda, int trans_a, const void* B,
+                              int64_t ldb, int trans_b, const void* bias, void* C, int64_t ldc,
+                              void* aux, int64_t ldaux, int64_t M, int64_t N, int64_t K, int out,
+                              int epilogue, void* stream) {
+    const tp_status s = check_matmul(A, lda, trans_a, B, ldb, trans_b, bias, C, ldc, aux, ldaux,
+                                     M, N, K, out, epilogue);
+    if (s != TP_OK) return s;
+    return launched(run_matmul(A, lda, trans_a, B, ldb, trans_b, bias, C, ldc, aux, ldaux, M, N,
+                               K, out, epilogue, as_stream(stream)));
+}
+
+// ---- MLP shard: training forward and backward ------------------------------
+namespace {
+struct MlpBwdWs {
+    int64_t dy, part, total;   // byte offsets: dY bf16 [M,f]; bias partials f32 [chunks,f]
+};
+MlpBwdWs mlp_bwd_ws(int64_t M, int64_t f) {
+    MlpBwdWs w;
+    w.dy = 0;
+    w.part = align_up(M * f * 2);
+    w.total = w.part + align_up(tpk::col_sum_chunks(M) * f * 4);
+    return w;
+}
+
+tp_status check_mlp_train(int64_t M, int64_t h, int64_t f) {
+    if (M <= 0 || h <= 0 || f <= 0 || M > kI32 || h > kI32 || f > kI32) return TP_ERR_SHAPE;
+    if (h % 8 || f % 8) return TP_ERR_SHAPE;
+    // K-contiguous operands have leading dimension h or f, M/N-contiguous ones too
+    if (!operand_fits(h, true) || !operand_fits(f, true)) return TP_ERR_SHAPE;
+    const int64_t big = M > h ? (M > f ? M : f) : (h > f ? h : f);
+    if (((big + 255) / 256) * ((big + 255) / 256) > kI32 / 8) return TP_ERR_SHAPE;
+    if (tpk::col_sum_chunks(M) > 65535) return TP_ERR_SHAPE;
+    return TP_OK;
+}
+}  // namespace
+
+TP_EXPORT tp_status tp_mlp_shard_train_fwd(const void* X, const void* A_i, const void* a_i,
+                                           const void* B_i, void* Z_i, void* Y_i, void* Yp_i,
+                                           int64_t M, int64_t h, int64_t f, int out,
+                                           void* stream) {
+    if (!X || !A_i || !B_i || !Z_i || !Y_i || !Yp_i) return TP_ERR_NULL;
+    if (!is_dtype(out)) return TP_ERR_DTYPE;
+    tp_status s = check_mlp_train(M, h, f);
+    if (s != TP_OK) return s;
+    if (!aligned16(X) || !aligned16(A_i) || !aligned16(B_i) || !aligned16(Z_i) ||
+        !aligned16(Y_i) || !aligned16(Yp_i) || (a_i && !aligned16(a_i)))
+        return TP_ERR_ALIGN;
+    const hipStream_t st = as_stream(stream);
+    // Y = X·A_i + a_i and Y' = GeLU(Y) in one epilogue; then Z_i = Y'·B_i
+    if (run_matmul(X, h, 0, A_i, f, 0, a_i, Yp_i, f, Y_i, f, M, f, h, TP_BF16,
+                   TP_EPI_GELU_SAVE, st))
+        return TP_ERR_LAUNCH;
+    return launched(run_matmul(Yp_i, f, 0, B_i, h, 0, nullptr, Z_i, h, nullptr, 0, M, h, f, out,
+                               TP_EPI_NONE, st));
+}
+
+TP_EXPORT size_t tp_mlp_shard_backward_workspace(int64_t M, int64_t f) {
+    if (M <= 0 || f <= 0) return 0;
+    return (size_t)mlp_bwd_ws(M, f).total;
+}
+
+TP_EXPORT tp_status tp_mlp_shard_backward(const void* X, const void* A_i, const void* B_i,
+                                          const void* Y_i, const void* Yp_i, const void* dZ,
+                                          void* dX_i, void* dA_i, void* dB_i, void* da_i,
+                                          void* ws, size_t ws_bytes, int64_t M, int64_t h,
+                                          int64_t f, int dx_dtype, void* stream) {
+    if (!X || !A_i || !B_i || !Y_i || !Yp_i || !dZ || !dX_i || !dA_i || !dB_i)
+        return TP_ERR_NULL;
+    if (!is_dtype(dx_dtype)) return TP_ERR_DTYPE;
+    tp_status s = check_mlp_train(M, h, f);
+    if (s != TP_OK) return s;
+    const MlpBwdWs w = mlp_bwd_ws(M, f);
+    if (!ws || ws_bytes < (size_t)w.total) return TP_ERR_WORKSPACE;
+    if (!aligned16(X) || !aligned16(A_i) || !aligned16(B_i) || !aligned16(Y_i) ||
+        !aligned16(Yp_i) || !aligned16(dZ) || !aligned16(dX_i) || !aligned16(dA_i) ||
+        !aligned16(dB_i) || (da_i && !aligned16(da_i)) || !aligned16(ws))
+        return TP_ERR_ALIGN;
+    const hipStream_t st = as_stream(stream);
+    char* base = (char*)ws;
+    void* dY = base + w.dy;
+    // dY = (dZ·B_i^T) ⊙ GeLU'(Y_i)            [M,f] bf16
+    if (run_matmul(dZ, h, 0, B_i, h, 1, nullptr, dY, f, (void*)Y_i, f, M, f, h, TP_BF16,
+                   TP_EPI_GELU_BWD, st))
+        return TP_ERR_LAUNCH;
+    // dB_i = Y'_i^T·dZ                         [f,h] f32
+    if (run_matmul(Yp_i, f, 1, dZ, h, 0, nullptr, dB_i, h, nullptr, 0, f, h, M, TP_F32,
+                   TP_EPI_NONE, st))
+        return TP_ERR_LAUNCH;
+    // dA_i = X^T·dY                            [h,f] f32
+    if (run_matmul(X, h, 1, dY, f, 0, nullptr, dA_i, f, nullptr, 0, h, f, M, TP_F32, TP_EPI_NONE,
+                   st))
+        return TP_ERR_LAUNCH;
+    // dX_i = dY·A_i^T                          [M,h] partial over ranks
+    if (run_matmul(dY, f, 0, A_i, f, 1, nullptr, dX_i, h, nullptr, 0, M, h, f, dx_dtype,
+                   TP_EPI_NONE, st))
+        return TP_ERR_LAUNCH;
+    if (da_i)
+        return launched(tpk::col_sum((float*)da_i, dY, f, M, f, (float*)(base + w.part), st));
+    return TP_OK;
 }
 
 TP_EXPORT size_t tp_attn_shard_workspace(int64_t b, int64_t s, int64_t H_l, int64_t d) {

@@ -6,18 +6,37 @@
 
 namespace tpk {
 
+// Operand layouts of the bf16 GEMM (row-major storage, leading dimensions in
+// elements): NN  A [M,K], B [K,N];  NT  A [M,K], B [N,K] (C = A·B^T);
+// TN  A [K,M], B [K,N] (C = A^T·B).
+enum GemmLayout { GEMM_NN = 0, GEMM_NT = 1, GEMM_TN = 2 };
+// Epilogues: v = acc + bias;  NONE  C = v;  GELU  C = GeLU(v);
+// GELU_BWD  C = v · GeLU'(aux) (aux: the saved bf16 pre-activation);
+// DUAL  C = bf16 GeLU(v) and aux = bf16 v (the training forward).
+enum GemmEpi { EPI_NONE = 0, EPI_GELU = 1, EPI_GELU_BWD = 2, EPI_DUAL = 3 };
+
 // Up to kMaxBatch independent GEMMs of one shape, launched together: group g
-// computes C[g] = epi(A[g]·B[g] + bias[g]).  Used for the emulated ranks of a
-// block, whose per-rank products have identical shapes.
+// computes C[g] = epi(op(A[g])·op(B[g]) + bias[g]).  Used for the emulated
+// ranks of a block, whose per-rank products have identical shapes.
 constexpr int kMaxBatch = 16;
 struct GemmBatch {
     const __bf16* A[kMaxBatch];
     const __bf16* B[kMaxBatch];
     const float* bias[kMaxBatch];
     void* C[kMaxBatch];
+    __bf16* aux[kMaxBatch];   // GELU_BWD: read, DUAL: written; [M,N] with ldaux
     int count;
     int band;       // set by the launcher: tile order for groups sharing A
 };
+// Supported (layout, epilogue, output) combinations: NN with NONE / GELU
+// (bf16 or f32) and DUAL (bf16); NT with NONE / GELU_BWD (bf16 or f32); TN with
+// NONE (bf16 or f32).  Others return hipErrorInvalidValue.  The caller checks
+// shapes: M, N, K multiples of 8 along contiguous dimensions, leading
+// dimensions multiples of 8.
+hipError_t gemm_bf16_batched(const GemmBatch& batch, int layout, int epi, int64_t lda,
+                             int64_t ldb, int64_t ldc, int64_t ldaux, int64_t M, int64_t N,
+                             int64_t K, bool out_bf16, hipStream_t stream);
+// The forward (NN) form: epilogue GELU or NONE.
 hipError_t gemm_bf16_batched(const GemmBatch& batch, int64_t lda, int64_t ldb, int64_t ldc,
                              int64_t M, int64_t N, int64_t K, bool out_bf16, bool gelu,
                              hipStream_t stream);
@@ -58,6 +77,14 @@ hipError_t partial_sum(void* Z, bool out_bf16, const void* parts, bool parts_bf1
 hipError_t row_sum(void* Z, bool out_bf16, const void* parts, bool parts_bf16, int P,
                    int64_t M, int64_t h, const float* bias, const void* residual, bool res_bf16,
                    void* ln_out, const float* gamma, const float* beta, float eps,
+                   hipStream_t stream);
+
+// out[n] = Σ_m X[m, n] for bf16 X [M, N] (N % 8 == 0, ldx % 8 == 0) in a
+// fixed order: row chunks of kColSumRows summed into part [chunks, N] f32
+// (chunks = col_sum_chunks(M) <= 65535), then the chunks in order.
+constexpr int64_t kColSumRows = 256;
+int64_t col_sum_chunks(int64_t M);
+hipError_t col_sum(float* out, const void* X, int64_t ldx, int64_t M, int64_t N, float* part,
                    hipStream_t stream);
 
 // Register-only MFMA 16x16x32 bf16 loop: `blocks` workgroups of 8 waves, each
