@@ -20,7 +20,13 @@ Besides the one JSON line the run reports, in the same line:
                 same workload;
   calibration   the throughput of a register-only MFMA loop on this GPU (the
                 matrix cores' ceiling under the current clock and power
-                limits) and of the vendor GEMM at the dominant kernel's shape.
+                limits) and of the vendor GEMM at the dominant kernel's shape;
+  training      (block workload) rank 0's MLP-share backward at the same
+                shape, timed with HIP events.
+
+--workload mlp_bwd_bf16_h12288_tp8 measures that backward as its own step
+(dY, dB_i, dA_i, da_i and the dX_i partial of one rank at the 175B layer
+shape), with the weight-gradient product X^T·dY as its dominant kernel.
 
 Modes for profiler runs: --mode kernel launches only the dominant kernel,
 --mode copy only a plain device copy of a known size (counter calibration).
@@ -43,7 +49,13 @@ METRIC = "TFLOP/s per TP shard (bf16) and % of MI355X dense bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 FLOP/clk x 2.4 GHz, dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 COPY_BYTES = 1 << 30
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_gelu_h12288_f6144_traffic.txt")
+# committed counter summaries of each workload's dominant kernel (HBM bytes per launch)
+TRAFFIC_FILES = {
+    "block_bf16_h12288_tp8": os.path.join(ROOT, "profiles", "gemm_gelu_h12288_f6144_traffic.txt"),
+    "mlp_bwd_bf16_h12288_tp8": os.path.join(ROOT, "profiles",
+                                            "gemm_tn_wgrad_h12288_f6144_traffic.txt"),
+}
+TRAFFIC_FILE = TRAFFIC_FILES["block_bf16_h12288_tp8"]
 
 
 def log(msg):
@@ -95,29 +107,31 @@ def blas_threads():
         return 1
 
 
-def calibration(tts, torch, X, W, stream):
+def calibration(tts, torch, X, W, stream, trans_a=False):
     """Two reference points measured on this GPU in this run, for reading the
     roofline fraction: the throughput of a register-only MFMA loop (the
     matrix cores' ceiling under the current clock and power limits), and the
     vendor GEMM (torch.mm, i.e. hipBLASLt) at the dominant kernel's per-rank
-    shape."""
+    shape and layout (X^T·W when trans_a)."""
     out = torch.empty(256 * 512, dtype=torch.float32, device=X.device)
     for _ in range(3):
         tts.tp_probe_mfma(256, 200, out=out)
     probe_flops = 256 * 8 * 32 * 200 * 16384
     ms, _ = event_time(lambda: tts.tp_probe_mfma(256, 200, out=out), 5, stream)
-    Y = torch.empty(X.shape[0], W.shape[1], dtype=torch.bfloat16, device=X.device)
+    Xop = X.t() if trans_a else X
+    Y = torch.empty(Xop.shape[0], W.shape[1], dtype=torch.bfloat16, device=X.device)
     for _ in range(2):
-        torch.mm(X, W, out=Y)
-    ms_mm, _ = event_time(lambda: torch.mm(X, W, out=Y), 5, stream)
-    mm_flops = 2 * X.shape[0] * X.shape[1] * W.shape[1]
+        torch.mm(Xop, W, out=Y)
+    ms_mm, _ = event_time(lambda: torch.mm(Xop, W, out=Y), 5, stream)
+    mm_flops = 2 * Xop.shape[0] * Xop.shape[1] * W.shape[1]
     return {
         "mfma_only": {"tflops": round(probe_flops / (ms * 1e-3) / 1e12, 1),
                       "frac_of_peak": round(probe_flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                       "kernel": "tp_probe_mfma: register-only MFMA 16x16x32 bf16, 2 waves/SIMD"},
         "vendor_gemm": {"tflops": round(mm_flops / (ms_mm * 1e-3) / 1e12, 1),
-                        "kernel": "torch.mm bf16 [%dx%d]x[%dx%d] (hipBLASLt)" % (
-                            X.shape[0], X.shape[1], W.shape[0], W.shape[1])},
+                        "kernel": "torch.mm bf16 %s[%dx%d]x[%dx%d] (hipBLASLt)" % (
+                            "transposed A " if trans_a else "", Xop.shape[0], Xop.shape[1],
+                            W.shape[0], W.shape[1])},
     }
 
 
@@ -129,6 +143,10 @@ def dominant_operands_cpu(w, wl):
     if w.kind == "mlp":
         X, A, _ = wl.mlp_inputs(w)
         return X, [A]
+    if w.kind == "mlp_bwd":
+        # the weight-gradient product X^T·dY; dY's values do not change its cost
+        X = wl.mlp_bwd_inputs(w)[0]
+        return X, [wl.normal((w.M, w.f), 1.0, w.seed, "preact", w.dtype)]
     X, Wqkv, _ = wl.attn_inputs(w)
     return X, [Wqkv]
 
@@ -141,6 +159,14 @@ def dominant_kernel(w, tts, torch, X, Ws, dev):
     projection."""
     M, K = X.shape
     N = Ws[0].shape[1]
+    if w.kind == "mlp_bwd":
+        # dA_i = X^T·dY: [h, M]·[M, f], K = the token count, f32 out
+        dA = torch.empty(K, N, dtype=torch.float32, device=dev)
+
+        def launch():
+            tts.tp_matmul(X, Ws[0], trans_a=True, out=dA)
+        name = "gemm_bf16_kernel<TN, f32 out> X^T·dY [%dx%d]x[%dx%d]" % (K, M, M, N)
+        return launch, 2 * M * N * K, name
     gelu = w.kind != "attn"
     outs = [torch.empty(M, N, dtype=torch.bfloat16, device=dev) for _ in Ws]
     if len(Ws) > 1:
@@ -161,6 +187,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="block_bf16_h12288_tp8")
+    ap.add_argument("--no-training", action="store_true",
+                    help="skip the MLP-backward measurement added to the block line")
     ap.add_argument("--mode", default="step", choices=["step", "kernel", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=768,
@@ -235,6 +263,24 @@ def main():
         def step():
             tts.tp_mlp_shard(x, A0, B0, out=out, ws=ws)
         X_k, W_k = x, [A0]
+    elif w.kind == "mlp_bwd":
+        X_cpu, A_cpu, B_cpu, a_cpu, dZ_cpu = wl.mlp_bwd_inputs(w)
+        x, A0, B0, a0, dZ = (t.to(dev) for t in (X_cpu, A_cpu, B_cpu, a_cpu, dZ_cpu))
+        M, h, f = w.M, w.h, w.f
+        # the saved activations come from the training forward, outside the timed step
+        _, Y0, Yp0 = tts.tp_mlp_shard_train_fwd(x, A0, B0, a0)
+        bwd_out = dict(dX_out=torch.empty(M, h, dtype=torch.float32, device=dev),
+                       dA_out=torch.empty(h, f, dtype=torch.float32, device=dev),
+                       dB_out=torch.empty(f, h, dtype=torch.float32, device=dev),
+                       da_out=torch.empty(f, dtype=torch.float32, device=dev),
+                       ws=torch.empty(tts.tp_mlp_shard_backward_workspace(M, f),
+                                      dtype=torch.uint8, device=dev))
+
+        def step():
+            tts.tp_mlp_shard_backward(x, A0, B0, Y0, Yp0, dZ, **bwd_out)
+        dY0 = tts.tp_matmul(dZ, B0, trans_b=True, epilogue="gelu_bwd", aux=Y0,
+                            out_dtype=torch.bfloat16)
+        X_k, W_k = x, [dY0]
     else:
         X_cpu, Wqkv_cpu, Wo_cpu = wl.attn_inputs(w)
         x, Wqkv0, Wo0 = X_cpu.to(dev), Wqkv_cpu.to(dev), Wo_cpu.to(dev)
@@ -274,9 +320,9 @@ def main():
 
     kern_ms, kern_all = event_time(kernel, max(args.steps, 5), stream)
     kern_tflops = kern_flops / (kern_ms * 1e-3) / 1e12
-    traffic = measured_traffic()
+    traffic = measured_traffic(TRAFFIC_FILES[w.name]) if w.name in TRAFFIC_FILES else None
     log(f"dominant kernel: {kern_ms:.3f} ms/launch, {kern_tflops:.1f} TFLOP/s")
-    calib = calibration(tts, torch, X_k, W_k[0], stream)
+    calib = calibration(tts, torch, X_k, W_k[0], stream, trans_a=w.kind == "mlp_bwd")
     log(f"calibration: {calib}")
 
     components = {}
@@ -324,6 +370,32 @@ def main():
             components[name] = c
             log(f"component {name}: {c}")
         del qkv_all, o_all, y_all, parts
+    if w.kind == "mlp_bwd":
+        fl1 = 2 * M * h * f
+        dYc = torch.empty(M, f, dtype=torch.bfloat16, device=dev)
+        items = {
+            "dY_gemm_nt_gelu_bwd": (lambda: tts.tp_matmul(dZ, B0, trans_b=True,
+                                                          epilogue="gelu_bwd", aux=Y0, out=dYc),
+                                    fl1, None),
+            "dB_gemm_tn": (lambda: tts.tp_matmul(Yp0, dZ, trans_a=True, out=bwd_out["dB_out"]),
+                           fl1, None),
+            "dA_gemm_tn": (lambda: tts.tp_matmul(x, dYc, trans_a=True, out=bwd_out["dA_out"]),
+                           fl1, None),
+            "dX_gemm_nt": (lambda: tts.tp_matmul(dYc, A0, trans_b=True, out=bwd_out["dX_out"]),
+                           fl1, None),
+        }
+        for name, (fn, fl, by) in items.items():
+            fn()
+            t, _ = event_time(fn, 3, stream)
+            c = {"ms": round(t, 4), "tflops": round(fl / (t * 1e-3) / 1e12, 1),
+                 "pct_peak": round(100 * fl / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 1)}
+            components[name] = c
+            log(f"component {name}: {c}")
+        del dYc
+
+    training = None
+    if w.kind == "block" and not args.no_training:
+        training = mlp_backward_rank0(w, wl, tts, torch, x, A[0], B[0], dev, stream)
 
     # ---------------------------------------------------------------- oracle
     cpu = None
@@ -365,7 +437,38 @@ def main():
         "calibration": calib,
         "components": components,
     }
+    if training is not None:
+        result["training"] = training
     print(json.dumps(result), flush=True)
+
+
+def mlp_backward_rank0(w, wl, tts, torch, x, A0, B0, dev, stream):
+    """Rank 0's MLP-share backward at the block's shape (the same X, A_0, B_0;
+    upstream gradient dZ ~ N(0,1) from the block's seed): its training forward
+    once, then the backward timed with HIP events."""
+    M, h, f = w.M, w.h, w.f
+    dZ = wl.normal((M, h), 1.0, w.seed, "dZ", w.dtype).to(dev)
+    a0 = torch.zeros(f, dtype=torch.float32, device=dev)
+    _, Y, Yp = tts.tp_mlp_shard_train_fwd(x, A0, B0, a0)
+    outs = dict(dX_out=torch.empty(M, h, dtype=torch.float32, device=dev),
+                dA_out=torch.empty(h, f, dtype=torch.float32, device=dev),
+                dB_out=torch.empty(f, h, dtype=torch.float32, device=dev),
+                da_out=torch.empty(f, dtype=torch.float32, device=dev),
+                ws=torch.empty(tts.tp_mlp_shard_backward_workspace(M, f), dtype=torch.uint8,
+                               device=dev))
+    fn = lambda: tts.tp_mlp_shard_backward(x, A0, B0, Y, Yp, dZ, **outs)
+    fn()
+    t, _ = event_time(fn, 5, stream)
+    fl = 8 * M * h * f
+    res = {"mlp_shard_backward_rank0": {
+        "ms": round(t, 4), "tflops": round(fl / (t * 1e-3) / 1e12, 1),
+        "pct_peak": round(100 * fl / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 1),
+        "flops": fl,
+        "what": "tp_mlp_shard_backward: dY = dZ·B_0^T ⊙ GeLU'(Y), dB_0, dA_0, da_0, dX_0 "
+                "partial, for %d tokens, h=%d, f=%d" % (M, h, f)}}
+    log(f"training: {res}")
+    del dZ, Y, Yp, outs
+    return res
 
 
 def cpu_baseline(w, rows_req, env):
@@ -397,6 +500,18 @@ def cpu_baseline(w, rows_req, env):
         dt = time.time() - t0
         fl = 4 * R * w.h * A_cpu.shape[1]
         sample = f"rows 0..{R - 1} of the MLP shard; {fl / 1e12:.3f} TFLOP"
+    elif w.kind == "mlp_bwd":
+        R = min(rows_req, w.M)
+        X_cpu, A_cpu, B_cpu, a_cpu, dZ_cpu = (env[k] for k in ("X_cpu", "A_cpu", "B_cpu",
+                                                               "a_cpu", "dZ_cpu"))
+        log(f"oracle: MLP backward over tokens 0..{R - 1}")
+        t0 = time.time()
+        oracle.mlp_shard_backward(X_cpu[:R], A_cpu, B_cpu, dZ_cpu[:R], a_cpu)
+        dt = time.time() - t0
+        fl = 8 * R * w.h * w.f
+        sample = (f"the MLP-share backward over tokens 0..{R - 1} (dA, dB, da and dX of that "
+                  f"batch); {fl / 1e12:.3f} TFLOP counted, the oracle's recomputation of Y "
+                  f"(a further {2 * R * w.h * w.f / 1e12:.3f} TFLOP) not counted")
     else:
         R = min(rows_req, w.s)
         X_cpu, Wqkv_cpu, Wo_cpu = env["X_cpu"], env["Wqkv_cpu"], env["Wo_cpu"]

@@ -16,7 +16,7 @@ import math
 import torch
 
 SUB = {"x": 0, "A": 1, "B": 2, "Wqkv": 3, "Wo": 4, "bias": 5, "partials": 6,
-       "gamma": 7, "beta": 8, "residual": 9}
+       "gamma": 7, "beta": 8, "residual": 9, "dZ": 10, "preact": 11}
 
 
 def normal(shape, sigma: float, seed: int, sub, dtype=torch.bfloat16):

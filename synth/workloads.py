@@ -1,4 +1,4 @@
-"""The five synthetic workloads: shapes, value distributions and seeds.
+"""The synthetic workloads: shapes, value distributions and seeds.
 
 Every input is N(0, sigma^2), drawn by ``synth.normal``; weights use
 sigma = 1/sqrt(fan_in) with fan_in the UNSHARDED input width (h for A, W_qkv
@@ -19,7 +19,7 @@ from . import normal, fan_in_sigma, rank_seed
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str            # "mlp" | "attn" | "block"
+    kind: str            # "mlp" | "attn" | "block" | "mlp_bwd"
     seed: int
     P: int               # tensor-parallel degree
     b: int
@@ -59,6 +59,9 @@ class Workload:
         """Matrix FLOPs of one call of the workload's entry point."""
         if self.kind == "mlp":
             return self.mlp_flops_rank() * (self.P if self.all_ranks else 1)
+        if self.kind == "mlp_bwd":
+            # dY' = dZ·B^T, dB = Y'^T·dZ, dA = X^T·dY, dX = dY·A^T: 4 products
+            return 2 * self.mlp_flops_rank()
         if self.kind == "attn":
             return self.attn_flops_rank()["total"]
         return self.P * (self.mlp_flops_rank() + self.attn_flops_rank()["total"])
@@ -74,6 +77,9 @@ WORKLOADS = {w.name: w for w in [
              description="bf16 MLP, one rank of tp=8 at the 175B layer shape, 16384 tokens"),
     Workload("attn_bf16_h4096_tp4", "attn", 1003, P=4, b=4, s=2048, h=4096, H=32,
              description="bf16 causal self-attention, one rank of tp=4: 8 local heads of 128"),
+    Workload("mlp_bwd_bf16_h12288_tp8", "mlp_bwd", 1005, P=8, b=8, s=2048, h=12288, F=49152,
+             description="bf16 backward of one rank's MLP share of tp=8 at the 175B layer "
+                         "shape, 16384 tokens: dA_i, dB_i, da_i and the dX_i partial"),
     Workload("block_bf16_h12288_tp8", "block", 1004, P=8, b=8, s=2048, h=12288, H=96, F=49152,
              all_ranks=True,
              description="bf16 pre-LN block at the 175B layer shape, all 8 ranks of tp=8 in turn"),
@@ -109,3 +115,15 @@ def block_rank_weights(w: Workload, r: int):
     A = normal((w.h, w.f), fan_in_sigma(w.h), sd, "A", w.dtype)
     B = normal((w.f, w.h), fan_in_sigma(w.F), sd, "B", w.dtype)
     return Wqkv, Wo, A, B
+
+
+def mlp_bwd_inputs(w: Workload):
+    """X, rank 0's A_i, B_i, a zero bias a_i and the upstream gradient dZ of
+    an MLP backward workload, on the CPU.  dZ ~ N(0, 1): the gradient of a
+    loss that weighs every output element alike."""
+    X = normal((w.M, w.h), 1.0, w.seed, "x", w.dtype)
+    A = normal((w.h, w.f), fan_in_sigma(w.h), w.seed, "A", w.dtype)
+    B = normal((w.f, w.h), fan_in_sigma(w.F), w.seed, "B", w.dtype)
+    a = torch.zeros(w.f, dtype=torch.float32)
+    dZ = normal((w.M, w.h), 1.0, w.seed, "dZ", w.dtype)
+    return X, A, B, a, dZ
