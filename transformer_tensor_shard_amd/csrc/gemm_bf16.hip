@@ -177,6 +177,14 @@ __device__ __forceinline__ bool tile_coords_band(int pid, int groups, int tiles_
     return true;
 }
 
+// Swizzle of an M/N-contiguous tile (64 K rows of 32 16-byte units): logical
+// unit u of K row r sits at physical unit u ^ mc_swz(r).  A transpose read
+// has each 16-lane group g read 32 contiguous bytes (two units) of the four
+// rows 8g..8g+3; the XOR spreads the eight rows that two neighbouring groups
+// read (r & 3 and r & 8 differ) over eight distinct 32-byte bank windows,
+// while keeping a row's two units adjacent.
+__device__ __forceinline__ int mc_swz(int r) { return ((r & 3) << 2) | (((r >> 3) & 1) << 1); }
+
 // K position, relative to the tile's k0, of the unit that lane fetches with
 // direct-to-LDS load j of a K-contiguous tile (row 32w + 8j + lane/8, logical
 // unit (lane % 8) ^ ((row >> 1) & 7)).  Only the K-tail variant tests it, and
@@ -225,7 +233,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
     //   K-contiguous tile (256 rows x 64 K, 128 B rows): row 32w + 8j + l/8,
     //     physical unit l%8, logical unit = physical ^ ((row >> 1) & 7);
     //   M/N-contiguous tile (64 K rows x 256, 512 B rows): K row 8w + 2j + l/32,
-    //     physical unit l%32, logical unit = physical ^ ((K row & 3) << 2).
+    //     physical unit l%32, logical unit = physical ^ mc_swz(K row).
     // The offsets are loop-invariant; a K step only moves the scalar base.
     unsigned a_off[LOADS], b_off[LOADS];
 #pragma unroll
@@ -233,7 +241,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
         const int r = 32 * wid + 8 * j + (lane >> 3);
         const int u = (lane & 7) ^ ((r >> 1) & 7);
         const int kr = 8 * wid + 2 * j + (lane >> 5);
-        const int ub = (lane & 31) ^ ((kr & 3) << 2);
+        const int ub = (lane & 31) ^ mc_swz(kr);
         if (A_MC)
             a_off[j] = (m0 + ub * 8) < M ? (unsigned)(kr * lda + ub * 8) * 2u : OOB;
         else
@@ -288,7 +296,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
     auto mc_rd = [&](int col) -> unsigned {      // col: first column of the block
         const int row = 8 * g + (gi >> 2);
         const int c = col + 4 * (gi & 3);
-        return row * 512 + (((c >> 3) ^ ((row & 3) << 2)) << 4) + (c & 7) * 2;
+        return row * 512 + (((c >> 3) ^ mc_swz(row)) << 4) + (c & 7) * 2;
     };
     // For an M-contiguous A, block mi's address is block 0's with bits 5-7
     // XOR-ed by mi (the 16-column blocks differ only in the swizzled unit
