@@ -16,6 +16,10 @@ in the order the pages give:
   slice of W_o (same page §3.1, §3.2);
 * ``partial_sum`` -- Z = sum_r Z_r (+ bias) (+ residual): the all-reduce's
   arithmetic (same page §1.1, §2.1);
+* ``mlp_shard_backward``, ``attention_backward``, ``attn_shard_backward`` --
+  the gradients of the MLP and attention shares by the chain rule (same page
+  §2.2 and §3.2, backward: same upstream gradient on every rank, local
+  parameter gradients, a partial input gradient summed over ranks);
 * ``block_rows``  -- the pre-LN block x + attn(LN1(x)), then + mlp(LN2(.)), as
   assembled in section 3.3 of the PyTorch tensor-parallel tutorial
   (hotelren.com/news/6074135), with every rank's share summed.
@@ -23,6 +27,7 @@ in the order the pages give:
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 
 import numpy as np
@@ -213,6 +218,73 @@ def attn_shard_rows(X, b: int, s: int, Wqkv, Wo, Hl: int, d: int, causal: bool,
         O[sel] = attention_rows(Q, np.ascontiguousarray(KV[:, :HD]),
                                 np.ascontiguousarray(KV[:, HD:]), t, Hl, d, causal)
     return matmul(O, Wo)
+
+
+def attention_backward(Q, K, V, dO, Hl: int, d: int, causal: bool):
+    """Gradients of O = softmax(Q·K^T/sqrt d + mask)·V for one sequence and
+    every local head, given the upstream gradient dO.
+
+    "图解Transformer并行计算" §3.2 (backward): each rank computes the
+    gradients of its own heads' parameters from the same upstream gradient.
+    Per head, with S = Q K^T / sqrt(d) (keys after the query masked out when
+    causal) and P the row-wise softmax of S, the chain rule gives
+        dV = P^T·dO,   dP = dO·V^T,
+        dS_ij = P_ij·(dP_ij - sum_k P_ik·dP_ik)   (the softmax Jacobian, row i)
+        dQ = dS·K / sqrt(d),   dK = dS^T·Q / sqrt(d).
+    The products are float64 library matmuls; softmax subtracts the row max.
+    Q, K, V, dO [s, Hl·d] (head j in columns j·d..j·d+d-1).  Returns
+    (dQ, dK, dV), each [s, Hl·d].
+    """
+    Q, K, V, dO = f64(Q), f64(K), f64(V), f64(dO)
+    s = Q.shape[0]
+    assert K.shape == V.shape == dO.shape == Q.shape == (s, Hl * d)
+    dQ, dK, dV = (np.zeros_like(Q) for _ in range(3))
+    visible = np.tril(np.ones((s, s), dtype=bool)) if causal else np.ones((s, s), dtype=bool)
+    for j in range(Hl):
+        c = slice(j * d, (j + 1) * d)
+        S = np.matmul(Q[:, c], K[:, c].T) / math.sqrt(d)
+        S = np.where(visible, S, -np.inf)
+        E = np.exp(S - S.max(axis=1, keepdims=True))
+        P = E / E.sum(axis=1, keepdims=True)
+        dV[:, c] = np.matmul(P.T, dO[:, c])
+        dP = np.matmul(dO[:, c], V[:, c].T)
+        dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+        dQ[:, c] = np.matmul(dS, K[:, c]) / math.sqrt(d)
+        dK[:, c] = np.matmul(dS.T, Q[:, c]) / math.sqrt(d)
+    return dQ, dK, dV
+
+
+def attn_shard_backward(X, b: int, s: int, Wqkv, Wo, dZ, Hl: int, d: int, causal: bool):
+    """Gradients of one rank's attention share Z_i = O_i·W_o,i, where O_i is
+    its local heads' attention over qkv = X·W_qkv,i ("图解Transformer并行计算"
+    §3.2, backward: the same dZ reaches every rank; each computes the
+    gradients of its own W_o,i and W_qkv,i and a local input gradient, which
+    one all-reduce sums over ranks into dX).  By the chain rule:
+        dW_o,i = O_i^T·dZ,        dO_i = dZ·W_o,i^T,
+        (dQ, dK, dV) = attention_backward per sequence -> dqkv [b·s, 3·Hl·d],
+        dW_qkv,i = X^T·dqkv,      dX_i = dqkv·W_qkv,i^T.
+    X [b·s, h] (token m = sequence m // s, position m % s); Wqkv [h, 3·Hl·d]
+    laid out [W_q | W_k | W_v]; Wo [Hl·d, h]; dZ [b·s, h].
+    Returns (dX_i, dW_qkv,i, dW_o,i)."""
+    X, Wqkv, Wo, dZ = f64(X), f64(Wqkv), f64(Wo), f64(dZ)
+    HD = Hl * d
+    M = b * s
+    assert X.shape[0] == M and Wqkv.shape[1] == 3 * HD and Wo.shape == (HD, X.shape[1])
+    qkv = matmul(X, Wqkv)
+    O = np.empty((M, HD), dtype=np.float64)
+    dqkv = np.empty((M, 3 * HD), dtype=np.float64)
+    dO = matmul(dZ, Wo.T.copy())
+    for beta in range(b):
+        r = slice(beta * s, (beta + 1) * s)
+        Qs, Ks, Vs = (np.ascontiguousarray(qkv[r, k * HD:(k + 1) * HD]) for k in range(3))
+        O[r] = attention_rows(Qs, Ks, Vs, np.arange(s), Hl, d, causal)
+        g = attention_backward(Qs, Ks, Vs, dO[r], Hl, d, causal)
+        for k in range(3):
+            dqkv[r, k * HD:(k + 1) * HD] = g[k]
+    dWo = matmul(O.T.copy(), dZ)
+    dWqkv = matmul(X.T.copy(), dqkv)
+    dX = matmul(dqkv, Wqkv.T.copy())
+    return dX, dWqkv, dWo
 
 
 def partial_sum(parts, bias=None, residual=None) -> np.ndarray:

@@ -488,3 +488,121 @@ def test_mlp_backward_needs_the_gelu_derivative():
     dYp = oracle.matmul(dZ, B.T.copy())
     wrong = oracle.matmul(X.T.copy(), dYp)                           # no GeLU' factor
     assert np.abs(wrong - dA).max() > 1e-3
+
+
+# --------------------------------------------------------------- attention backward
+def _sdpa_grads(Q, K, V, dO, Hl, d, causal):
+    """float64 autograd through torch's scaled_dot_product_attention, heads
+    split out of the [s, Hl·d] layout."""
+    s = Q.shape[0]
+    t = [torch.tensor(v, requires_grad=True) for v in (Q, K, V)]
+    heads = lambda x: x.view(s, Hl, d).transpose(0, 1)
+    o = torch.nn.functional.scaled_dot_product_attention(heads(t[0]), heads(t[1]), heads(t[2]),
+                                                         is_causal=causal)
+    o.transpose(0, 1).reshape(s, Hl * d).backward(torch.tensor(dO))
+    return [v.grad.numpy() for v in t]
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_attention_backward_matches_autograd(causal):
+    rng = np.random.default_rng(21)
+    s, Hl, d = 11, 3, 5
+    Q, K, V, dO = (rng.normal(size=(s, Hl * d)) for _ in range(4))
+    ours = oracle.attention_backward(Q, K, V, dO, Hl, d, causal)
+    for mine, ref in zip(ours, _sdpa_grads(Q, K, V, dO, Hl, d, causal)):
+        assert np.abs(mine - ref).max() < 1e-12
+
+
+def test_attention_backward_finite_differences():
+    """Brute force: <grad, W> is the central difference of <dO, O> along W,
+    with O from the oracle's own forward loop (a different code path)."""
+    rng = np.random.default_rng(22)
+    s, Hl, d = 6, 2, 3
+    Q, K, V, dO = (rng.normal(size=(s, Hl * d)) for _ in range(4))
+    grads = oracle.attention_backward(Q, K, V, dO, Hl, d, True)
+    loss = lambda Q, K, V: float((dO * oracle.attention_rows(Q, K, V, np.arange(s), Hl, d,
+                                                              True)).sum())
+    eps = 1e-6
+    for k, g in enumerate(grads):
+        W = rng.normal(size=g.shape)
+        args = [Q, K, V]
+        plus = [v + eps * W if i == k else v for i, v in enumerate(args)]
+        minus = [v - eps * W if i == k else v for i, v in enumerate(args)]
+        fd = (loss(*plus) - loss(*minus)) / (2 * eps)
+        assert abs(fd - float((g * W).sum())) < 1e-7 * max(1.0, abs(fd))
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_attention_backward_key_shift_invariance(causal):
+    """Adding one vector c to every key adds q·c/sqrt d to a whole score row,
+    which softmax ignores: the loss does not depend on c, so the key
+    gradients of each head sum to zero (each dS row sums to zero)."""
+    rng = np.random.default_rng(23)
+    s, Hl, d = 9, 2, 4
+    Q, K, V, dO = (rng.normal(size=(s, Hl * d)) for _ in range(4))
+    _, dK, _ = oracle.attention_backward(Q, K, V, dO, Hl, d, causal)
+    assert np.abs(dK.sum(axis=0)).max() < 1e-12 * np.abs(dK).max() * s
+
+
+def test_attention_backward_single_key():
+    """s = 1: the softmax over one key is the constant 1, so O = V: dV = dO
+    and Q, K get no gradient."""
+    rng = np.random.default_rng(24)
+    Q, K, V, dO = (rng.normal(size=(1, 6)) for _ in range(4))
+    dQ, dK, dV = oracle.attention_backward(Q, K, V, dO, 2, 3, True)
+    assert np.abs(dQ).max() == 0 and np.abs(dK).max() == 0
+    assert np.array_equal(dV, dO)
+
+
+def test_attention_backward_needs_the_softmax_row_term():
+    """Negative control: dropping the row term sum_k P_ik dP_ik from dS changes
+    dQ, so the softmax Jacobian's second term is pinned."""
+    rng = np.random.default_rng(25)
+    s, Hl, d = 7, 1, 4
+    Q, K, V, dO = (rng.normal(size=(s, Hl * d)) for _ in range(4))
+    dQ, _, _ = oracle.attention_backward(Q, K, V, dO, Hl, d, True)
+    S = np.where(np.tril(np.ones((s, s), bool)), Q @ K.T / math.sqrt(d), -np.inf)
+    P = np.exp(S - S.max(1, keepdims=True))
+    P /= P.sum(1, keepdims=True)
+    wrong = (P * (dO @ V.T)) @ K / math.sqrt(d)
+    assert np.abs(wrong - dQ).max() > 1e-3
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_attn_shard_backward_matches_autograd(causal):
+    """The whole attention share, X -> qkv -> attention -> W_o, through torch
+    autograd in float64."""
+    b, s, H, d = 2, 5, 2, 3
+    X, Wq, Wk, Wv, Wo = _attn_setup(b, s, H, d)
+    Wqkv = _rank_qkv(Wq, Wk, Wv, 0, H, d)
+    dZ = np.random.default_rng(26).normal(size=(b * s, X.shape[1]))
+    dX, dWqkv, dWo = oracle.attn_shard_backward(X, b, s, Wqkv, Wo, dZ, H, d, causal)
+    t = [torch.tensor(v, requires_grad=True) for v in (X, Wqkv, Wo)]
+    qkv = t[0] @ t[1]
+    sp = lambda k: qkv[:, k * H * d:(k + 1) * H * d].reshape(b, s, H, d).transpose(1, 2)
+    o = torch.nn.functional.scaled_dot_product_attention(sp(0), sp(1), sp(2), is_causal=causal)
+    (o.transpose(1, 2).reshape(b * s, H * d) @ t[2]).backward(torch.tensor(dZ))
+    for mine, ref in zip((dX, dWqkv, dWo), t):
+        assert np.abs(mine - ref.grad.numpy()).max() < 1e-11
+
+
+@pytest.mark.parametrize("P", [2, 4])
+def test_attn_shard_backward_ranks_sum_to_unsharded(P):
+    """§3.2's backward: the rank partials dX_r sum to the unsharded dX, each
+    rank's dW_qkv,r holds its heads' columns of the unsharded [dW_q|dW_k|dW_v]
+    and dW_o,r its row block of dW_o."""
+    b, s, H, d = 2, 6, 4, 3
+    X, Wq, Wk, Wv, Wo = _attn_setup(b, s, H, d)
+    dZ = np.random.default_rng(27 + P).normal(size=(b * s, X.shape[1]))
+    full = oracle.attn_shard_backward(X, b, s, _rank_qkv(Wq, Wk, Wv, 0, H, d), Wo, dZ, H, d, True)
+    Hl, HD = H // P, H * d
+    dX = 0
+    for r in range(P):
+        rows = slice(r * Hl * d, (r + 1) * Hl * d)
+        g = oracle.attn_shard_backward(X, b, s, _rank_qkv(Wq, Wk, Wv, r, Hl, d),
+                                       np.ascontiguousarray(Wo[rows]), dZ, Hl, d, True)
+        dX = dX + g[0]
+        want = np.concatenate([full[1][:, k * HD:(k + 1) * HD][:, rows] for k in range(3)], axis=1)
+        assert np.abs(g[1] - want).max() < 1e-12
+        assert np.abs(g[2] - full[2][rows]).max() < 1e-12
+    assert np.abs(dX - full[0]).max() < 1e-12
