@@ -137,6 +137,36 @@ tp_status tp_attn_shard(const void* X, const void* W_qkv_i, const void* W_o_i, v
                         int64_t H_l, int64_t d, int causal, int out, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Training: the attention share's forward keeping its activations, and its
+ * backward.  [Megatron explainer] §3.2 (backward): dZ = ∂L/∂Z reaches every
+ * rank; each computes the gradients of its own W_o,i and W_qkv,i and a local
+ * input gradient whose sum over ranks (one all-reduce) is ∂L/∂X:
+ *     dO = dZ·W_o,i^T,   dW_o,i = O_i^T·dZ,
+ *     (dQ, dK, dV) = tp_attention_core_backward(...),
+ *     dW_qkv,i = X^T·[dQ|dK|dV],   dX_i = [dQ|dK|dV]·W_qkv,i^T.
+ *
+ * tp_attn_shard_train_fwd -- Z_i as tp_attn_shard, also storing
+ *   qkv [b·s, 3·H_l·d] bf16, O [b·s, H_l·d] bf16 and lse f32 [b·H_l·s]
+ * (see tp_attention_core_train), which the backward takes back. */
+tp_status tp_attn_shard_train_fwd(const void* X, const void* W_qkv_i, const void* W_o_i,
+                                  void* Z_i, void* qkv, void* O, float* lse, int64_t b, int64_t s,
+                                  int64_t h, int64_t H_l, int64_t d, int causal, int out,
+                                  void* stream);
+
+/* tp_attn_shard_backward -- the gradients above.
+ *   X [b·s, h], W_qkv_i [h, 3·H_l·d], W_o_i [H_l·d, h], dZ [b·s, h]: bf16
+ *   qkv, O, lse: from tp_attn_shard_train_fwd
+ *   dX_i [b·s, h] in dtype `dx_dtype` (this rank's partial);
+ *   dW_qkv_i [h, 3·H_l·d], dW_o_i [H_l·d, h]: f32
+ *   ws >= tp_attn_shard_backward_workspace(b, s, H_l, d) bytes (dO, dqkv, D). */
+size_t tp_attn_shard_backward_workspace(int64_t b, int64_t s, int64_t H_l, int64_t d);
+tp_status tp_attn_shard_backward(const void* X, const void* W_qkv_i, const void* W_o_i,
+                                 const void* qkv, const void* O, const float* lse,
+                                 const void* dZ, void* dX_i, void* dW_qkv_i, void* dW_o_i,
+                                 void* ws, size_t ws_bytes, int64_t b, int64_t s, int64_t h,
+                                 int64_t H_l, int64_t d, int causal, int dx_dtype, void* stream);
+
+/* ------------------------------------------------------------------------
  * tp_partial_sum -- the arithmetic of the all-reduce on one GPU.
  * [Megatron explainer] §1.1 (row split: the partial products are summed) and
  * §2.1 (Z = Z1 + Z2):
@@ -254,6 +284,28 @@ tp_status tp_matmul(const void* A, int64_t lda, int trans_a, const void* B, int6
 tp_status tp_attention_core(const void* qkv, int64_t ld_qkv, void* O,
                             int64_t b, int64_t s, int64_t H_l, int64_t d, int causal,
                             void* stream);
+
+/* tp_attention_core_train -- tp_attention_core that also stores, for every
+ * (sequence, local head, query), the base-2 log of the softmax normaliser,
+ *     lse = log2 sum_k 2^(log2(e)·q·k/sqrt d)   over the visible keys k,
+ * as f32 [b][H_l][s] (what the backward needs to recompute the softmax). */
+tp_status tp_attention_core_train(const void* qkv, int64_t ld_qkv, void* O, float* lse,
+                                  int64_t b, int64_t s, int64_t H_l, int64_t d, int causal,
+                                  void* stream);
+
+/* tp_attention_core_backward -- gradients of tp_attention_core
+ * ([Megatron explainer] §3.2, backward; per head, with P the softmax of
+ * S = Q·K^T/sqrt d): dV = P^T·dO, dP = dO·V^T, dS = P ⊙ (dP - rowsum(dO ⊙ O)),
+ * dQ = dS·K/sqrt d, dK = dS^T·Q/sqrt d.
+ *   qkv [b·s, ld_qkv], O and dO [b·s, H_l·d] bf16 (layouts of tp_attention_core);
+ *   lse from tp_attention_core_train;
+ *   dqkv [b·s, 3·H_l·d] bf16: dQ, dK, dV in qkv's column layout;
+ *   D_ws f32 scratch of b·H_l·s elements (receives rowsum(dO ⊙ O)).
+ * Deterministic: no atomics; d must be 128. */
+tp_status tp_attention_core_backward(const void* qkv, int64_t ld_qkv, const void* O,
+                                     const void* dO, const float* lse, void* dqkv, float* D_ws,
+                                     int64_t b, int64_t s, int64_t H_l, int64_t d, int causal,
+                                     void* stream);
 
 /* tp_layernorm -- y = (x - mean)/sqrt(var + eps)·gamma + beta over each row of
  * x [M,h] (population variance, f32 statistics), the block's nn.LayerNorm(h)

@@ -12,6 +12,11 @@ the last averages thousands).  With a tensor-wide rms no implementation that
 keeps Q, K, V or O in bf16 meets the bar on the first rows (rounding V alone
 gives 0.054 * rms at s=2048), while per row an exact emulation of the bf16
 roundings gives 0.019 * rms_row.
+
+A reference row that is exactly zero has no scale of its own; such rows occur
+where the mathematics fixes a zero (under a causal mask the first query
+attends to one key, and a softmax over one key has zero gradient, so that
+query's dQ row is 0).  Their error is measured against the whole tensor's rms.
 """
 import numpy as np
 import torch
@@ -35,6 +40,7 @@ def errors(g, r):
     d = np.abs(g2 - r2)
     rms = float(np.sqrt(np.mean(r2 * r2))) if r2.size else 0.0
     rms_row = np.sqrt(np.mean(r2 * r2, axis=1, keepdims=True))
+    rms_row = np.where(rms_row == 0.0, rms, rms_row)
     fro = float(np.linalg.norm(g2 - r2) / max(np.linalg.norm(r2), 1e-300))
     out = {"fro": fro, "rms": rms, "finite": bool(np.isfinite(g2).all())}
     if r2.size:

@@ -36,7 +36,7 @@ def test_matmul_nt(M, N, K):
     """C = A·B^T with B stored [N,K] (the input gradient dY·W^T)."""
     banner(f"matmul NT M={M} N={N} K={K}")
     A = gen((M, K), 1.0, 201, "x")
-    Bt = gen((N, K), 1 / math.sqrt(K), 201, "w")
+    Bt = gen((N, K), 1 / math.sqrt(K), 201, "A")
     bias = gen((N,), 0.5, 201, "bias", torch.float32)
     C = tts.tp_matmul(A.to(DEV), Bt.to(DEV), bias.to(DEV), trans_b=True)
     torch.cuda.synchronize()
@@ -49,7 +49,7 @@ def test_matmul_tn(M, N, K):
     alignment here, so odd K exercises the row-range tail of both operands."""
     banner(f"matmul TN M={M} N={N} K={K}")
     At = gen((K, M), 1.0, 202, "x")
-    B = gen((K, N), 1 / math.sqrt(K), 202, "w")
+    B = gen((K, N), 1 / math.sqrt(K), 202, "A")
     C = tts.tp_matmul(At.to(DEV), B.to(DEV), trans_a=True)
     torch.cuda.synchronize()
     assert_f32(C, oracle.matmul(oracle.f64(At).T, B), bar=1e-4)
@@ -60,7 +60,7 @@ def test_matmul_bf16_out(ta, tb):
     M, N, K = 392, 776, 200 if ta else 192
     banner(f"matmul bf16 out ta={ta} tb={tb} M={M} N={N} K={K}")
     A = gen((K, M) if ta else (M, K), 1.0, 203, "x")
-    B = gen((N, K) if tb else (K, N), 1 / math.sqrt(K), 203, "w")
+    B = gen((N, K) if tb else (K, N), 1 / math.sqrt(K), 203, "A")
     C = tts.tp_matmul(A.to(DEV), B.to(DEV), trans_a=bool(ta), trans_b=bool(tb),
                       out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
@@ -75,12 +75,12 @@ def test_matmul_strided_leading_dims():
     banner("matmul strided")
     M, N, K = 304, 136, 264
     Abig = gen((K, M + 40), 1.0, 204, "x")
-    Bbig = gen((N, K + 24), 1 / math.sqrt(K), 204, "w")
+    Bbig = gen((N, K + 24), 1 / math.sqrt(K), 204, "A")
     L = tts.lib()
     Ad, Bd = Abig.to(DEV), Bbig.to(DEV)
     for ta, tb in [(1, 0), (0, 1)]:
         if ta:
-            Bk = gen((K, N + 8), 1 / math.sqrt(K), 205, "w").to(DEV)
+            Bk = gen((K, N + 8), 1 / math.sqrt(K), 205, "A").to(DEV)
             Cd = torch.full((M, N + 16), 7.0, device=DEV)
             st = L.tp_matmul(tts._dev(Ad, "A"), M + 40, 1, tts._dev(Bk, "B"), N + 8, 0, None,
                              tts._dev(Cd, "C"), N + 16, None, 0, M, N, K, 0, 0, None)
@@ -105,8 +105,8 @@ def test_matmul_gelu_bwd(M, N, K, out):
     layer's GeLU, with aux the saved pre-activation."""
     banner(f"matmul NT gelu_bwd M={M} N={N} K={K} out={out}")
     A = gen((M, K), 1.0, 207, "x")
-    Bt = gen((N, K), 1 / math.sqrt(K), 207, "w")
-    aux = gen((M, N), 1.5, 207, "y")
+    Bt = gen((N, K), 1 / math.sqrt(K), 207, "A")
+    aux = gen((M, N), 1.5, 207, "preact")
     C = tts.tp_matmul(A.to(DEV), Bt.to(DEV), trans_b=True, epilogue="gelu_bwd",
                       aux=aux.to(DEV), out_dtype=out)
     torch.cuda.synchronize()
@@ -123,7 +123,7 @@ def test_matmul_gelu_save(M, N, K):
     """C = GeLU(A·B + bias) and aux = A·B + bias in one epilogue."""
     banner(f"matmul NN gelu_save M={M} N={N} K={K}")
     A = gen((M, K), 1.0, 208, "x")
-    B = gen((K, N), 1 / math.sqrt(K), 208, "w")
+    B = gen((K, N), 1 / math.sqrt(K), 208, "A")
     bias = gen((N,), 0.5, 208, "bias", torch.float32)
     C, aux = tts.tp_matmul(A.to(DEV), B.to(DEV), bias.to(DEV), epilogue="gelu_save",
                            out_dtype=torch.bfloat16)
@@ -142,7 +142,7 @@ def mlp_inputs(M, h, f, seed):
     X = gen((M, h), 1.0, seed, "x")
     A = gen((h, f), 1 / math.sqrt(h), seed, "A")
     B = gen((f, h), 1 / math.sqrt(f), seed, "B")
-    a = gen((f,), 0.5, seed, "a", torch.float32)
+    a = gen((f,), 0.5, seed, "bias", torch.float32)
     dZ = gen((M, h), 1.0, seed, "dZ")
     return X, A, B, a, dZ
 
@@ -215,4 +215,109 @@ def test_mlp_backward_ranks_sum_to_unsharded():
     dX = tts.tp_partial_sum(torch.stack(parts))
     torch.cuda.synchronize()
     rX = oracle.mlp_shard_backward(X, A, B, dZ, a)[0]
+    assert_bf16(dX, rX)
+
+
+# ------------------------------------------------------------------ attention training
+def _heads(t, beta, s, k, HD):
+    """sequence beta's block k (0 = Q, 1 = K, 2 = V) of a [b·s, 3·HD] tensor."""
+    return oracle.f64(t)[beta * s:(beta + 1) * s, k * HD:(k + 1) * HD]
+
+
+@pytest.mark.parametrize("b,s,Hl,causal", [(2, 128, 2, True), (1, 200, 3, True),
+                                           (2, 384, 1, True), (1, 200, 2, False),
+                                           (3, 64, 2, False), (2, 1, 2, True),
+                                           (1, 520, 1, True)])
+def test_attention_core_backward(b, s, Hl, causal):
+    """dQ, dK, dV of the attention core against the oracle's softmax chain
+    rule, per sequence, with ragged sequence ends and both masks."""
+    banner(f"attention core backward b={b} s={s} Hl={Hl} causal={causal}")
+    d, HD = 128, Hl * 128
+    qkv = gen((b * s, 3 * HD), 1.0, 220, "x")
+    dO = gen((b * s, HD), 1.0, 220, "dZ")
+    qd = qkv.to(DEV)
+    O, lse = tts.tp_attention_core_train(qd, b, s, Hl, d, causal)
+    dqkv = tts.tp_attention_core_backward(qd, O, dO.to(DEV), lse, b, s, Hl, d, causal)
+    torch.cuda.synchronize()
+    for beta in range(b):
+        ref = oracle.attention_backward(_heads(qkv, beta, s, 0, HD), _heads(qkv, beta, s, 1, HD),
+                                        _heads(qkv, beta, s, 2, HD),
+                                        oracle.f64(dO)[beta * s:(beta + 1) * s], Hl, d, causal)
+        got = dqkv[beta * s:(beta + 1) * s]
+        for k in range(3):
+            g = got[:, k * HD:(k + 1) * HD]
+            if s == 1 and k < 2:
+                # one key: the softmax is constant and Q, K get zero gradient;
+                # the kernel's dS = P·(dP - D) keeps only the rounding residue
+                # of two dot products of the same vectors taken in different
+                # orders, far below the scale of dV = dO
+                scale = float(np.sqrt(np.mean(oracle.f64(dO) ** 2)))
+                assert float(g.abs().max()) <= 1e-4 * scale
+            else:
+                assert_bf16(g, ref[k])
+
+
+def test_attention_train_forward_unchanged():
+    """The training forward's O equals the inference forward's bit for bit."""
+    banner("attention train forward == forward")
+    b, s, Hl = 2, 300, 2
+    qkv = gen((b * s, 3 * Hl * 128), 1.0, 221, "x").to(DEV)
+    O1 = tts.tp_attention_core(qkv, b, s, Hl)
+    O2, lse = tts.tp_attention_core_train(qkv, b, s, Hl)
+    torch.cuda.synchronize()
+    assert torch.equal(O1, O2)
+    assert torch.isfinite(lse).all()
+
+
+@pytest.mark.parametrize("b,s,h,Hl,causal,dx", [(2, 256, 256, 2, True, torch.float32),
+                                                (1, 200, 264, 1, True, torch.bfloat16),
+                                                (2, 136, 128, 2, False, torch.float32)])
+def test_attn_shard_backward(b, s, h, Hl, causal, dx):
+    """Every gradient of one rank's attention share (dX_i partial, dW_qkv,i,
+    dW_o,i) against the oracle, through the training forward's activations."""
+    banner(f"attn shard backward b={b} s={s} h={h} Hl={Hl} causal={causal} dx={dx}")
+    HD = Hl * 128
+    X = gen((b * s, h), 1.0, 222, "x")
+    Wqkv = gen((h, 3 * HD), 1 / math.sqrt(h), 222, "Wqkv")
+    Wo = gen((HD, h), 1 / math.sqrt(h), 222, "Wo")
+    dZ = gen((b * s, h), 1.0, 222, "dZ")
+    Xd, Wqd, Wod = X.to(DEV), Wqkv.to(DEV), Wo.to(DEV)
+    Z, qkv, O, lse = tts.tp_attn_shard_train_fwd(Xd, Wqd, Wod, b, s, Hl, causal=causal)
+    dX, dWqkv, dWo = tts.tp_attn_shard_backward(Xd, Wqd, Wod, qkv, O, lse, dZ.to(DEV), b, s, Hl,
+                                                causal=causal, dx_dtype=dx)
+    torch.cuda.synchronize()
+    assert_bf16(Z, oracle.attn_shard_rows(X, b, s, Wqkv, Wo, Hl, 128, causal))
+    rX, rWqkv, rWo = oracle.attn_shard_backward(X, b, s, Wqkv, Wo, dZ, Hl, 128, causal)
+    assert_bf16(dX, rX)
+    assert_bf16(dWqkv, rWqkv)
+    assert_bf16(dWo, rWo)
+
+
+def test_attn_backward_deterministic_and_ranks_sum():
+    """Two emulated ranks (heads split) summed with tp_partial_sum against the
+    unsharded share's dX; and a repeated call gives identical bits."""
+    banner("attn backward 2 ranks + repeat")
+    b, s, h, H, P = 1, 256, 256, 2, 2
+    HD = H * 128
+    X = gen((b * s, h), 1.0, 223, "x")
+    Wq, Wk, Wv = (gen((h, HD), 1 / math.sqrt(h), 223 + k, "Wqkv") for k in range(3))
+    Wo = gen((HD, h), 1 / math.sqrt(h), 223, "Wo")
+    dZ = gen((b * s, h), 1.0, 223, "dZ")
+    Xd, dZd = X.to(DEV), dZ.to(DEV)
+    parts = []
+    for r in range(P):
+        c = slice(r * 128, (r + 1) * 128)
+        Wqkv_r = torch.cat([Wq[:, c], Wk[:, c], Wv[:, c]], dim=1).contiguous().to(DEV)
+        Wo_r = Wo[c].contiguous().to(DEV)
+        _, qkv, O, lse = tts.tp_attn_shard_train_fwd(Xd, Wqkv_r, Wo_r, b, s, 1)
+        g1 = tts.tp_attn_shard_backward(Xd, Wqkv_r, Wo_r, qkv, O, lse, dZd, b, s, 1)
+        g2 = tts.tp_attn_shard_backward(Xd, Wqkv_r, Wo_r, qkv, O, lse, dZd, b, s, 1)
+        torch.cuda.synchronize()
+        for u, v in zip(g1, g2):
+            assert torch.equal(u, v)
+        parts.append(g1[0])
+    dX = tts.tp_partial_sum(torch.stack(parts))
+    torch.cuda.synchronize()
+    Wqkv_full = torch.cat([Wq, Wk, Wv], dim=1)
+    rX = oracle.attn_shard_backward(X, b, s, Wqkv_full, Wo, dZ, H, 128, True)[0]
     assert_bf16(dX, rX)

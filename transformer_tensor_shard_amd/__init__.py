@@ -23,7 +23,9 @@ __all__ = [
     "tp_attn_shard_workspace", "tp_partial_sum", "tp_block_shard", "tp_block_shard_workspace",
     "tp_linear", "tp_linear_batched", "tp_attention_core", "tp_layernorm", "tp_probe_mfma",
     "tp_matmul", "tp_mlp_shard_train_fwd", "tp_mlp_shard_backward",
-    "tp_mlp_shard_backward_workspace", "lib",
+    "tp_mlp_shard_backward_workspace", "tp_attention_core_train", "tp_attention_core_backward",
+    "tp_attn_shard_train_fwd", "tp_attn_shard_backward", "tp_attn_shard_backward_workspace",
+    "lib",
 ]
 
 
@@ -297,6 +299,88 @@ def tp_attention_core(qkv, b: int, s: int, H_l: int, d: int = 128, causal=True, 
                                        H_l, d, int(bool(causal)), _stream(stream))
     _check(st, "tp_attention_core")
     return out
+
+
+def tp_attention_core_train(qkv, b: int, s: int, H_l: int, d: int = 128, causal=True, *,
+                            out=None, lse=None, stream=None):
+    """tp_attention_core that also returns the per-query base-2 log of the
+    softmax normaliser: (O [b·s, H_l·d] bf16, lse [b, H_l, s] f32)."""
+    dev = qkv.device
+    if out is None:
+        out = torch.empty(b * s, H_l * d, dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty(b, H_l, s, dtype=torch.float32, device=dev)
+    st = _lib.load().tp_attention_core_train(_dev(qkv, "qkv"), qkv.shape[1], _dev(out, "out"),
+                                             _dev(lse, "lse"), b, s, H_l, d, int(bool(causal)),
+                                             _stream(stream))
+    _check(st, "tp_attention_core_train")
+    return out, lse
+
+
+def tp_attention_core_backward(qkv, O, dO, lse, b: int, s: int, H_l: int, d: int = 128,
+                               causal=True, *, dqkv=None, D_ws=None, stream=None):
+    """dQ, dK, dV of tp_attention_core in qkv's layout: dqkv [b·s, 3·H_l·d] bf16."""
+    dev = qkv.device
+    if dqkv is None:
+        dqkv = torch.empty(b * s, 3 * H_l * d, dtype=torch.bfloat16, device=dev)
+    if D_ws is None:
+        D_ws = torch.empty(b * H_l * s, dtype=torch.float32, device=dev)
+    st = _lib.load().tp_attention_core_backward(
+        _dev(qkv, "qkv"), qkv.shape[1], _dev(O, "O"), _dev(dO, "dO"), _dev(lse, "lse"),
+        _dev(dqkv, "dqkv"), _dev(D_ws, "D_ws"), b, s, H_l, d, int(bool(causal)), _stream(stream))
+    _check(st, "tp_attention_core_backward")
+    return dqkv
+
+
+def tp_attn_shard_train_fwd(X, W_qkv_i, W_o_i, b: int, s: int, H_l: int, d: int = 128,
+                            causal=True, *, out=None, out_dtype=torch.float32, qkv_out=None,
+                            O_out=None, lse_out=None, stream=None):
+    """Z_i as tp_attn_shard plus the saved activations: (Z_i, qkv, O, lse)."""
+    M, h = X.shape
+    dev = X.device
+    HD = H_l * d
+    if out is None:
+        out = torch.empty(M, h, dtype=out_dtype, device=dev)
+    if qkv_out is None:
+        qkv_out = torch.empty(M, 3 * HD, dtype=torch.bfloat16, device=dev)
+    if O_out is None:
+        O_out = torch.empty(M, HD, dtype=torch.bfloat16, device=dev)
+    if lse_out is None:
+        lse_out = torch.empty(b, H_l, s, dtype=torch.float32, device=dev)
+    st = _lib.load().tp_attn_shard_train_fwd(
+        _dev(X, "X"), _dev(W_qkv_i, "W_qkv_i"), _dev(W_o_i, "W_o_i"), _dev(out, "out"),
+        _dev(qkv_out, "qkv_out"), _dev(O_out, "O_out"), _dev(lse_out, "lse_out"), b, s, h, H_l,
+        d, int(bool(causal)), _code(out.dtype), _stream(stream))
+    _check(st, "tp_attn_shard_train_fwd")
+    return out, qkv_out, O_out, lse_out
+
+
+def tp_attn_shard_backward_workspace(b: int, s: int, H_l: int, d: int = 128) -> int:
+    return int(_lib.load().tp_attn_shard_backward_workspace(b, s, H_l, d))
+
+
+def tp_attn_shard_backward(X, W_qkv_i, W_o_i, qkv, O, lse, dZ, b: int, s: int, H_l: int,
+                           d: int = 128, causal=True, *, dx_dtype=torch.float32, dX_out=None,
+                           dWqkv_out=None, dWo_out=None, ws=None, stream=None):
+    """One rank's attention gradients from the saved activations:
+    (dX_i [b·s, h] partial, dW_qkv,i [h, 3·H_l·d] f32, dW_o,i [H_l·d, h] f32)."""
+    M, h = X.shape
+    dev = X.device
+    HD = H_l * d
+    if dX_out is None:
+        dX_out = torch.empty(M, h, dtype=dx_dtype, device=dev)
+    if dWqkv_out is None:
+        dWqkv_out = torch.empty(h, 3 * HD, dtype=torch.float32, device=dev)
+    if dWo_out is None:
+        dWo_out = torch.empty(HD, h, dtype=torch.float32, device=dev)
+    ws = _ws(ws, tp_attn_shard_backward_workspace(b, s, H_l, d), dev)
+    st = _lib.load().tp_attn_shard_backward(
+        _dev(X, "X"), _dev(W_qkv_i, "W_qkv_i"), _dev(W_o_i, "W_o_i"), _dev(qkv, "qkv"),
+        _dev(O, "O"), _dev(lse, "lse"), _dev(dZ, "dZ"), _dev(dX_out, "dX_out"),
+        _dev(dWqkv_out, "dWqkv_out"), _dev(dWo_out, "dWo_out"), _dev(ws, "ws"), _bytes(ws), b, s,
+        h, H_l, d, int(bool(causal)), _code(dX_out.dtype), _stream(stream))
+    _check(st, "tp_attn_shard_backward")
+    return dX_out, dWqkv_out, dWo_out
 
 
 def tp_layernorm(x, gamma=None, beta=None, eps=1e-5, *, out=None, stream=None):

@@ -55,6 +55,14 @@ SIGNATURES = {
     "tp_mlp_shard_train_fwd": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int,
                                       _vp]),
     "tp_mlp_shard_backward_workspace": (_sz, [_i64, _i64]),
+    "tp_attention_core_train": (_int, [_vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _int, _vp]),
+    "tp_attention_core_backward": (_int, [_vp, _i64, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64,
+                                          _i64, _int, _vp]),
+    "tp_attn_shard_train_fwd": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
+                                       _i64, _int, _int, _vp]),
+    "tp_attn_shard_backward_workspace": (_sz, [_i64, _i64, _i64, _i64]),
+    "tp_attn_shard_backward": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
+                                      _i64, _i64, _i64, _i64, _i64, _int, _int, _vp]),
     "tp_mlp_shard_backward": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                                      _i64, _i64, _i64, _int, _vp]),
 }

@@ -22,7 +22,8 @@
 //    end, and the accumulator is rescaled only when a running max moved;
 //  * LDS tiles are XOR-swizzled in 16-byte units (64 banks, conflict-free for
 //    the 16-byte K reads and the transpose V reads);
-//  * the output block is staged through LDS and written with 16-byte stores.
+//  * the output block is staged through LDS and written with 16-byte stores;
+//    the training forward also writes each query's log2 softmax normaliser.
 #include "tp_kernels.h"
 
 #include <math.h>
@@ -54,7 +55,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
 
 __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(
     const __bf16* __restrict__ qkv, int64_t ld, int64_t qkv_rank_stride,
-    __bf16* __restrict__ O, int64_t ldo, int64_t o_rank_stride,
+    __bf16* __restrict__ O, int64_t ldo, int64_t o_rank_stride, float* __restrict__ lse,
     int s, int b, int Hl, int nqb, int n_bh, int causal, float scale_log2)
 {
     __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE_BYTES];
@@ -249,6 +250,11 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(
     // 32dt + 8(r>>2) + 4hi + (r&3).  Stage the wave's 32x128 block in LDS.
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    // the training forward keeps log2 of each query's softmax normaliser,
+    // L = m + log2(sum 2^(s·c - m)) with c = log2(e)/sqrt(d), so that the
+    // backward recomputes P = 2^(s·c - L) without the running statistics
+    if (lse && hi == 0 && my_q < s)
+        lse[((int64_t)(rank * b + beta) * Hl + head) * s + my_q] = m_run + log2f(l_tot);
     char* stage = lds + w * (32 * 256);
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
@@ -276,7 +282,7 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(
 
 hipError_t attention_fwd(const void* qkv, int64_t ld_qkv, void* O,
                          int64_t b, int64_t s, int64_t H_l, bool causal, hipStream_t stream,
-                         int ranks, int64_t qkv_rank_stride, int64_t o_rank_stride)
+                         int ranks, int64_t qkv_rank_stride, int64_t o_rank_stride, float* lse)
 {
     const int nqb = (int)((s + BQ - 1) / BQ);
     const int n_bh = (int)(ranks * b * H_l);
@@ -284,7 +290,7 @@ hipError_t attention_fwd(const void* qkv, int64_t ld_qkv, void* O,
     const int groups_per_xcd = (n_bh + 7) / 8;
     hipLaunchKernelGGL(attn_fwd_kernel, dim3(8 * groups_per_xcd * nqb), dim3(NT), 0, stream,
                        (const __bf16*)qkv, ld_qkv, qkv_rank_stride, (__bf16*)O, H_l * D,
-                       o_rank_stride, (int)s, (int)b, (int)H_l, nqb, n_bh, causal ? 1 : 0,
+                       o_rank_stride, lse, (int)s, (int)b, (int)H_l, nqb, n_bh, causal ? 1 : 0,
                        scale_log2);
     return hipGetLastError();
 }

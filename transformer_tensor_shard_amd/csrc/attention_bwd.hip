@@ -1,0 +1,434 @@
+// Backward of the head-sharded attention core for gfx950, d = 128
+// ("图解Transformer并行计算" §3.2, backward: each rank computes the gradients
+// of its own heads from the same upstream gradient).  Per (sequence, head),
+// with S = Q·K^T/sqrt(d) (causal keys masked), P = softmax(S) recomputed from
+// the forward's log2 normaliser L (P = 2^(S·log2(e) - L)) and dO the upstream
+// gradient:
+//     D_q = sum_d dO·O  (= sum_k P·dP per query),   dP = dO·V^T,
+//     dS = P ⊙ (dP - D),   dQ = dS·K/sqrt(d),   dK = dS^T·Q/sqrt(d),   dV = P^T·dO.
+//
+// Two kernels, no atomics, so the result is bitwise reproducible:
+//  * query-stationary (dQ): the forward kernel's structure -- one workgroup
+//    of 4 waves = 128 queries of one (sequence, head), each wave holding Q
+//    and dO of its 32 queries in registers as MFMA B operands; 64-key K/V
+//    tiles stream through LDS, double-buffered.  Per tile a wave computes
+//    S^T = K·Q^T and dP^T = V·dO^T (MFMA 32x32x16, A = K/V rows from LDS), so
+//    every lane holds one query's column and P, dS are lane-local; then
+//    dQ^T += K^T·dS^T with K^T from the LDS transpose read.  It also forms
+//    D_q from dO and O and stores it for the second kernel;
+//  * key-stationary (dK, dV): one workgroup = 128 keys, each wave holding K
+//    and V of its 32 keys in registers; 64-query tiles of Q, dO, L and D
+//    stream through LDS.  Per tile a wave computes S = Q·K^T and dP = dO·V^T
+//    (each lane one key's column), P and dS element-wise with the per-query L
+//    and D read from LDS, then dV^T += dO^T·P and dK^T += Q^T·dS with dO^T and
+//    Q^T from transpose reads.
+// When an accumulator feeds the next MFMA as its B operand, the lane's eight
+// k values are rows {4h..4h+3, 8+4h..8+4h+3} of a 16-row step (h = lane/32),
+// and the A operand's transpose reads take the same rows, so nothing is
+// shuffled between lanes.  Tiles are XOR-swizzled in 16-byte units by
+// (row & 15); causal workgroups with the most tiles are dispatched first.
+#include "tp_kernels.h"
+
+#include <math.h>
+
+namespace tpk {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+constexpr int D = 128, NW = 4, NT = 64 * NW;
+constexpr int BQ = 32 * NW;          // queries per dQ workgroup
+constexpr int BK = 32 * NW;          // keys per dK/dV workgroup
+constexpr int T64 = 64;              // rows per streamed tile
+constexpr int TILE = T64 * D * 2;    // 16 KiB: 64 rows x 256 B
+constexpr int CP = 1024 / NT;        // 16-byte units per thread per tile
+constexpr unsigned OOB = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7ffffff0,
+                                             0x00020000);
+}
+
+// byte offset of element (row, col) of a [rows][128] bf16 tile whose 16-byte
+// units are XOR-swizzled by (row & 15)
+__device__ __forceinline__ unsigned tile_off(int row, int col) {
+    return row * 256 + (((col >> 3) ^ (row & 15)) << 4) + (col & 7) * 2;
+}
+
+__device__ __forceinline__ bf16x8 ld8(__amdgpu_buffer_rsrc_t r, unsigned off) {
+    return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// MFMA A operand "rows of the tile transposed": lane (h = lane/32, column
+// lane & 31 of the 32-wide block at col0) receives the 8 values of rows
+// {4h..4h+3, 8+4h..8+4h+3} (+ row0) -- the k order of a B operand taken from
+// an accumulator.  lo/hi are the lane's addresses of the two 4-row reads.
+__device__ __forceinline__ bf16x8 tr_read(const char* base, unsigned lo, unsigned hi) {
+    const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, base + lo));
+    const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, base + hi));
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// stage a wave's [128 dims x 32 rows] f32 accumulator (acc[dt][r] holds dim
+// 32dt + 8(r>>2) + 4h + (r&3) of row lane&31) as bf16 rows of 256 B, times
+// `mul`; 32 rows x 256 B at `stage`
+__device__ __forceinline__ void stage_rows(char* stage, const f32x16 (&acc)[4], float mul,
+                                           int l32, int h) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+            bf16x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[dt][4 * rq + e] * mul);
+            const int d0 = 32 * dt + 8 * rq + 4 * h;
+            *(bf16x4*)(stage + l32 * 256 + (((d0 >> 3) ^ (l32 & 15)) << 4) + (d0 & 7) * 2) = v;
+        }
+}
+
+// write 32 staged rows to dst rows row0.., columns col..col+127 (ld elements)
+__device__ __forceinline__ void store_rows(const char* stage, __bf16* dst, int64_t ld, int row0,
+                                           int nrows_valid, int col, int lane) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int idx = i * 64 + lane;
+        const int row = idx >> 4, unit = idx & 15;
+        const u32x4 v = *(const u32x4*)(stage + row * 256 + ((unit ^ (row & 15)) << 4));
+        if (row < nrows_valid) *(u32x4*)(dst + (int64_t)(row0 + row) * ld + col + unit * 8) = v;
+    }
+}
+
+// --------------------------------------------------------------------- dQ
+__global__ __launch_bounds__(NT, 1) void attn_bwd_dq_kernel(
+    const __bf16* __restrict__ qkv, int64_t ld, const __bf16* __restrict__ O,
+    const __bf16* __restrict__ dO, int64_t ldo, const float* __restrict__ lse,
+    float* __restrict__ Dvec, __bf16* __restrict__ dqkv, int64_t ldd, int s, int Hl, int nqb,
+    int n_bh, int causal, float scale_log2, float scale)
+{
+    __shared__ __attribute__((aligned(1024))) char lds[2 * 2 * TILE];   // 2 x (K tile, V tile)
+
+    // all query blocks of a (sequence, head) on one XCD, heaviest first
+    const int id = blockIdx.x;
+    const int xcd = id & 7, local = id >> 3;
+    const int bh = (local / nqb) * 8 + xcd;
+    if (bh >= n_bh) return;
+    const int qb = nqb - 1 - local % nqb;
+    const int beta = bh / Hl, head = bh % Hl;
+    const int q0 = qb * BQ;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int l32 = lane & 31, h = lane >> 5;
+
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(qkv + (int64_t)beta * s * ld);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(O + (int64_t)beta * s * ldo);
+    const __amdgpu_buffer_rsrc_t rdo = make_rsrc(dO + (int64_t)beta * s * ldo);
+    const int qcol = head * D, kcol = Hl * D + head * D, vcol = 2 * Hl * D + head * D;
+    const int64_t stat = ((int64_t)beta * Hl + head) * s;
+
+    // Q and dO of the lane's query as B operands (dims 16kk + 8h .. +7), and
+    // D_q = sum over the head's dims of dO·O
+    const int my_q = q0 + 32 * w + l32;
+    const bool qok = my_q < s;
+    bf16x8 qf[8], dof[8];
+    float dsum = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+        const unsigned qoff = qok ? (unsigned)((int64_t)my_q * ld + qcol + kk * 16 + 8 * h) * 2u : OOB;
+        const unsigned ooff = qok ? (unsigned)((int64_t)my_q * ldo + head * D + kk * 16 + 8 * h) * 2u : OOB;
+        qf[kk] = ld8(rs, qoff);
+        dof[kk] = ld8(rdo, ooff);
+        const bf16x8 of = ld8(ro, ooff);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dsum = fmaf((float)dof[kk][e], (float)of[e], dsum);
+    }
+    const float Dq = dsum + __shfl_xor(dsum, 32);
+    if (qok && h == 0) Dvec[stat + my_q] = Dq;
+    const float L2 = qok ? lse[stat + my_q] : 0.0f;
+
+    // K/V tile copy: thread owns unit (tid & 15) of rows (tid >> 4) + 16 i
+    const int c_unit = tid & 15, c_row0 = tid >> 4;
+    const unsigned st_off = c_row0 * 256 + ((c_unit ^ (c_row0 & 15)) << 4);   // + 4096 i
+    u32x4 rk[CP], rv[CP];
+    auto load_kv = [&](int kv0) {
+#pragma unroll
+        for (int i = 0; i < CP; ++i) {
+            const int r = kv0 + c_row0 + 16 * i;
+            const unsigned base = (unsigned)((int64_t)r * ld + c_unit * 8) * 2u;
+            rk[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, r < s ? base + kcol * 2u : OOB, 0, 0);
+            rv[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, r < s ? base + vcol * 2u : OOB, 0, 0);
+        }
+    };
+    auto store_kv = [&](char* stage) {
+#pragma unroll
+        for (int i = 0; i < CP; ++i) {
+            *(u32x4*)(stage + st_off + 4096 * i) = rk[i];
+            *(u32x4*)(stage + TILE + st_off + 4096 * i) = rv[i];
+        }
+    };
+    // row reads (A = K or V rows 32t + l32, dims 16kk + 8h..)
+    unsigned rd[8];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) rd[kk] = l32 * 256 + (((2 * kk + h) ^ (lane & 15)) << 4);
+    // transpose reads of K (A = K^T: dims 32dt + (lane & 31), keys in B order)
+    const int G = lane >> 4, gi = lane & 15;
+    unsigned tlo[4], thi[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+        const int col = 32 * dt + 16 * (G & 1) + 4 * (gi & 3);
+        tlo[dt] = tile_off(4 * h + (gi >> 2), col);
+        thi[dt] = tile_off(8 + 4 * h + (gi >> 2), col);
+    }
+
+    f32x16 dq[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dq[dt][r] = 0.0f;
+
+    const int kv_end = causal ? min(s, q0 + BQ) : s;
+    const int n_kv = (kv_end + T64 - 1) / T64;
+    const int qw_lo = q0 + 32 * w, qw_hi = qw_lo + 31;
+    const int lim = causal ? min(my_q, s - 1) : s - 1;
+
+    load_kv(0);
+    store_kv(lds);
+    __syncthreads();
+    for (int kb = 0; kb < n_kv; ++kb) {
+        const int kv0 = kb * T64;
+        const bool has_next = kb + 1 < n_kv;
+        if (has_next) load_kv(kv0 + T64);
+        const char* base = lds + (kb & 1) * 2 * TILE;
+        if (!causal || kv0 <= qw_hi) {
+            f32x16 sacc[2], pacc[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sacc[t][r] = pacc[t][r] = 0.0f;
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const bf16x8 kf = *(const bf16x8*)(base + rd[kk] + t * 32 * 256);
+                    const bf16x8 vf = *(const bf16x8*)(base + TILE + rd[kk] + t * 32 * 256);
+                    sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sacc[t], 0, 0, 0);
+                    pacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, dof[kk], pacc[t], 0, 0, 0);
+                }
+            const bool edge = (causal && kv0 + T64 - 1 > qw_lo) || kv0 + T64 > s;
+            bf16x8 dsk[2][2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = kv0 + 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
+                    float p = __builtin_amdgcn_exp2f(fmaf(sacc[t][r], scale_log2, -L2));
+                    if (edge && key > lim) p = 0.0f;
+                    dsk[t][r >> 3][r & 7] = (__bf16)(p * (pacc[t][r] - Dq));
+                }
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    const char* kb_base = base + (32 * t + 16 * half) * 256;
+#pragma unroll
+                    for (int dt = 0; dt < 4; ++dt)
+                        dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            tr_read(kb_base, tlo[dt], thi[dt]), dsk[t][half], dq[dt], 0, 0, 0);
+                }
+        }
+        if (has_next) store_kv(lds + ((kb + 1) & 1) * 2 * TILE);
+        __syncthreads();
+    }
+
+    char* stage = lds + w * (32 * 256);
+    stage_rows(stage, dq, scale, l32, h);
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();
+    store_rows(stage, dqkv + (int64_t)beta * s * ldd, ldd, qw_lo, s - qw_lo, qcol, lane);
+}
+
+// ------------------------------------------------------------------ dK, dV
+constexpr int STAGE_KV = 2 * TILE + 512;     // Q tile, dO tile, L[64], D[64]
+
+__global__ __launch_bounds__(NT, 1) void attn_bwd_dkv_kernel(
+    const __bf16* __restrict__ qkv, int64_t ld, const __bf16* __restrict__ dO, int64_t ldo,
+    const float* __restrict__ lse, const float* __restrict__ Dvec, __bf16* __restrict__ dqkv,
+    int64_t ldd, int s, int Hl, int nkb, int n_bh, int causal, float scale_log2, float scale)
+{
+    __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE_KV];
+
+    // all key blocks of a (sequence, head) on one XCD; key block 0 (under a
+    // causal mask the one with the most query tiles) first
+    const int id = blockIdx.x;
+    const int xcd = id & 7, local = id >> 3;
+    const int bh = (local / nkb) * 8 + xcd;
+    if (bh >= n_bh) return;
+    const int kb = local % nkb;
+    const int beta = bh / Hl, head = bh % Hl;
+    const int k0 = kb * BK;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int l32 = lane & 31, h = lane >> 5;
+
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(qkv + (int64_t)beta * s * ld);
+    const __amdgpu_buffer_rsrc_t rdo = make_rsrc(dO + (int64_t)beta * s * ldo);
+    const int qcol = head * D, kcol = Hl * D + head * D, vcol = 2 * Hl * D + head * D;
+    const int64_t stat = ((int64_t)beta * Hl + head) * s;
+
+    // K and V of the lane's key as B operands
+    const int kw0 = k0 + 32 * w;
+    const int my_k = kw0 + l32;
+    bf16x8 kf[8], vf[8];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+        const unsigned off = my_k < s ? (unsigned)((int64_t)my_k * ld + kk * 16 + 8 * h) * 2u : OOB;
+        kf[kk] = ld8(rs, off == OOB ? OOB : off + kcol * 2u);
+        vf[kk] = ld8(rs, off == OOB ? OOB : off + vcol * 2u);
+    }
+
+    // Q / dO tile copy (as the K/V copy above) and the tile's L and D:
+    // threads 0..63 load L of query q0 + tid, 64..127 D of query q0 + tid - 64
+    const int c_unit = tid & 15, c_row0 = tid >> 4;
+    const unsigned st_off = c_row0 * 256 + ((c_unit ^ (c_row0 & 15)) << 4);
+    u32x4 rq[CP], rdq[CP];
+    float rstat = 0.0f;
+    auto load_q = [&](int q0) {
+#pragma unroll
+        for (int i = 0; i < CP; ++i) {
+            const int r = q0 + c_row0 + 16 * i;
+            const bool ok = r < s;
+            rq[i] = __builtin_amdgcn_raw_buffer_load_b128(
+                rs, ok ? (unsigned)((int64_t)r * ld + qcol + c_unit * 8) * 2u : OOB, 0, 0);
+            rdq[i] = __builtin_amdgcn_raw_buffer_load_b128(
+                rdo, ok ? (unsigned)((int64_t)r * ldo + head * D + c_unit * 8) * 2u : OOB, 0, 0);
+        }
+        if (tid < 128) {
+            const int q = q0 + (tid & 63);
+            rstat = q < s ? (tid < 64 ? lse[stat + q] : Dvec[stat + q]) : 0.0f;
+        }
+    };
+    auto store_q = [&](char* stage) {
+#pragma unroll
+        for (int i = 0; i < CP; ++i) {
+            *(u32x4*)(stage + st_off + 4096 * i) = rq[i];
+            *(u32x4*)(stage + TILE + st_off + 4096 * i) = rdq[i];
+        }
+        if (tid < 128) *(float*)(stage + 2 * TILE + 4 * tid) = rstat;
+    };
+    unsigned rd[8];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) rd[kk] = l32 * 256 + (((2 * kk + h) ^ (lane & 15)) << 4);
+    const int G = lane >> 4, gi = lane & 15;
+    unsigned tlo[4], thi[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+        const int col = 32 * dt + 16 * (G & 1) + 4 * (gi & 3);
+        tlo[dt] = tile_off(4 * h + (gi >> 2), col);
+        thi[dt] = tile_off(8 + 4 * h + (gi >> 2), col);
+    }
+
+    f32x16 dk[4], dv[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dk[dt][r] = dv[dt][r] = 0.0f;
+
+    const int qt0 = causal ? k0 / T64 : 0;
+    const int nqt = (s + T64 - 1) / T64;
+    load_q(qt0 * T64);
+    store_q(lds);
+    __syncthreads();
+    for (int qt = qt0; qt < nqt; ++qt) {
+        const int q0 = qt * T64;
+        const bool has_next = qt + 1 < nqt;
+        if (has_next) load_q(q0 + T64);
+        const char* base = lds + ((qt - qt0) & 1) * STAGE_KV;
+        const float* Ls = (const float*)(base + 2 * TILE);
+        const float* Ds = Ls + T64;
+        if (!causal || q0 + T64 - 1 >= kw0) {
+            f32x16 sacc[2], pacc[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sacc[t][r] = pacc[t][r] = 0.0f;
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const bf16x8 qa = *(const bf16x8*)(base + rd[kk] + t * 32 * 256);
+                    const bf16x8 da = *(const bf16x8*)(base + TILE + rd[kk] + t * 32 * 256);
+                    sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[kk], sacc[t], 0, 0, 0);
+                    pacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[kk], pacc[t], 0, 0, 0);
+                }
+            const bool edge = (causal && q0 < kw0 + 31) || q0 + T64 > s;
+            bf16x8 pk[2][2], dsk[2][2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int rq4 = 0; rq4 < 4; ++rq4) {
+                    const int qi = 32 * t + 8 * rq4 + 4 * h;      // tile query of element e = 0
+                    const f32x4 Lv = *(const f32x4*)(Ls + qi);
+                    const f32x4 Dv = *(const f32x4*)(Ds + qi);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 4 * rq4 + e, q = q0 + qi + e;
+                        float p = __builtin_amdgcn_exp2f(fmaf(sacc[t][r], scale_log2, -Lv[e]));
+                        if (edge && (q >= s || (causal && q < my_k))) p = 0.0f;
+                        pk[t][r >> 3][r & 7] = (__bf16)p;
+                        dsk[t][r >> 3][r & 7] = (__bf16)(p * (pacc[t][r] - Dv[e]));
+                    }
+                }
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    const char* qb_base = base + (32 * t + 16 * half) * 256;
+#pragma unroll
+                    for (int dt = 0; dt < 4; ++dt) {
+                        dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            tr_read(qb_base + TILE, tlo[dt], thi[dt]), pk[t][half], dv[dt], 0, 0, 0);
+                        dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            tr_read(qb_base, tlo[dt], thi[dt]), dsk[t][half], dk[dt], 0, 0, 0);
+                    }
+                }
+        }
+        if (has_next) store_q(lds + ((qt + 1 - qt0) & 1) * STAGE_KV);
+        __syncthreads();
+    }
+
+    char* stage = lds + w * (2 * 32 * 256);
+    stage_rows(stage, dk, scale, l32, h);
+    stage_rows(stage + 32 * 256, dv, 1.0f, l32, h);
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();
+    __bf16* rows = dqkv + (int64_t)beta * s * ldd;
+    store_rows(stage, rows, ldd, kw0, s - kw0, kcol, lane);
+    store_rows(stage + 32 * 256, rows, ldd, kw0, s - kw0, vcol, lane);
+}
+
+}  // namespace
+
+hipError_t attention_bwd(const void* qkv, int64_t ld_qkv, const void* O, const void* dO,
+                         const float* lse, float* Dvec, void* dqkv, int64_t b, int64_t s,
+                         int64_t H_l, bool causal, hipStream_t stream)
+{
+    const int n_bh = (int)(b * H_l);
+    const int groups_per_xcd = (n_bh + 7) / 8;
+    const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
+    const float scale = (float)(1.0 / sqrt((double)D));
+    const int nqb = (int)((s + BQ - 1) / BQ), nkb = (int)((s + BK - 1) / BK);
+    const int64_t ldo = H_l * D, ldd = 3 * H_l * D;
+    hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3(8 * groups_per_xcd * nqb), dim3(NT), 0, stream,
+                       (const __bf16*)qkv, ld_qkv, (const __bf16*)O, (const __bf16*)dO, ldo, lse,
+                       Dvec, (__bf16*)dqkv, ldd, (int)s, (int)H_l, nqb, n_bh, causal ? 1 : 0,
+                       scale_log2, scale);
+    hipLaunchKernelGGL(attn_bwd_dkv_kernel, dim3(8 * groups_per_xcd * nkb), dim3(NT), 0, stream,
+                       (const __bf16*)qkv, ld_qkv, (const __bf16*)dO, ldo, lse,
+                       (const float*)Dvec, (__bf16*)dqkv, ldd, (int)s, (int)H_l, nkb, n_bh,
+                       causal ? 1 : 0, scale_log2, scale);
+    return hipGetLastError();
+}
+
+}  // namespace tpk

@@ -441,6 +441,124 @@ TP_EXPORT tp_status tp_attention_core(const void* qkv, int64_t ld_qkv, void* O, 
     return launched(tpk::attention_fwd(qkv, ld_qkv, O, b, s, H_l, causal != 0, as_stream(stream)));
 }
 
+// ---- attention: training forward and backward ----------------------------
+namespace {
+tp_status check_core(int64_t ld_qkv, int64_t b, int64_t s, int64_t H_l, int64_t d) {
+    if (b <= 0 || s <= 0 || H_l <= 0 || d != kHeadDim || ld_qkv < 3 * H_l * d || ld_qkv % 8)
+        return TP_ERR_SHAPE;
+    if (s * ld_qkv * 2 >= kI32 || ((s + 127) / 128) * (b * H_l + 7) > kI32) return TP_ERR_SHAPE;
+    return TP_OK;
+}
+
+struct AttnBwdWs { int64_t dO, dqkv, D, total; };
+AttnBwdWs attn_bwd_ws(int64_t b, int64_t s, int64_t H_l, int64_t d) {
+    const int64_t M = b * s;
+    AttnBwdWs w;
+    w.dO = 0;
+    w.dqkv = align_up(M * H_l * d * 2);
+    w.D = w.dqkv + align_up(M * 3 * H_l * d * 2);
+    w.total = w.D + align_up(M * H_l * 4);
+    return w;
+}
+}  // namespace
+
+TP_EXPORT tp_status tp_attention_core_train(const void* qkv, int64_t ld_qkv, void* O, float* lse,
+                                            int64_t b, int64_t s, int64_t H_l, int64_t d,
+                                            int causal, void* stream) {
+    if (!qkv || !O || !lse) return TP_ERR_NULL;
+    tp_status st = check_core(ld_qkv, b, s, H_l, d);
+    if (st != TP_OK) return st;
+    if (!aligned16(qkv) || !aligned16(O) || !aligned16(lse)) return TP_ERR_ALIGN;
+    return launched(tpk::attention_fwd(qkv, ld_qkv, O, b, s, H_l, causal != 0, as_stream(stream),
+                                       1, 0, 0, lse));
+}
+
+TP_EXPORT tp_status tp_attention_core_backward(const void* qkv, int64_t ld_qkv, const void* O,
+                                               const void* dO, const float* lse, void* dqkv,
+                                               float* D_ws, int64_t b, int64_t s, int64_t H_l,
+                                               int64_t d, int causal, void* stream) {
+    if (!qkv || !O || !dO || !lse || !dqkv || !D_ws) return TP_ERR_NULL;
+    tp_status st = check_core(ld_qkv, b, s, H_l, d);
+    if (st != TP_OK) return st;
+    if (!aligned16(qkv) || !aligned16(O) || !aligned16(dO) || !aligned16(lse) ||
+        !aligned16(dqkv) || !aligned16(D_ws))
+        return TP_ERR_ALIGN;
+    return launched(tpk::attention_bwd(qkv, ld_qkv, O, dO, lse, D_ws, dqkv, b, s, H_l,
+                                       causal != 0, as_stream(stream)));
+}
+
+TP_EXPORT tp_status tp_attn_shard_train_fwd(const void* X, const void* W_qkv_i,
+                                            const void* W_o_i, void* Z_i, void* qkv, void* O,
+                                            float* lse, int64_t b, int64_t s, int64_t h,
+                                            int64_t H_l, int64_t d, int causal, int out,
+                                            void* stream) {
+    if (!X || !W_qkv_i || !W_o_i || !Z_i || !qkv || !O || !lse) return TP_ERR_NULL;
+    if (!is_dtype(out)) return TP_ERR_DTYPE;
+    tp_status st = check_attn_shape(b, s, h, H_l, d);
+    if (st != TP_OK) return st;
+    const void* ptrs[] = {X, W_qkv_i, W_o_i, Z_i, qkv, O, lse};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return TP_ERR_ALIGN;
+    const hipStream_t stm = as_stream(stream);
+    const int64_t M = b * s, HD = H_l * d, n3 = 3 * HD;
+    if (tpk::gemm_bf16(X, h, W_qkv_i, n3, nullptr, qkv, n3, M, n3, h, true, false, stm))
+        return TP_ERR_LAUNCH;
+    if (tpk::attention_fwd(qkv, n3, O, b, s, H_l, causal != 0, stm, 1, 0, 0, lse))
+        return TP_ERR_LAUNCH;
+    return launched(tpk::gemm_bf16(O, HD, W_o_i, h, nullptr, Z_i, h, M, h, HD, out == TP_BF16,
+                                   false, stm));
+}
+
+TP_EXPORT size_t tp_attn_shard_backward_workspace(int64_t b, int64_t s, int64_t H_l, int64_t d) {
+    if (b <= 0 || s <= 0 || H_l <= 0 || d <= 0) return 0;
+    return (size_t)attn_bwd_ws(b, s, H_l, d).total;
+}
+
+TP_EXPORT tp_status tp_attn_shard_backward(const void* X, const void* W_qkv_i, const void* W_o_i,
+                                           const void* qkv, const void* O, const float* lse,
+                                           const void* dZ, void* dX_i, void* dW_qkv_i,
+                                           void* dW_o_i, void* ws, size_t ws_bytes, int64_t b,
+                                           int64_t s, int64_t h, int64_t H_l, int64_t d,
+                                           int causal, int dx_dtype, void* stream) {
+    if (!X || !W_qkv_i || !W_o_i || !qkv || !O || !lse || !dZ || !dX_i || !dW_qkv_i || !dW_o_i)
+        return TP_ERR_NULL;
+    if (!is_dtype(dx_dtype)) return TP_ERR_DTYPE;
+    tp_status st = check_attn_shape(b, s, h, H_l, d);
+    if (st != TP_OK) return st;
+    const int64_t M = b * s, HD = H_l * d, n3 = 3 * HD;
+    // the weight-gradient products read X, O and dqkv with the token as their row
+    if (!operand_fits(h, false) || !operand_fits(n3, true) || !operand_fits(h, true))
+        return TP_ERR_SHAPE;
+    const AttnBwdWs w = attn_bwd_ws(b, s, H_l, d);
+    if (!ws || ws_bytes < (size_t)w.total) return TP_ERR_WORKSPACE;
+    const void* ptrs[] = {X, W_qkv_i, W_o_i, qkv, O, lse, dZ, dX_i, dW_qkv_i, dW_o_i, ws};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return TP_ERR_ALIGN;
+    const hipStream_t stm = as_stream(stream);
+    char* base = (char*)ws;
+    void* dO = base + w.dO;
+    void* dqkv = base + w.dqkv;
+    float* Dv = (float*)(base + w.D);
+    // dO = dZ·W_o,i^T                           [M, H_l·d] bf16
+    if (run_matmul(dZ, h, 0, W_o_i, h, 1, nullptr, dO, HD, nullptr, 0, M, HD, h, TP_BF16,
+                   TP_EPI_NONE, stm))
+        return TP_ERR_LAUNCH;
+    // dW_o,i = O^T·dZ                            [H_l·d, h] f32
+    if (run_matmul(O, HD, 1, dZ, h, 0, nullptr, dW_o_i, h, nullptr, 0, HD, h, M, TP_F32,
+                   TP_EPI_NONE, stm))
+        return TP_ERR_LAUNCH;
+    // dQ, dK, dV of the local heads            [M, 3·H_l·d] bf16
+    if (tpk::attention_bwd(qkv, n3, O, dO, lse, Dv, dqkv, b, s, H_l, causal != 0, stm))
+        return TP_ERR_LAUNCH;
+    // dW_qkv,i = X^T·dqkv                        [h, 3·H_l·d] f32
+    if (run_matmul(X, h, 1, dqkv, n3, 0, nullptr, dW_qkv_i, n3, nullptr, 0, h, n3, M, TP_F32,
+                   TP_EPI_NONE, stm))
+        return TP_ERR_LAUNCH;
+    // dX_i = dqkv·W_qkv,i^T                      [M, h] partial over ranks
+    return launched(run_matmul(dqkv, n3, 0, W_qkv_i, n3, 1, nullptr, dX_i, h, nullptr, 0, M, h,
+                               n3, dx_dtype, TP_EPI_NONE, stm));
+}
+
 TP_EXPORT tp_status tp_layernorm(const void* x, int in, void* y, const void* gamma,
                                  const void* beta, float eps, int64_t M, int64_t h,
                                  void* stream) {

@@ -57,10 +57,21 @@ hipError_t gemm_f32(const float* A, int64_t lda, const float* B, int64_t ldb,
 // Causal / full softmax(Q K^T / sqrt(d)) V for every (rank, sequence, local
 // head); d == 128.  Rank r's qkv is [b*s, ld_qkv] bf16 at qkv + r*qkv_rank_stride,
 // its O is [b*s, H_l*128] bf16 at O + r*o_rank_stride (strides in elements).
+// If lse is not NULL it receives, per (rank, sequence, head, query), the log2
+// softmax normaliser L = log2 sum_k 2^(s_k·log2(e)/sqrt(d)) as f32
+// [ranks][b][H_l][s].
 hipError_t attention_fwd(const void* qkv, int64_t ld_qkv, void* O,
                          int64_t b, int64_t s, int64_t H_l, bool causal,
                          hipStream_t stream, int ranks = 1, int64_t qkv_rank_stride = 0,
-                         int64_t o_rank_stride = 0);
+                         int64_t o_rank_stride = 0, float* lse = nullptr);
+
+// Backward of attention_fwd for one rank: from qkv, O, the upstream gradient
+// dO ([b*s, H_l*128] bf16, leading dimension H_l*128) and lse, writes
+// dqkv [b*s, 3*H_l*128] bf16 (dQ, dK, dV in qkv's column layout) and
+// D = rowsum(dO ⊙ O) into Dvec (f32 [b][H_l][s]).
+hipError_t attention_bwd(const void* qkv, int64_t ld_qkv, const void* O, const void* dO,
+                         const float* lse, float* Dvec, void* dqkv, int64_t b, int64_t s,
+                         int64_t H_l, bool causal, hipStream_t stream);
 
 // y = LayerNorm(x) rows of length h, y in bf16.
 hipError_t layernorm(const void* x, bool x_bf16, void* y, const float* gamma,
