@@ -21,12 +21,15 @@ Besides the one JSON line the run reports, in the same line:
   calibration   the throughput of a register-only MFMA loop on this GPU (the
                 matrix cores' ceiling under the current clock and power
                 limits) and of the vendor GEMM at the dominant kernel's shape;
-  training      (block workload) rank 0's MLP-share backward at the same
-                shape, timed with HIP events.
+  training      (block workload) rank 0's MLP-share and attention-share
+                backward at the same shape, timed with HIP events.
 
 --workload mlp_bwd_bf16_h12288_tp8 measures that backward as its own step
 (dY, dB_i, dA_i, da_i and the dX_i partial of one rank at the 175B layer
-shape), with the weight-gradient product X^T·dY as its dominant kernel.
+shape), with the weight-gradient product X^T·dY as its dominant kernel;
+--workload attn_bwd_bf16_h12288_tp8 the attention share's backward (dO,
+dW_o,i, the attention-core backward, dW_qkv,i, dX_i) with the input-gradient
+product dqkv·W_qkv^T as its dominant kernel.
 
 Modes for profiler runs: --mode kernel launches only the dominant kernel,
 --mode copy only a plain device copy of a known size (counter calibration).
@@ -144,9 +147,20 @@ def dominant_operands_cpu(w, wl):
         X, A, _ = wl.mlp_inputs(w)
         return X, [A]
     if w.kind == "mlp_bwd":
-        # the weight-gradient product X^T·dY; dY's values do not change its cost
-        X = wl.mlp_bwd_inputs(w)[0]
-        return X, [wl.normal((w.M, w.f), 1.0, w.seed, "preact", w.dtype)]
+        # the weight-gradient products Y'^T·dZ and X^T·dY; the values of the
+        # activations dY and Y' do not change their cost
+        X, _, _, _, dZ = wl.mlp_bwd_inputs(w)
+        dY = wl.normal((w.M, w.f), 1.0, w.seed, "preact", w.dtype)
+        Yp = wl.normal((w.M, w.f), 1.0, w.seed, "partials", w.dtype)
+        return X, [dY, Yp, dZ]
+    if w.kind == "attn_bwd":
+        # the weight-gradient products X^T·dqkv and O^T·dZ (values of the
+        # activations dqkv and O do not change their cost)
+        X, _, _, dZ = wl.attn_bwd_inputs(w)
+        HD = w.Hl * w.d
+        dqkv = wl.normal((w.M, 3 * HD), 1.0, w.seed, "preact", w.dtype)
+        O = wl.normal((w.M, HD), 1.0, w.seed, "partials", w.dtype)
+        return X, [dqkv, O, dZ]
     X, Wqkv, _ = wl.attn_inputs(w)
     return X, [Wqkv]
 
@@ -160,13 +174,29 @@ def dominant_kernel(w, tts, torch, X, Ws, dev):
     M, K = X.shape
     N = Ws[0].shape[1]
     if w.kind == "mlp_bwd":
-        # dA_i = X^T·dY: [h, M]·[M, f], K = the token count, f32 out
-        dA = torch.empty(K, N, dtype=torch.float32, device=dev)
+        # dB_i = Y'^T·dZ [f, h] and dA_i = X^T·dY [h, f] in one grouped launch
+        dY, Yp, dZ = Ws
+        f, h = dY.shape[1], K
+        dA = torch.empty(h, f, dtype=torch.float32, device=dev)
+        dB = torch.empty(f, h, dtype=torch.float32, device=dev)
 
         def launch():
-            tts.tp_matmul(X, Ws[0], trans_a=True, out=dA)
-        name = "gemm_bf16_kernel<TN, f32 out> X^T·dY [%dx%d]x[%dx%d]" % (K, M, M, N)
-        return launch, 2 * M * N * K, name
+            tts.tp_matmul_grouped([Yp, X], [dZ, dY], trans_a=True, outs=[dB, dA])
+        name = ("gemm_bf16_kernel<TN, f32 out> grouped: Y'^T·dZ [%dx%d]x[%dx%d] and "
+                "X^T·dY [%dx%d]x[%dx%d]" % (f, M, M, h, h, M, M, f))
+        return launch, 2 * (2 * M * h * f), name
+    if w.kind == "attn_bwd":
+        # dW_qkv,i = X^T·dqkv and dW_o,i = O^T·dZ in one grouped launch
+        dqkv, O, dZ = Ws
+        h, n3, HD = K, dqkv.shape[1], O.shape[1]
+        dWqkv = torch.empty(h, n3, dtype=torch.float32, device=dev)
+        dWo = torch.empty(HD, h, dtype=torch.float32, device=dev)
+
+        def launch():
+            tts.tp_matmul_grouped([X, O], [dqkv, dZ], trans_a=True, outs=[dWqkv, dWo])
+        name = ("gemm_bf16_kernel<TN, f32 out> grouped: X^T·dqkv [%dx%d]x[%dx%d] and "
+                "O^T·dZ [%dx%d]x[%dx%d]" % (h, M, M, n3, HD, M, M, h))
+        return launch, 2 * M * h * n3 + 2 * M * HD * h, name
     gelu = w.kind != "attn"
     outs = [torch.empty(M, N, dtype=torch.bfloat16, device=dev) for _ in Ws]
     if len(Ws) > 1:
@@ -280,7 +310,26 @@ def main():
             tts.tp_mlp_shard_backward(x, A0, B0, Y0, Yp0, dZ, **bwd_out)
         dY0 = tts.tp_matmul(dZ, B0, trans_b=True, epilogue="gelu_bwd", aux=Y0,
                             out_dtype=torch.bfloat16)
-        X_k, W_k = x, [dY0]
+        X_k, W_k = x, [dY0, Yp0, dZ]
+    elif w.kind == "attn_bwd":
+        X_cpu, Wqkv_cpu, Wo_cpu, dZ_cpu = wl.attn_bwd_inputs(w)
+        x, Wqkv0, Wo0, dZ = (t.to(dev) for t in (X_cpu, Wqkv_cpu, Wo_cpu, dZ_cpu))
+        M, h, HD = w.M, w.h, w.Hl * w.d
+        f = 3 * HD
+        # the saved activations come from the training forward, outside the timed step
+        _, qkv0, O0, lse0 = tts.tp_attn_shard_train_fwd(x, Wqkv0, Wo0, w.b, w.s, w.Hl, w.d)
+        bwd_out = dict(dX_out=torch.empty(M, h, dtype=torch.float32, device=dev),
+                       dWqkv_out=torch.empty(h, 3 * HD, dtype=torch.float32, device=dev),
+                       dWo_out=torch.empty(HD, h, dtype=torch.float32, device=dev),
+                       ws=torch.empty(tts.tp_attn_shard_backward_workspace(w.b, w.s, w.Hl, w.d),
+                                      dtype=torch.uint8, device=dev))
+
+        def step():
+            tts.tp_attn_shard_backward(x, Wqkv0, Wo0, qkv0, O0, lse0, dZ, w.b, w.s, w.Hl, w.d,
+                                       **bwd_out)
+        dO0 = tts.tp_matmul(dZ, Wo0, trans_b=True, out_dtype=torch.bfloat16)
+        dqkv0 = tts.tp_attention_core_backward(qkv0, O0, dO0, lse0, w.b, w.s, w.Hl, w.d)
+        X_k, W_k = x, [dqkv0, O0, dZ]
     else:
         X_cpu, Wqkv_cpu, Wo_cpu = wl.attn_inputs(w)
         x, Wqkv0, Wo0 = X_cpu.to(dev), Wqkv_cpu.to(dev), Wo_cpu.to(dev)
@@ -322,7 +371,7 @@ def main():
     kern_tflops = kern_flops / (kern_ms * 1e-3) / 1e12
     traffic = measured_traffic(TRAFFIC_FILES[w.name]) if w.name in TRAFFIC_FILES else None
     log(f"dominant kernel: {kern_ms:.3f} ms/launch, {kern_tflops:.1f} TFLOP/s")
-    calib = calibration(tts, torch, X_k, W_k[0], stream, trans_a=w.kind == "mlp_bwd")
+    calib = calibration(tts, torch, X_k, W_k[0], stream, trans_a=w.kind.endswith("_bwd"))
     log(f"calibration: {calib}")
 
     components = {}
@@ -377,10 +426,9 @@ def main():
             "dY_gemm_nt_gelu_bwd": (lambda: tts.tp_matmul(dZ, B0, trans_b=True,
                                                           epilogue="gelu_bwd", aux=Y0, out=dYc),
                                     fl1, None),
-            "dB_gemm_tn": (lambda: tts.tp_matmul(Yp0, dZ, trans_a=True, out=bwd_out["dB_out"]),
-                           fl1, None),
-            "dA_gemm_tn": (lambda: tts.tp_matmul(x, dYc, trans_a=True, out=bwd_out["dA_out"]),
-                           fl1, None),
+            "dB_dA_gemm_tn_grouped": (lambda: tts.tp_matmul_grouped(
+                [Yp0, x], [dZ, dYc], trans_a=True, outs=[bwd_out["dB_out"], bwd_out["dA_out"]]),
+                2 * fl1, None),
             "dX_gemm_nt": (lambda: tts.tp_matmul(dYc, A0, trans_b=True, out=bwd_out["dX_out"]),
                            fl1, None),
         }
@@ -393,9 +441,34 @@ def main():
             log(f"component {name}: {c}")
         del dYc
 
+    if w.kind == "attn_bwd":
+        Dws = torch.empty(w.b * w.Hl * w.s, dtype=torch.float32, device=dev)
+        dqkv_c = torch.empty(M, 3 * HD, dtype=torch.bfloat16, device=dev)
+        dO_c = torch.empty(M, HD, dtype=torch.bfloat16, device=dev)
+        fl = w.attn_bwd_flops_rank()
+        items = {
+            "dO_gemm_nt": (lambda: tts.tp_matmul(dZ, Wo0, trans_b=True, out=dO_c), fl["wo"] // 2),
+            "attention_core_backward": (lambda: tts.tp_attention_core_backward(
+                qkv0, O0, dO_c, lse0, w.b, w.s, w.Hl, w.d, dqkv=dqkv_c, D_ws=Dws), fl["core"]),
+            "dWqkv_dWo_gemm_tn_grouped": (lambda: tts.tp_matmul_grouped(
+                [x, O0], [dqkv_c, dZ], trans_a=True,
+                outs=[bwd_out["dWqkv_out"], bwd_out["dWo_out"]]), (fl["qkv"] + fl["wo"]) // 2),
+            "dX_gemm_nt": (lambda: tts.tp_matmul(dqkv_c, Wqkv0, trans_b=True,
+                                                 out=bwd_out["dX_out"]), fl["qkv"] // 2),
+        }
+        for name, (fn, flc) in items.items():
+            fn()
+            t, _ = event_time(fn, 3, stream)
+            c = {"ms": round(t, 4), "tflops": round(flc / (t * 1e-3) / 1e12, 1),
+                 "pct_peak": round(100 * flc / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 1)}
+            components[name] = c
+            log(f"component {name}: {c}")
+        del Dws, dqkv_c, dO_c
+
     training = None
     if w.kind == "block" and not args.no_training:
         training = mlp_backward_rank0(w, wl, tts, torch, x, A[0], B[0], dev, stream)
+        training.update(attn_backward_rank0(w, wl, tts, torch, x, Wqkv[0], Wo[0], dev, stream))
 
     # ---------------------------------------------------------------- oracle
     cpu = None
@@ -471,6 +544,34 @@ def mlp_backward_rank0(w, wl, tts, torch, x, A0, B0, dev, stream):
     return res
 
 
+def attn_backward_rank0(w, wl, tts, torch, x, Wqkv0, Wo0, dev, stream):
+    """Rank 0's attention-share backward at the block's shape: its training
+    forward once, then the backward timed with HIP events."""
+    M, h, HD = w.M, w.h, w.Hl * w.d
+    dZ = wl.normal((M, h), 1.0, w.seed, "dZ", w.dtype).to(dev)
+    _, qkv, O, lse = tts.tp_attn_shard_train_fwd(x, Wqkv0, Wo0, w.b, w.s, w.Hl, w.d)
+    outs = dict(dX_out=torch.empty(M, h, dtype=torch.float32, device=dev),
+                dWqkv_out=torch.empty(h, 3 * HD, dtype=torch.float32, device=dev),
+                dWo_out=torch.empty(HD, h, dtype=torch.float32, device=dev),
+                ws=torch.empty(tts.tp_attn_shard_backward_workspace(w.b, w.s, w.Hl, w.d),
+                               dtype=torch.uint8, device=dev))
+    fn = lambda: tts.tp_attn_shard_backward(x, Wqkv0, Wo0, qkv, O, lse, dZ, w.b, w.s, w.Hl,
+                                            w.d, **outs)
+    fn()
+    t, _ = event_time(fn, 5, stream)
+    fl = w.attn_bwd_flops_rank()["total"]
+    res = {"attn_shard_backward_rank0": {
+        "ms": round(t, 4), "tflops": round(fl / (t * 1e-3) / 1e12, 1),
+        "pct_peak": round(100 * fl / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 1),
+        "flops": fl,
+        "what": "tp_attn_shard_backward: dO, dW_o,0, attention-core backward (dQ, dK, dV), "
+                "dW_qkv,0, dX_0 partial, for %d sequences of %d, %d local heads" % (
+                    w.b, w.s, w.Hl)}}
+    log(f"training: {res}")
+    del dZ, qkv, O, lse, outs
+    return res
+
+
 def cpu_baseline(w, rows_req, env):
     """The fp64 oracle, as it stands, on the first tokens of sequence 0."""
     import numpy as np
@@ -500,6 +601,20 @@ def cpu_baseline(w, rows_req, env):
         dt = time.time() - t0
         fl = 4 * R * w.h * A_cpu.shape[1]
         sample = f"rows 0..{R - 1} of the MLP shard; {fl / 1e12:.3f} TFLOP"
+    elif w.kind == "attn_bwd":
+        # whole sequences: the backward of a causal sequence involves all of it
+        R = min(rows_req, w.s)
+        X_cpu, Wqkv_cpu, Wo_cpu, dZ_cpu = (env[k] for k in ("X_cpu", "Wqkv_cpu", "Wo_cpu",
+                                                             "dZ_cpu"))
+        log(f"oracle: attention backward over sequence 0 truncated to {R} tokens")
+        t0 = time.time()
+        oracle.attn_shard_backward(X_cpu[:R], 1, R, Wqkv_cpu, Wo_cpu, dZ_cpu[:R], w.Hl, w.d, True)
+        dt = time.time() - t0
+        HD = w.Hl * w.d
+        fl = 2 * (2 * R * w.h * 3 * HD) + 2 * (2 * R * HD * w.h) + 10 * w.Hl * w.d * R * (R + 1) // 2
+        sample = (f"the attention-share backward of one sequence of {R} tokens (its causal "
+                  f"prefix of sequence 0); {fl / 1e12:.3f} TFLOP counted, the oracle's "
+                  f"recomputation of the forward not counted")
     elif w.kind == "mlp_bwd":
         R = min(rows_req, w.M)
         X_cpu, A_cpu, B_cpu, a_cpu, dZ_cpu = (env[k] for k in ("X_cpu", "A_cpu", "B_cpu",

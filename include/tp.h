@@ -275,6 +275,20 @@ tp_status tp_matmul(const void* A, int64_t lda, int trans_a, const void* B, int6
                     int64_t ldaux, int64_t M, int64_t N, int64_t K, int out, int epilogue,
                     void* stream);
 
+/* tp_matmul_grouped -- `count` (1..16) products C[g] = op(A[g])·op(B[g]) of
+ * one layout (trans_a, trans_b as in tp_matmul, no epilogue), one output
+ * dtype and one inner size K, each with its own M[g], N[g] and leading
+ * dimensions, in a single launch.  A backward pass's weight gradients
+ * ([Megatron explainer] §2.2, §3.2: every rank forms the gradients of its
+ * own weight slices) are such a set: launched together, one product's tiles
+ * fill the partly idle last wave of the other's.  All arguments are HOST
+ * arrays of `count` entries (device pointers, sizes); each group must
+ * satisfy tp_matmul's conditions. */
+tp_status tp_matmul_grouped(const void* const* A, const int64_t* lda, int trans_a,
+                            const void* const* B, const int64_t* ldb, int trans_b,
+                            void* const* C, const int64_t* ldc, const int64_t* M,
+                            const int64_t* N, int count, int64_t K, int out, void* stream);
+
 /* tp_attention_core -- per (sequence, local head) softmax(Q·K^T/sqrt d)·V
  * ([Megatron explainer] §3.1) on projections already in memory.
  *   qkv [b·s, ld_qkv] bf16: for local head j, Q at columns j·d, K at

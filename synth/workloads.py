@@ -19,7 +19,7 @@ from . import normal, fan_in_sigma, rank_seed
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str            # "mlp" | "attn" | "block" | "mlp_bwd"
+    kind: str            # "mlp" | "attn" | "block" | "mlp_bwd" | "attn_bwd"
     seed: int
     P: int               # tensor-parallel degree
     b: int
@@ -55,6 +55,16 @@ class Workload:
         wo = 2 * self.M * self.Hl * self.d * self.h
         return {"qkv": qkv, "core": core, "wo": wo, "total": qkv + core + wo}
 
+    def attn_bwd_flops_rank(self) -> dict:
+        """Backward of one rank's attention share: the projections' input and
+        weight gradients (two products each, of the forward's size) and the
+        core's five products per visible (query, key) pair (S and dP
+        recomputed, dV, dQ, dK: 10·d FLOPs per pair and head)."""
+        f = self.attn_flops_rank()
+        core = 10 * self.Hl * self.d * (self.b * self.s * (self.s + 1) // 2)
+        return {"qkv": 2 * f["qkv"], "core": core, "wo": 2 * f["wo"],
+                "total": 2 * f["qkv"] + core + 2 * f["wo"]}
+
     def flops(self) -> int:
         """Matrix FLOPs of one call of the workload's entry point."""
         if self.kind == "mlp":
@@ -64,6 +74,8 @@ class Workload:
             return 2 * self.mlp_flops_rank()
         if self.kind == "attn":
             return self.attn_flops_rank()["total"]
+        if self.kind == "attn_bwd":
+            return self.attn_bwd_flops_rank()["total"]
         return self.P * (self.mlp_flops_rank() + self.attn_flops_rank()["total"])
 
 
@@ -80,6 +92,10 @@ WORKLOADS = {w.name: w for w in [
     Workload("mlp_bwd_bf16_h12288_tp8", "mlp_bwd", 1005, P=8, b=8, s=2048, h=12288, F=49152,
              description="bf16 backward of one rank's MLP share of tp=8 at the 175B layer "
                          "shape, 16384 tokens: dA_i, dB_i, da_i and the dX_i partial"),
+    Workload("attn_bwd_bf16_h12288_tp8", "attn_bwd", 1006, P=8, b=8, s=2048, h=12288, H=96,
+             description="bf16 backward of one rank's causal attention share of tp=8 at the "
+                         "175B layer shape (12 local heads of 128, 8 sequences of 2048): "
+                         "dW_qkv,i, dW_o,i and the dX_i partial"),
     Workload("block_bf16_h12288_tp8", "block", 1004, P=8, b=8, s=2048, h=12288, H=96, F=49152,
              all_ranks=True,
              description="bf16 pre-LN block at the 175B layer shape, all 8 ranks of tp=8 in turn"),
@@ -127,3 +143,11 @@ def mlp_bwd_inputs(w: Workload):
     a = torch.zeros(w.f, dtype=torch.float32)
     dZ = normal((w.M, w.h), 1.0, w.seed, "dZ", w.dtype)
     return X, A, B, a, dZ
+
+
+def attn_bwd_inputs(w: Workload):
+    """X, rank 0's W_qkv_0, W_o_0 and the upstream gradient dZ ~ N(0, 1) of an
+    attention backward workload, on the CPU."""
+    X, Wqkv, Wo = attn_inputs(w)
+    dZ = normal((w.M, w.h), 1.0, w.seed, "dZ", w.dtype)
+    return X, Wqkv, Wo, dZ

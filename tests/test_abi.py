@@ -261,3 +261,23 @@ def test_mlp_train_fwd_rejects():
     assert call(h=20) == _lib.TP_ERR_SHAPE
     assert call(o=9) == _lib.TP_ERR_DTYPE
     assert call(Yp=FAKE_ODD) == _lib.TP_ERR_ALIGN
+
+
+def test_matmul_grouped_rejects():
+    L = tts.lib()
+    P2 = ctypes.c_void_p * 2
+    I2 = ctypes.c_int64 * 2
+    ok, hole = P2(FAKE.value, FAKE.value), P2(FAKE.value, None)
+    odd = P2(FAKE.value, FAKE_ODD.value)
+    call = lambda A=ok, lda=I2(64, 128), ta=1, C=ok, M=I2(64, 128), N=I2(32, 64), count=2, K=100: \
+        L.tp_matmul_grouped(A, lda, ta, ok, I2(64, 64), 0, C, I2(64, 64), M, N, count, K,
+                            _lib.TP_F32, None)
+    assert call(A=hole) == _lib.TP_ERR_NULL
+    assert call(count=0) == _lib.TP_ERR_SHAPE
+    assert call(count=17) == _lib.TP_ERR_SHAPE
+    assert call(M=I2(64, 60)) == _lib.TP_ERR_SHAPE      # TN: M is A's contiguous dimension
+    assert call(lda=I2(64, 32)) == _lib.TP_ERR_SHAPE    # group 1's lda < M
+    assert call(ta=2) == _lib.TP_ERR_DTYPE
+    assert call(C=odd) == _lib.TP_ERR_ALIGN
+    assert L.tp_matmul_grouped(None, I2(64, 64), 1, ok, I2(64, 64), 0, ok, I2(64, 64), I2(64, 64),
+                               I2(64, 64), 2, 64, 0, None) == _lib.TP_ERR_NULL

@@ -321,3 +321,24 @@ def test_attn_backward_deterministic_and_ranks_sum():
     Wqkv_full = torch.cat([Wq, Wk, Wv], dim=1)
     rX = oracle.attn_shard_backward(X, b, s, Wqkv_full, Wo, dZ, H, 128, True)[0]
     assert_bf16(dX, rX)
+
+
+@pytest.mark.parametrize("ta,tb,shapes,K", [
+    (1, 0, [(264, 520), (520, 264), (8, 16)], 333),     # weight gradients: A stored [K, M]
+    (1, 0, [(512, 256), (256, 768)], 1024),
+    (0, 1, [(600, 520), (40, 264)], 328),
+    (0, 0, [(300, 264), (16, 8), (256, 512)], 200)])
+def test_matmul_grouped(ta, tb, shapes, K):
+    """One launch of products with different M and N (and leading
+    dimensions): every group against the oracle."""
+    banner(f"matmul grouped ta={ta} tb={tb} shapes={shapes} K={K}")
+    As = [gen((K, m) if ta else (m, K), 1.0, 230 + g, "x") for g, (m, n) in enumerate(shapes)]
+    Bs = [gen((n, K) if tb else (K, n), 1 / math.sqrt(K), 230 + g, "A")
+          for g, (m, n) in enumerate(shapes)]
+    outs = tts.tp_matmul_grouped([A.to(DEV) for A in As], [B.to(DEV) for B in Bs],
+                                 trans_a=bool(ta), trans_b=bool(tb))
+    torch.cuda.synchronize()
+    for g in range(len(shapes)):
+        a = oracle.f64(As[g]).T if ta else As[g]
+        b = oracle.f64(Bs[g]).T if tb else Bs[g]
+        assert_f32(outs[g], oracle.matmul(a, b), bar=1e-4)

@@ -22,7 +22,7 @@ __all__ = [
     "TpError", "tp_abi_version", "tp_mlp_shard", "tp_mlp_shard_workspace", "tp_attn_shard",
     "tp_attn_shard_workspace", "tp_partial_sum", "tp_block_shard", "tp_block_shard_workspace",
     "tp_linear", "tp_linear_batched", "tp_attention_core", "tp_layernorm", "tp_probe_mfma",
-    "tp_matmul", "tp_mlp_shard_train_fwd", "tp_mlp_shard_backward",
+    "tp_matmul", "tp_matmul_grouped", "tp_mlp_shard_train_fwd", "tp_mlp_shard_backward",
     "tp_mlp_shard_backward_workspace", "tp_attention_core_train", "tp_attention_core_backward",
     "tp_attn_shard_train_fwd", "tp_attn_shard_backward", "tp_attn_shard_backward_workspace",
     "lib",
@@ -288,6 +288,32 @@ def tp_matmul(A, B, bias=None, *, trans_a=False, trans_b=False, epilogue="none",
         _stream(stream))
     _check(st, "tp_matmul")
     return (out, aux) if epilogue == "gelu_save" else out
+
+
+def tp_matmul_grouped(As, Bs, *, trans_a=False, trans_b=False, outs=None,
+                      out_dtype=torch.float32, stream=None):
+    """C[g] = op(A[g])·op(B[g]) for every g in one launch; the products share
+    layout and K but may differ in M and N.  Returns the list of C[g]."""
+    count = len(As)
+    if len(Bs) != count or (outs is not None and len(outs) != count):
+        raise ValueError("As, Bs and outs must have the same length")
+    Ms = [A.shape[1] if trans_a else A.shape[0] for A in As]
+    Ks = {A.shape[0] if trans_a else A.shape[1] for A in As}
+    Ks |= {B.shape[1] if trans_b else B.shape[0] for B in Bs}
+    if len(Ks) != 1:
+        raise ValueError("all products must share the inner size K")
+    K = Ks.pop()
+    Ns = [B.shape[0] if trans_b else B.shape[1] for B in Bs]
+    if outs is None:
+        outs = [torch.empty(m, n, dtype=out_dtype, device=As[0].device) for m, n in zip(Ms, Ns)]
+    I64 = ctypes.c_int64 * count
+    st = _lib.load().tp_matmul_grouped(
+        _ptr_array(As, "A"), I64(*[A.shape[1] for A in As]), int(bool(trans_a)),
+        _ptr_array(Bs, "B"), I64(*[B.shape[1] for B in Bs]), int(bool(trans_b)),
+        _ptr_array(outs, "out"), I64(*[C.shape[1] for C in outs]), I64(*Ms), I64(*Ns), count, K,
+        _code(outs[0].dtype), _stream(stream))
+    _check(st, "tp_matmul_grouped")
+    return outs
 
 
 def tp_attention_core(qkv, b: int, s: int, H_l: int, d: int = 128, causal=True, *, out=None,

@@ -52,6 +52,10 @@ SIGNATURES = {
     "tp_probe_mfma": (_int, [_vp, _int, _int, _vp]),
     "tp_matmul": (_int, [_vp, _i64, _int, _vp, _i64, _int, _vp, _vp, _i64, _vp, _i64, _i64, _i64,
                          _i64, _int, _int, _vp]),
+    "tp_matmul_grouped": (_int, [ctypes.POINTER(_vp), ctypes.POINTER(_i64), _int,
+                                 ctypes.POINTER(_vp), ctypes.POINTER(_i64), _int,
+                                 ctypes.POINTER(_vp), ctypes.POINTER(_i64), ctypes.POINTER(_i64),
+                                 ctypes.POINTER(_i64), _int, _i64, _int, _vp]),
     "tp_mlp_shard_train_fwd": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int,
                                       _vp]),
     "tp_mlp_shard_backward_workspace": (_sz, [_i64, _i64]),

@@ -132,25 +132,31 @@ __device__ __forceinline__ float gelu_grad(float x) {
 // of group 1, ...: all XCDs work on the same group (the same weight matrix)
 // at the same time and one group's tail overlaps the next group's head.
 // Inside a range, tiles walk the output GROUP_M tile-rows at a time.  Returns
-// false for the few padding workgroups of XCDs with one tile fewer per group.
-__device__ __forceinline__ bool tile_coords(int pid, int groups, int tiles_m, int tiles_n,
-                                            int& g, int& tm, int& tn) {
-    const int ntiles = tiles_m * tiles_n;
-    const int xcd = pid & 7, local = pid >> 3;
-    const int per = ntiles >> 3, rem = ntiles & 7;
-    const int cnt = per + (xcd < rem ? 1 : 0);         // this XCD's tiles per group
-    if (cnt == 0) return false;
-    g = local / cnt;
-    if (g >= groups) return false;
-    const int id = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + local % cnt;
-    const int width = GROUP_M * tiles_n;
-    const int group = id / width;
-    const int first_m = group * GROUP_M;
-    const int gsize = min(tiles_m - first_m, GROUP_M);
-    const int in_group = id - group * width;
-    tm = first_m + in_group % gsize;
-    tn = in_group / gsize;
-    return true;
+// false for the few padding workgroups of XCDs with fewer tiles.
+__device__ __forceinline__ bool tile_coords(int pid, const GemmBatch& b, int& g, int& tm,
+                                            int& tn) {
+    const int xcd = pid & 7;
+    int local = pid >> 3;
+    for (g = 0; g < b.count; ++g) {
+        const int tiles_m = (b.M[g] + BM - 1) / BM, tiles_n = (b.N[g] + BN - 1) / BN;
+        const int ntiles = tiles_m * tiles_n;
+        const int per = ntiles >> 3, rem = ntiles & 7;
+        const int cnt = per + (xcd < rem ? 1 : 0);          // this XCD's tiles of group g
+        if (local < cnt) {
+            const int id = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) +
+                           local;
+            const int width = GROUP_M * tiles_n;
+            const int group = id / width;
+            const int first_m = group * GROUP_M;
+            const int gsize = min(tiles_m - first_m, GROUP_M);
+            const int in_group = id - group * width;
+            tm = first_m + in_group % gsize;
+            tn = in_group / gsize;
+            return true;
+        }
+        local -= cnt;
+    }
+    return false;
 }
 
 // The order used when every group shares its A operand (the activations X
@@ -195,8 +201,7 @@ __device__ __forceinline__ int kc_kpos(int lane, int j) {
 
 template <int LAYOUT, int EPI, bool OUT_BF16, bool CHECK_K>
 __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
-    GemmBatch batch, int64_t lda, int64_t ldb, int64_t ldc, int64_t ldaux,
-    int M, int N, int K, int tiles_m, int tiles_n)
+    GemmBatch batch, int64_t ldaux, int K)
 {
     constexpr bool A_MC = LAYOUT == GEMM_TN;    // A stored [K,M]: M contiguous
     constexpr bool B_KC = LAYOUT == GEMM_NT;    // B stored [N,K]: K contiguous
@@ -207,9 +212,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
     __shared__ __attribute__((aligned(1024))) char lds1[STAGE_BYTES];
 
     int grp, tm, tn;
-    if (batch.band ? !tile_coords_band(blockIdx.x, batch.count, tiles_m, tiles_n, grp, tm, tn)
-                   : !tile_coords(blockIdx.x, batch.count, tiles_m, tiles_n, grp, tm, tn))
+    if (batch.band ? !tile_coords_band(blockIdx.x, batch.count, (batch.M[0] + BM - 1) / BM,
+                                       (batch.N[0] + BN - 1) / BN, grp, tm, tn)
+                   : !tile_coords(blockIdx.x, batch, grp, tm, tn))
         return;
+    const int M = batch.M[grp], N = batch.N[grp];
+    const int64_t lda = batch.lda[grp], ldb = batch.ldb[grp], ldc = batch.ldc[grp];
     const int m0 = tm * BM, n0 = tn * BN;
     const __bf16* __restrict__ A = batch.A[grp];
     const __bf16* __restrict__ B = batch.B[grp];
@@ -478,28 +486,29 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
 
 }  // namespace
 
-hipError_t gemm_bf16_batched(const GemmBatch& batch, int layout, int epi, int64_t lda,
-                             int64_t ldb, int64_t ldc, int64_t ldaux, int64_t M, int64_t N,
-                             int64_t K, bool out_bf16, hipStream_t stream)
+namespace {
+hipError_t launch(const GemmBatch& b, int layout, int epi, int64_t ldaux, int64_t K,
+                  bool out_bf16, hipStream_t stream)
 {
-    if (M <= 0 || N <= 0 || batch.count <= 0) return hipSuccess;
-    const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
-    GemmBatch b = batch;
-    bool shared_a = b.count > 1;
-    for (int i = 1; i < b.count; ++i) shared_a = shared_a && b.A[i] == b.A[0];
-    b.band = (shared_a && tiles_m % 8 == 0) ? 1 : 0;
-    const int per_xcd = b.band ? ((tiles_m / 8 + GROUP_M - 1) / GROUP_M) * GROUP_M * tiles_n
-                               : (tiles_m * tiles_n + 7) / 8;
-    const dim3 grid(8 * per_xcd * b.count), block(NTHREADS);
+    int per_xcd = 0;
+    if (b.band) {
+        const int tiles_m = (b.M[0] + BM - 1) / BM, tiles_n = (b.N[0] + BN - 1) / BN;
+        per_xcd = ((tiles_m / 8 + GROUP_M - 1) / GROUP_M) * GROUP_M * tiles_n * b.count;
+    } else {
+        for (int g = 0; g < b.count; ++g)
+            per_xcd += (((b.M[g] + BM - 1) / BM) * ((b.N[g] + BN - 1) / BN) + 7) / 8;
+    }
+    if (per_xcd == 0) return hipSuccess;
+    const dim3 grid(8 * per_xcd), block(NTHREADS);
     const bool ck = (K % BK) != 0;
 #define TP_GEMM(L, E, OB)                                                                      \
     do {                                                                                       \
         if (ck)                                                                                \
             hipLaunchKernelGGL((gemm_bf16_kernel<L, E, OB, true>), grid, block, 0, stream, b,  \
-                               lda, ldb, ldc, ldaux, (int)M, (int)N, (int)K, tiles_m, tiles_n); \
+                               ldaux, (int)K);                                                 \
         else                                                                                   \
             hipLaunchKernelGGL((gemm_bf16_kernel<L, E, OB, false>), grid, block, 0, stream, b, \
-                               lda, ldb, ldc, ldaux, (int)M, (int)N, (int)K, tiles_m, tiles_n); \
+                               ldaux, (int)K);                                                 \
         return hipGetLastError();                                                              \
     } while (0)
     switch (layout) {
@@ -518,6 +527,36 @@ hipError_t gemm_bf16_batched(const GemmBatch& batch, int layout, int epi, int64_
     }
 #undef TP_GEMM
     return hipErrorInvalidValue;      // a layout / epilogue pair with no kernel
+}
+}  // namespace
+
+hipError_t gemm_bf16_grouped(const GemmBatch& batch, int layout, int epi, int64_t ldaux,
+                             int64_t K, bool out_bf16, hipStream_t stream)
+{
+    if (batch.count <= 0 || batch.count > kMaxBatch || K <= 0) return hipSuccess;
+    GemmBatch b = batch;
+    b.band = 0;
+    return launch(b, layout, epi, ldaux, K, out_bf16, stream);
+}
+
+hipError_t gemm_bf16_batched(const GemmBatch& batch, int layout, int epi, int64_t lda,
+                             int64_t ldb, int64_t ldc, int64_t ldaux, int64_t M, int64_t N,
+                             int64_t K, bool out_bf16, hipStream_t stream)
+{
+    if (M <= 0 || N <= 0 || batch.count <= 0) return hipSuccess;
+    GemmBatch b = batch;
+    for (int g = 0; g < b.count; ++g) {
+        b.M[g] = (int)M;
+        b.N[g] = (int)N;
+        b.lda[g] = lda;
+        b.ldb[g] = ldb;
+        b.ldc[g] = ldc;
+    }
+    const int tiles_m = (int)((M + BM - 1) / BM);
+    bool shared_a = b.count > 1;
+    for (int i = 1; i < b.count; ++i) shared_a = shared_a && b.A[i] == b.A[0];
+    b.band = (shared_a && tiles_m % 8 == 0) ? 1 : 0;
+    return launch(b, layout, epi, ldaux, K, out_bf16, stream);
 }
 
 hipError_t gemm_bf16_batched(const GemmBatch& batch, int64_t lda, int64_t ldb, int64_t ldc,

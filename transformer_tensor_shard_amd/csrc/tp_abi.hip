@@ -122,6 +122,30 @@ hipError_t run_matmul(const void* A, int64_t lda, int ta, const void* B, int64_t
                                   out == TP_BF16, st);
 }
 
+// `n` bf16 products of one layout, output type and K but their own shapes in
+// one grouped launch (no epilogue); the caller has validated every group
+struct Product {
+    const void* A; int64_t lda; const void* B; int64_t ldb; void* C; int64_t ldc;
+    int64_t M, N;
+};
+hipError_t run_grouped(const Product* p, int n, int64_t K, int ta, int tb, int out,
+                       hipStream_t st) {
+    tpk::GemmBatch gb = {};
+    gb.count = n;
+    for (int i = 0; i < n; ++i) {
+        gb.A[i] = (const __bf16*)p[i].A;
+        gb.B[i] = (const __bf16*)p[i].B;
+        gb.C[i] = p[i].C;
+        gb.M[i] = (int)p[i].M;
+        gb.N[i] = (int)p[i].N;
+        gb.lda[i] = p[i].lda;
+        gb.ldb[i] = p[i].ldb;
+        gb.ldc[i] = p[i].ldc;
+    }
+    const int layout = ta ? tpk::GEMM_TN : (tb ? tpk::GEMM_NT : tpk::GEMM_NN);
+    return tpk::gemm_bf16_grouped(gb, layout, tpk::EPI_NONE, 0, K, out == TP_BF16, st);
+}
+
 // ---- MLP shard ------------------------------------------------------------
 int64_t mlp_ws(int64_t M, int64_t f, int in) { return align_up(M * f * esize(in)); }
 
@@ -319,6 +343,24 @@ TP_EXPORT tp_status tp_matmul(const void* A, int64_t lda, int trans_a, const voi
                                K, out, epilogue, as_stream(stream)));
 }
 
+TP_EXPORT tp_status tp_matmul_grouped(const void* const* A, const int64_t* lda, int trans_a,
+                                      const void* const* B, const int64_t* ldb, int trans_b,
+                                      void* const* C, const int64_t* ldc, const int64_t* M,
+                                      const int64_t* N, int count, int64_t K, int out,
+                                      void* stream) {
+    if (!A || !lda || !B || !ldb || !C || !ldc || !M || !N) return TP_ERR_NULL;
+    if (count <= 0 || count > tpk::kMaxBatch) return TP_ERR_SHAPE;
+    Product p[tpk::kMaxBatch];
+    for (int g = 0; g < count; ++g) {
+        const tp_status s = check_matmul(A[g], lda[g], trans_a, B[g], ldb[g], trans_b, nullptr,
+                                         C[g], ldc[g], nullptr, 0, M[g], N[g], K, out,
+                                         TP_EPI_NONE);
+        if (s != TP_OK) return s;
+        p[g] = {A[g], lda[g], B[g], ldb[g], C[g], ldc[g], M[g], N[g]};
+    }
+    return launched(run_grouped(p, count, K, trans_a, trans_b, out, as_stream(stream)));
+}
+
 // ---- MLP shard: training forward and backward ------------------------------
 namespace {
 struct MlpBwdWs {
@@ -392,14 +434,10 @@ TP_EXPORT tp_status tp_mlp_shard_backward(const void* X, const void* A_i, const 
     if (run_matmul(dZ, h, 0, B_i, h, 1, nullptr, dY, f, (void*)Y_i, f, M, f, h, TP_BF16,
                    TP_EPI_GELU_BWD, st))
         return TP_ERR_LAUNCH;
-    // dB_i = Y'_i^T·dZ                         [f,h] f32
-    if (run_matmul(Yp_i, f, 1, dZ, h, 0, nullptr, dB_i, h, nullptr, 0, f, h, M, TP_F32,
-                   TP_EPI_NONE, st))
-        return TP_ERR_LAUNCH;
-    // dA_i = X^T·dY                            [h,f] f32
-    if (run_matmul(X, h, 1, dY, f, 0, nullptr, dA_i, f, nullptr, 0, h, f, M, TP_F32, TP_EPI_NONE,
-                   st))
-        return TP_ERR_LAUNCH;
+    // dB_i = Y'_i^T·dZ [f,h] and dA_i = X^T·dY [h,f], f32, in one grouped
+    // launch: each alone leaves a partly filled last wave of tiles
+    const Product wgrad[2] = {{Yp_i, f, dZ, h, dB_i, h, f, h}, {X, h, dY, f, dA_i, f, h, f}};
+    if (run_grouped(wgrad, 2, M, 1, 0, TP_F32, st)) return TP_ERR_LAUNCH;
     // dX_i = dY·A_i^T                          [M,h] partial over ranks
     if (run_matmul(dY, f, 0, A_i, f, 1, nullptr, dX_i, h, nullptr, 0, M, h, f, dx_dtype,
                    TP_EPI_NONE, st))
@@ -543,17 +581,14 @@ TP_EXPORT tp_status tp_attn_shard_backward(const void* X, const void* W_qkv_i, c
     if (run_matmul(dZ, h, 0, W_o_i, h, 1, nullptr, dO, HD, nullptr, 0, M, HD, h, TP_BF16,
                    TP_EPI_NONE, stm))
         return TP_ERR_LAUNCH;
-    // dW_o,i = O^T·dZ                            [H_l·d, h] f32
-    if (run_matmul(O, HD, 1, dZ, h, 0, nullptr, dW_o_i, h, nullptr, 0, HD, h, M, TP_F32,
-                   TP_EPI_NONE, stm))
-        return TP_ERR_LAUNCH;
     // dQ, dK, dV of the local heads            [M, 3·H_l·d] bf16
     if (tpk::attention_bwd(qkv, n3, O, dO, lse, Dv, dqkv, b, s, H_l, causal != 0, stm))
         return TP_ERR_LAUNCH;
-    // dW_qkv,i = X^T·dqkv                        [h, 3·H_l·d] f32
-    if (run_matmul(X, h, 1, dqkv, n3, 0, nullptr, dW_qkv_i, n3, nullptr, 0, h, n3, M, TP_F32,
-                   TP_EPI_NONE, stm))
-        return TP_ERR_LAUNCH;
+    // dW_qkv,i = X^T·dqkv [h, 3·H_l·d] and dW_o,i = O^T·dZ [H_l·d, h], f32, in
+    // one grouped launch (dW_o,i alone has too few tiles to fill the GPU)
+    const Product wgrad[2] = {{X, h, dqkv, n3, dW_qkv_i, n3, h, n3},
+                              {O, HD, dZ, h, dW_o_i, h, HD, h}};
+    if (run_grouped(wgrad, 2, M, 1, 0, TP_F32, stm)) return TP_ERR_LAUNCH;
     // dX_i = dqkv·W_qkv,i^T                      [M, h] partial over ranks
     return launched(run_matmul(dqkv, n3, 0, W_qkv_i, n3, 1, nullptr, dX_i, h, nullptr, 0, M, h,
                                n3, dx_dtype, TP_EPI_NONE, stm));

@@ -15,9 +15,11 @@ enum GemmLayout { GEMM_NN = 0, GEMM_NT = 1, GEMM_TN = 2 };
 // DUAL  C = bf16 GeLU(v) and aux = bf16 v (the training forward).
 enum GemmEpi { EPI_NONE = 0, EPI_GELU = 1, EPI_GELU_BWD = 2, EPI_DUAL = 3 };
 
-// Up to kMaxBatch independent GEMMs of one shape, launched together: group g
-// computes C[g] = epi(op(A[g])·op(B[g]) + bias[g]).  Used for the emulated
-// ranks of a block, whose per-rank products have identical shapes.
+// Up to kMaxBatch independent GEMMs launched together: group g computes
+// C[g] = epi(op(A[g])·op(B[g]) + bias[g]), an [M[g], N[g]] product with
+// leading dimensions lda[g], ldb[g], ldc[g]; layout, epilogue, K and output
+// type are common.  Used for the emulated ranks of a block (identical
+// shapes) and for the weight gradients of a backward (different shapes).
 constexpr int kMaxBatch = 16;
 struct GemmBatch {
     const __bf16* A[kMaxBatch];
@@ -25,6 +27,8 @@ struct GemmBatch {
     const float* bias[kMaxBatch];
     void* C[kMaxBatch];
     __bf16* aux[kMaxBatch];   // GELU_BWD: read, DUAL: written; [M,N] with ldaux
+    int M[kMaxBatch], N[kMaxBatch];
+    int64_t lda[kMaxBatch], ldb[kMaxBatch], ldc[kMaxBatch];
     int count;
     int band;       // set by the launcher: tile order for groups sharing A
 };
@@ -35,6 +39,10 @@ struct GemmBatch {
 // dimensions multiples of 8.
 hipError_t gemm_bf16_batched(const GemmBatch& batch, int layout, int epi, int64_t lda,
                              int64_t ldb, int64_t ldc, int64_t ldaux, int64_t M, int64_t N,
+                             int64_t K, bool out_bf16, hipStream_t stream);
+// Groups with their own M[g], N[g], lda[g], ldb[g], ldc[g] (filled by the
+// caller; groups with M or N of 0 are skipped), common K.
+hipError_t gemm_bf16_grouped(const GemmBatch& batch, int layout, int epi, int64_t ldaux,
                              int64_t K, bool out_bf16, hipStream_t stream);
 // The forward (NN) form: epilogue GELU or NONE.
 hipError_t gemm_bf16_batched(const GemmBatch& batch, int64_t lda, int64_t ldb, int64_t ldc,
