@@ -35,9 +35,16 @@ def _flags():
             "-Wno-unused-command-line-argument"]
 
 
+# Per-source code-generation options.  The attention backward kernels keep
+# their MFMA accumulators in VGPRs (the default AGPR form costs hundreds of
+# register moves per tile there, to zero the score accumulators and to read
+# them for the exponentials).
+FILE_FLAGS = {"attention_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *_flags(), "-c", src, "-o", obj]
+    cmd = [hipcc(), *_flags(), *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
