@@ -35,11 +35,12 @@ def _flags():
             "-Wno-unused-command-line-argument"]
 
 
-# Per-source code-generation options.  The attention backward kernels keep
-# their MFMA accumulators in VGPRs (the default AGPR form costs hundreds of
-# register moves per tile there, to zero the score accumulators and to read
-# them for the exponentials).
-FILE_FLAGS = {"attention_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# Per-source code-generation options.  The attention kernels keep their MFMA
+# accumulators in VGPRs (the default AGPR form costs hundreds of register
+# moves per tile there, to zero the score accumulators and to read them for
+# the exponentials).
+FILE_FLAGS = {"attention_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+              "attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src: str, verbose: bool) -> str:

@@ -7,8 +7,10 @@
 //  * one workgroup = NW waves = 32*NW queries of one (sequence, head); all query
 //    blocks of a head run on one XCD side by side (their K/V is read from that
 //    XCD's L2), longest causal rows first so the tail of the launch is short;
-//  * keys/values stream through LDS in 64-key tiles, double-buffered, the next
-//    tile's global loads in flight during this tile's MFMAs;
+//  * keys/values stream through LDS in 64-key tiles, double-buffered, by the
+//    gfx950 direct-to-LDS buffer loads (no staging registers; the buffer
+//    range ends at the sequence's last row, so rows past it read as zeros),
+//    the next tile's loads in flight during this tile's MFMAs;
 //  * each wave owns 32 queries and computes S^T = K·Q^T with MFMA 32x32x16
 //    (A operand = K rows from LDS, B operand = Q held in registers), so every
 //    lane ends up holding the scores of ONE query: the online-softmax max and
@@ -20,8 +22,9 @@
 //  * exp is the hardware exp2 with log2(e)/sqrt(d) folded into one FMA per
 //    score; the mask is applied only on tiles that reach the diagonal or the
 //    end, and the accumulator is rescaled only when a running max moved;
-//  * LDS tiles are XOR-swizzled in 16-byte units (64 banks, conflict-free for
-//    the 16-byte K reads and the transpose V reads);
+//  * LDS tiles are XOR-swizzled in 16-byte units (conflict-free for both the
+//    16-byte K reads and the transpose V reads), two stages as two arrays so
+//    every LDS address is static;
 //  * the output block is staged through LDS and written with 16-byte stores;
 //    the training forward also writes each query's log2 softmax normaliser.
 #include "tp_kernels.h"
@@ -47,10 +50,21 @@ constexpr int D = 128, BQ = 32 * NW, BKV = 64;
 constexpr int TILE_BYTES = BKV * D * 2;      // 16 KiB (64 rows x 256 B)
 constexpr int STAGE_BYTES = 2 * TILE_BYTES;  // K tile + V tile
 constexpr unsigned OOB = 0x80000000u;
+constexpr int VMCNT0 = 0x0F70;               // s_waitcnt vmcnt(0)
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
-                                             0x7ffffff0, 0x00020000);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes,
+                                             0x00020000);
+}
+
+// Tile swizzle: logical 16-byte unit u of row r sits at physical unit
+// u ^ swz(r) -- 16 distinct values over 16 consecutive rows (16-byte row
+// reads of one unit by 16 lanes hit distinct banks) and distinct bits 2-3
+// over rows 4j..4j+3 (a transpose read of 32 columns over four rows touches
+// four distinct 64-byte windows).
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ unsigned tile_off(int row, int col) {
+    return row * 256 + (((col >> 3) ^ swz(row)) << 4) + (col & 7) * 2;
 }
 
 __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(
@@ -58,7 +72,10 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(
     __bf16* __restrict__ O, int64_t ldo, int64_t o_rank_stride, float* __restrict__ lse,
     int s, int b, int Hl, int nqb, int n_bh, int causal, float scale_log2)
 {
-    __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE_BYTES];
+    // two stages (K tile, V tile), each its own array: every LDS address is
+    // static and a stage's reads do not wait on the other stage's loads
+    __shared__ __attribute__((aligned(1024))) char lds0[STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char lds1[STAGE_BYTES];
 
     // Workgroups are dealt round-robin to the 8 XCDs.  All query blocks of one
     // (rank, sequence, head) go to the same XCD back to back, heaviest causal
@@ -76,69 +93,66 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(
     qkv += rank * qkv_rank_stride;
     O += rank * o_rank_stride;
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hi = lane >> 5;
 
     const __bf16* seq = qkv + (int64_t)beta * s * ld;
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(seq);
     const int qcol = head * D, kcol = Hl * D + head * D, vcol = 2 * Hl * D + head * D;
 
     // ---- Q operand in registers: lane = query (q0 + 32w + l32), 8 k-steps of
     // 16 head dims, lane half `hi` holds dims 8*hi..8*hi+7 of each step.
     const int qrow = q0 + 32 * w + l32;
     bf16x8 qf[8];
+    {
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(seq, 0x7ffffff0);
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-        const unsigned off = (qrow < s) ? (unsigned)((int64_t)qrow * ld + qcol + kk * 16 + 8 * hi) * 2u : OOB;
-        u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
-        qf[kk] = __builtin_bit_cast(bf16x8, v);
+        for (int kk = 0; kk < 8; ++kk) {
+            const unsigned off = (qrow < s) ? (unsigned)((int64_t)qrow * ld + qcol + kk * 16 + 8 * hi) * 2u : OOB;
+            qf[kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+        }
     }
 
-    // ---- K/V tile copy assignment: 64 rows x 16 units; thread owns unit
-    // (tid & 15) of rows (tid >> 4) + (NT/16) i.
-    constexpr int CP = 1024 / NT;            // 16-byte units per thread per tile
-    const int c_unit = tid & 15, c_row0 = tid >> 4;
-    unsigned k_lds[CP], v_lds[CP];
+    // ---- K/V tiles by direct-to-LDS loads: wave w fills the 1 KiB chunks
+    // 4w..4w+3 of each tile (rows 4c..4c+3 of chunk c); lane l fetches row
+    // 4c + l/16, logical unit (l % 16) ^ swz(row).  The buffer range of a tile
+    // ends at the sequence's last row, so rows past it read as zeros.
+    unsigned voff[4];
 #pragma unroll
-    for (int i = 0; i < CP; ++i) {
-        const int r = c_row0 + (NT / 16) * i;
-        k_lds[i] = r * 256 + ((c_unit ^ (r & 15)) << 4);
-        v_lds[i] = TILE_BYTES + r * 256 + ((c_unit ^ ((r & 3) << 2)) << 4);
+    for (int j = 0; j < 4; ++j) {
+        const int r = 4 * (4 * w + j) + (lane >> 4);
+        voff[j] = (unsigned)((int64_t)r * ld + (((lane & 15) ^ swz(r)) * 8)) * 2u;
     }
-    u32x4 rk[CP], rv[CP];
-    auto load_kv = [&](int kv0) {
+    auto dma_tile = [&](char* tile, int kv0, int col) {
+        const int64_t bytes = (int64_t)(s - kv0) * ld * 2;
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(
+            seq + (int64_t)kv0 * ld + col,
+            __builtin_amdgcn_readfirstlane((int)(bytes < 0x7ffffff0 ? bytes : 0x7ffffff0)));
 #pragma unroll
-        for (int i = 0; i < CP; ++i) {
-            const int r = kv0 + c_row0 + (NT / 16) * i;
-            const bool ok = r < s;
-            const unsigned base = (unsigned)((int64_t)r * ld + c_unit * 8) * 2u;
-            rk[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, ok ? base + kcol * 2u : OOB, 0, 0);
-            rv[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, ok ? base + vcol * 2u : OOB, 0, 0);
-        }
+        for (int j = 0; j < 4; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDS_PTR(void, tile + (4 * w + j) * 1024),
+                                                     16, voff[j], 0, 0, 0);
     };
-    auto store_kv = [&](int stage) {
-        char* b = lds + stage * STAGE_BYTES;
-#pragma unroll
-        for (int i = 0; i < CP; ++i) {
-            *(u32x4*)(b + k_lds[i]) = rk[i];
-            *(u32x4*)(b + v_lds[i]) = rv[i];
-        }
+    auto dma_kv = [&](char* stage, int kv0) {
+        dma_tile(stage, kv0, kcol);
+        dma_tile(stage + TILE_BYTES, kv0, vcol);
     };
 
     // K operand reads (A of S^T = K·Q^T): lane reads key row (32t + l32),
-    // 16-byte unit (2kk + hi), swizzled by (row & 15) = (lane & 15).
+    // dims 16kk + 8hi .. +7.
     unsigned k_rd[8];
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) k_rd[kk] = l32 * 256 + (((2 * kk + hi) ^ (lane & 15)) << 4);
+    for (int kk = 0; kk < 8; ++kk) k_rd[kk] = tile_off(l32, 16 * kk + 8 * hi);
     // V^T operand via transpose reads: 16-lane group G reads 4 key rows x 16
-    // dims; lane gi addresses row (gi >> 2), dims 4*(gi & 3)..+3.
+    // dims; lane gi addresses row (gi >> 2), dims 4*(gi & 3)..+3; the second
+    // read takes the rows 8 further on (the key order of P's B operand).
     const int G = lane >> 4, gi = lane & 15;
-    unsigned v_rd[4];
+    unsigned v_lo[4], v_hi[4];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
-        const int row = 4 * (G >> 1) + (gi >> 2);
         const int col = 32 * dt + 16 * (G & 1) + 4 * (gi & 3);
-        v_rd[dt] = TILE_BYTES + row * 256 + (((col >> 3) ^ ((row & 3) << 2)) << 4) + (col & 7) * 2;
+        v_lo[dt] = TILE_BYTES + tile_off(4 * hi + (gi >> 2), col);
+        v_hi[dt] = TILE_BYTES + tile_off(8 + 4 * hi + (gi >> 2), col);
     }
 
     f32x16 oacc[4];
@@ -153,97 +167,98 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(
     const int qw_lo = q0 + 32 * w, qw_hi = qw_lo + 31;   // this wave's queries
     const int my_q = qw_lo + l32;
 
-    load_kv(0);
-    store_kv(0);
-    __syncthreads();
-
-    for (int kb = 0; kb < n_kv; ++kb) {
-        const int cur = kb & 1;
-        const bool has_next = kb + 1 < n_kv;
-        const int kv0 = kb * BKV;
-        if (has_next) load_kv(kv0 + BKV);
-        const char* base = lds + cur * STAGE_BYTES;
-        const bool active = !causal || kv0 <= qw_hi;
-        if (active) {
-            f32x16 sacc[2];
+    auto compute = [&](const char* base, int kv0) {
+        if (causal && kv0 > qw_hi) return;           // every key after the wave's queries
+        f32x16 sacc[2];
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) sacc[t][r] = 0.0f;
+            for (int r = 0; r < 16; ++r) sacc[t][r] = 0.0f;
 #pragma unroll
-            for (int kk = 0; kk < 8; ++kk) {
+        for (int kk = 0; kk < 8; ++kk) {
 #pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const bf16x8 kf = *(const bf16x8*)(base + k_rd[kk] + t * 32 * 256);
-                    sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sacc[t], 0, 0, 0);
-                }
+            for (int t = 0; t < 2; ++t) {
+                const bf16x8 kf = *(const bf16x8*)(base + k_rd[kk] + t * 32 * 256);
+                sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sacc[t], 0, 0, 0);
             }
-            // mask keys past the diagonal or the end (only tiles that reach
-            // them); the raw score -inf gives weight exactly 0 below
-            if ((causal && kv0 + BKV - 1 > qw_lo) || kv0 + BKV > s) {
-                const int lim = causal ? min(my_q, s - 1) : s - 1;
-#pragma unroll
-                for (int t = 0; t < 2; ++t)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = kv0 + 32 * t + 8 * (r >> 2) + 4 * hi + (r & 3);
-                        sacc[t][r] = key > lim ? -INFINITY : sacc[t][r];
-                    }
-            }
-            // online softmax in the log2 domain: the scale log2(e)/sqrt(d) > 0
-            // commutes with max, so p = 2^(s*scale - m) is one FMA and one exp
-            float mloc = -INFINITY;
+        }
+        // mask keys past the diagonal or the end (only tiles that reach
+        // them); the raw score -inf gives weight exactly 0 below
+        if ((causal && kv0 + BKV - 1 > qw_lo) || kv0 + BKV > s) {
+            const int lim = causal ? min(my_q, s - 1) : s - 1;
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sacc[t][r]);
-            mloc = fmaxf(mloc, __shfl_xor(mloc, 32)) * scale_log2;
-            const float m_new = fmaxf(m_run, mloc);
-            const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-            m_run = m_new;
-            // probabilities rounded to bf16 (the MFMA operand); the normaliser
-            // sums the same rounded weights, two at a time with a bf16 dot
-            float lsum = 0.0f;
-            bf16x8 pk[2][2];
-            const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int r = 0; r < 16; r += 2) {
-                    bf16x2 pb;
-                    pb[0] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[t][r], scale_log2, -m_use));
-                    pb[1] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[t][r + 1], scale_log2, -m_use));
-                    lsum = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, lsum, false);
-                    pk[t][r >> 3][r & 7] = pb[0];
-                    pk[t][r >> 3][(r & 7) + 1] = pb[1];
-                }
-            l_run = l_run * alpha + lsum;
-            // rescale the accumulator only when some lane's running max moved
-            if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
-#pragma unroll
-                for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
-            }
-            // O^T += V^T · P^T over the 4 k-steps of 16 keys
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    const int koff = (32 * t + 16 * half) * 256;
-#pragma unroll
-                    for (int dt = 0; dt < 4; ++dt) {
-                        const char* p = base + v_rd[dt] + koff;
-                        bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, p));
-                        bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, p + 8 * 256));
-                        const bf16x8 vf = __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-                        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pk[t][half], oacc[dt], 0, 0, 0);
-                    }
+                for (int r = 0; r < 16; ++r) {
+                    const int key = kv0 + 32 * t + 8 * (r >> 2) + 4 * hi + (r & 3);
+                    sacc[t][r] = key > lim ? -INFINITY : sacc[t][r];
                 }
         }
-        if (has_next) store_kv(cur ^ 1);
+        // online softmax in the log2 domain: the scale log2(e)/sqrt(d) > 0
+        // commutes with max, so p = 2^(s*scale - m) is one FMA and one exp
+        float mloc = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sacc[t][r]);
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 32)) * scale_log2;
+        const float m_new = fmaxf(m_run, mloc);
+        const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+        m_run = m_new;
+        // probabilities rounded to bf16 (the MFMA operand); the normaliser
+        // sums the same rounded weights, two at a time with a bf16 dot
+        float lsum = 0.0f;
+        bf16x8 pk[2][2];
+        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                bf16x2 pb;
+                pb[0] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[t][r], scale_log2, -m_use));
+                pb[1] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[t][r + 1], scale_log2, -m_use));
+                lsum = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, lsum, false);
+                pk[t][r >> 3][r & 7] = pb[0];
+                pk[t][r >> 3][(r & 7) + 1] = pb[1];
+            }
+        l_run = l_run * alpha + lsum;
+        // rescale the accumulator only when some lane's running max moved
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+        }
+        // O^T += V^T · P^T over the 4 k-steps of 16 keys
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const char* vb = base + (32 * t + 16 * half) * 256;
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt) {
+                    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, vb + v_lo[dt]));
+                    const bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, vb + v_hi[dt]));
+                    const bf16x8 vf = __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+                    oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pk[t][half], oacc[dt], 0, 0, 0);
+                }
+            }
+    };
+    // tile i in stage (i & 1); the barrier after a tile publishes the next
+    // tile's LDS and frees the one just read
+    auto step = [&](char* cur, char* nxt, int i) {
+        if (i + 1 < n_kv) dma_kv(nxt, (i + 1) * BKV);
+        compute(cur, i * BKV);
+        __builtin_amdgcn_s_waitcnt(VMCNT0);
         __syncthreads();
+    };
+    dma_kv(lds0, 0);
+    __builtin_amdgcn_s_waitcnt(VMCNT0);
+    __syncthreads();
+    for (int i = 0; i < n_kv; i += 2) {
+        step(lds0, lds1, i);
+        if (i + 1 < n_kv) step(lds1, lds0, i + 1);
     }
 
     // ---- normalise and write: lane holds query l32, dims
@@ -255,7 +270,7 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(
     // backward recomputes P = 2^(s·c - L) without the running statistics
     if (lse && hi == 0 && my_q < s)
         lse[((int64_t)(rank * b + beta) * Hl + head) * s + my_q] = m_run + log2f(l_tot);
-    char* stage = lds + w * (32 * 256);
+    char* stage = lds0 + w * (32 * 256);
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
