@@ -57,6 +57,8 @@ TRAFFIC_FILES = {
     "block_bf16_h12288_tp8": os.path.join(ROOT, "profiles", "gemm_gelu_h12288_f6144_traffic.txt"),
     "mlp_bwd_bf16_h12288_tp8": os.path.join(ROOT, "profiles",
                                             "gemm_tn_wgrad_h12288_f6144_traffic.txt"),
+    "attn_bwd_bf16_h12288_tp8": os.path.join(ROOT, "profiles",
+                                             "gemm_tn_wgrad_attn_h12288_hd1536_traffic.txt"),
 }
 TRAFFIC_FILE = TRAFFIC_FILES["block_bf16_h12288_tp8"]
 

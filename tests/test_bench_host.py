@@ -18,11 +18,15 @@ def test_traffic_parser(tmp_path):
     assert bench.measured_traffic(str(tmp_path / "missing.txt"), "abc123") is None
 
 
-def test_committed_traffic_file_parses():
-    # the committed summary names the kernel source it was taken on
-    kv = dict(l.split(":", 1) for l in open(bench.TRAFFIC_FILE) if ":" in l and not l.startswith("#"))
-    h = kv["gemm_bf16_hip_sha256_16"].strip()
-    assert bench.measured_traffic(bench.TRAFFIC_FILE, h) > 0
+def test_committed_traffic_files_parse():
+    # each committed summary names the kernel source it was taken on; the
+    # current GEMM source is the one they were taken on
+    for path in bench.TRAFFIC_FILES.values():
+        kv = dict(l.split(":", 1) for l in open(path) if ":" in l and not l.startswith("#"))
+        h = kv["gemm_bf16_hip_sha256_16"].strip()
+        assert bench.measured_traffic(path, h) > 0
+        assert h == bench.kernel_source_hash(), path
+        assert float(kv["hbm_bytes_per_launch"]) > float(kv["algorithmic_bytes_per_launch"])
 
 
 def test_more_than_one_gpu_is_refused():
