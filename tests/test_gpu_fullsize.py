@@ -104,3 +104,60 @@ def test_block_fullsize_sampled():
     # the residual dominates: check each sub-layer's summed partials on its own
     assert_bf16(g_x1 - xr, x1_ref - xr)
     assert_bf16(g_out - g_x1, out_ref - x1_ref)
+
+
+def test_mlp_backward_fullsize_sampled():
+    """The MLP-share backward at the 175B layer shape (one rank of tp=8), launched
+    as the benchmark launches it: the training forward, then tp_mlp_shard_backward.
+    The share is separable over its f hidden columns -- a column subset J has exact
+    dA[:, J], dB[J, :] and da[J] from the oracle on A[:, J], B[J, :] alone -- and
+    dX rows are independent, so a row subset gives exact dX rows."""
+    w = wl.WORKLOADS["mlp_bwd_bf16_h12288_tp8"]
+    banner(f"{w.name}: M={w.M} h={w.h} f={w.f}")
+    X, A, B, a, dZ = wl.mlp_bwd_inputs(w)
+    Xd, Ad, Bd, ad, dZd = (t.to(DEV) for t in (X, A, B, a, dZ))
+    _, Y, Yp = tts.tp_mlp_shard_train_fwd(Xd, Ad, Bd, ad)
+    dX, dA, dB, da = tts.tp_mlp_shard_backward(Xd, Ad, Bd, Y, Yp, dZd)
+    torch.cuda.synchronize()
+    del Y, Yp, Xd, Ad, Bd, ad, dZd
+    rng = np.random.default_rng(w.seed)
+    J = torch.from_numpy(np.unique(np.concatenate([[0, 255, 256, w.f - 1],
+                                                   rng.integers(0, w.f, 12)])))
+    _, rA, rB, ra = oracle.mlp_shard_backward(X, A[:, J], B[J], dZ, a[J])
+    assert_bf16(dA.cpu()[:, J].T, rA.T)
+    assert_bf16(dB.cpu()[J], rB)
+    assert_bf16(da.cpu()[J].reshape(1, -1), ra.reshape(1, -1))
+    rows = torch.from_numpy(np.unique(np.concatenate([[0, 255, 256, w.M - 1],
+                                                      rng.integers(0, w.M, 40)])))
+    rX = oracle.mlp_shard_backward(X[rows], A, B, dZ[rows], a)[0]
+    assert_bf16(dX.cpu()[rows], rX)
+
+
+def test_attn_backward_fullsize_sampled():
+    """The attention-share backward at the 175B layer shape (one rank of tp=8: 8
+    sequences of 2048, 12 local heads), launched as the benchmark launches it.
+    The share is separable over its heads: one head's dW_qkv columns and dW_o rows
+    follow exactly from the oracle on that head's W_q, W_k, W_v columns and W_o
+    rows over all sequences.  dX rows need every head and their whole sequence:
+    the oracle runs the whole share on one sequence."""
+    w = wl.WORKLOADS["attn_bwd_bf16_h12288_tp8"]
+    d, HD = w.d, w.Hl * w.d
+    banner(f"{w.name}: b={w.b} s={w.s} h={w.h} H_l={w.Hl}")
+    X, Wqkv, Wo, dZ = wl.attn_bwd_inputs(w)
+    Xd, Wqd, Wod = X.to(DEV), Wqkv.to(DEV), Wo.to(DEV)
+    _, qkv, O, lse = tts.tp_attn_shard_train_fwd(Xd, Wqd, Wod, w.b, w.s, w.Hl, d)
+    dX, dWqkv, dWo = tts.tp_attn_shard_backward(Xd, Wqd, Wod, qkv, O, lse, dZ.to(DEV), w.b,
+                                                w.s, w.Hl, d)
+    torch.cuda.synchronize()
+    dX, dWqkv, dWo = dX.cpu(), dWqkv.cpu(), dWo.cpu()
+    del qkv, O, lse, Xd, Wqd, Wod
+    j = 7                                                  # one local head
+    cols = torch.cat([torch.arange(k * HD + j * d, k * HD + (j + 1) * d) for k in range(3)])
+    _, rWqkv, rWo = oracle.attn_shard_backward(X, w.b, w.s, Wqkv[:, cols], Wo[j * d:(j + 1) * d],
+                                               dZ, 1, d, True)
+    assert_bf16(dWqkv[:, cols].T, rWqkv.T)
+    assert_bf16(dWo[j * d:(j + 1) * d], rWo)
+    beta = 5                                               # one whole sequence
+    seq = slice(beta * w.s, (beta + 1) * w.s)
+    rX = oracle.attn_shard_backward(X[seq], 1, w.s, Wqkv, Wo, dZ[seq], w.Hl, d, True)[0]
+    assert_bf16(dX[seq], rX)
