@@ -287,7 +287,7 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dq_kernel(
 // ------------------------------------------------------------------ dK, dV
 constexpr int STAGE_KV = 2 * TILE + 512;     // Q tile, dO tile, L[64], D[64]
 
-__global__ __launch_bounds__(NT, 1) void attn_bwd_dkv_kernel(
+__global__ __launch_bounds__(NT, 2) void attn_bwd_dkv_kernel(
     const __bf16* __restrict__ qkv, int64_t ld, const __bf16* __restrict__ dO, int64_t ldo,
     const float* __restrict__ lse, const float* __restrict__ Dvec, __bf16* __restrict__ dqkv,
     int64_t ldd, int s, int Hl, int nkb, int n_bh, int causal, float scale_log2, float scale)
@@ -329,14 +329,16 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dkv_kernel(
         }
     }
 
-    unsigned voff_q[4], voff_o[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        voff_q[j] = dma_voff(w, j, lane, ld);
-        voff_o[j] = dma_voff(w, j, lane, ldo);
-    }
-    // the tile's Q, dO, and (wave 0) its 64 L and 64 D values as f32
+    // the tile's Q, dO, and (wave 0) its 64 L and 64 D values as f32; the
+    // lane offsets are recomputed per tile (a few integer operations) rather
+    // than held in registers across the loop
     auto dma_q = [&](char* stage, int q0) {
+        unsigned voff_q[4], voff_o[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            voff_q[j] = dma_voff(w, j, lane, ld);
+            voff_o[j] = dma_voff(w, j, lane, ldo);
+        }
         dma_tile(rows_rsrc(seq, ld, q0, qcol, s), stage, voff_q, w);
         dma_tile(rows_rsrc(dseq, ldo, q0, head * D, s), stage + TILE, voff_o, w);
         if (w == 0) {
@@ -349,9 +351,9 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dkv_kernel(
                                                      4u * lane, 0, 0, 0);
         }
     };
-    unsigned rd[8];
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) rd[kk] = tile_off(l32, 16 * kk + 8 * h);
+    // row reads: dims 16kk + 8h of row 32t + l32 sit at rd0 ^ (kk << 5) (the
+    // unit index 2kk + h XOR-ed by swz(l32); kk moves only unit bits 1-3)
+    const unsigned rd0 = tile_off(l32, 8 * h);
     const int G = lane >> 4, gi = lane & 15;
     unsigned tlo[4], thi[4];
 #pragma unroll
@@ -380,8 +382,9 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dkv_kernel(
             zero(pacc);
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk) {
-                const bf16x8 qa = *(const bf16x8*)(base + rd[kk] + t * 32 * 256);
-                const bf16x8 da = *(const bf16x8*)(base + TILE + rd[kk] + t * 32 * 256);
+                const unsigned rd = rd0 ^ (kk << 5);
+                const bf16x8 qa = *(const bf16x8*)(base + rd + t * 32 * 256);
+                const bf16x8 da = *(const bf16x8*)(base + TILE + rd + t * 32 * 256);
                 sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[kk], sacc, 0, 0, 0);
                 pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[kk], pacc, 0, 0, 0);
             }
@@ -392,29 +395,32 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dkv_kernel(
                     sacc[r] = (q >= s || (causal && q < my_k)) ? -INFINITY : sacc[r];
                 }
             }
-            bf16x8 pk[2], dsk[2];
-#pragma unroll
-            for (int rq4 = 0; rq4 < 4; ++rq4) {
-                const int qi = 32 * t + 8 * rq4 + 4 * h;       // tile query of element e = 0
-                const f32x4 Lv = *(const f32x4*)(Ls + qi);
-                const f32x4 Dv = *(const f32x4*)(Ds + qi);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * rq4 + e;
-                    const float p = __builtin_amdgcn_exp2f(fmaf(sacc[r], scale_log2, -Lv[e]));
-                    pk[r >> 3][r & 7] = (__bf16)p;
-                    dsk[r >> 3][r & 7] = (__bf16)(p * (pacc[r] - Dv[e]));
-                }
-            }
+            // P and dS one 16-query step at a time (accumulator elements
+            // 8·half .. +7), each consumed by its MFMAs right away
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
+                bf16x8 pk, dsk;
+#pragma unroll
+                for (int rq2 = 0; rq2 < 2; ++rq2) {
+                    const int rq4 = 2 * half + rq2;
+                    const int qi = 32 * t + 8 * rq4 + 4 * h;   // tile query of element e = 0
+                    const f32x4 Lv = *(const f32x4*)(Ls + qi);
+                    const f32x4 Dv = *(const f32x4*)(Ds + qi);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 4 * rq4 + e;
+                        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[r], scale_log2, -Lv[e]));
+                        pk[r & 7] = (__bf16)p;
+                        dsk[r & 7] = (__bf16)(p * (pacc[r] - Dv[e]));
+                    }
+                }
                 const char* qb_base = base + (32 * t + 16 * half) * 256;
 #pragma unroll
                 for (int dt = 0; dt < 4; ++dt) {
                     dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        tr_read(qb_base + TILE, tlo[dt], thi[dt]), pk[half], dv[dt], 0, 0, 0);
+                        tr_read(qb_base + TILE, tlo[dt], thi[dt]), pk, dv[dt], 0, 0, 0);
                     dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        tr_read(qb_base, tlo[dt], thi[dt]), dsk[half], dk[dt], 0, 0, 0);
+                        tr_read(qb_base, tlo[dt], thi[dt]), dsk, dk[dt], 0, 0, 0);
                 }
             }
         }
