@@ -20,6 +20,9 @@ in the order the pages give:
   the gradients of the MLP and attention shares by the chain rule (same page
   §2.2 and §3.2, backward: same upstream gradient on every rank, local
   parameter gradients, a partial input gradient summed over ranks);
+* ``vocab_embedding_shard``, ``vocab_ce_shard_stats``, ``vocab_ce_combine`` --
+  the vocab-parallel input embedding and the stable parallel cross-entropy
+  (same page §4.1, §4.2);
 * ``block_rows``  -- the pre-LN block x + attn(LN1(x)), then + mlp(LN2(.)), as
   assembled in section 3.3 of the PyTorch tensor-parallel tutorial
   (hotelren.com/news/6074135), with every rank's share summed.
@@ -298,6 +301,55 @@ def partial_sum(parts, bias=None, residual=None) -> np.ndarray:
     Z = np.empty((M, h), dtype=np.float64)
     _load().orc_partial_sum(_p(parts), P, M, h, _p(bias), _p(residual), _p(Z))
     return Z
+
+
+# ---------------------------------------------------------------- vocabulary ends
+def vocab_embedding_shard(tokens, E_r, vocab_start: int) -> np.ndarray:
+    """One rank's share of the vocab-parallel input embedding
+    ("图解Transformer并行计算" §4.1): the rank holds rows vocab_start ..
+    vocab_start + V_r - 1 of the table E [V, h]; a token in that range gets its
+    row, any other token a zero vector, so the sum over ranks (the all-reduce)
+    is the full lookup.  tokens [M] integers, E_r [V_r, h].  Returns [M, h]."""
+    E_r = f64(E_r)
+    t = np.asarray(tokens, dtype=np.int64).reshape(-1)
+    out = np.zeros((t.size, E_r.shape[1]), dtype=np.float64)
+    local = t - int(vocab_start)
+    mine = (local >= 0) & (local < E_r.shape[0])
+    out[mine] = E_r[local[mine]]
+    return out
+
+
+def vocab_ce_shard_stats(H, E_r, targets, vocab_start: int):
+    """One rank's local part of the vocab-parallel cross-entropy
+    ("图解Transformer并行计算" §4.2): its logits are H·E_r^T over its vocab
+    range (the output layer shares the input embedding's table).  In the stable
+    form (reading: the page's exp-sum over raw logits overflows; the row maximum
+    is reduced first), the rank reports per token row
+        m_r = max_j logit_j,  s_r = sum_j exp(logit_j - m_r),
+        t_r = the target's logit if the target is in the rank's range, else 0.
+    H [M, h], E_r [V_r, h], targets [M].  Returns (m_r, s_r, t_r), each [M]."""
+    H, E_r = f64(H), f64(E_r)
+    t = np.asarray(targets, dtype=np.int64).reshape(-1)
+    logits = np.matmul(H, E_r.T)
+    m = logits.max(axis=1)
+    s = np.exp(logits - m[:, None]).sum(axis=1)
+    local = t - int(vocab_start)
+    mine = (local >= 0) & (local < E_r.shape[0])
+    tl = np.zeros(t.size, dtype=np.float64)
+    tl[mine] = logits[np.nonzero(mine)[0], local[mine]]
+    return m, s, tl
+
+
+def vocab_ce_combine(stats):
+    """The all-reduces of the vocab-parallel cross-entropy and the loss
+    ("图解Transformer并行计算" §4.2): over the ranks' (m_r, s_r, t_r), the global
+    maximum m = max_r m_r, the global exp-sum s = sum_r s_r·exp(m_r - m) and the
+    target logit t = sum_r t_r (one rank holds it); the per-token loss is
+    -log softmax(target) = log(s) + m - t.  Returns the loss [M]."""
+    m = np.max(np.stack([np.asarray(st[0], dtype=np.float64) for st in stats]), axis=0)
+    s = sum(np.asarray(st[1], dtype=np.float64) * np.exp(np.asarray(st[0]) - m) for st in stats)
+    t = sum(np.asarray(st[2], dtype=np.float64) for st in stats)
+    return np.log(s) + m - t
 
 
 # ---------------------------------------------------------------- composites

@@ -16,7 +16,8 @@ import math
 import torch
 
 SUB = {"x": 0, "A": 1, "B": 2, "Wqkv": 3, "Wo": 4, "bias": 5, "partials": 6,
-       "gamma": 7, "beta": 8, "residual": 9, "dZ": 10, "preact": 11}
+       "gamma": 7, "beta": 8, "residual": 9, "dZ": 10, "preact": 11, "tokens": 12,
+       "targets": 13, "E": 14}
 
 
 def normal(shape, sigma: float, seed: int, sub, dtype=torch.bfloat16):
@@ -38,3 +39,11 @@ def fan_in_sigma(fan_in: int) -> float:
 def rank_seed(seed: int, rank: int) -> int:
     """Seed for rank ``rank``'s weights when several ranks are drawn."""
     return int(seed) * 64 + int(rank)
+
+
+def token_ids(n: int, vocab: int, seed: int, sub) -> torch.Tensor:
+    """n token ids uniform on [0, vocab) as int32, on the CPU."""
+    if isinstance(sub, str):
+        sub = SUB[sub]
+    g = torch.Generator(device="cpu").manual_seed(int(seed) * 16 + int(sub))
+    return torch.randint(0, int(vocab), (int(n),), generator=g, dtype=torch.int64).to(torch.int32)

@@ -606,3 +606,86 @@ def test_attn_shard_backward_ranks_sum_to_unsharded(P):
         assert np.abs(g[1] - want).max() < 1e-12
         assert np.abs(g[2] - full[2][rows]).max() < 1e-12
     assert np.abs(dX - full[0]).max() < 1e-12
+
+
+# --------------------------------------------------------------- vocabulary ends
+@pytest.mark.parametrize("P", [2, 4])
+def test_vocab_embedding_ranks_sum_to_lookup(P):
+    """§4.1: each rank looks up its vocab range and returns zeros elsewhere; the
+    sum over ranks is the full table's row, exactly (one non-zero term)."""
+    rng = np.random.default_rng(31 + P)
+    V, h, M = 8 * P, 5, 23
+    E = rng.normal(size=(V, h))
+    tokens = np.concatenate([[0, V - 1, V // P - 1, V // P], rng.integers(0, V, M - 4)])
+    Vr = V // P
+    parts = [oracle.vocab_embedding_shard(tokens, E[r * Vr:(r + 1) * Vr], r * Vr) for r in range(P)]
+    assert np.array_equal(sum(parts), E[tokens])
+    for r, part in enumerate(parts):
+        outside = (tokens < r * Vr) | (tokens >= (r + 1) * Vr)
+        assert not part[outside].any()
+
+
+@pytest.mark.parametrize("P", [1, 2, 4])
+def test_vocab_ce_matches_library(P):
+    """The sharded, stable cross-entropy equals torch's cross_entropy on the
+    full logits H·E^T in float64."""
+    rng = np.random.default_rng(41 + P)
+    V, h, M = 12 * P, 7, 19
+    H, E = rng.normal(size=(M, h)), rng.normal(size=(V, h))
+    targets = rng.integers(0, V, M)
+    Vr = V // P
+    stats = [oracle.vocab_ce_shard_stats(H, E[r * Vr:(r + 1) * Vr], targets, r * Vr)
+             for r in range(P)]
+    loss = oracle.vocab_ce_combine(stats)
+    ref = torch.nn.functional.cross_entropy(torch.tensor(H @ E.T), torch.tensor(targets),
+                                            reduction="none").numpy()
+    assert np.abs(loss - ref).max() < 1e-12
+
+
+def test_vocab_ce_brute_force():
+    """Pure-Python loops on a tiny case: -log(exp(l_t) / sum_j exp(l_j))."""
+    rng = np.random.default_rng(43)
+    V, h, M, P = 6, 3, 4, 3
+    H, E = rng.normal(size=(M, h)), rng.normal(size=(V, h))
+    targets = [0, 5, 2, 3]
+    Vr = V // P
+    loss = oracle.vocab_ce_combine([oracle.vocab_ce_shard_stats(H, E[r * Vr:(r + 1) * Vr],
+                                                                targets, r * Vr) for r in range(P)])
+    for i in range(M):
+        logit = [math.fsum(H[i, k] * E[j, k] for k in range(h)) for j in range(V)]
+        ref = math.log(math.fsum(math.exp(v) for v in logit)) - logit[targets[i]]
+        assert abs(loss[i] - ref) < 1e-12
+
+
+def test_vocab_ce_stable_for_large_logits():
+    """Logits of order 1e3 overflow exp in float64; the max-first form stays
+    finite and equals the shifted computation (negative control: the page's
+    exp-sum over raw logits is inf)."""
+    rng = np.random.default_rng(44)
+    V, h, M, P = 8, 4, 5, 2
+    H, E = 400 * rng.normal(size=(M, h)), rng.normal(size=(V, h))
+    targets = rng.integers(0, V, M)
+    Vr = V // P
+    stats = [oracle.vocab_ce_shard_stats(H, E[r * Vr:(r + 1) * Vr], targets, r * Vr)
+             for r in range(P)]
+    loss = oracle.vocab_ce_combine(stats)
+    assert np.isfinite(loss).all()
+    with np.errstate(over="ignore"):
+        assert not np.isfinite(np.exp(H @ E.T).sum(axis=1)).all()
+    L = H @ E.T
+    ref = np.log(np.exp(L - L.max(1, keepdims=True)).sum(1)) + L.max(1) - L[np.arange(M), targets]
+    assert np.abs(loss - ref).max() < 1e-9 * np.abs(ref).max()
+
+
+def test_vocab_ce_target_logit_from_one_rank():
+    """Exactly one rank holds each target; the others report 0."""
+    rng = np.random.default_rng(45)
+    V, h, M, P = 12, 3, 30, 3
+    H, E = rng.normal(size=(M, h)), rng.normal(size=(V, h))
+    targets = rng.integers(0, V, M)
+    Vr = V // P
+    for r in range(P):
+        _, _, t = oracle.vocab_ce_shard_stats(H, E[r * Vr:(r + 1) * Vr], targets, r * Vr)
+        mine = (targets >= r * Vr) & (targets < (r + 1) * Vr)
+        assert not t[~mine].any()
+        assert np.allclose(t[mine], (H @ E.T)[np.nonzero(mine)[0], targets[mine]], atol=1e-13)
