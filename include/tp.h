@@ -329,6 +329,56 @@ tp_status tp_layernorm(const void* x, int in, void* y, const void* gamma,
                        const void* beta, float eps, int64_t M, int64_t h, void* stream);
 
 /* ========================================================================
+ * The vocabulary ends of the model, vocab-parallel ([Megatron explainer] §4).
+ * The table E [V, h] (bf16) is split by rows: rank r holds E_r = rows
+ * [vocab_start, vocab_start + V_r).  Token ids are int32 (4-byte aligned).
+ * ====================================================================== */
+
+/* tp_vocab_embedding_shard -- §4.1: out[m] = E_r[tokens[m] - vocab_start] for a
+ * token in the rank's range, a zero row for any other token; summing the
+ * ranks' outputs (tp_partial_sum, the all-reduce) gives the full lookup.
+ *   out [M, h] in dtype out_dtype (TP_F32 or TP_BF16).  h % 8 == 0, V_r % 8 == 0. */
+tp_status tp_vocab_embedding_shard(const int32_t* tokens, int64_t M, const void* E_r,
+                                   int64_t V_r, int64_t h, int64_t vocab_start, void* out,
+                                   int out_dtype, void* stream);
+
+/* tp_vocab_ce_shard -- §4.2, one rank's local part of the cross-entropy with
+ * the output layer tied to the input embedding: logits = H·E_r^T [M, V_r]
+ * (never stored), and per token row, in the stable form (the row maximum
+ * first; the page's exp-sum over raw logits overflows):
+ *   stats[0..M)    m_r = max over the rank's logits,
+ *   stats[M..2M)   s_r = sum exp(logit - m_r),
+ *   stats[2M..3M)  t_r = the target's logit if the target is in the rank's
+ *                  range, else 0.
+ *   H [M, h] bf16, targets [M] int32, stats f32 [3·M];
+ *   ws >= tp_vocab_ce_shard_workspace(M, V_r) bytes (per-tile statistics).
+ * h % 8 == 0, V_r % 8 == 0. */
+size_t tp_vocab_ce_shard_workspace(int64_t M, int64_t V_r);
+tp_status tp_vocab_ce_shard(const void* H, const void* E_r, const int32_t* targets, int64_t M,
+                            int64_t h, int64_t V_r, int64_t vocab_start, float* stats, void* ws,
+                            size_t ws_bytes, void* stream);
+
+/* tp_vocab_ce_combine -- the all-reduces of §4.2 and the loss: from P ranks'
+ * stats (rank r's [3·M] at stats + 3·M·r): m = max_r m_r,
+ * s = sum_r s_r·exp(m_r - m), t = sum_r t_r, and per token
+ *   loss[m] = log(s) + m - t   (= -log softmax(logits)[target]);
+ * loss_mean (one float, or NULL) receives the mean over the M tokens.  Every
+ * sum is taken in a fixed order. */
+tp_status tp_vocab_ce_combine(const float* stats, int P, int64_t M, float* loss,
+                              float* loss_mean, void* stream);
+
+/* tp_vocab_parallel_ce -- all P ranks of the vocab-parallel cross-entropy on
+ * this GPU: rank r's table E[r] (a HOST array of P device pointers) covers
+ * vocabulary rows [r·V_r, (r+1)·V_r); the ranks' logits run as one grouped
+ * launch (they share H), then each rank's statistics and the combine as
+ * above.  ws >= tp_vocab_parallel_ce_workspace(M, V_r, P) bytes. */
+size_t tp_vocab_parallel_ce_workspace(int64_t M, int64_t V_r, int P);
+tp_status tp_vocab_parallel_ce(const void* H, const void* const* E, int P,
+                               const int32_t* targets, int64_t M, int64_t h, int64_t V_r,
+                               float* loss, float* loss_mean, void* ws, size_t ws_bytes,
+                               void* stream);
+
+/* ========================================================================
  * Measurement support (not part of the method).
  * ====================================================================== */
 

@@ -281,3 +281,36 @@ def test_matmul_grouped_rejects():
     assert call(C=odd) == _lib.TP_ERR_ALIGN
     assert L.tp_matmul_grouped(None, I2(64, 64), 1, ok, I2(64, 64), 0, ok, I2(64, 64), I2(64, 64),
                                I2(64, 64), 2, 64, 0, None) == _lib.TP_ERR_NULL
+
+
+def test_vocab_rejects():
+    L = tts.lib()
+    T4 = ctypes.c_void_p(0x100000)          # 4-byte aligned token ids
+    T_odd = ctypes.c_void_p(0x100002)
+    emb = lambda tok=T4, M=10, V=64, h=32, o=_lib.TP_F32, out=FAKE: L.tp_vocab_embedding_shard(
+        tok, M, FAKE, V, h, 0, out, o, None)
+    assert emb(tok=None) == _lib.TP_ERR_NULL
+    assert emb(M=0) == _lib.TP_ERR_SHAPE
+    assert emb(h=20) == _lib.TP_ERR_SHAPE
+    assert emb(V=60) == _lib.TP_ERR_SHAPE
+    assert emb(o=3) == _lib.TP_ERR_DTYPE
+    assert emb(tok=T_odd) == _lib.TP_ERR_ALIGN
+    assert emb(out=FAKE_ODD) == _lib.TP_ERR_ALIGN
+    ce = lambda H=FAKE, V=64, stats=FAKE, ws=FAKE, wsb=BIG: L.tp_vocab_ce_shard(
+        H, FAKE, T4, 10, 32, V, 0, stats, ws, wsb, None)
+    assert ce(H=None) == _lib.TP_ERR_NULL
+    assert ce(V=12) == _lib.TP_ERR_SHAPE
+    assert ce(ws=None) == _lib.TP_ERR_WORKSPACE
+    assert ce(wsb=8) == _lib.TP_ERR_WORKSPACE
+    assert ce(stats=FAKE_ODD) == _lib.TP_ERR_ALIGN
+    assert L.tp_vocab_ce_shard_workspace(300, 520) == 7424   # 300 rows x 3 tiles x 8 B, to 256 B
+    assert L.tp_vocab_ce_combine(None, 2, 10, FAKE, None, None) == _lib.TP_ERR_NULL
+    assert L.tp_vocab_ce_combine(FAKE, 0, 10, FAKE, None, None) == _lib.TP_ERR_SHAPE
+    two = (ctypes.c_void_p * 2)(FAKE.value, FAKE.value)
+    hole = (ctypes.c_void_p * 2)(FAKE.value, None)
+    par = lambda E=two, P=2, wsb=BIG: L.tp_vocab_parallel_ce(FAKE, E, P, T4, 10, 32, 64, FAKE,
+                                                             None, FAKE, wsb, None)
+    assert par(E=hole) == _lib.TP_ERR_NULL
+    assert par(P=0) == _lib.TP_ERR_SHAPE
+    assert par(wsb=100) == _lib.TP_ERR_WORKSPACE
+    assert L.tp_vocab_parallel_ce_workspace(10, 64, 2) > 0

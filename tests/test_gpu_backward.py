@@ -342,3 +342,59 @@ def test_matmul_grouped(ta, tb, shapes, K):
         a = oracle.f64(As[g]).T if ta else As[g]
         b = oracle.f64(Bs[g]).T if tb else Bs[g]
         assert_f32(outs[g], oracle.matmul(a, b), bar=1e-4)
+
+
+# ------------------------------------------------------------------ vocabulary ends
+@pytest.mark.parametrize("M,h,V_r,P,out", [(300, 64, 520, 2, torch.float32),
+                                           (1024, 256, 64, 4, torch.bfloat16)])
+def test_vocab_embedding(M, h, V_r, P, out):
+    """Each rank's lookup is exact (a copy), and the ranks' partial sum is the
+    full table's rows, bit for bit."""
+    banner(f"vocab embedding M={M} h={h} V_r={V_r} P={P} out={out}")
+    V = V_r * P
+    E = gen((V, h), 0.02, 240, "E")
+    tokens = synth.token_ids(M, V, 240, "tokens")
+    tokens[:4] = torch.tensor([0, V - 1, V_r - 1, V_r], dtype=torch.int32)
+    td = tokens.to(DEV)
+    parts = torch.stack([tts.tp_vocab_embedding_shard(td, E[r * V_r:(r + 1) * V_r].contiguous().to(DEV),
+                                                      r * V_r, out_dtype=torch.float32)
+                         for r in range(P)])
+    Z = tts.tp_partial_sum(parts)
+    one = tts.tp_vocab_embedding_shard(td, E[:V_r].contiguous().to(DEV), 0, out_dtype=out)
+    torch.cuda.synchronize()
+    for r in range(P):
+        ref = oracle.vocab_embedding_shard(tokens.numpy(), E[r * V_r:(r + 1) * V_r], r * V_r)
+        assert np.array_equal(parts[r].cpu().double().numpy(), ref)
+    assert np.array_equal(Z.cpu().double().numpy(), oracle.f64(E)[tokens.long().numpy()])
+    assert np.array_equal(one.cpu().double().numpy(),
+                          oracle.vocab_embedding_shard(tokens.numpy(), E[:V_r], 0))
+
+
+@pytest.mark.parametrize("M,h,V_r,P", [(300, 264, 520, 3), (512, 512, 6400 // 8, 8),
+                                       (1, 64, 8, 2), (700, 128, 1032, 1)])
+def test_vocab_cross_entropy(M, h, V_r, P):
+    """Per-rank statistics and the combined loss against the oracle; the
+    all-ranks entry point equals the per-rank path bit for bit."""
+    banner(f"vocab cross-entropy M={M} h={h} V_r={V_r} P={P}")
+    V = V_r * P
+    H = gen((M, h), 1.0, 241, "x")
+    E = gen((V, h), 0.02 * math.sqrt(4096 / h), 241, "E")
+    targets = synth.token_ids(M, V, 241, "targets")
+    Hd, td = H.to(DEV), targets.to(DEV)
+    Es = [E[r * V_r:(r + 1) * V_r].contiguous().to(DEV) for r in range(P)]
+    stats = torch.stack([tts.tp_vocab_ce_shard(Hd, Es[r], td, r * V_r) for r in range(P)])
+    loss, mean = tts.tp_vocab_ce_combine(stats)
+    loss2, mean2 = tts.tp_vocab_parallel_ce(Hd, Es, td)
+    torch.cuda.synchronize()
+    ref_stats = [oracle.vocab_ce_shard_stats(H, E[r * V_r:(r + 1) * V_r], targets.numpy(), r * V_r)
+                 for r in range(P)]
+    for r in range(P):
+        m, s, t = ref_stats[r]
+        assert_f32(stats[r, 0].reshape(1, -1), m.reshape(1, -1), bar=1e-4)
+        assert_f32(stats[r, 1].reshape(1, -1), s.reshape(1, -1), bar=1e-4)
+        # the target logit is 0 exactly off the rank, the f32 logit on it
+        assert_f32(stats[r, 2].reshape(1, -1), t.reshape(1, -1), bar=1e-4)
+    ref = oracle.vocab_ce_combine(ref_stats)
+    assert_f32(loss.reshape(1, -1), ref.reshape(1, -1), bar=1e-4)
+    assert abs(float(mean) - ref.mean()) <= 1e-4 * abs(ref.mean())
+    assert torch.equal(loss, loss2) and torch.equal(mean, mean2)

@@ -25,7 +25,8 @@ __all__ = [
     "tp_matmul", "tp_matmul_grouped", "tp_mlp_shard_train_fwd", "tp_mlp_shard_backward",
     "tp_mlp_shard_backward_workspace", "tp_attention_core_train", "tp_attention_core_backward",
     "tp_attn_shard_train_fwd", "tp_attn_shard_backward", "tp_attn_shard_backward_workspace",
-    "lib",
+    "tp_vocab_embedding_shard", "tp_vocab_ce_shard", "tp_vocab_ce_shard_workspace",
+    "tp_vocab_ce_combine", "tp_vocab_parallel_ce", "tp_vocab_parallel_ce_workspace", "lib",
 ]
 
 
@@ -407,6 +408,82 @@ def tp_attn_shard_backward(X, W_qkv_i, W_o_i, qkv, O, lse, dZ, b: int, s: int, H
         h, H_l, d, int(bool(causal)), _code(dX_out.dtype), _stream(stream))
     _check(st, "tp_attn_shard_backward")
     return dX_out, dWqkv_out, dWo_out
+
+
+# ------------------------------------------------------------------ vocabulary ends
+def _tokens(t, name):
+    if t.dtype != torch.int32:
+        raise TypeError(f"{name} must be int32")
+    return _dev(t, name)
+
+
+def tp_vocab_embedding_shard(tokens, E_r, vocab_start: int, *, out=None,
+                             out_dtype=torch.float32, stream=None):
+    """One rank's embedding share: E_r[token - vocab_start] or a zero row."""
+    M = tokens.numel()
+    V_r, h = E_r.shape
+    if out is None:
+        out = torch.empty(M, h, dtype=out_dtype, device=E_r.device)
+    st = _lib.load().tp_vocab_embedding_shard(_tokens(tokens, "tokens"), M, _dev(E_r, "E_r"), V_r,
+                                              h, int(vocab_start), _dev(out, "out"),
+                                              _code(out.dtype), _stream(stream))
+    _check(st, "tp_vocab_embedding_shard")
+    return out
+
+
+def tp_vocab_ce_shard_workspace(M: int, V_r: int) -> int:
+    return int(_lib.load().tp_vocab_ce_shard_workspace(M, V_r))
+
+
+def tp_vocab_ce_shard(H, E_r, targets, vocab_start: int, *, stats=None, ws=None, stream=None):
+    """One rank's cross-entropy statistics [3, M] f32: row max, exp-sum, target logit."""
+    M, h = H.shape
+    V_r = E_r.shape[0]
+    if stats is None:
+        stats = torch.empty(3, M, dtype=torch.float32, device=H.device)
+    ws = _ws(ws, tp_vocab_ce_shard_workspace(M, V_r), H.device)
+    st = _lib.load().tp_vocab_ce_shard(_dev(H, "H"), _dev(E_r, "E_r"), _tokens(targets, "targets"),
+                                       M, h, V_r, int(vocab_start), _dev(stats, "stats"),
+                                       _dev(ws, "ws"), _bytes(ws), _stream(stream))
+    _check(st, "tp_vocab_ce_shard")
+    return stats
+
+
+def tp_vocab_ce_combine(stats, *, loss=None, loss_mean=None, stream=None):
+    """Combine ranks' statistics [P, 3, M] into the loss [M] and its mean [1]."""
+    P, three, M = stats.shape
+    if loss is None:
+        loss = torch.empty(M, dtype=torch.float32, device=stats.device)
+    if loss_mean is None:
+        loss_mean = torch.empty(1, dtype=torch.float32, device=stats.device)
+    st = _lib.load().tp_vocab_ce_combine(_dev(stats, "stats"), P, M, _dev(loss, "loss"),
+                                         _dev(loss_mean, "loss_mean"), _stream(stream))
+    _check(st, "tp_vocab_ce_combine")
+    return loss, loss_mean
+
+
+def tp_vocab_parallel_ce_workspace(M: int, V_r: int, P: int) -> int:
+    return int(_lib.load().tp_vocab_parallel_ce_workspace(M, V_r, P))
+
+
+def tp_vocab_parallel_ce(H, Es: Sequence, targets, *, loss=None, loss_mean=None, ws=None,
+                         stream=None):
+    """All ranks of the vocab-parallel cross-entropy: rank r's table Es[r]
+    covers rows [r·V_r, (r+1)·V_r).  Returns (loss [M], mean [1])."""
+    M, h = H.shape
+    P, V_r = len(Es), Es[0].shape[0]
+    dev = H.device
+    if loss is None:
+        loss = torch.empty(M, dtype=torch.float32, device=dev)
+    if loss_mean is None:
+        loss_mean = torch.empty(1, dtype=torch.float32, device=dev)
+    ws = _ws(ws, tp_vocab_parallel_ce_workspace(M, V_r, P), dev)
+    st = _lib.load().tp_vocab_parallel_ce(_dev(H, "H"), _ptr_array(Es, "E"), P,
+                                          _tokens(targets, "targets"), M, h, V_r,
+                                          _dev(loss, "loss"), _dev(loss_mean, "loss_mean"),
+                                          _dev(ws, "ws"), _bytes(ws), _stream(stream))
+    _check(st, "tp_vocab_parallel_ce")
+    return loss, loss_mean
 
 
 def tp_layernorm(x, gamma=None, beta=None, eps=1e-5, *, out=None, stream=None):

@@ -56,6 +56,13 @@ SIGNATURES = {
                                  ctypes.POINTER(_vp), ctypes.POINTER(_i64), _int,
                                  ctypes.POINTER(_vp), ctypes.POINTER(_i64), ctypes.POINTER(_i64),
                                  ctypes.POINTER(_i64), _int, _i64, _int, _vp]),
+    "tp_vocab_embedding_shard": (_int, [_vp, _i64, _vp, _i64, _i64, _i64, _vp, _int, _vp]),
+    "tp_vocab_ce_shard_workspace": (_sz, [_i64, _i64]),
+    "tp_vocab_ce_shard": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _vp, _sz, _vp]),
+    "tp_vocab_ce_combine": (_int, [_vp, _int, _i64, _vp, _vp, _vp]),
+    "tp_vocab_parallel_ce_workspace": (_sz, [_i64, _i64, _int]),
+    "tp_vocab_parallel_ce": (_int, [_vp, ctypes.POINTER(_vp), _int, _vp, _i64, _i64, _i64, _vp,
+                                    _vp, _vp, _sz, _vp]),
     "tp_mlp_shard_train_fwd": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int,
                                       _vp]),
     "tp_mlp_shard_backward_workspace": (_sz, [_i64, _i64]),

@@ -14,8 +14,10 @@
 // layout is; nothing is transposed in memory.
 //
 // Epilogues: none; + bias and GeLU; GeLU backward (C = (A·B)·GeLU'(Y) with the
-// saved pre-activation Y read as `aux`); and the training forward's dual store
-// (C = GeLU(A·B + bias) and aux = A·B + bias, both bf16).
+// saved pre-activation Y read as `aux`); the training forward's dual store
+// (C = GeLU(A·B + bias) and aux = A·B + bias, both bf16); and the
+// cross-entropy statistics of vocab-parallel logits (per row and column tile
+// the maximum and the exp-sum, plus the target's logit; no logits stored).
 //
 // Design: one 256x256 output tile per workgroup of 8 waves (two per SIMD).
 //  * wave w owns a 128x64 sub-tile: rows 128*((w&3)>>1), columns
@@ -445,6 +447,38 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
                     }
             }
             __syncthreads();
+            if constexpr (EPI == EPI_CE_STATS) {
+                // one wave holds one whole row of the tile per iteration (its
+                // 64 lanes the row's 64 units): the row's maximum and exp-sum
+                // over the tile's columns, and the target's logit
+                const int ntn = (N + BN - 1) / BN;
+#pragma unroll 2
+                for (int i = 0; i < 8192 / NTHREADS; ++i) {
+                    const int lrow = i * (NTHREADS / 64) + wid, q = lrow & 63;
+                    const int grow = m0 + (lrow >> 6) * 128 + 64 * p + q, gcol = n0 + lane * 4;
+                    if (grow >= M) continue;                // wave-uniform
+                    const f32x4 v = *(const f32x4*)((lrow < 64 ? lds0 : lds1) + q * 1024 +
+                                                     ((lane ^ (((q >> 2) & 3) << 2)) << 4));
+                    float mx = -INFINITY;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) mx = fmaxf(mx, gcol + e < N ? v[e] : -INFINITY);
+#pragma unroll
+                    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+                    float sm = 0.0f;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        sm += gcol + e < N ? __builtin_amdgcn_exp2f((v[e] - mx) * 1.44269504088896341f)
+                                           : 0.0f;
+#pragma unroll
+                    for (int o = 32; o >= 1; o >>= 1) sm += __shfl_xor(sm, o);
+                    if (lane == 0)
+                        *(float2*)((float*)C + ((int64_t)grow * ntn + tn) * 2) = make_float2(mx, sm);
+                    const int tl = batch.targets[grow] - batch.vstart[grp] - gcol;
+                    if (tl >= 0 && tl < 4 && gcol + tl < N) ((float*)aux)[grow] = v[tl];
+                }
+                if (p == 0) __syncthreads();
+                continue;
+            }
 #pragma unroll
             for (int i = 0; i < 8192 / NTHREADS; ++i) {
                 const int idx = i * NTHREADS + tid;
@@ -520,6 +554,7 @@ hipError_t launch(const GemmBatch& b, int layout, int epi, int64_t ldaux, int64_
     case GEMM_NT:
         if (epi == EPI_NONE) { if (out_bf16) TP_GEMM(GEMM_NT, EPI_NONE, true); TP_GEMM(GEMM_NT, EPI_NONE, false); }
         if (epi == EPI_GELU_BWD) { if (out_bf16) TP_GEMM(GEMM_NT, EPI_GELU_BWD, true); TP_GEMM(GEMM_NT, EPI_GELU_BWD, false); }
+        if (epi == EPI_CE_STATS && !out_bf16) TP_GEMM(GEMM_NT, EPI_CE_STATS, false);
         break;
     case GEMM_TN:
         if (epi == EPI_NONE) { if (out_bf16) TP_GEMM(GEMM_TN, EPI_NONE, true); TP_GEMM(GEMM_TN, EPI_NONE, false); }

@@ -594,6 +594,125 @@ TP_EXPORT tp_status tp_attn_shard_backward(const void* X, const void* W_qkv_i, c
                                n3, dx_dtype, TP_EPI_NONE, stm));
 }
 
+// ---- vocabulary ends: vocab-parallel embedding and cross-entropy -----------
+namespace {
+int64_t ce_ntn(int64_t V_r) { return (V_r + 255) / 256; }
+int64_t ce_tiles_bytes(int64_t M, int64_t V_r) { return align_up(M * ce_ntn(V_r) * 2 * 4); }
+int64_t ce_stats_bytes(int64_t M) { return align_up(3 * M * 4); }
+
+tp_status check_vocab(int64_t M, int64_t h, int64_t V_r) {
+    if (M <= 0 || h <= 0 || V_r <= 0 || M > kI32 || h > kI32 || V_r > kI32) return TP_ERR_SHAPE;
+    if (h % 8 || V_r % 8) return TP_ERR_SHAPE;
+    return TP_OK;
+}
+
+// logits H·E_r^T of `count` ranks (one grouped NT launch) reduced to each
+// rank's [3][M] statistics at stats + 3·M·g; tiles: [count][M][ntn][2] scratch
+hipError_t run_ce_ranks(const void* H, const void* const* E, int count, const int* targets,
+                        int64_t M, int64_t h, int64_t V_r, int64_t vstart0, float* stats,
+                        float* tiles, hipStream_t st) {
+    const int64_t ntn = ce_ntn(V_r);
+    for (int g0 = 0; g0 < count; g0 += tpk::kMaxBatch) {
+        const int n = count - g0 < tpk::kMaxBatch ? count - g0 : tpk::kMaxBatch;
+        tpk::GemmBatch gb = {};
+        gb.count = n;
+        gb.targets = targets;
+        for (int i = 0; i < n; ++i) {
+            const int g = g0 + i;
+            float* sg = stats + 3 * M * g;
+            if (hipError_t e = tpk::fill_zero(sg + 2 * M, M, st)) return e;
+            gb.A[i] = (const __bf16*)H;
+            gb.B[i] = (const __bf16*)E[g];
+            gb.C[i] = tiles + M * ntn * 2 * g;
+            gb.aux[i] = (__bf16*)(sg + 2 * M);
+            gb.vstart[i] = (int)(vstart0 + V_r * g);
+        }
+        if (hipError_t e = tpk::gemm_bf16_batched(gb, tpk::GEMM_NT, tpk::EPI_CE_STATS, h, h, 0, 0,
+                                                  M, V_r, h, false, st))
+            return e;
+    }
+    for (int g = 0; g < count; ++g)
+        if (hipError_t e = tpk::ce_rank_reduce(tiles + M * ntn * 2 * g, (int)ntn, M,
+                                               stats + 3 * M * g, st))
+            return e;
+    return hipSuccess;
+}
+}  // namespace
+
+TP_EXPORT tp_status tp_vocab_embedding_shard(const int32_t* tokens, int64_t M, const void* E_r,
+                                             int64_t V_r, int64_t h, int64_t vocab_start,
+                                             void* out, int out_dtype, void* stream) {
+    if (!tokens || !E_r || !out) return TP_ERR_NULL;
+    if (!is_dtype(out_dtype)) return TP_ERR_DTYPE;
+    if (tp_status s = check_vocab(M, h, V_r)) return s;
+    if (!aligned16(E_r) || !aligned16(out) || (reinterpret_cast<uintptr_t>(tokens) & 3))
+        return TP_ERR_ALIGN;
+    return launched(tpk::embed_shard(tokens, M, E_r, V_r, h, vocab_start, out,
+                                     out_dtype == TP_BF16, as_stream(stream)));
+}
+
+TP_EXPORT size_t tp_vocab_ce_shard_workspace(int64_t M, int64_t V_r) {
+    if (M <= 0 || V_r <= 0) return 0;
+    return (size_t)ce_tiles_bytes(M, V_r);
+}
+
+TP_EXPORT tp_status tp_vocab_ce_shard(const void* H, const void* E_r, const int32_t* targets,
+                                      int64_t M, int64_t h, int64_t V_r, int64_t vocab_start,
+                                      float* stats, void* ws, size_t ws_bytes, void* stream) {
+    if (!H || !E_r || !targets || !stats) return TP_ERR_NULL;
+    if (tp_status s = check_vocab(M, h, V_r)) return s;
+    if (!operand_fits(h, true) || ((M + 255) / 256) * ce_ntn(V_r) > kI32 / 8) return TP_ERR_SHAPE;
+    if (!ws || ws_bytes < (size_t)ce_tiles_bytes(M, V_r)) return TP_ERR_WORKSPACE;
+    if (!aligned16(H) || !aligned16(E_r) || !aligned16(stats) || !aligned16(ws) ||
+        (reinterpret_cast<uintptr_t>(targets) & 3))
+        return TP_ERR_ALIGN;
+    const void* E[1] = {E_r};
+    return launched(run_ce_ranks(H, E, 1, targets, M, h, V_r, vocab_start, stats, (float*)ws,
+                                 as_stream(stream)));
+}
+
+TP_EXPORT tp_status tp_vocab_ce_combine(const float* stats, int P, int64_t M, float* loss,
+                                        float* loss_mean, void* stream) {
+    if (!stats || !loss) return TP_ERR_NULL;
+    if (P <= 0 || M <= 0 || M > kI32) return TP_ERR_SHAPE;
+    if (!aligned16(stats) || !aligned16(loss) || (loss_mean && (reinterpret_cast<uintptr_t>(loss_mean) & 3)))
+        return TP_ERR_ALIGN;
+    return launched(tpk::ce_combine(stats, P, M, loss, loss_mean, as_stream(stream)));
+}
+
+TP_EXPORT size_t tp_vocab_parallel_ce_workspace(int64_t M, int64_t V_r, int P) {
+    if (M <= 0 || V_r <= 0 || P <= 0) return 0;
+    return (size_t)(P * (ce_stats_bytes(M) + ce_tiles_bytes(M, V_r)));
+}
+
+TP_EXPORT tp_status tp_vocab_parallel_ce(const void* H, const void* const* E, int P,
+                                         const int32_t* targets, int64_t M, int64_t h,
+                                         int64_t V_r, float* loss, float* loss_mean, void* ws,
+                                         size_t ws_bytes, void* stream) {
+    if (!H || !E || !targets || !loss) return TP_ERR_NULL;
+    if (P <= 0) return TP_ERR_SHAPE;
+    if (tp_status s = check_vocab(M, h, V_r)) return s;
+    if (!operand_fits(h, true) || ((M + 255) / 256) * ce_ntn(V_r) > kI32 / 8 ||
+        V_r * P > kI32)
+        return TP_ERR_SHAPE;
+    for (int r = 0; r < P; ++r) {
+        if (!E[r]) return TP_ERR_NULL;
+        if (!aligned16(E[r])) return TP_ERR_ALIGN;
+    }
+    if (!ws || ws_bytes < tp_vocab_parallel_ce_workspace(M, V_r, P)) return TP_ERR_WORKSPACE;
+    if (!aligned16(H) || !aligned16(loss) || !aligned16(ws) ||
+        (reinterpret_cast<uintptr_t>(targets) & 3) ||
+        (loss_mean && (reinterpret_cast<uintptr_t>(loss_mean) & 3)))
+        return TP_ERR_ALIGN;
+    const hipStream_t st = as_stream(stream);
+    // ranks' statistics contiguous with stride 3·M floats (the combine's
+    // layout), then the tile statistics
+    float* stats = (float*)ws;                                   // [P][3][M]
+    float* tiles = (float*)((char*)ws + P * ce_stats_bytes(M));  // [P][M][ntn][2]
+    if (run_ce_ranks(H, E, P, targets, M, h, V_r, 0, stats, tiles, st)) return TP_ERR_LAUNCH;
+    return launched(tpk::ce_combine(stats, P, M, loss, loss_mean, st));
+}
+
 TP_EXPORT tp_status tp_layernorm(const void* x, int in, void* y, const void* gamma,
                                  const void* beta, float eps, int64_t M, int64_t h,
                                  void* stream) {

@@ -13,7 +13,12 @@ enum GemmLayout { GEMM_NN = 0, GEMM_NT = 1, GEMM_TN = 2 };
 // Epilogues: v = acc + bias;  NONE  C = v;  GELU  C = GeLU(v);
 // GELU_BWD  C = v · GeLU'(aux) (aux: the saved bf16 pre-activation);
 // DUAL  C = bf16 GeLU(v) and aux = bf16 v (the training forward).
-enum GemmEpi { EPI_NONE = 0, EPI_GELU = 1, EPI_GELU_BWD = 2, EPI_DUAL = 3 };
+// CE_STATS (the vocab-parallel cross-entropy's logits, NT, f32): no C is
+// written; for every output row and 256-column tile tn, C[g] (as float*)
+// receives at [(row·ceil(N/256) + tn)·2] the tile's row maximum m and
+// sum_j exp(logit_j - m); aux[g] (as float*) receives logit[row][targets[row]
+// - vstart[g]] at [row] when that column is in range (the caller zeroes it).
+enum GemmEpi { EPI_NONE = 0, EPI_GELU = 1, EPI_GELU_BWD = 2, EPI_DUAL = 3, EPI_CE_STATS = 4 };
 
 // Up to kMaxBatch independent GEMMs launched together: group g computes
 // C[g] = epi(op(A[g])·op(B[g]) + bias[g]), an [M[g], N[g]] product with
@@ -29,12 +34,14 @@ struct GemmBatch {
     __bf16* aux[kMaxBatch];   // GELU_BWD: read, DUAL: written; [M,N] with ldaux
     int M[kMaxBatch], N[kMaxBatch];
     int64_t lda[kMaxBatch], ldb[kMaxBatch], ldc[kMaxBatch];
+    const int* targets;       // CE_STATS: target token id per row
+    int vstart[kMaxBatch];    // CE_STATS: first vocab id of group g's columns
     int count;
     int band;       // set by the launcher: tile order for groups sharing A
 };
 // Supported (layout, epilogue, output) combinations: NN with NONE / GELU
-// (bf16 or f32) and DUAL (bf16); NT with NONE / GELU_BWD (bf16 or f32); TN with
-// NONE (bf16 or f32).  Others return hipErrorInvalidValue.  The caller checks
+// (bf16 or f32) and DUAL (bf16); NT with NONE / GELU_BWD (bf16 or f32) and
+// CE_STATS (f32); TN with NONE (bf16 or f32).  Others return hipErrorInvalidValue.  The caller checks
 // shapes: M, N, K multiples of 8 along contiguous dimensions, leading
 // dimensions multiples of 8.
 hipError_t gemm_bf16_batched(const GemmBatch& batch, int layout, int epi, int64_t lda,
@@ -105,6 +112,19 @@ constexpr int64_t kColSumRows = 256;
 int64_t col_sum_chunks(int64_t M);
 hipError_t col_sum(float* out, const void* X, int64_t ldx, int64_t M, int64_t N, float* part,
                    hipStream_t stream);
+
+// Vocab-parallel ends.  embed_shard: out[m] = E_r[tokens[m] - vstart] when
+// that row exists, else zeros (h % 8 == 0).  fill_zero: p[0..n) = 0.
+// ce_rank_reduce: CE_STATS tile statistics [M][ntn][2] -> m_r (stats[0..M)),
+// s_r (stats[M..2M)).  ce_combine: ranks' [3][M] statistics (rank r at
+// stats + 3·M·r) -> loss [M]; if loss_mean is not NULL also its mean.
+hipError_t embed_shard(const int* tokens, int64_t M, const void* E_r, int64_t V_r, int64_t h,
+                       int64_t vstart, void* out, bool out_bf16, hipStream_t stream);
+hipError_t fill_zero(float* p, int64_t n, hipStream_t stream);
+hipError_t ce_rank_reduce(const float* tiles, int ntn, int64_t M, float* stats,
+                          hipStream_t stream);
+hipError_t ce_combine(const float* stats, int P, int64_t M, float* loss, float* loss_mean,
+                      hipStream_t stream);
 
 // Register-only MFMA 16x16x32 bf16 loop: `blocks` workgroups of 8 waves, each
 // wave issuing 32 * iters MFMAs; out receives blocks * 512 floats.
