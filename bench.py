@@ -28,8 +28,10 @@ Besides the one JSON line the run reports, in the same line:
 (dY, dB_i, dA_i, da_i and the dX_i partial of one rank at the 175B layer
 shape), with the weight-gradient product X^T·dY as its dominant kernel;
 --workload attn_bwd_bf16_h12288_tp8 the attention share's backward (dO,
-dW_o,i, the attention-core backward, dW_qkv,i, dX_i) with the input-gradient
-product dqkv·W_qkv^T as its dominant kernel.
+dW_o,i, the attention-core backward, dW_qkv,i, dX_i) with its grouped
+weight-gradient launch as its dominant kernel; --workload vocab_bf16_h12288_tp8
+the vocab-parallel ends of all 8 ranks (embedding lookup and partial sum, the
+stable cross-entropy) with the grouped logits GEMM as its dominant kernel.
 
 Modes for profiler runs: --mode kernel launches only the dominant kernel,
 --mode copy only a plain device copy of a known size (counter calibration).
@@ -59,6 +61,7 @@ TRAFFIC_FILES = {
                                             "gemm_tn_wgrad_h12288_f6144_traffic.txt"),
     "attn_bwd_bf16_h12288_tp8": os.path.join(ROOT, "profiles",
                                              "gemm_tn_wgrad_attn_h12288_hd1536_traffic.txt"),
+    "vocab_bf16_h12288_tp8": os.path.join(ROOT, "profiles", "gemm_ce_h12288_v51200_traffic.txt"),
 }
 TRAFFIC_FILE = TRAFFIC_FILES["block_bf16_h12288_tp8"]
 
@@ -155,6 +158,11 @@ def dominant_operands_cpu(w, wl):
         dY = wl.normal((w.M, w.f), 1.0, w.seed, "preact", w.dtype)
         Yp = wl.normal((w.M, w.f), 1.0, w.seed, "partials", w.dtype)
         return X, [dY, Yp, dZ]
+    if w.kind == "vocab":
+        # the cross-entropy logits of all ranks: H and the ranks' tables
+        _, targets, H, E = wl.vocab_inputs(w)
+        Vr = w.V // w.P
+        return H, [targets] + [E[r * Vr:(r + 1) * Vr].contiguous() for r in range(w.P)]
     if w.kind == "attn_bwd":
         # the weight-gradient products X^T·dqkv and O^T·dZ (values of the
         # activations dqkv and O do not change their cost)
@@ -174,6 +182,22 @@ def dominant_kernel(w, tts, torch, X, Ws, dev):
     launch; for the MLP shard its GeLU GEMM; for the attention shard its QKV
     projection."""
     M, K = X.shape
+    if w.kind == "vocab":
+        # the grouped logits GEMM of all ranks with the cross-entropy-statistics
+        # epilogue, as tp_vocab_parallel_ce launches it (its per-rank statistics
+        # and combine launches, a few tens of microseconds, are included)
+        targets, Es = Ws[0], Ws[1:]
+        ws = torch.empty(tts.tp_vocab_parallel_ce_workspace(M, Es[0].shape[0], len(Es)),
+                         dtype=torch.uint8, device=dev)
+        loss = torch.empty(M, dtype=torch.float32, device=dev)
+        mean = torch.empty(1, dtype=torch.float32, device=dev)
+
+        def launch():
+            tts.tp_vocab_parallel_ce(X, Es, targets, loss=loss, loss_mean=mean, ws=ws)
+        V = sum(E.shape[0] for E in Es)
+        name = ("gemm_bf16_kernel<NT, epi=ce_stats> grouped over %d ranks, each [%dx%d]x[%dx%d]^T "
+                "(+ statistics combine)" % (len(Es), M, K, Es[0].shape[0], K))
+        return launch, 2 * M * K * V, name
     N = Ws[0].shape[1]
     if w.kind == "mlp_bwd":
         # dB_i = Y'^T·dZ [f, h] and dA_i = X^T·dY [h, f] in one grouped launch
@@ -313,6 +337,25 @@ def main():
         dY0 = tts.tp_matmul(dZ, B0, trans_b=True, epilogue="gelu_bwd", aux=Y0,
                             out_dtype=torch.bfloat16)
         X_k, W_k = x, [dY0, Yp0, dZ]
+    elif w.kind == "vocab":
+        tokens_cpu, targets_cpu, H_cpu, E_cpu = wl.vocab_inputs(w)
+        Vr = w.V // w.P
+        tokens, targets, x = tokens_cpu.to(dev), targets_cpu.to(dev), H_cpu.to(dev)
+        Es = [E_cpu[r * Vr:(r + 1) * Vr].contiguous().to(dev) for r in range(w.P)]
+        M, h = w.M, w.h
+        parts = torch.empty(w.P, M, h, dtype=torch.float32, device=dev)
+        emb = torch.empty(M, h, dtype=torch.float32, device=dev)
+        loss = torch.empty(M, dtype=torch.float32, device=dev)
+        mean = torch.empty(1, dtype=torch.float32, device=dev)
+        ce_ws = torch.empty(tts.tp_vocab_parallel_ce_workspace(M, Vr, w.P), dtype=torch.uint8,
+                            device=dev)
+
+        def step():
+            for r in range(w.P):
+                tts.tp_vocab_embedding_shard(tokens, Es[r], r * Vr, out=parts[r])
+            tts.tp_partial_sum(parts, out=emb)
+            tts.tp_vocab_parallel_ce(x, Es, targets, loss=loss, loss_mean=mean, ws=ce_ws)
+        X_k, W_k = x, [targets] + Es
     elif w.kind == "attn_bwd":
         X_cpu, Wqkv_cpu, Wo_cpu, dZ_cpu = wl.attn_bwd_inputs(w)
         x, Wqkv0, Wo0, dZ = (t.to(dev) for t in (X_cpu, Wqkv_cpu, Wo_cpu, dZ_cpu))
@@ -373,7 +416,10 @@ def main():
     kern_tflops = kern_flops / (kern_ms * 1e-3) / 1e12
     traffic = measured_traffic(TRAFFIC_FILES[w.name]) if w.name in TRAFFIC_FILES else None
     log(f"dominant kernel: {kern_ms:.3f} ms/launch, {kern_tflops:.1f} TFLOP/s")
-    calib = calibration(tts, torch, X_k, W_k[0], stream, trans_a=w.kind.endswith("_bwd"))
+    if w.kind == "vocab":
+        calib = calibration(tts, torch, X_k, W_k[1].t(), stream)
+    else:
+        calib = calibration(tts, torch, X_k, W_k[0], stream, trans_a=w.kind.endswith("_bwd"))
     log(f"calibration: {calib}")
 
     components = {}
@@ -467,6 +513,30 @@ def main():
             log(f"component {name}: {c}")
         del Dws, dqkv_c, dO_c
 
+    if w.kind == "vocab":
+        Vr = w.V // w.P
+        items = {
+            "embedding_all_ranks": (lambda: [tts.tp_vocab_embedding_shard(
+                tokens, Es[r], r * Vr, out=parts[r]) for r in range(w.P)], None,
+                w.P * M * h * 4 + w.M * h * 2),
+            "embedding_partial_sum": (lambda: tts.tp_partial_sum(parts, out=emb), None,
+                                      (w.P + 1) * M * h * 4),
+            "cross_entropy_all_ranks": (lambda: tts.tp_vocab_parallel_ce(
+                x, Es, targets, loss=loss, loss_mean=mean, ws=ce_ws), w.flops(), None),
+        }
+        for name, (fn, fl, by) in items.items():
+            fn()
+            t, _ = event_time(fn, 3, stream)
+            c = {"ms": round(t, 4)}
+            if fl:
+                c["tflops"] = round(fl / (t * 1e-3) / 1e12, 1)
+                c["pct_peak"] = round(100 * fl / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 1)
+            if by:
+                c["gbs"] = round(by / (t * 1e-3) / 1e9, 1)
+                c["pct_hbm"] = round(100 * by / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 1)
+            components[name] = c
+            log(f"component {name}: {c}")
+
     training = None
     if w.kind == "block" and not args.no_training:
         training = mlp_backward_rank0(w, wl, tts, torch, x, A[0], B[0], dev, stream)
@@ -494,6 +564,7 @@ def main():
         "config": {"workload": w.name, "description": w.description, "tokens": w.M, "h": w.h,
                    "heads": w.H, "head_dim": w.d if w.H else None, "ffn": w.F, "tp": w.P,
                    "ranks_emulated": w.P if w.all_ranks else 1, "flops_per_step": flops,
+                   "vocab": w.V or None,
                    "parallelism": "tp%d emulated on 1 GPU" % w.P},
         "roofline": {
             "kernel": kern_name,
@@ -603,6 +674,22 @@ def cpu_baseline(w, rows_req, env):
         dt = time.time() - t0
         fl = 4 * R * w.h * A_cpu.shape[1]
         sample = f"rows 0..{R - 1} of the MLP shard; {fl / 1e12:.3f} TFLOP"
+    elif w.kind == "vocab":
+        R = min(rows_req, w.M)
+        tokens_cpu, targets_cpu, H_cpu, E_cpu = (env[k] for k in ("tokens_cpu", "targets_cpu",
+                                                                  "H_cpu", "E_cpu"))
+        Vr = w.V // w.P
+        log(f"oracle: vocab ends over tokens 0..{R - 1}, all {w.P} ranks")
+        t0 = time.time()
+        for r in range(w.P):
+            oracle.vocab_embedding_shard(tokens_cpu[:R].numpy(), E_cpu[r * Vr:(r + 1) * Vr], r * Vr)
+        oracle.vocab_ce_combine([oracle.vocab_ce_shard_stats(H_cpu[:R], E_cpu[r * Vr:(r + 1) * Vr],
+                                                             targets_cpu[:R].numpy(), r * Vr)
+                                 for r in range(w.P)])
+        dt = time.time() - t0
+        fl = 2 * R * w.h * w.V
+        sample = (f"tokens 0..{R - 1}: the embedding lookup and the cross-entropy of all {w.P} "
+                  f"ranks; {fl / 1e12:.3f} TFLOP")
     elif w.kind == "attn_bwd":
         # whole sequences: the backward of a causal sequence involves all of it
         R = min(rows_req, w.s)

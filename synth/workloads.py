@@ -19,7 +19,7 @@ from . import normal, fan_in_sigma, rank_seed
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str            # "mlp" | "attn" | "block" | "mlp_bwd" | "attn_bwd"
+    kind: str            # "mlp" | "attn" | "block" | "mlp_bwd" | "attn_bwd" | "vocab"
     seed: int
     P: int               # tensor-parallel degree
     b: int
@@ -28,6 +28,7 @@ class Workload:
     F: int = 0           # full FFN width
     H: int = 0           # total heads
     d: int = 128         # head dimension
+    V: int = 0           # vocabulary size (vocab-parallel ends)
     dtype: torch.dtype = torch.bfloat16
     all_ranks: bool = False
     description: str = ""
@@ -76,6 +77,8 @@ class Workload:
             return self.attn_flops_rank()["total"]
         if self.kind == "attn_bwd":
             return self.attn_bwd_flops_rank()["total"]
+        if self.kind == "vocab":
+            return 2 * self.M * self.h * self.V       # the logits H·E^T of all ranks
         return self.P * (self.mlp_flops_rank() + self.attn_flops_rank()["total"])
 
 
@@ -96,6 +99,11 @@ WORKLOADS = {w.name: w for w in [
              description="bf16 backward of one rank's causal attention share of tp=8 at the "
                          "175B layer shape (12 local heads of 128, 8 sequences of 2048): "
                          "dW_qkv,i, dW_o,i and the dX_i partial"),
+    Workload("vocab_bf16_h12288_tp8", "vocab", 1007, P=8, b=8, s=2048, h=12288, V=51200,
+             all_ranks=True,
+             description="bf16 vocab-parallel ends at the 175B layer shape, all 8 ranks of tp=8: "
+                         "embedding lookup of 16384 tokens and the stable cross-entropy over "
+                         "V = 51200 (GPT-3's 50257 padded to a multiple of 128·8), table tied"),
     Workload("block_bf16_h12288_tp8", "block", 1004, P=8, b=8, s=2048, h=12288, H=96, F=49152,
              all_ranks=True,
              description="bf16 pre-LN block at the 175B layer shape, all 8 ranks of tp=8 in turn"),
@@ -151,3 +159,16 @@ def attn_bwd_inputs(w: Workload):
     X, Wqkv, Wo = attn_inputs(w)
     dZ = normal((w.M, w.h), 1.0, w.seed, "dZ", w.dtype)
     return X, Wqkv, Wo, dZ
+
+
+def vocab_inputs(w: Workload):
+    """Token ids and targets (uniform on [0, V), int32), the final hidden
+    states H ~ N(0, 1) [M, h] and the tied table E ~ N(0, 0.02^2) [V, h] (the
+    usual embedding initialisation; logits then have std 0.02·sqrt(h)), on the
+    CPU."""
+    from . import token_ids
+    tokens = token_ids(w.M, w.V, w.seed, "tokens")
+    targets = token_ids(w.M, w.V, w.seed, "targets")
+    H = normal((w.M, w.h), 1.0, w.seed, "x", w.dtype)
+    E = normal((w.V, w.h), 0.02, w.seed, "E", w.dtype)
+    return tokens, targets, H, E
