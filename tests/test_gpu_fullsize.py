@@ -161,3 +161,36 @@ def test_attn_backward_fullsize_sampled():
     seq = slice(beta * w.s, (beta + 1) * w.s)
     rX = oracle.attn_shard_backward(X[seq], 1, w.s, Wqkv, Wo, dZ[seq], w.Hl, d, True)[0]
     assert_bf16(dX[seq], rX)
+
+
+def test_vocab_fullsize_sampled():
+    """The vocab-parallel ends at the 175B layer shape, all 8 ranks, launched as
+    the benchmark launches them: every rank's embedding lookup and their partial
+    sum, then tp_vocab_parallel_ce.  Token rows are independent, so sampled rows
+    are exact checks: the summed embedding row is the table's row bit for bit;
+    the loss row is the oracle's stable cross-entropy over all 51200 words."""
+    w = wl.WORKLOADS["vocab_bf16_h12288_tp8"]
+    banner(f"{w.name}: M={w.M} h={w.h} V={w.V} P={w.P}")
+    tokens, targets, H, E = wl.vocab_inputs(w)
+    Vr = w.V // w.P
+    Es = [E[r * Vr:(r + 1) * Vr].contiguous().to(DEV) for r in range(w.P)]
+    td = tokens.to(DEV)
+    parts = torch.empty(w.P, w.M, w.h, device=DEV)
+    for r in range(w.P):
+        tts.tp_vocab_embedding_shard(td, Es[r], r * Vr, out=parts[r])
+    emb = tts.tp_partial_sum(parts)
+    loss, mean = tts.tp_vocab_parallel_ce(H.to(DEV), Es, targets.to(DEV))
+    torch.cuda.synchronize()
+    del parts
+    rng = np.random.default_rng(w.seed)
+    rows = np.unique(np.concatenate([[0, 255, 256, w.M - 1], rng.integers(0, w.M, 28)]))
+    rt = torch.from_numpy(rows)
+    assert np.array_equal(emb.cpu()[rt].double().numpy(),
+                          oracle.f64(E)[tokens[rt].long().numpy()])
+    ref = oracle.vocab_ce_combine([oracle.vocab_ce_shard_stats(H[rt], E[r * Vr:(r + 1) * Vr],
+                                                               targets[rt].numpy(), r * Vr)
+                                   for r in range(w.P)])
+    assert_f32(loss.cpu()[rt].reshape(1, -1), ref.reshape(1, -1), bar=1e-4)
+    # the mean is over all tokens; check it against the GPU's own per-token losses
+    # summed in float64 (a property of the mean, independent of the order)
+    assert abs(float(mean) - float(loss.double().mean())) <= 1e-5 * abs(float(mean))
