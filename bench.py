@@ -75,9 +75,10 @@ def kernel_source_hash() -> str:
     return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
 
 
-def measured_traffic(path=TRAFFIC_FILE, source_hash=None):
-    """HBM bytes per launch of the dominant kernel from the committed counter
-    summary, or None when it is missing or was taken on another kernel source."""
+def measured_counters(path=TRAFFIC_FILE, source_hash=None):
+    """The committed counter summary of the dominant kernel as {key: float}
+    (HBM bytes per launch, shader clock, MFMA-busy fraction), or None when it
+    is missing or was taken on another kernel source."""
     if not os.path.exists(path):
         return None
     kv = {}
@@ -87,10 +88,20 @@ def measured_traffic(path=TRAFFIC_FILE, source_hash=None):
             kv[k.strip()] = v.strip()
     if kv.get("gemm_bf16_hip_sha256_16") != (source_hash or kernel_source_hash()):
         return None
-    try:
-        return float(kv["hbm_bytes_per_launch"])
-    except (KeyError, ValueError):
-        return None
+    out = {}
+    for k, v in kv.items():
+        try:
+            out[k] = float(v)
+        except ValueError:
+            pass
+    return out
+
+
+def measured_traffic(path=TRAFFIC_FILE, source_hash=None):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, or None when it is missing or was taken on another kernel source."""
+    c = measured_counters(path, source_hash)
+    return c.get("hbm_bytes_per_launch") if c else None
 
 
 def event_time(fn, reps, stream):
@@ -414,7 +425,9 @@ def main():
 
     kern_ms, kern_all = event_time(kernel, max(args.steps, 5), stream)
     kern_tflops = kern_flops / (kern_ms * 1e-3) / 1e12
-    traffic = measured_traffic(TRAFFIC_FILES[w.name]) if w.name in TRAFFIC_FILES else None
+    counters = measured_counters(TRAFFIC_FILES[w.name]) if w.name in TRAFFIC_FILES else None
+    traffic = counters.get("hbm_bytes_per_launch") if counters else None
+    clock = counters.get("shader_clock_ghz") if counters else None
     log(f"dominant kernel: {kern_ms:.3f} ms/launch, {kern_tflops:.1f} TFLOP/s")
     if w.kind == "vocab":
         calib = calibration(tts, torch, X_k, W_k[1].t(), stream)
@@ -576,6 +589,13 @@ def main():
             "traffic": traffic,
             "algorithmic_flops_per_launch": kern_flops,
             "frac_of_mfma_only": round(kern_tflops / calib["mfma_only"]["tflops"], 4),
+            # the peak rescaled to the shader clock this kernel runs at under
+            # the power limit (GRBM_GUI_ACTIVE over its duration, from the
+            # committed counter run of the same launch)
+            "clock_ghz": clock,
+            "peak_at_clock": round(PEAK_BF16_TFLOPS * clock / 2.4, 1) if clock else None,
+            "frac_at_clock": round(kern_tflops / (PEAK_BF16_TFLOPS * clock / 2.4), 4)
+            if clock else None,
             "avg_launch_ms": round(kern_ms, 4),
             "launches_timed": len(kern_all),
         },

@@ -16,6 +16,10 @@ def test_traffic_parser(tmp_path):
     assert bench.measured_traffic(str(f), "abc123") == 12345.0
     assert bench.measured_traffic(str(f), "other") is None      # stale: kernel changed
     assert bench.measured_traffic(str(tmp_path / "missing.txt"), "abc123") is None
+    f.write_text("gemm_bf16_hip_sha256_16: abc123\nhbm_bytes_per_launch: 12345\n"
+                 "shader_clock_ghz: 1.8\n")
+    assert bench.measured_counters(str(f), "abc123")["shader_clock_ghz"] == 1.8
+    assert bench.measured_counters(str(f), "other") is None
 
 
 def test_committed_traffic_files_parse():
@@ -27,6 +31,8 @@ def test_committed_traffic_files_parse():
         assert bench.measured_traffic(path, h) > 0
         assert h == bench.kernel_source_hash(), path
         assert float(kv["hbm_bytes_per_launch"]) > float(kv["algorithmic_bytes_per_launch"])
+        c = bench.measured_counters(path, h)
+        assert 1.0 < c["shader_clock_ghz"] <= 2.4 and 0.0 < c["mfma_busy"] <= 1.0
 
 
 def test_more_than_one_gpu_is_refused():

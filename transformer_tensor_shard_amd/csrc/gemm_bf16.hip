@@ -50,13 +50,21 @@
 //    (workgroups are dealt round-robin to the 8 XCDs, each with its own L2)
 //    and walk the output in groups of 4 tile-rows; a grouped launch whose
 //    groups share the activations walks row bands across all groups;
-//  * epilogue: the tile is staged through the (then idle) LDS and written with
-//    16-byte row-contiguous stores: one pass for a bf16 tile, two for f32.
+//  * epilogue: a plain f32 tile is stored straight from the accumulators (64-byte
+//    row segments, no LDS, no barrier); a bf16 tile, and the epilogues that
+//    read a second operand or reduce along rows, are staged through the (then
+//    idle) LDS and written with 16-byte row-contiguous stores.
 //
-// Measured on MI355X the kernel is bound by the chip's power limit rather than
-// by any one unit: sustained MFMA issue alone pulls the shader clock from 2.4
-// to about 1.6-1.8 GHz, and every byte moved (HBM, L2, LDS) competes for the
-// same budget.
+// Measured on MI355X (rocprofv3 counters, GeLU GEMM at the 175B layer shape):
+// the shader clock settles at ~1.75 GHz under the power limit and the matrix
+// cores are busy ~72% of it.  What idles them is the global -> LDS stream:
+// without the K loop's loads (a probe that reuses stale tiles) MFMA busy
+// reaches ~85% at the same clock.  The texture data path that carries the
+// loads is busy ~96% of the time, over half of it waiting on the L2 (~400
+// cycles per request on average); more pipeline stages do not help (a
+// 4-stage BK=32 version measured the same), and cache-policy bits do not
+// either (non-temporal loads halve throughput: they defeat the L2 sharing
+// that the tile order sets up).
 #include "tp_kernels.h"
 
 namespace tpk {
@@ -403,7 +411,38 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
         const float v = acc[mi][nj][r] + bv[nj];
         return EPI == EPI_GELU ? gelu(v) : v;
     };
-    if constexpr (OUT_BF16 && (EPI == EPI_NONE || EPI == EPI_GELU)) {
+    if constexpr (!OUT_BF16 && EPI == EPI_NONE) {
+        // f32 tiles go from the accumulators straight to memory: one store
+        // instruction writes four 64-byte row segments (16 lanes x 4 B each),
+        // the neighbouring column block fills the other half of each 128-byte
+        // line.  No LDS staging and no barrier: the stores drain while the
+        // next workgroup on this CU starts its K loop.
+        float* __restrict__ Cf = (float*)C;
+        const int gr0 = m0 + wm * 128 + 4 * (lane >> 4);
+        const int gc0 = n0 + lcol;
+        if (m0 + BM <= M && n0 + BN <= N) {
+#pragma unroll
+            for (int mi = 0; mi < NI; ++mi)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float* row = Cf + (int64_t)(gr0 + mi * 16 + r) * ldc + gc0;
+#pragma unroll
+                    for (int nj = 0; nj < NJ; ++nj) row[16 * nj] = value(mi, nj, r);
+                }
+        } else {
+#pragma unroll
+            for (int mi = 0; mi < NI; ++mi)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int gr = gr0 + mi * 16 + r;
+                    if (gr >= M) continue;
+                    float* row = Cf + (int64_t)gr * ldc + gc0;
+#pragma unroll
+                    for (int nj = 0; nj < NJ; ++nj)
+                        if (gc0 + 16 * nj < N) row[16 * nj] = value(mi, nj, r);
+                }
+        }
+    } else if constexpr (OUT_BF16 && (EPI == EPI_NONE || EPI == EPI_GELU)) {
         char* half = wm ? lds1 : lds0;
 #pragma unroll
         for (int nj = 0; nj < NJ; ++nj) {
