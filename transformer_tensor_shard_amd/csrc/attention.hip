@@ -21,7 +21,8 @@
 //    row-major V tile via the gfx950 LDS transpose read (ds_read_b64_tr_b16);
 //  * exp is the hardware exp2 with log2(e)/sqrt(d) folded into one FMA per
 //    score; the mask is applied only on tiles that reach the diagonal or the
-//    end, and the accumulator is rescaled only when a running max moved;
+//    end; the running max moves only when a tile's max exceeds it by more
+//    than 8 (log2 units), so the accumulator is rarely rescaled;
 //  * LDS tiles are XOR-swizzled in 16-byte units (conflict-free for both the
 //    16-byte K reads and the transpose V reads), two stages as two arrays so
 //    every LDS address is static;
@@ -66,6 +67,29 @@ __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 
 __device__ __forceinline__ unsigned tile_off(int row, int col) {
     return row * 256 + (((col >> 3) ^ swz(row)) << 4) + (col & 7) * 2;
 }
+
+// max / sum of v over lanes l and l ^ 32 with the gfx950 lane-half swap (one
+// VALU op, no LDS round trip).  With the same register as both operands the
+// two results hold, in every lane, the lower half's and the upper half's
+// value in that order, so both lanes get the same bits.
+__device__ __forceinline__ float halves_max(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                    false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                    false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// The running maximum moves only when a tile's maximum exceeds it by more than
+// this many log2 units; until then the weights 2^(s·c - m) stay below 2^8
+// (exact in f32, and bf16 keeps its relative precision at any magnitude) and
+// the accumulator keeps its scale, so rescaling it is rare after the first
+// tile.  Numerator and normaliser always share the same m, so the result does
+// not depend on when m moves.
+constexpr float M_SLACK = 8.0f;
 
 __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(
     const __bf16* __restrict__ qkv, int64_t ld, int64_t qkv_rank_stride,
@@ -201,10 +225,11 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(
         for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sacc[t][r]);
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 32)) * scale_log2;
-        const float m_new = fmaxf(m_run, mloc);
+        mloc = halves_max(mloc) * scale_log2;
+        const bool move = mloc > m_run + M_SLACK;
+        const float m_new = move ? mloc : m_run;
         const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+        const float alpha = move ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.0f;
         m_run = m_new;
         // probabilities rounded to bf16 (the MFMA operand); the normaliser
         // sums the same rounded weights, two at a time with a bf16 dot
@@ -263,7 +288,7 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(
 
     // ---- normalise and write: lane holds query l32, dims
     // 32dt + 8(r>>2) + 4hi + (r&3).  Stage the wave's 32x128 block in LDS.
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float l_tot = halves_sum(l_run);
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
     // the training forward keeps log2 of each query's softmax normaliser,
     // L = m + log2(sum 2^(s·c - m)) with c = log2(e)/sqrt(d), so that the
