@@ -244,6 +244,27 @@ def test_attention_core(b, s, Hl, causal):
     assert_bf16(O, ref)
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_attention_core_moving_max(causal):
+    """Keys whose scale grows along the sequence (x1 at the first key, x17 at
+    the last): each query's maximum score rises by many log2 units from tile
+    to tile, so the kernel's running maximum moves past its slack and the
+    accumulator is rescaled on many tiles, not just the first."""
+    banner(f"attention core, growing key scale, causal={causal}")
+    b, s, Hl, d = 2, 512, 2, 128
+    n3 = 3 * Hl * d
+    qkv = gen((b * s, n3), 1.0, 53, "x").float()
+    scale = 1.0 + torch.arange(s, dtype=torch.float32).repeat(b) / 32.0
+    qkv[:, Hl * d:2 * Hl * d] *= scale[:, None]
+    qkv = qkv.to(torch.bfloat16)
+    O = tts.tp_attention_core(qkv.to(DEV), b, s, Hl, d, causal)
+    torch.cuda.synchronize()
+    eye = np.eye(n3)
+    ref = oracle.attn_shard_rows(qkv, b, s, eye, np.ascontiguousarray(eye[:Hl * d]), Hl, d,
+                                 causal)[:, :Hl * d]
+    assert_bf16(O, ref)
+
+
 def test_attention_single_token_is_value():
     banner("attention s=1")
     b, s, Hl, d = 5, 1, 2, 128
