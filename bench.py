@@ -354,8 +354,11 @@ def main():
         tokens, targets, x = tokens_cpu.to(dev), targets_cpu.to(dev), H_cpu.to(dev)
         Es = [E_cpu[r * Vr:(r + 1) * Vr].contiguous().to(dev) for r in range(w.P)]
         M, h = w.M, w.h
-        parts = torch.empty(w.P, M, h, dtype=torch.float32, device=dev)
-        emb = torch.empty(M, h, dtype=torch.float32, device=dev)
+        # bf16 partials: each token's row comes from exactly one rank and the
+        # others contribute zeros, so the sum over ranks is exact in bf16 (the
+        # model's activation dtype) and bit-identical to an f32 sum
+        parts = torch.empty(w.P, M, h, dtype=torch.bfloat16, device=dev)
+        emb = torch.empty(M, h, dtype=torch.bfloat16, device=dev)
         loss = torch.empty(M, dtype=torch.float32, device=dev)
         mean = torch.empty(1, dtype=torch.float32, device=dev)
         ce_ws = torch.empty(tts.tp_vocab_parallel_ce_workspace(M, Vr, w.P), dtype=torch.uint8,
@@ -531,9 +534,9 @@ def main():
         items = {
             "embedding_all_ranks": (lambda: [tts.tp_vocab_embedding_shard(
                 tokens, Es[r], r * Vr, out=parts[r]) for r in range(w.P)], None,
-                w.P * M * h * 4 + w.M * h * 2),
+                w.P * M * h * 2 + w.M * h * 2),
             "embedding_partial_sum": (lambda: tts.tp_partial_sum(parts, out=emb), None,
-                                      (w.P + 1) * M * h * 4),
+                                      (w.P + 1) * M * h * 2),
             "cross_entropy_all_ranks": (lambda: tts.tp_vocab_parallel_ce(
                 x, Es, targets, loss=loss, loss_mean=mean, ws=ce_ws), w.flops(), None),
         }

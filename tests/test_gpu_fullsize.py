@@ -175,10 +175,12 @@ def test_vocab_fullsize_sampled():
     Vr = w.V // w.P
     Es = [E[r * Vr:(r + 1) * Vr].contiguous().to(DEV) for r in range(w.P)]
     td = tokens.to(DEV)
-    parts = torch.empty(w.P, w.M, w.h, device=DEV)
+    # bf16 partials and a bf16 sum, as the benchmark runs them (each row has
+    # one nonzero term, so the sum is exact in bf16)
+    parts = torch.empty(w.P, w.M, w.h, dtype=torch.bfloat16, device=DEV)
     for r in range(w.P):
         tts.tp_vocab_embedding_shard(td, Es[r], r * Vr, out=parts[r])
-    emb = tts.tp_partial_sum(parts)
+    emb = tts.tp_partial_sum(parts, out_dtype=torch.bfloat16)
     loss, mean = tts.tp_vocab_parallel_ce(H.to(DEV), Es, targets.to(DEV))
     torch.cuda.synchronize()
     del parts

@@ -128,33 +128,50 @@ __global__ __launch_bounds__(256) void partial_sum_kernel(
 
 // RES: 0 none, 1 f32, 2 bf16.  The summation order is the one of
 // partial_sum_kernel (ranks ascending, then bias, then residual), so both give
-// bit-identical sums.
-template <bool PART_BF16, int RES, bool OUT_BF16, bool LN>
+// bit-identical sums.  E is the number of consecutive elements a thread owns
+// per unit: 4 with f32 partials (16-byte loads), 8 with bf16 partials or none
+// (16-byte bf16 loads); h % E == 0.
+template <int E> struct vec_of;
+template <> struct vec_of<4> {
+    typedef float f __attribute__((ext_vector_type(4)));
+    typedef __bf16 b __attribute__((ext_vector_type(4)));
+};
+template <> struct vec_of<8> {
+    typedef float f __attribute__((ext_vector_type(8)));
+    typedef __bf16 b __attribute__((ext_vector_type(8)));
+};
+
+template <bool PART_BF16, int RES, bool OUT_BF16, bool LN, int E>
 __global__ __launch_bounds__(256) void row_sum_kernel(
-    void* __restrict__ Z, const void* __restrict__ parts, int P, int64_t n4, int h,
+    void* __restrict__ Z, const void* __restrict__ parts, int P, int64_t n_units, int h,
     const float* __restrict__ bias, const void* __restrict__ res,
     __bf16* __restrict__ y, const float* __restrict__ gamma, const float* __restrict__ beta,
     float eps)
 {
-    constexpr int MAXV = 16;                      // 16 x 256 x 4 = 16384 columns
+    typedef typename vec_of<E>::f fv;
+    typedef typename vec_of<E>::b bv;
+    constexpr int MAXV = 16384 / (256 * E);       // units per thread: rows up to 16384 wide
     __shared__ float red[4];
-    const int64_t row4 = (int64_t)blockIdx.x * (h / 4);
-    const int nv = h / 4;
-    f32x4 acc[MAXV];
+    const int nv = h / E;
+    const int64_t row0 = (int64_t)blockIdx.x * nv;  // first unit of the row
+    fv acc[MAXV];
 #pragma unroll
-    for (int i = 0; i < MAXV; ++i) acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int i = 0; i < MAXV; ++i)
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[i][e] = 0.0f;
     for (int r = 0; r < P; ++r) {
-        f32x4 t[MAXV];
+        fv t[MAXV];
 #pragma unroll
         for (int i = 0; i < MAXV; ++i) {
             const int c = threadIdx.x + 256 * i;
             if (c < nv) {
-                const int64_t k = r * n4 + row4 + c;
-                if (PART_BF16) {
-                    const bf16x4 b = ((const bf16x4*)parts)[k];
-                    t[i] = f32x4{(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
+                const int64_t k = r * n_units + row0 + c;
+                if constexpr (PART_BF16) {
+                    const bv b = ((const bv*)parts)[k];
+#pragma unroll
+                    for (int e = 0; e < E; ++e) t[i][e] = (float)b[e];
                 } else {
-                    t[i] = __builtin_nontemporal_load((const f32x4*)parts + k);
+                    t[i] = __builtin_nontemporal_load((const fv*)parts + k);
                 }
             }
         }
@@ -167,21 +184,26 @@ __global__ __launch_bounds__(256) void row_sum_kernel(
     for (int i = 0; i < MAXV; ++i) {
         const int c = threadIdx.x + 256 * i;
         if (c >= nv) continue;
-        if (bias) acc[i] += *(const f32x4*)(bias + 4 * c);
-        if (RES == 1) acc[i] += ((const f32x4*)res)[row4 + c];
+        if (bias) acc[i] += *(const fv*)(bias + E * c);
+        if (RES == 1) acc[i] += ((const fv*)res)[row0 + c];
         if (RES == 2) {
-            const bf16x4 b = ((const bf16x4*)res)[row4 + c];
-            acc[i] += f32x4{(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
+            const bv b = ((const bv*)res)[row0 + c];
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[i][e] += (float)b[e];
         }
         if (Z && OUT_BF16) {
-            bf16x4 o;
+            bv o;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = (__bf16)acc[i][e];
-            ((bf16x4*)Z)[row4 + c] = o;
+            for (int e = 0; e < E; ++e) o[e] = (__bf16)acc[i][e];
+            ((bv*)Z)[row0 + c] = o;
         } else if (Z) {
-            ((f32x4*)Z)[row4 + c] = acc[i];
+            ((fv*)Z)[row0 + c] = acc[i];
         }
-        if (LN) sum += (acc[i][0] + acc[i][1]) + (acc[i][2] + acc[i][3]);
+        if (LN) {
+            float u = (acc[i][0] + acc[i][1]) + (acc[i][2] + acc[i][3]);
+            if constexpr (E == 8) u += (acc[i][4] + acc[i][5]) + (acc[i][6] + acc[i][7]);
+            sum += u;
+        }
     }
     if (!LN) return;
     // LayerNorm of the summed row (f32 statistics, population variance,
@@ -192,21 +214,21 @@ __global__ __launch_bounds__(256) void row_sum_kernel(
     for (int i = 0; i < MAXV; ++i)
         if (threadIdx.x + 256 * i < nv)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) { const float d = acc[i][e] - mean; q += d * d; }
+            for (int e = 0; e < E; ++e) { const float d = acc[i][e] - mean; q += d * d; }
     const float inv = rsqrtf(block_sum(q, red) / (float)h + eps);
 #pragma unroll
     for (int i = 0; i < MAXV; ++i) {
         const int c = threadIdx.x + 256 * i;
         if (c >= nv) continue;
-        bf16x4 o;
+        bv o;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
+        for (int e = 0; e < E; ++e) {
             float v = (acc[i][e] - mean) * inv;
-            if (gamma) v *= gamma[4 * c + e];
-            if (beta) v += beta[4 * c + e];
+            if (gamma) v *= gamma[E * c + e];
+            if (beta) v += beta[E * c + e];
             o[e] = (__bf16)v;
         }
-        ((bf16x4*)y)[row4 + c] = o;
+        ((bv*)y)[row0 + c] = o;
     }
 }
 
@@ -262,12 +284,22 @@ hipError_t row_sum(void* Z, bool out_bf16, const void* parts, bool parts_bf16, i
                    void* ln_out, const float* gamma, const float* beta, float eps,
                    hipStream_t stream)
 {
-    const int64_t n4 = M * h / 4;
+    // 8-element units when no f32 partial is read (16-byte bf16 loads), else 4
+    const bool e8 = (P == 0 || parts_bf16) && h % 8 == 0;
     const int res = residual ? (res_bf16 ? 2 : 1) : 0;
     const dim3 grid((unsigned)M), block(256);
     __bf16* y = (__bf16*)ln_out;
-#define TP_RS(PB, R, OB, L) hipLaunchKernelGGL((row_sum_kernel<PB, R, OB, L>), grid, block, 0, \
-        stream, Z, parts, P, n4, (int)h, bias, residual, y, gamma, beta, eps)
+#define TP_RS(PB, R, OB, L)                                                                    \
+    do {                                                                                       \
+        if (e8)                                                                                \
+            hipLaunchKernelGGL((row_sum_kernel<PB, R, OB, L, 8>), grid, block, 0, stream, Z,   \
+                               parts, P, M * h / 8, (int)h, bias, residual, y, gamma, beta,    \
+                               eps);                                                           \
+        else                                                                                   \
+            hipLaunchKernelGGL((row_sum_kernel<PB, R, OB, L, 4>), grid, block, 0, stream, Z,   \
+                               parts, P, M * h / 4, (int)h, bias, residual, y, gamma, beta,    \
+                               eps);                                                           \
+    } while (0)
 #define TP_RS_RES(PB, OB, L) { if (res == 0) TP_RS(PB, 0, OB, L); \
         else if (res == 1) TP_RS(PB, 1, OB, L); else TP_RS(PB, 2, OB, L); }
     if (ln_out) {
