@@ -20,6 +20,10 @@ in the order the pages give:
   the gradients of the MLP and attention shares by the chain rule (same page
   §2.2 and §3.2, backward: same upstream gradient on every rank, local
   parameter gradients, a partial input gradient summed over ranks);
+* ``attention_kv_split`` -- attention with Q, K, V split along the feature
+  dimension: partial scores summed over ranks before the softmax, each rank
+  the feature slice of the output (ops-transformer article
+  (intelliparadigm.com/article/weixin_42537919/2252113) §3.1, strategy B);
 * ``vocab_embedding_shard``, ``vocab_ce_shard_stats``, ``vocab_ce_combine`` --
   the vocab-parallel input embedding and the stable parallel cross-entropy
   (same page §4.1, §4.2);
@@ -221,6 +225,56 @@ def attn_shard_rows(X, b: int, s: int, Wqkv, Wo, Hl: int, d: int, causal: bool,
         O[sel] = attention_rows(Q, np.ascontiguousarray(KV[:, :HD]),
                                 np.ascontiguousarray(KV[:, HD:]), t, Hl, d, causal)
     return matmul(O, Wo)
+
+
+def attention_kv_split(Q, K, V, P: int, causal: bool):
+    """One head's attention with Q, K and V split along the feature dimension
+    over P ranks (strategy B, "K/V splitting", of the ops-transformer article
+    (intelliparadigm.com/article/weixin_42537919/2252113) §3.1).
+
+    Rank r holds the features F_r = [r·d/P, (r+1)·d/P) of Q, K, V [s, d] and
+    computes the partial scores S_r = Q[:, F_r]·K[:, F_r]^T.  The softmax is
+    not linear, so the partial scores are summed over the ranks first (in
+    rank order); then P = softmax(S/sqrt(d) + causal mask) row by row (the
+    maximum subtracted, two passes), and rank r forms its feature slice of
+    the output, O[:, F_r] = P·V[:, F_r].  Returns (S_parts [P, s, s],
+    O [s, d]) in float64.
+    """
+    Q, K, V = f64(Q), f64(K), f64(V)
+    s, d = Q.shape
+    assert K.shape == (s, d) and V.shape == (s, d) and d % P == 0
+    w = d // P
+    parts = np.stack([Q[:, r * w:(r + 1) * w] @ K[:, r * w:(r + 1) * w].T for r in range(P)])
+    S = parts[0].copy()
+    for r in range(1, P):
+        S += parts[r]
+    S /= math.sqrt(d)
+    if causal:
+        S[np.triu_indices(s, 1)] = -np.inf
+    S -= S.max(axis=1, keepdims=True)
+    E = np.exp(S)
+    Pm = E / E.sum(axis=1, keepdims=True)
+    O = np.concatenate([Pm @ V[:, r * w:(r + 1) * w] for r in range(P)], axis=1)
+    return parts, O
+
+
+def attention_kv_split_rows(qkv, b: int, s: int, H: int, d: int, P: int, causal: bool):
+    """attention_kv_split for every (sequence, head) of a fused projection
+    qkv [b·s, 3·H·d] laid out [Q | K | V], head-major within each block;
+    returns O [b·s, H·d] (head-major columns, each head's features in rank
+    order)."""
+    qkv = f64(qkv)
+    HD = H * d
+    assert qkv.shape == (b * s, 3 * HD)
+    O = np.empty((b * s, HD), dtype=np.float64)
+    for beta in range(b):
+        rows = slice(beta * s, (beta + 1) * s)
+        for hd in range(H):
+            c = slice(hd * d, (hd + 1) * d)
+            O[rows, c] = attention_kv_split(qkv[rows, c], qkv[rows, HD + hd * d:HD + (hd + 1) * d],
+                                            qkv[rows, 2 * HD + hd * d:2 * HD + (hd + 1) * d],
+                                            P, causal)[1]
+    return O
 
 
 def attention_backward(Q, K, V, dO, Hl: int, d: int, causal: bool):

@@ -689,3 +689,91 @@ def test_vocab_ce_target_logit_from_one_rank():
         mine = (targets >= r * Vr) & (targets < (r + 1) * Vr)
         assert not t[~mine].any()
         assert np.allclose(t[mine], (H @ E.T)[np.nonzero(mine)[0], targets[mine]], atol=1e-13)
+
+
+# ---------------------------------------------- K/V-split attention (strategy B)
+def _sdpa64(Q, K, V, causal):
+    q, k, v = (torch.from_numpy(np.ascontiguousarray(t))[None, None] for t in (Q, K, V))
+    return torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=causal)[0, 0].numpy()
+
+
+@pytest.mark.parametrize("P", [1, 2, 4, 8])
+@pytest.mark.parametrize("causal", [True, False])
+def test_kv_split_matches_library_attention(P, causal):
+    """Summing the feature slices' partial scores before the softmax and
+    concatenating the ranks' output slices gives the head's attention: the
+    same as float64 scaled_dot_product_attention on the unsplit Q, K, V."""
+    rng = np.random.default_rng(100 + P)
+    s, d = 37, 32
+    Q, K, V = (rng.standard_normal((s, d)) for _ in range(3))
+    _, O = oracle.attention_kv_split(Q, K, V, P, causal)
+    ref = _sdpa64(Q, K, V, causal)
+    assert np.abs(O - ref).max() <= 1e-12 * np.abs(ref).max()
+
+
+def test_kv_split_partial_scores_sum_to_full_scores():
+    rng = np.random.default_rng(7)
+    s, d, P = 19, 16, 4
+    Q, K, V = (rng.standard_normal((s, d)) for _ in range(3))
+    parts, _ = oracle.attention_kv_split(Q, K, V, P, True)
+    assert parts.shape == (P, s, s)
+    full = Q @ K.T
+    assert np.abs(parts.sum(axis=0) - full).max() <= 1e-12 * np.abs(full).max()
+    # every partial is a product over its own features only
+    w = d // P
+    assert np.array_equal(parts[2], Q[:, 2 * w:3 * w] @ K[:, 2 * w:3 * w].T)
+
+
+def test_kv_split_softmax_of_partials_is_wrong():
+    """Negative control: finishing each rank's softmax on its own partial
+    scores (and averaging the ranks' outputs) is not the attention; the sum of
+    the partial scores must come first."""
+    rng = np.random.default_rng(8)
+    s, d, P = 24, 16, 2
+    Q, K, V = (rng.standard_normal((s, d)) * 2 for _ in range(3))
+    parts, O = oracle.attention_kv_split(Q, K, V, P, False)
+    w = d // P
+    wrong = []
+    for r in range(P):
+        S = parts[r] / math.sqrt(d)
+        E = np.exp(S - S.max(axis=1, keepdims=True))
+        wrong.append((E / E.sum(axis=1, keepdims=True)) @ V)
+    wrong = sum(wrong) / P
+    assert np.abs(wrong - O).max() > 0.1 * np.abs(O).max()
+
+
+def test_kv_split_brute_force():
+    """Tiny case by scalar loops: s = 3, d = 4, P = 2, causal."""
+    Q = [[0.5, -1.0, 2.0, 0.25], [1.5, 0.0, -0.5, 1.0], [-2.0, 1.0, 0.5, -0.75]]
+    K = [[1.0, 0.5, -0.5, 2.0], [-1.0, 1.5, 0.25, 0.0], [0.5, -2.0, 1.0, 1.0]]
+    V = [[1.0, 2.0, 3.0, 4.0], [-1.0, 0.5, 0.0, 2.0], [0.25, -0.5, 1.5, -1.0]]
+    s, d, P = 3, 4, 2
+    w = d // P
+    ref = [[0.0] * d for _ in range(s)]
+    for t in range(s):
+        sc = []
+        for u in range(t + 1):
+            part = [math.fsum(Q[t][c] * K[u][c] for c in range(r * w, (r + 1) * w)) for r in range(P)]
+            sc.append(math.fsum(part) / math.sqrt(d))
+        mx = max(sc)
+        e = [math.exp(x - mx) for x in sc]
+        z = math.fsum(e)
+        for c in range(d):
+            ref[t][c] = math.fsum(e[u] / z * V[u][c] for u in range(t + 1))
+    _, O = oracle.attention_kv_split(np.array(Q), np.array(K), np.array(V), P, True)
+    assert np.abs(O - np.array(ref)).max() <= 1e-14
+
+
+def test_kv_split_rows_layout():
+    """The fused-projection wrapper splits heads and Q/K/V blocks as the
+    attention core's layout does: it equals the per-head attention oracle."""
+    rng = np.random.default_rng(9)
+    b, s, H, d, P = 2, 11, 3, 16, 4
+    qkv = rng.standard_normal((b * s, 3 * H * d))
+    O = oracle.attention_kv_split_rows(qkv, b, s, H, d, P, True)
+    HD = H * d
+    for beta in range(b):
+        rows = slice(beta * s, (beta + 1) * s)
+        ref = oracle.attention_rows(qkv[rows, :HD], qkv[rows, HD:2 * HD], qkv[rows, 2 * HD:],
+                                    np.arange(s), H, d, True)
+        assert np.abs(O[rows] - ref).max() <= 1e-12
