@@ -251,8 +251,8 @@ def dominant_kernel(w, tts, torch, X, Ws, dev):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="block_bf16_h12288_tp8")
     ap.add_argument("--no-training", action="store_true",
                     help="skip the MLP-backward measurement added to the block line")
@@ -412,16 +412,25 @@ def main():
         step()
     torch.cuda.synchronize()
     log(f"timing {args.steps} step(s)")
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # one event after every step: the whole region gives the mean, the
+    # differences the per-step spread
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     wall0 = time.time()
-    start.record(stream)
-    for _ in range(args.steps):
+    evs[0].record(stream)
+    for i in range(args.steps):
         step()
-    end.record(stream)
+        evs[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.time() - wall0
-    ms = start.elapsed_time(end) / args.steps
+    ms = evs[0].elapsed_time(evs[-1]) / args.steps
+    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
+    step_stats = {"min": round(per_step[0], 4),
+                  "median": round(per_step[len(per_step) // 2] if len(per_step) % 2
+                                  else 0.5 * (per_step[len(per_step) // 2 - 1]
+                                              + per_step[len(per_step) // 2]), 4),
+                  "p90": round(per_step[min(len(per_step) - 1,
+                                            int(math.ceil(0.9 * len(per_step))) - 1)], 4)}
     flops = w.flops()
     tflops = flops / (ms * 1e-3) / 1e12
     log(f"{ms:.3f} ms/step, {tflops:.1f} TFLOP/s (wall {wall:.2f} s)")
@@ -572,6 +581,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "step_ms": step_stats,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

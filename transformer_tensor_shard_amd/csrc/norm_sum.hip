@@ -130,7 +130,8 @@ __global__ __launch_bounds__(256) void partial_sum_kernel(
 // partial_sum_kernel (ranks ascending, then bias, then residual), so both give
 // bit-identical sums.  E is the number of consecutive elements a thread owns
 // per unit: 4 with f32 partials (16-byte loads), 8 with bf16 partials or none
-// (16-byte bf16 loads); h % E == 0.
+// (16-byte bf16 loads); h % E == 0.  Outputs are stored with the
+// non-temporal hint (written once, read by a later launch): ~1.5% faster.
 template <int E> struct vec_of;
 template <> struct vec_of<4> {
     typedef float f __attribute__((ext_vector_type(4)));
@@ -195,9 +196,9 @@ __global__ __launch_bounds__(256) void row_sum_kernel(
             bv o;
 #pragma unroll
             for (int e = 0; e < E; ++e) o[e] = (__bf16)acc[i][e];
-            ((bv*)Z)[row0 + c] = o;
+            __builtin_nontemporal_store(o, (bv*)Z + row0 + c);
         } else if (Z) {
-            ((fv*)Z)[row0 + c] = acc[i];
+            __builtin_nontemporal_store(acc[i], (fv*)Z + row0 + c);
         }
         if (LN) {
             float u = (acc[i][0] + acc[i][1]) + (acc[i][2] + acc[i][3]);
@@ -228,7 +229,7 @@ __global__ __launch_bounds__(256) void row_sum_kernel(
             if (beta) v += beta[E * c + e];
             o[e] = (__bf16)v;
         }
-        ((bv*)y)[row0 + c] = o;
+        __builtin_nontemporal_store(o, (bv*)y + row0 + c);
     }
 }
 
