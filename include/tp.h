@@ -10,6 +10,9 @@
  *       pre-LN block: x + attention(norm1(x)), then x + mlp(norm2(x))),
  *       section 2.2 (heads per rank = num_heads / world_size) and section 3.2
  *       (a shape that does not divide by the world size is rejected).
+ *   [ops-transformer] intelliparadigm.com/article/weixin_42537919/2252113,
+ *       §3.1 (attention parallelisation: strategy B, K/V split along the
+ *       feature dimension, partial scores combined across devices).
  *
  * Conventions shared by every entry point:
  *  - Matrices are row-major with the X·W convention: a weight of a linear
@@ -288,6 +291,28 @@ tp_status tp_matmul_grouped(const void* const* A, const int64_t* lda, int trans_
                             const void* const* B, const int64_t* ldb, int trans_b,
                             void* const* C, const int64_t* ldc, const int64_t* M,
                             const int64_t* N, int count, int64_t K, int out, void* stream);
+
+/* tp_attention_kv_split -- attention with Q, K and V split along the feature
+ * dimension over P emulated ranks ("strategy B", K/V splitting, of the
+ * ops-transformer article [ops-transformer] §3.1): rank r holds the features
+ * F_r = [r·d/P, (r+1)·d/P) of every head's Q, K and V, computes the partial
+ * scores S_r = Q_r·K_r^T (the exchange step sums them over the ranks before
+ * the softmax, which is not linear), and forms its feature slice of the head
+ * output, O[:, F_r] = softmax(S/sqrt(d) + causal mask)·V_r.  The partial
+ * scores are materialised in f32 ([s, s] per rank and head), the softmax
+ * weights in bf16 (unnormalised, the row maximum's weight exactly 1), the
+ * products with V in f32, divided by the sum of the same rounded weights;
+ * (sequence, head) pairs run 16 at a time.
+ *   qkv  [b·s, ld_qkv] bf16, columns [Q | K | V], each H·d wide, head-major
+ *   O    [b·s, ldo] bf16: head h's features at columns h·d .. h·d + d - 1, the
+ *        ranks' slices in rank order
+ *   ws   >= tp_attention_kv_split_workspace(b, s, H, d, P) bytes
+ * Needs d % P == 0, (d/P) % 8 == 0, s % 8 == 0, s <= 8192, ld_qkv >= 3·H·d and
+ * ldo >= H·d (both multiples of 8); otherwise TP_ERR_SHAPE. */
+size_t    tp_attention_kv_split_workspace(int64_t b, int64_t s, int64_t H, int64_t d, int P);
+tp_status tp_attention_kv_split(const void* qkv, int64_t ld_qkv, void* O, int64_t ldo,
+                                int64_t b, int64_t s, int64_t H, int64_t d, int P, int causal,
+                                void* ws, size_t ws_bytes, void* stream);
 
 /* tp_attention_core -- per (sequence, local head) softmax(Q·K^T/sqrt d)·V
  * ([Megatron explainer] §3.1) on projections already in memory.

@@ -314,3 +314,33 @@ def test_vocab_rejects():
     assert par(P=0) == _lib.TP_ERR_SHAPE
     assert par(wsb=100) == _lib.TP_ERR_WORKSPACE
     assert L.tp_vocab_parallel_ce_workspace(10, 64, 2) > 0
+
+
+def test_kv_split_rejects():
+    L = tts.lib()
+    kv = lambda qkv=FAKE, ld=3 * 4 * 128, O=FAKE, ldo=4 * 128, b=2, s=64, H=4, d=128, P=4, \
+        ws=FAKE, wsb=BIG: L.tp_attention_kv_split(qkv, ld, O, ldo, b, s, H, d, P, 1, ws, wsb, None)
+    assert kv(qkv=None) == _lib.TP_ERR_NULL
+    assert kv(O=None) == _lib.TP_ERR_NULL
+    assert kv(P=3) == _lib.TP_ERR_SHAPE          # d not divisible by P
+    assert kv(P=32) == _lib.TP_ERR_SHAPE         # d/P = 4 features: not a 16-byte slice
+    assert kv(s=60) == _lib.TP_ERR_SHAPE         # s % 8
+    assert kv(s=8200) == _lib.TP_ERR_SHAPE       # rows longer than 8192
+    assert kv(ld=3 * 4 * 128 - 8) == _lib.TP_ERR_SHAPE
+    assert kv(ldo=4 * 128 - 8) == _lib.TP_ERR_SHAPE
+    assert kv(b=0) == _lib.TP_ERR_SHAPE
+    assert kv(ws=None) == _lib.TP_ERR_WORKSPACE
+    assert kv(wsb=1024) == _lib.TP_ERR_WORKSPACE
+    assert kv(O=FAKE_ODD) == _lib.TP_ERR_ALIGN
+    assert kv(ws=FAKE_ODD) == _lib.TP_ERR_ALIGN
+
+
+def test_kv_split_workspace_size():
+    L = tts.lib()
+    # 16 pairs at most in flight
+    # per pair: P f32 partial-score matrices and a bf16 weight matrix of s x s,
+    # the f32 product with V [s, d] and the row sums [s]
+    assert L.tp_attention_kv_split_workspace(2, 64, 4, 128, 4) == 8 * (64 * 64 * 18 + 64 * 516)
+    assert L.tp_attention_kv_split_workspace(4, 2048, 32, 128, 4) == \
+        16 * (2048 * 2048 * 18 + 2048 * 516)
+    assert L.tp_attention_kv_split_workspace(0, 64, 4, 128, 4) == 0

@@ -26,7 +26,8 @@ __all__ = [
     "tp_mlp_shard_backward_workspace", "tp_attention_core_train", "tp_attention_core_backward",
     "tp_attn_shard_train_fwd", "tp_attn_shard_backward", "tp_attn_shard_backward_workspace",
     "tp_vocab_embedding_shard", "tp_vocab_ce_shard", "tp_vocab_ce_shard_workspace",
-    "tp_vocab_ce_combine", "tp_vocab_parallel_ce", "tp_vocab_parallel_ce_workspace", "lib",
+    "tp_vocab_ce_combine", "tp_vocab_parallel_ce", "tp_vocab_parallel_ce_workspace",
+    "tp_attention_kv_split", "tp_attention_kv_split_workspace", "lib",
 ]
 
 
@@ -65,6 +66,14 @@ def _dev(t: Optional[torch.Tensor], name: str):
         raise ValueError(f"{name} must be a GPU tensor")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _dev_rows(t: torch.Tensor, name: str):
+    """A 2-D GPU tensor whose rows are contiguous, at any row pitch (passed to
+    the library as its leading dimension)."""
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be a 2-D GPU tensor with contiguous rows")
     return ctypes.c_void_p(t.data_ptr())
 
 
@@ -315,6 +324,31 @@ def tp_matmul_grouped(As, Bs, *, trans_a=False, trans_b=False, outs=None,
         _code(outs[0].dtype), _stream(stream))
     _check(st, "tp_matmul_grouped")
     return outs
+
+
+def tp_attention_kv_split_workspace(b: int, s: int, H: int, P: int, d: int = 128) -> int:
+    return int(_lib.load().tp_attention_kv_split_workspace(b, s, H, d, P))
+
+
+def tp_attention_kv_split(qkv, b: int, s: int, H: int, P: int, d: int = 128, causal=True, *,
+                          out=None, ws=None, stream=None):
+    """Attention with Q, K, V split along the feature dimension over P ranks:
+    partial scores per rank, summed before the softmax, each rank its output
+    feature slice.  qkv [b·s, ld] bf16 ([Q | K | V], H·d each); returns O
+    [b·s, H·d] bf16."""
+    dev = qkv.device
+    if out is None:
+        out = torch.empty(b * s, H * d, dtype=torch.bfloat16, device=dev)
+    if ws is None:
+        ws = torch.empty(tp_attention_kv_split_workspace(b, s, H, P, d), dtype=torch.uint8,
+                         device=dev)
+    st = _lib.load().tp_attention_kv_split(_dev_rows(qkv, "qkv"), qkv.stride(0),
+                                           _dev_rows(out, "out"),
+                                           out.stride(0), b, s, H, d, P, int(bool(causal)),
+                                           _dev(ws, "ws"), ws.numel() * ws.element_size(),
+                                           _stream(stream))
+    _check(st, "tp_attention_kv_split")
+    return out
 
 
 def tp_attention_core(qkv, b: int, s: int, H_l: int, d: int = 128, causal=True, *, out=None,

@@ -48,6 +48,9 @@ SIGNATURES = {
                                  ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i64, _int, _i64, _i64,
                                  _i64, _int, _int, _int, _vp]),
     "tp_attention_core": (_int, [_vp, _i64, _vp, _i64, _i64, _i64, _i64, _int, _vp]),
+    "tp_attention_kv_split_workspace": (_sz, [_i64, _i64, _i64, _i64, _int]),
+    "tp_attention_kv_split": (_int, [_vp, _i64, _vp, _i64, _i64, _i64, _i64, _i64, _int, _int,
+                                      _vp, _sz, _vp]),
     "tp_layernorm": (_int, [_vp, _int, _vp, _vp, _vp, ctypes.c_float, _i64, _i64, _vp]),
     "tp_probe_mfma": (_int, [_vp, _int, _int, _vp]),
     "tp_matmul": (_int, [_vp, _i64, _int, _vp, _i64, _int, _vp, _vp, _i64, _vp, _i64, _i64, _i64,

@@ -479,6 +479,28 @@ TP_EXPORT tp_status tp_attention_core(const void* qkv, int64_t ld_qkv, void* O, 
     return launched(tpk::attention_fwd(qkv, ld_qkv, O, b, s, H_l, causal != 0, as_stream(stream)));
 }
 
+// ---- attention with Q, K, V split along the feature dimension -------------
+TP_EXPORT size_t tp_attention_kv_split_workspace(int64_t b, int64_t s, int64_t H, int64_t d,
+                                                 int P) {
+    if (b <= 0 || s <= 0 || H <= 0 || d <= 0 || P <= 0) return 0;
+    return (size_t)tpk::kv_split_workspace_bytes(b * H, s, d, P);
+}
+
+TP_EXPORT tp_status tp_attention_kv_split(const void* qkv, int64_t ld_qkv, void* O, int64_t ldo,
+                                          int64_t b, int64_t s, int64_t H, int64_t d, int P,
+                                          int causal, void* ws, size_t ws_bytes, void* stream) {
+    if (!qkv || !O) return TP_ERR_NULL;
+    if (b <= 0 || s <= 0 || H <= 0 || d <= 0 || P <= 0 || d % P || (d / P) % 8 || s % 8 ||
+        s > tpk::kKvMaxS || ld_qkv < 3 * H * d || ld_qkv % 8 || ldo < H * d || ldo % 8)
+        return TP_ERR_SHAPE;
+    if (s * ld_qkv * 2 >= kI32 || b * H > kI32 / s) return TP_ERR_SHAPE;
+    if (!ws || ws_bytes < tp_attention_kv_split_workspace(b, s, H, d, P)) return TP_ERR_WORKSPACE;
+    if (!aligned16(qkv) || !aligned16(O) || !aligned16(ws)) return TP_ERR_ALIGN;
+    return launched(tpk::kv_split_attention((const __bf16*)qkv, ld_qkv, (__bf16*)O, ldo, (int)b,
+                                            (int)s, (int)H, (int)d, P, causal != 0, ws,
+                                            as_stream(stream)));
+}
+
 // ---- attention: training forward and backward ----------------------------
 namespace {
 tp_status check_core(int64_t ld_qkv, int64_t b, int64_t s, int64_t H_l, int64_t d) {

@@ -51,6 +51,15 @@ hipError_t gemm_bf16_batched(const GemmBatch& batch, int layout, int epi, int64_
 // caller; groups with M or N of 0 are skipped), common K.
 hipError_t gemm_bf16_grouped(const GemmBatch& batch, int layout, int epi, int64_t ldaux,
                              int64_t K, bool out_bf16, hipStream_t stream);
+
+// Attention with Q, K, V split along the feature dimension over P ranks
+// (kv_split.hip): partial scores per rank, their sum and the softmax, then
+// O = P·V.  (sequence, head) pairs run kKvChunk at a time; rows up to kKvMaxS.
+constexpr int kKvChunk = 16;
+constexpr int kKvMaxS = 8192;
+int64_t kv_split_workspace_bytes(int64_t pairs, int64_t s, int64_t d, int P);
+hipError_t kv_split_attention(const __bf16* qkv, int64_t ld, __bf16* O, int64_t ldo, int b, int s,
+                              int H, int d, int P, bool causal, void* ws, hipStream_t stream);
 // The forward (NN) form: epilogue GELU or NONE.
 hipError_t gemm_bf16_batched(const GemmBatch& batch, int64_t lda, int64_t ldb, int64_t ldc,
                              int64_t M, int64_t N, int64_t K, bool out_bf16, bool gelu,
