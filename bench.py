@@ -126,6 +126,17 @@ def blas_threads():
         return 1
 
 
+def hbm_copy_calibration(torch, dev, stream):
+    """A plain device copy of COPY_BYTES measured in this run: the practical
+    HBM ceiling for a kernel that reads and writes."""
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    ms, _ = event_time(lambda: dst.copy_(src), 5, stream)
+    return {"gbs": round(2 * COPY_BYTES / (ms * 1e-3) / 1e9, 1), "bytes": 2 * COPY_BYTES,
+            "kernel": "torch copy_ of a 1 GiB f32 buffer"}
+
+
 def calibration(tts, torch, X, W, stream, trans_a=False):
     """Two reference points measured on this GPU in this run, for reading the
     roofline fraction: the throughput of a register-only MFMA loop (the
@@ -174,6 +185,8 @@ def dominant_operands_cpu(w, wl):
         _, targets, H, E = wl.vocab_inputs(w)
         Vr = w.V // w.P
         return H, [targets] + [E[r * Vr:(r + 1) * Vr].contiguous() for r in range(w.P)]
+    if w.kind == "kvsplit":
+        return wl.kvsplit_inputs(w), []
     if w.kind == "attn_bwd":
         # the weight-gradient products X^T·dqkv and O^T·dZ (values of the
         # activations dqkv and O do not change their cost)
@@ -193,6 +206,19 @@ def dominant_kernel(w, tts, torch, X, Ws, dev):
     launch; for the MLP shard its GeLU GEMM; for the attention shard its QKV
     projection."""
     M, K = X.shape
+    if w.kind == "kvsplit":
+        # the whole call: the partial-score GEMMs, the sum-and-softmax rows,
+        # the e·V GEMMs and the normalisation; HBM bound (kvsplit_bytes)
+        O = torch.empty(M, w.H * w.d, dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(tts.tp_attention_kv_split_workspace(w.b, w.s, w.H, w.P, w.d),
+                         dtype=torch.uint8, device=dev)
+
+        def launch():
+            tts.tp_attention_kv_split(X, w.b, w.s, w.H, w.P, w.d, True, out=O, ws=ws)
+        name = ("tp_attention_kv_split: %d sequences x %d heads, s=%d, d=%d split over %d ranks "
+                "(partial-score GEMMs, kv_softmax_kernel, e·V GEMMs, kv_normalize_kernel)"
+                % (w.b, w.H, w.s, w.d, w.P))
+        return launch, w.flops(), name
     if w.kind == "vocab":
         # the grouped logits GEMM of all ranks with the cross-entropy-statistics
         # epilogue, as tp_vocab_parallel_ce launches it (its per-rank statistics
@@ -370,6 +396,17 @@ def main():
             tts.tp_partial_sum(parts, out=emb)
             tts.tp_vocab_parallel_ce(x, Es, targets, loss=loss, loss_mean=mean, ws=ce_ws)
         X_k, W_k = x, [targets] + Es
+    elif w.kind == "kvsplit":
+        qkv_cpu = wl.kvsplit_inputs(w)
+        qkv = qkv_cpu.to(dev)
+        M, h = w.M, w.h
+        O = torch.empty(M, w.H * w.d, dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(tts.tp_attention_kv_split_workspace(w.b, w.s, w.H, w.P, w.d),
+                         dtype=torch.uint8, device=dev)
+
+        def step():
+            tts.tp_attention_kv_split(qkv, w.b, w.s, w.H, w.P, w.d, True, out=O, ws=ws)
+        X_k, W_k = qkv, []
     elif w.kind == "attn_bwd":
         X_cpu, Wqkv_cpu, Wo_cpu, dZ_cpu = wl.attn_bwd_inputs(w)
         x, Wqkv0, Wo0, dZ = (t.to(dev) for t in (X_cpu, Wqkv_cpu, Wo_cpu, dZ_cpu))
@@ -441,7 +478,9 @@ def main():
     traffic = counters.get("hbm_bytes_per_launch") if counters else None
     clock = counters.get("shader_clock_ghz") if counters else None
     log(f"dominant kernel: {kern_ms:.3f} ms/launch, {kern_tflops:.1f} TFLOP/s")
-    if w.kind == "vocab":
+    if w.kind == "kvsplit":
+        calib = {"hbm_copy": hbm_copy_calibration(torch, dev, stream)}
+    elif w.kind == "vocab":
         calib = calibration(tts, torch, X_k, W_k[1].t(), stream)
     else:
         calib = calibration(tts, torch, X_k, W_k[0], stream, trans_a=w.kind.endswith("_bwd"))
@@ -601,7 +640,8 @@ def main():
             "frac": round(kern_tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
             "algorithmic_flops_per_launch": kern_flops,
-            "frac_of_mfma_only": round(kern_tflops / calib["mfma_only"]["tflops"], 4),
+            "frac_of_mfma_only": (round(kern_tflops / calib["mfma_only"]["tflops"], 4)
+                                  if "mfma_only" in calib else None),
             # the peak rescaled to the shader clock this kernel runs at under
             # the power limit (GRBM_GUI_ACTIVE over its duration, from the
             # committed counter run of the same launch)
@@ -616,6 +656,17 @@ def main():
         "calibration": calib,
         "components": components,
     }
+    if w.kind == "kvsplit":
+        # HBM bound by construction: the exchange materialises every rank's
+        # partial scores
+        by = w.kvsplit_bytes()
+        gbs = by / (kern_ms * 1e-3) / 1e9
+        result["roofline"] = {
+            "kernel": kern_name, "bound": "hbm", "achieved": round(gbs, 1),
+            "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "traffic": None, "algorithmic_bytes_per_launch": by,
+            "frac_of_copy": round(gbs / calib["hbm_copy"]["gbs"], 4),
+            "avg_launch_ms": round(kern_ms, 4), "launches_timed": len(kern_all)}
     if training is not None:
         result["training"] = training
     print(json.dumps(result), flush=True)
@@ -723,6 +774,23 @@ def cpu_baseline(w, rows_req, env):
         fl = 2 * R * w.h * w.V
         sample = (f"tokens 0..{R - 1}: the embedding lookup and the cross-entropy of all {w.P} "
                   f"ranks; {fl / 1e12:.3f} TFLOP")
+    elif w.kind == "kvsplit":
+        n = min(96, w.b * w.H)                      # about 10 s of host time
+        qkv_cpu = env["qkv_cpu"]
+        HD = w.H * w.d
+        log(f"oracle: K/V-split attention of {n} (sequence, head) pairs")
+        t0 = time.time()
+        for pair in range(n):
+            rows = slice((pair // w.H) * w.s, (pair // w.H + 1) * w.s)
+            hd = pair % w.H
+            oracle.attention_kv_split(qkv_cpu[rows, hd * w.d:(hd + 1) * w.d],
+                                      qkv_cpu[rows, HD + hd * w.d:HD + (hd + 1) * w.d],
+                                      qkv_cpu[rows, 2 * HD + hd * w.d:2 * HD + (hd + 1) * w.d],
+                                      w.P, True)
+        dt = time.time() - t0
+        fl = n * 4 * w.d * w.s * (w.s + 1) // 2
+        sample = (f"{n} (sequence, head) pairs, all {w.P} ranks' partial scores, the softmax and "
+                  f"the output slices; {fl / 1e12:.4f} TFLOP counted as on the GPU")
     elif w.kind == "attn_bwd":
         # whole sequences: the backward of a causal sequence involves all of it
         R = min(rows_req, w.s)

@@ -19,7 +19,7 @@ from . import normal, fan_in_sigma, rank_seed
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str            # "mlp" | "attn" | "block" | "mlp_bwd" | "attn_bwd" | "vocab"
+    kind: str            # "mlp" | "attn" | "block" | "mlp_bwd" | "attn_bwd" | "vocab" | "kvsplit"
     seed: int
     P: int               # tensor-parallel degree
     b: int
@@ -66,6 +66,17 @@ class Workload:
         return {"qkv": 2 * f["qkv"], "core": core, "wo": 2 * f["wo"],
                 "total": 2 * f["qkv"] + core + 2 * f["wo"]}
 
+    def kvsplit_bytes(self) -> int:
+        """Minimum HBM bytes of the K/V-split attention under the causal mask:
+        every rank's f32 partial scores of the visible (query, key) pairs
+        written once (the exchange's message) and read once, the bf16 softmax
+        weights of those pairs written and read, Q, K, V read and O written
+        (the kernels move more: whole 256x256 score tiles on the diagonal and
+        whole weight rows)."""
+        s, pairs, vis = self.s, self.b * self.H, self.s * (self.s + 1) // 2
+        per = 2 * 4 * self.P * vis + 2 * 2 * vis + 2 * 4 * s * self.d
+        return pairs * per
+
     def flops(self) -> int:
         """Matrix FLOPs of one call of the workload's entry point."""
         if self.kind == "mlp":
@@ -79,6 +90,11 @@ class Workload:
             return self.attn_bwd_flops_rank()["total"]
         if self.kind == "vocab":
             return 2 * self.M * self.h * self.V       # the logits H·E^T of all ranks
+        if self.kind == "kvsplit":
+            # the attention's matrix FLOPs, as for the head-sharded core: 4·d
+            # per visible (query, key) pair and head (the ranks' partial
+            # scores together make up Q·K^T)
+            return 4 * self.H * self.d * self.b * self.s * (self.s + 1) // 2
         return self.P * (self.mlp_flops_rank() + self.attn_flops_rank()["total"])
 
 
@@ -104,6 +120,12 @@ WORKLOADS = {w.name: w for w in [
              description="bf16 vocab-parallel ends at the 175B layer shape, all 8 ranks of tp=8: "
                          "embedding lookup of 16384 tokens and the stable cross-entropy over "
                          "V = 51200 (GPT-3's 50257 padded to a multiple of 128·8), table tied"),
+    Workload("kvsplit_bf16_h4096_tp4", "kvsplit", 1008, P=4, b=4, s=2048, h=4096, H=32,
+             all_ranks=True,
+             description="bf16 causal self-attention with Q, K, V split along the feature "
+                         "dimension over tp=4 (32 of each head's 128 features per rank, the "
+                         "ranks' partial scores summed before the softmax), all 4 ranks: 4 "
+                         "sequences of 2048, 32 heads, the head-sharded tp=4 attention shape"),
     Workload("block_bf16_h12288_tp8", "block", 1004, P=8, b=8, s=2048, h=12288, H=96, F=49152,
              all_ranks=True,
              description="bf16 pre-LN block at the 175B layer shape, all 8 ranks of tp=8 in turn"),
@@ -159,6 +181,12 @@ def attn_bwd_inputs(w: Workload):
     X, Wqkv, Wo = attn_inputs(w)
     dZ = normal((w.M, w.h), 1.0, w.seed, "dZ", w.dtype)
     return X, Wqkv, Wo, dZ
+
+
+def kvsplit_inputs(w: Workload):
+    """The fused projection qkv [M, 3·H·d] ~ N(0, 1) (the entries of X·W_qkv
+    for X ~ N(0, 1) and W ~ N(0, 1/h)), on the CPU."""
+    return normal((w.M, 3 * w.H * w.d), 1.0, w.seed, "x", w.dtype)
 
 
 def vocab_inputs(w: Workload):

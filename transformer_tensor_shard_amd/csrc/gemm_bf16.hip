@@ -235,6 +235,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
                                        (batch.N[0] + BN - 1) / BN, grp, tm, tn)
                    : !tile_coords(blockIdx.x, batch, grp, tm, tn))
         return;
+    static_assert(BM == BN, "skip_upper compares tile indices");
+    if (batch.skip_upper && tn > tm) return;     // n0 >= m0 + BM
     const int M = batch.M[grp], N = batch.N[grp];
     const int64_t lda = batch.lda[grp], ldb = batch.ldb[grp], ldc = batch.ldc[grp];
     const int m0 = tm * BM, n0 = tn * BN;

@@ -7,7 +7,9 @@
 // its feature slice of the output, O[:, F_r] = softmax(S/sqrt(d) + mask)·V_r.
 // On one GPU, per (sequence, head) pair:
 //  * the P partial-score products are NT GEMMs with K = d/P (f32 out, one
-//    [s, s] matrix per rank), in grouped launches;
+//    [s, s] matrix per rank), in grouped launches; under the causal mask the
+//    256x256 tiles that lie wholly past the diagonal are skipped (no query
+//    reads them);
 //  * kv_softmax_kernel sums a query row's P partial rows in rank order,
 //    scales, masks, and writes the unnormalised weights e = 2^(x - max) in
 //    bf16 (the largest is exactly 1) and the sum of those same rounded
@@ -145,6 +147,7 @@ hipError_t kv_split_attention(const __bf16* qkv, int64_t ld, __bf16* O, int64_t 
         const int n = pairs - p0 < kKvChunk ? pairs - p0 : kKvChunk;
         // the partial scores of every rank of the chunk's pairs
         GemmBatch gb = {};
+        gb.skip_upper = causal ? 1 : 0;
         for (int k = 0; k < n * P; ++k) {
             const int i = k / P, r = k % P, pair = p0 + i;
             const int64_t seq = (int64_t)(pair / H) * s * ld, head = (int64_t)(pair % H) * d;
@@ -161,6 +164,7 @@ hipError_t kv_split_attention(const __bf16* qkv, int64_t ld, __bf16* O, int64_t 
                 if (hipError_t e = gemm_bf16_grouped(gb, GEMM_NT, EPI_NONE, 0, w, false, stream))
                     return e;
                 gb = GemmBatch{};
+                gb.skip_upper = causal ? 1 : 0;
             }
         }
         hipLaunchKernelGGL(kv_softmax_kernel, dim3((unsigned)(n * (int64_t)s)), dim3(256), 0,
