@@ -235,8 +235,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
                                        (batch.N[0] + BN - 1) / BN, grp, tm, tn)
                    : !tile_coords(blockIdx.x, batch, grp, tm, tn))
         return;
-    static_assert(BM == BN, "skip_upper compares tile indices");
-    if (batch.skip_upper && tn > tm) return;     // n0 >= m0 + BM
     const int M = batch.M[grp], N = batch.N[grp];
     const int64_t lda = batch.lda[grp], ldb = batch.ldb[grp], ldc = batch.ldc[grp];
     const int m0 = tm * BM, n0 = tn * BN;
@@ -310,7 +308,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
                 br, LDS_PTR(void, sb + j * 1024), 16,
                 (!CHECK_K || !B_KC || k0 + kc_kpos(lane, j) < K) ? b_off[j] : OOB, 0, 0, 0);
     };
-    const int nk = (K + BK - 1) / BK;
+    // with a lower-triangular A only the K steps up to the tile's last row
+    // contribute (causal_k); the loop and the tail handling see a shorter K
+    const int nk_all = (K + BK - 1) / BK;
+    const int nk = batch.causal_k ? min(nk_all, (m0 + BM + BK - 1) / BK) : nk_all;
 
     // ---- LDS -> register operand addresses (MFMA 16x16x32) -------------------
     // An MFMA operand block: lane holds row/column (lane & 15) of 16 and the K

@@ -6,10 +6,10 @@
 // ranks (the softmax is not linear, so the sum comes first), and rank r forms
 // its feature slice of the output, O[:, F_r] = softmax(S/sqrt(d) + mask)·V_r.
 // On one GPU, per (sequence, head) pair:
-//  * the P partial-score products are NT GEMMs with K = d/P (f32 out, one
-//    [s, s] matrix per rank), in grouped launches; under the causal mask the
-//    256x256 tiles that lie wholly past the diagonal are skipped (no query
-//    reads them);
+//  * kv_scores_kernel forms the P partial-score products, K = d/P (f32 out,
+//    one [s, s] matrix per rank), operands loaded straight into registers;
+//    under the causal mask the 128x128 tiles that lie wholly past the
+//    diagonal are skipped (no query reads them);
 //  * kv_softmax_kernel sums a query row's P partial rows in rank order,
 //    scales, masks, and writes the unnormalised weights e = 2^(x - max) in
 //    bf16 (the largest is exactly 1) and the sum of those same rounded
@@ -17,7 +17,9 @@
 //  * O = e·V is one NN GEMM per pair with N = d (f32 out): its column block
 //    F_r is exactly rank r's product with V_r (each output column depends
 //    only on its own column of V), so the ranks' slices are formed side by
-//    side; kv_normalize_kernel divides each row by its sum and rounds to
+//    side (under the causal mask a row tile's K loop stops at its last row:
+//    the weights past the diagonal are zero); kv_normalize_kernel divides
+//    each row by its sum and rounds to
 //    bf16 once.  The weights applied to V thus sum to one exactly, as in the
 //    head-sharded attention kernel.
 // Pairs are processed in chunks of kKvChunk, the workspace holding one
@@ -49,9 +51,86 @@ __device__ __forceinline__ float wg_reduce(float v, float* red, bool is_max) {
     return t;
 }
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+constexpr unsigned KV_OOB = 0x80000000u;     // buffer offset past any range: reads 0
+
+// Partial scores of a small feature slice: S_r = Q_r·K_r^T, [s, s] f32 per
+// (chunk pair, rank), w = d/P <= 128 features.  One workgroup of 4 waves per
+// 128x128 tile (wave: 64 query rows x 64 keys as 4x4 MFMA 16x16x32 blocks).
+// With a K of one to four 32-wide steps there is nothing to stage: each lane
+// loads its MFMA operand fragments (16 bytes of one row) straight from
+// memory, features past w read as zeros, and the f32 tile is stored from the
+// accumulators with the non-temporal hint.  No LDS, so several workgroups
+// share a CU and their stores overlap.  Under the causal mask a tile wholly
+// past the diagonal is not computed (no query reads it).
+__global__ __launch_bounds__(256) void kv_scores_kernel(const __bf16* __restrict__ qkv, int64_t ld,
+                                                        int s, int H, int d, int P, int pair0,
+                                                        int causal, float* __restrict__ parts)
+{
+    const int ntiles = (s + 127) / 128;           // a ragged last tile is bounds-checked
+    const int64_t id = blockIdx.x;
+    const int tn = (int)(id % ntiles), tm = (int)((id / ntiles) % ntiles);
+    const int64_t k = id / ((int64_t)ntiles * ntiles);      // chunk pair * P + rank
+    if (causal && tn > tm) return;
+    const int i = (int)(k / P), r = (int)(k % P), pair = pair0 + i;
+    const int w = d / P;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int m0 = tm * 128 + (wv >> 1) * 64, n0 = tn * 128 + (wv & 1) * 64;
+    const __bf16* base = qkv + (int64_t)(pair / H) * s * ld + (int64_t)(pair % H) * d + r * w;
+    const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<__bf16*>(base), (short)0, (int)((int64_t)s * ld * 2 < 0x7ffffff0 ? (int64_t)s * ld * 2 : 0x7ffffff0), 0x00020000);
+    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<__bf16*>(base + (int64_t)H * d), (short)0,
+        (int)((int64_t)s * ld * 2 < 0x7ffffff0 ? (int64_t)s * ld * 2 : 0x7ffffff0), 0x00020000);
+    typedef float f32x4v __attribute__((ext_vector_type(4)));
+    f32x4v acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
+    const int kq = 8 * (lane >> 4);                // this lane's 8 features of a 32-wide step
+    for (int k0 = 0; k0 < w; k0 += 32) {
+        const bool in_k = k0 + kq < w;
+        bf16x8 fa[4], fb[4];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            const int row = m0 + 16 * a + (lane & 15);
+            const unsigned off = (in_k && row < s) ? (unsigned)(((int64_t)row * ld + k0 + kq) * 2) : KV_OOB;
+            fa[a] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qr, off, 0, 0));
+        }
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int key = n0 + 16 * b + (lane & 15);
+            const unsigned off = (in_k && key < s) ? (unsigned)(((int64_t)key * ld + k0 + kq) * 2) : KV_OOB;
+            fb[b] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(kr, off, 0, 0));
+        }
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[a], fb[b], acc[a][b], 0, 0, 0);
+    }
+    // lane holds key (lane & 15) and query rows 4·(lane >> 4) + e of each block
+    const int64_t ss = (int64_t)s * s;
+    float* out = parts + k * ss;
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int row = m0 + 16 * a + 4 * (lane >> 4) + e;
+            if (row >= s) continue;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const int key = n0 + 16 * b + (lane & 15);
+                if (key < s) __builtin_nontemporal_store(acc[a][b][e], out + (int64_t)row * s + key);
+            }
+        }
+}
+
 // One workgroup per query row t of chunk pair p: parts [n][P][s][s] f32,
 // weights [n][s][s] bf16, rowsum [n][s] f32.  Keys past the diagonal
 // (causal) are neither read nor given weight.
+template <int PT>   // the rank count when known at compile time (loads all in flight), else 0
 __global__ __launch_bounds__(256) void kv_softmax_kernel(const float* __restrict__ parts, int P,
                                                          int s, int causal, float scale_log2,
                                                          __bf16* __restrict__ probs,
@@ -72,7 +151,14 @@ __global__ __launch_bounds__(256) void kv_softmax_kernel(const float* __restrict
         acc[i] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
         if (c >= nv || (causal && 4 * c > t)) continue;
         f32x4 v = __builtin_nontemporal_load((const f32x4*)base + c);
-        for (int r = 1; r < P; ++r) v += __builtin_nontemporal_load((const f32x4*)(base + r * ss) + c);
+        if constexpr (PT > 0) {
+#pragma unroll
+            for (int r = 1; r < PT; ++r)
+                v += __builtin_nontemporal_load((const f32x4*)(base + r * ss) + c);
+        } else {
+            for (int r = 1; r < P; ++r)
+                v += __builtin_nontemporal_load((const f32x4*)(base + r * ss) + c);
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const bool keep = !causal || 4 * c + e <= t;
@@ -146,30 +232,20 @@ hipError_t kv_split_attention(const __bf16* qkv, int64_t ld, __bf16* O, int64_t 
     for (int p0 = 0; p0 < pairs; p0 += kKvChunk) {
         const int n = pairs - p0 < kKvChunk ? pairs - p0 : kKvChunk;
         // the partial scores of every rank of the chunk's pairs
-        GemmBatch gb = {};
-        gb.skip_upper = causal ? 1 : 0;
-        for (int k = 0; k < n * P; ++k) {
-            const int i = k / P, r = k % P, pair = p0 + i;
-            const int64_t seq = (int64_t)(pair / H) * s * ld, head = (int64_t)(pair % H) * d;
-            const int g = gb.count++;
-            gb.A[g] = qkv + seq + head + r * w;
-            gb.B[g] = qkv + seq + HD + head + r * w;
-            gb.C[g] = parts + (int64_t)k * ss;
-            gb.M[g] = s;
-            gb.N[g] = s;
-            gb.lda[g] = ld;
-            gb.ldb[g] = ld;
-            gb.ldc[g] = s;
-            if (gb.count == kMaxBatch || k + 1 == n * P) {
-                if (hipError_t e = gemm_bf16_grouped(gb, GEMM_NT, EPI_NONE, 0, w, false, stream))
-                    return e;
-                gb = GemmBatch{};
-                gb.skip_upper = causal ? 1 : 0;
-            }
-        }
-        hipLaunchKernelGGL(kv_softmax_kernel, dim3((unsigned)(n * (int64_t)s)), dim3(256), 0,
-                           stream, (const float*)parts, P, s, causal ? 1 : 0, scale_log2, probs,
-                           rowsum);
+        const int64_t ntiles = (s + 127) / 128;
+        hipLaunchKernelGGL(kv_scores_kernel, dim3((unsigned)(n * (int64_t)P * ntiles * ntiles)),
+                           dim3(256), 0, stream, qkv, ld, s, H, d, P, p0, causal ? 1 : 0, parts);
+        if (hipError_t e = hipGetLastError()) return e;
+        const dim3 rows_grid((unsigned)(n * (int64_t)s));
+#define TP_KVS(PT) hipLaunchKernelGGL(kv_softmax_kernel<PT>, rows_grid, dim3(256), 0, stream, \
+                                      (const float*)parts, P, s, causal ? 1 : 0, scale_log2, \
+                                      probs, rowsum)
+        if (P == 1) TP_KVS(1);
+        else if (P == 2) TP_KVS(2);
+        else if (P == 4) TP_KVS(4);
+        else if (P == 8) TP_KVS(8);
+        else TP_KVS(0);
+#undef TP_KVS
         if (hipError_t e = hipGetLastError()) return e;
         // e·V per pair, all ranks' feature slices side by side, then the
         // division by the row sums
@@ -187,6 +263,7 @@ hipError_t kv_split_attention(const __bf16* qkv, int64_t ld, __bf16* O, int64_t 
             pv.ldc[i] = d;
         }
         pv.count = n;
+        pv.causal_k = causal ? 1 : 0;       // weights are zero past the diagonal
         if (hipError_t e = gemm_bf16_grouped(pv, GEMM_NN, EPI_NONE, 0, s, false, stream)) return e;
         const int64_t units = (int64_t)n * s * (d / 4);
         hipLaunchKernelGGL(kv_normalize_kernel, dim3((unsigned)((units + 255) / 256)), dim3(256), 0,

@@ -38,8 +38,8 @@ struct GemmBatch {
     int vstart[kMaxBatch];    // CE_STATS: first vocab id of group g's columns
     int count;
     int band;       // set by the launcher: tile order for groups sharing A
-    int skip_upper; // tiles whose every column lies past every row (n0 >= m0 + 256) are
-                    // not computed: causal scores that no query reads
+    int causal_k;   // A is zero past its diagonal (A[m][k] = 0 for k > m, NN layout): a
+                    // tile's K loop stops after its last row (only zero terms are dropped)
 };
 // Supported (layout, epilogue, output) combinations: NN with NONE / GELU
 // (bf16 or f32) and DUAL (bf16); NT with NONE / GELU_BWD (bf16 or f32) and
