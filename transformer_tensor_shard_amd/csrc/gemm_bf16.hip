@@ -90,17 +90,25 @@ constexpr int LOADS = 4;                      // A (and B) loads per wave per K 
 // Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
 constexpr int SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100;
 
+// MFMAs of a k-step over which its V direct-to-LDS loads are spread.  The
+// loads go out early, over the first 20 of the 32 MFMAs (measured on the
+// three forward GEMMs of the block at the 175B layer shape: +2% over spreading
+// them across all 32; over the first 8, 12 or 16 or the last 16 it was
+// slower).
+constexpr int DMA_WINDOW = 20;
+
 // One 32-wide k-step of a wave: 32 MFMAs (A block mi = I/4 against the 4 B
 // blocks); the next k-step's B reads (DB LDS instructions per block) go out
 // over the first 8 MFMAs and each A block's reload (DA instructions) right
-// after its last MFMA; V direct-to-LDS loads are spread one per 32/V MFMAs.
+// after its last MFMA; V direct-to-LDS loads are spread evenly over the
+// first DMA_WINDOW MFMAs.
 template <int V, int DA, int DB, int I>
 __device__ __forceinline__ void sched_step() {
     __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
     constexpr int nb = I < 8 ? ((I + 1) * 4 * DB) / 8 - (I * 4 * DB) / 8 : 0;
     constexpr int nds = nb + (I % 4 == 3 ? DA : 0);
     if constexpr (nds > 0) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, nds, 0);
-    constexpr int nv = ((I + 1) * V) / 32 - (I * V) / 32;
+    constexpr int nv = I < DMA_WINDOW ? ((I + 1) * V) / DMA_WINDOW - (I * V) / DMA_WINDOW : 0;
     if constexpr (nv > 0) __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, nv, 0);
     if constexpr (I + 1 < 32) sched_step<V, DA, DB, I + 1>();
 }
