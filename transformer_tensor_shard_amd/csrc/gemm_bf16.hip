@@ -19,10 +19,7 @@
 // cross-entropy statistics of vocab-parallel logits (per row and column tile
 // the maximum and the exp-sum, plus the target's logit; no logits stored).
 //
-// Design: 256x256 output tiles, computed by workgroups of 8 waves (two per
-// SIMD); in the NN and NT layouts one persistent workgroup per CU loops over
-// its tiles and, when the epilogue leaves LDS idle, loads the next tile's
-// first K tile while the current tile's stores go out.
+// Design: one 256x256 output tile per workgroup of 8 waves (two per SIMD).
 //  * wave w owns a 128x64 sub-tile: rows 128*((w&3)>>1), columns
 //    128*(w&1) + 64*(w>>2); that is 8x4 MFMA 16x16x32 bf16 blocks with 128
 //    f32 accumulators per lane.  The two waves on a SIMD (w and w+4) take the
@@ -54,11 +51,9 @@
 //    (workgroups are dealt round-robin to the 8 XCDs, each with its own L2)
 //    and walk the output in groups of 4 tile-rows; a grouped launch whose
 //    groups share the activations walks row bands across all groups;
-//  * epilogue: a plain f32 tile is stored straight from the accumulators (64-byte
-//    row segments, no LDS, no barrier); a bf16 tile, and the epilogues that
-//    read a second operand or reduce along rows, are staged through the (then
-//    idle) LDS and written with 16-byte row-contiguous stores.  All output
-//    stores carry the non-temporal hint (they stream past the L2).
+//  * epilogue: every output tile is staged through the (then idle) LDS and
+//    written with 16-byte row-contiguous stores; all output stores carry the
+//    non-temporal hint (they stream past the L2);
 //
 // Measured on MI355X (rocprofv3 counters, GeLU GEMM at the 175B layer shape):
 // the shader clock settles at ~1.7 GHz under the power limit and the matrix
@@ -230,18 +225,9 @@ __device__ __forceinline__ int kc_kpos(int lane, int j) {
 template <typename T>
 __device__ __forceinline__ void st_out(T v, T* p) { __builtin_nontemporal_store(v, p); }
 
-// Which variants run persistent workgroups (one per CU, each looping over
-// tiles): the NN and NT layouts without a K tail.  Measured at the 175B layer
-// shape: the W_o product (K = 1536, f32 out) +2.7%, the NT input-gradient
-// product +1%, the long-K NN products unchanged; the TN weight-gradient
-// products were 1.7% slower, and the K-tail variants spill in a loop.
-__host__ __device__ constexpr bool persistent_variant(int layout, bool check_k) {
-    return !check_k && layout != GEMM_TN;
-}
-
 template <int LAYOUT, int EPI, bool OUT_BF16, bool CHECK_K>
 __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
-    GemmBatch batch, int64_t ldaux, int K, int npids)
+    GemmBatch batch, int64_t ldaux, int K)
 {
     constexpr bool A_MC = LAYOUT == GEMM_TN;    // A stored [K,M]: M contiguous
     constexpr bool B_KC = LAYOUT == GEMM_NT;    // B stored [N,K]: K contiguous
@@ -251,25 +237,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
     __shared__ __attribute__((aligned(1024))) char lds0[STAGE_BYTES];
     __shared__ __attribute__((aligned(1024))) char lds1[STAGE_BYTES];
 
-    // Persistent: workgroup w computes the tiles of ids w, w + gridDim.x, ...
-    // below npids (gridDim.x is a multiple of 8, so every id keeps w's XCD);
-    // ids that map to no tile are skipped.  Every wave of the workgroup walks
-    // the same ids, so all of them leave the loop together.  The variants
-    // that are not persistent (persistent_variant) are launched with one
-    // workgroup per id and run the body once.
-    auto coords = [&](int pid, int& g, int& m, int& n) -> bool {
-        return batch.band ? tile_coords_band(pid, batch.count, (batch.M[0] + BM - 1) / BM,
-                                             (batch.N[0] + BN - 1) / BN, g, m, n)
-                          : tile_coords(pid, batch, g, m, n);
-    };
-    // the f32 epilogue stores straight from the accumulators and leaves LDS
-    // idle: the next tile's first K tile is loaded while its stores go out
-    constexpr bool PERSISTENT = persistent_variant(LAYOUT, CHECK_K);
-    constexpr bool PREFETCH = PERSISTENT && !OUT_BF16 && EPI == EPI_NONE;
-    bool prefetched = false;
-    for (int pid = blockIdx.x; pid < npids; pid += gridDim.x) {
     int grp, tm, tn;
-    if (!coords(pid, grp, tm, tn)) continue;
+    if (batch.band ? !tile_coords_band(blockIdx.x, batch.count, (batch.M[0] + BM - 1) / BM,
+                                       (batch.N[0] + BN - 1) / BN, grp, tm, tn)
+                   : !tile_coords(blockIdx.x, batch, grp, tm, tn))
+        return;
     const int M = batch.M[grp], N = batch.N[grp];
     const int64_t lda = batch.lda[grp], ldb = batch.ldb[grp], ldc = batch.ldc[grp];
     const int m0 = tm * BM, n0 = tn * BN;
@@ -279,11 +251,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
     void* __restrict__ C = batch.C[grp];
     __bf16* aux = batch.aux[grp];
 
-    // re-derived every tile: the per-lane addresses below then live only
-    // within one tile instead of being hoisted out of the tile loop, which
-    // would hold them in registers across the K loop
-    int tid = threadIdx.x;
-    asm volatile("" : "+v"(tid));
+    const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int wm = (wid & 3) >> 1, wn = wid & 1, wh = wid >> 2;
@@ -421,7 +389,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
         }
     };
 
-    if (!prefetched) dma_tile(0, lds0);
+    dma_tile(0, lds0);
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's DMA has landed
     __syncthreads();
     dma_tile(BK, lds1);
@@ -449,50 +417,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
 
-    prefetched = false;
-    if constexpr (PREFETCH) {
-        // the first K tile of this workgroup's next tile, into stage 0 (the
-        // loads past the last K tile above have landed; stage 0 is free)
-        int g2, tm2, tn2, pid2 = pid + gridDim.x;
-        bool ok = false;
-        for (; pid2 < npids; pid2 += gridDim.x)
-            if (coords(pid2, g2, tm2, tn2)) { ok = true; break; }
-        if (ok) {
-            const int M2 = batch.M[g2], N2 = batch.N[g2];
-            const int64_t lda2 = batch.lda[g2], ldb2 = batch.ldb[g2];
-            const int m2 = tm2 * BM, n2 = tn2 * BN;
-            const __bf16* a2 = A_MC ? batch.A[g2] + m2 : batch.A[g2] + (int64_t)m2 * lda2;
-            const __bf16* b2 = B_KC ? batch.B[g2] + (int64_t)n2 * ldb2 : batch.B[g2] + n2;
-            const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(
-                const_cast<__bf16*>(a2), (short)0, 0x7ffffff0, 0x00020000);
-            const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
-                const_cast<__bf16*>(b2), (short)0, 0x7ffffff0, 0x00020000);
-#pragma unroll
-            for (int j = 0; j < LOADS; ++j) {
-                const int r = 32 * wid + 8 * j + (lane >> 3);
-                const int u = (lane & 7) ^ ((r >> 1) & 7);
-                const int kr = 8 * wid + 2 * j + (lane >> 5);
-                const int ub = (lane & 31) ^ mc_swz(kr);
-                const unsigned ao = A_MC ? ((m2 + ub * 8) < M2 ? (unsigned)(kr * lda2 + ub * 8) * 2u : OOB)
-                                         : ((m2 + r) < M2 ? (unsigned)(r * lda2 + u * 8) * 2u : OOB);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    ar, LDS_PTR(void, lds0 + wid * 4096 + j * 1024), 16, ao, 0, 0, 0);
-            }
-#pragma unroll
-            for (int j = 0; j < LOADS; ++j) {
-                const int r = 32 * wid + 8 * j + (lane >> 3);
-                const int u = (lane & 7) ^ ((r >> 1) & 7);
-                const int kr = 8 * wid + 2 * j + (lane >> 5);
-                const int ub = (lane & 31) ^ mc_swz(kr);
-                const unsigned bo = B_KC ? ((n2 + r) < N2 ? (unsigned)(r * ldb2 + u * 8) * 2u : OOB)
-                                         : ((n2 + ub * 8) < N2 ? (unsigned)(kr * ldb2 + ub * 8) * 2u : OOB);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    br, LDS_PTR(void, lds0 + A_BYTES + wid * 4096 + j * 1024), 16, bo, 0, 0, 0);
-            }
-            prefetched = true;
-        }
-    }
-
     // ---- epilogue ------------------------------------------------------------
     // Lane holds column (lane & 15) and rows 4*(lane >> 4) + i of each 16x16
     // block.  Staged rows r and r+4, r+8, r+12 (one store instruction) get
@@ -506,38 +430,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
         const float v = acc[mi][nj][r] + bv[nj];
         return EPI == EPI_GELU ? gelu(v) : v;
     };
-    if constexpr (!OUT_BF16 && EPI == EPI_NONE) {
-        // f32 tiles go from the accumulators straight to memory: one store
-        // instruction writes four 64-byte row segments (16 lanes x 4 B each),
-        // the neighbouring column block fills the other half of each 128-byte
-        // line.  No LDS staging and no barrier: the stores drain while the
-        // next workgroup on this CU starts its K loop.
-        float* __restrict__ Cf = (float*)C;
-        const int gr0 = m0 + wm * 128 + 4 * (lane >> 4);
-        const int gc0 = n0 + lcol;
-        if (m0 + BM <= M && n0 + BN <= N) {
-#pragma unroll
-            for (int mi = 0; mi < NI; ++mi)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float* row = Cf + (int64_t)(gr0 + mi * 16 + r) * ldc + gc0;
-#pragma unroll
-                    for (int nj = 0; nj < NJ; ++nj) st_out(value(mi, nj, r), &row[16 * nj]);
-                }
-        } else {
-#pragma unroll
-            for (int mi = 0; mi < NI; ++mi)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int gr = gr0 + mi * 16 + r;
-                    if (gr >= M) continue;
-                    float* row = Cf + (int64_t)gr * ldc + gc0;
-#pragma unroll
-                    for (int nj = 0; nj < NJ; ++nj)
-                        if (gc0 + 16 * nj < N) st_out(value(mi, nj, r), &row[16 * nj]);
-                }
-        }
-    } else if constexpr (OUT_BF16 && (EPI == EPI_NONE || EPI == EPI_GELU)) {
+    if constexpr (OUT_BF16 && (EPI == EPI_NONE || EPI == EPI_GELU)) {
         char* half = wm ? lds1 : lds0;
 #pragma unroll
         for (int nj = 0; nj < NJ; ++nj) {
@@ -563,8 +456,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
                 st_out(*(const bf16x8*)src, (bf16x8*)((__bf16*)C + (int64_t)grow * ldc + gcol));
         }
     } else {
-        // f32 staging in two passes of 64 rows per half; the store phase applies
-        // the element-wise epilogues that need a second operand or output
+        // f32 staging in two passes of 64 rows per half; the store phase writes
+        // 1 KiB of one row per store instruction and applies the element-wise
+        // epilogues that need a second operand or output.  (Storing a plain
+        // f32 tile straight from the accumulators, four 64-byte row segments
+        // per instruction, wrote at ~3.1 TB/s against ~5.6 TB/s staged, at
+        // K = 64 where the writes bound the launch: staging is +3.9% on the
+        // W_o product, K = 1536, and +1.1% on the row product, K = 6144.)
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
             char* half = wm ? lds1 : lds0;
@@ -650,25 +548,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
             if (p == 0) __syncthreads();
         }
     }
-    __syncthreads();      // the epilogue's LDS reads are done before the next tile's loads
-    if constexpr (!PERSISTENT) break;   // launched with one workgroup per tile id
-    }
-}
-
-// Workgroups of a persistent launch: one per compute unit of the current
-// device (a multiple of 8, the XCD count), cached per device.
-int persistent_workgroups() {
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
-        int cus = 0;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            cus < 8)
-            cus = 256;
-        cached[dev] = cus / 8 * 8;
-    }
-    return cached[dev];
 }
 
 }  // namespace
@@ -686,18 +565,16 @@ hipError_t launch(const GemmBatch& b, int layout, int epi, int64_t ldaux, int64_
             per_xcd += (((b.M[g] + BM - 1) / BM) * ((b.N[g] + BN - 1) / BN) + 7) / 8;
     }
     if (per_xcd == 0) return hipSuccess;
-    const int npids = 8 * per_xcd;
+    const dim3 grid(8 * per_xcd), block(NTHREADS);
     const bool ck = (K % BK) != 0;
-    const dim3 grid(persistent_variant(layout, ck) ? std::min(npids, persistent_workgroups())
-                                                   : npids), block(NTHREADS);
 #define TP_GEMM(L, E, OB)                                                                      \
     do {                                                                                       \
         if (ck)                                                                                \
             hipLaunchKernelGGL((gemm_bf16_kernel<L, E, OB, true>), grid, block, 0, stream, b,  \
-                               ldaux, (int)K, npids);                                          \
+                               ldaux, (int)K);                                                 \
         else                                                                                   \
             hipLaunchKernelGGL((gemm_bf16_kernel<L, E, OB, false>), grid, block, 0, stream, b, \
-                               ldaux, (int)K, npids);                                          \
+                               ldaux, (int)K);                                                 \
         return hipGetLastError();                                                              \
     } while (0)
     switch (layout) {
