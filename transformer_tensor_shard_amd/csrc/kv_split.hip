@@ -59,10 +59,11 @@ constexpr unsigned KV_OOB = 0x80000000u;     // buffer offset past any range: re
 // 128x128 tile (wave: 64 query rows x 64 keys as 4x4 MFMA 16x16x32 blocks).
 // With a K of one to four 32-wide steps there is nothing to stage: each lane
 // loads its MFMA operand fragments (16 bytes of one row) straight from
-// memory, features past w read as zeros, and the f32 tile is stored from the
-// accumulators with the non-temporal hint.  No LDS, so several workgroups
-// share a CU and their stores overlap.  Under the causal mask a tile wholly
-// past the diagonal is not computed (no query reads it).
+// memory, features past w read as zeros, and each wave's f32 block is staged
+// through 8 KiB of LDS (32 KiB per workgroup, so several workgroups share a
+// CU and their stores overlap) and stored with the non-temporal hint in whole
+// 256-byte row segments.  Under the causal mask a tile wholly past the
+// diagonal is not computed (no query reads it).
 __global__ __launch_bounds__(256) void kv_scores_kernel(const __bf16* __restrict__ qkv, int64_t ld,
                                                         int s, int H, int d, int P, int pair0,
                                                         int causal, float* __restrict__ parts)
@@ -72,6 +73,7 @@ __global__ __launch_bounds__(256) void kv_scores_kernel(const __bf16* __restrict
     const int tn = (int)(id % ntiles), tm = (int)((id / ntiles) % ntiles);
     const int64_t k = id / ((int64_t)ntiles * ntiles);      // chunk pair * P + rank
     if (causal && tn > tm) return;
+    __shared__ __attribute__((aligned(16))) char stage[4][32 * 256];
     const int i = (int)(k / P), r = (int)(k % P), pair = pair0 + i;
     const int w = d / P;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -110,21 +112,44 @@ __global__ __launch_bounds__(256) void kv_scores_kernel(const __bf16* __restrict
             for (int b = 0; b < 4; ++b)
                 acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[a], fb[b], acc[a][b], 0, 0, 0);
     }
-    // lane holds key (lane & 15) and query rows 4·(lane >> 4) + e of each block
+    // Lane holds key (lane & 15) and query rows 4·(lane >> 4) + e of each
+    // block.  The wave's 64x64 f32 block goes out through its own 8 KiB of
+    // LDS in two passes of 32 rows, so that each store instruction writes four
+    // whole 256-byte row segments (storing from the accumulators wrote 64-byte
+    // segments, half of a 128-byte line each, at about half the write rate).
+    // The 16-byte unit of a staged row is XOR-ed with bits 2-3 of the row:
+    // the four row groups of one LDS write then hit distinct banks.  s % 8 == 0,
+    // so a unit's four keys are all inside or all past the row's end.
     const int64_t ss = (int64_t)s * s;
     float* out = parts + k * ss;
+    char* const st = stage[wv];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int p = 0; p < 2; ++p) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int row = m0 + 16 * a + 4 * (lane >> 4) + e;
-            if (row >= s) continue;
+        for (int a2 = 0; a2 < 2; ++a2)
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const int key = n0 + 16 * b + (lane & 15);
-                if (key < s) __builtin_nontemporal_store(acc[a][b][e], out + (int64_t)row * s + key);
+            for (int e = 0; e < 4; ++e) {
+                const int rl = 16 * a2 + 4 * (lane >> 4) + e;      // row within the pass
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const int unit = 4 * b + ((lane & 15) >> 2);
+                    *(float*)(st + rl * 256 + ((unit ^ (((rl >> 2) & 3) << 2)) << 4) +
+                              (lane & 3) * 4) = acc[2 * p + a2][b][e];
+                }
             }
+        __builtin_amdgcn_s_waitcnt(0xC07F);               // lgkmcnt(0): the wave's writes are done
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int idx = i * 64 + lane, rl = idx >> 4, unit = idx & 15;
+            const f32x4 v = *(const f32x4*)(st + rl * 256 + ((unit ^ (((rl >> 2) & 3) << 2)) << 4));
+            const int row = m0 + 32 * p + rl, key = n0 + 4 * unit;
+            if (row < s && key < s)
+                __builtin_nontemporal_store(v, (f32x4*)(out + (int64_t)row * s + key));
         }
+        __builtin_amdgcn_s_waitcnt(0xC07F);               // reads done before the next pass writes
+        __builtin_amdgcn_wave_barrier();
+    }
 }
 
 // One workgroup per query row t of chunk pair p: parts [n][P][s][s] f32,
