@@ -465,6 +465,41 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
         // W_o product, K = 1536, and +1.1% on the row product, K = 6144.)
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
+            // GeLU backward: the pass's saved pre-activations are loaded before
+            // its staging, so that their latency overlaps it instead of
+            // stalling the store loop; units past M or N get an offset beyond
+            // the buffer range (zeros).  With bf16 output a lane takes two
+            // adjacent staged units per step (8 outputs, one 16-byte store;
+            // 8-byte stores made the launch ~6% slower), with f32 output one.
+            [[maybe_unused]] bf16x4 ypre[8192 / NTHREADS];
+            [[maybe_unused]] bf16x8 ypre8[4096 / NTHREADS];
+            if constexpr (EPI == EPI_GELU_BWD) {
+                const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
+                    aux + (int64_t)m0 * ldaux + n0, (short)0, 0x7ffffff0, 0x00020000);
+                if constexpr (OUT_BF16) {
+#pragma unroll
+                    for (int i = 0; i < 4096 / NTHREADS; ++i) {
+                        const int idx = i * NTHREADS + tid;
+                        const int lrow = idx >> 5, u2 = idx & 31, q = lrow & 63;
+                        const int r = (lrow >> 6) * 128 + 64 * p + q, c = u2 * 8;
+                        const unsigned off = (m0 + r < M && n0 + c < N)
+                                                 ? (unsigned)(((int64_t)r * ldaux + c) * 2) : OOB;
+                        ypre8[i] = __builtin_bit_cast(
+                            bf16x8, __builtin_amdgcn_raw_buffer_load_b128(yr, off, 0, 0));
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 8192 / NTHREADS; ++i) {
+                        const int idx = i * NTHREADS + tid;
+                        const int lrow = idx >> 6, unit = idx & 63, q = lrow & 63;
+                        const int r = (lrow >> 6) * 128 + 64 * p + q, c = unit * 4;
+                        const unsigned off = (m0 + r < M && n0 + c < N)
+                                                 ? (unsigned)(((int64_t)r * ldaux + c) * 2) : OOB;
+                        ypre[i] = __builtin_bit_cast(
+                            bf16x4, __builtin_amdgcn_raw_buffer_load_b64(yr, off, 0, 0));
+                    }
+                }
+            }
             char* half = wm ? lds1 : lds0;
 #pragma unroll
             for (int nj = 0; nj < NJ; ++nj) {
@@ -511,6 +546,46 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
                 if (p == 0) __syncthreads();
                 continue;
             }
+            if constexpr (OUT_BF16) {
+                // GeLU backward or the dual store with bf16 output: lane takes
+                // the staged units 2·u2 and 2·u2 + 1 of a row (the XOR keeps
+                // them adjacent), 8 outputs per 16-byte store
+#pragma unroll
+                for (int i = 0; i < 4096 / NTHREADS; ++i) {
+                    const int idx = i * NTHREADS + tid;
+                    const int lrow = idx >> 5, u2 = idx & 31, q = lrow & 63;
+                    const char* rowp = (lrow < 64 ? lds0 : lds1) + q * 1024;
+                    const int sw = ((q >> 2) & 3) << 2;
+                    const f32x4 v0 = *(const f32x4*)(rowp + (((2 * u2) ^ sw) << 4));
+                    const f32x4 v1 = *(const f32x4*)(rowp + (((2 * u2 + 1) ^ sw) << 4));
+                    const int grow = m0 + (lrow >> 6) * 128 + 64 * p + q, gcol = n0 + u2 * 8;
+                    if (grow < M && gcol < N) {
+                        float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+                        const int64_t o = (int64_t)grow * ldc + gcol;
+                        if constexpr (EPI == EPI_GELU_BWD) {
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) v[e] *= gelu_grad((float)ypre8[i][e]);
+                        }
+                        if constexpr (EPI == EPI_DUAL) {
+                            bf16x8 y, yp;
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) {
+                                y[e] = (__bf16)v[e];
+                                yp[e] = (__bf16)gelu(v[e]);
+                            }
+                            st_out(y, (bf16x8*)(aux + (int64_t)grow * ldaux + gcol));
+                            st_out(yp, (bf16x8*)((__bf16*)C + o));
+                        } else {
+                            bf16x8 c;
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) c[e] = (__bf16)v[e];
+                            st_out(c, (bf16x8*)((__bf16*)C + o));
+                        }
+                    }
+                }
+                if (p == 0) __syncthreads();
+                continue;
+            }
 #pragma unroll
             for (int i = 0; i < 8192 / NTHREADS; ++i) {
                 const int idx = i * NTHREADS + tid;
@@ -522,27 +597,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
                     f32x4 v = *(const f32x4*)src;
                     const int64_t o = (int64_t)grow * ldc + gcol;
                     if constexpr (EPI == EPI_GELU_BWD) {
-                        const bf16x4 y = *(const bf16x4*)(aux + (int64_t)grow * ldaux + gcol);
+                        const bf16x4 y = ypre[i];
 #pragma unroll
                         for (int e = 0; e < 4; ++e) v[e] *= gelu_grad((float)y[e]);
                     }
-                    if constexpr (EPI == EPI_DUAL) {
-                        bf16x4 y, yp;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            y[e] = (__bf16)v[e];
-                            yp[e] = (__bf16)gelu(v[e]);
-                        }
-                        st_out(y, (bf16x4*)(aux + (int64_t)grow * ldaux + gcol));
-                        st_out(yp, (bf16x4*)((__bf16*)C + o));
-                    } else if constexpr (OUT_BF16) {
-                        bf16x4 c;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) c[e] = (__bf16)v[e];
-                        st_out(c, (bf16x4*)((__bf16*)C + o));
-                    } else {
-                        st_out(v, (f32x4*)((float*)C + o));
-                    }
+                    st_out(v, (f32x4*)((float*)C + o));
                 }
             }
             if (p == 0) __syncthreads();
