@@ -333,11 +333,16 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_dkv_kernel(
     // lane offsets are recomputed per tile (a few integer operations) rather
     // than held in registers across the loop
     auto dma_q = [&](char* stage, int q0) {
+        // the empty asm makes the lane index opaque here, so the compiler
+        // cannot hoist these offsets out of the tile loop (where it spilled
+        // them to scratch and reloaded them every tile)
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
         unsigned voff_q[4], voff_o[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            voff_q[j] = dma_voff(w, j, lane, ld);
-            voff_o[j] = dma_voff(w, j, lane, ldo);
+            voff_q[j] = dma_voff(w, j, ln, ld);
+            voff_o[j] = dma_voff(w, j, ln, ldo);
         }
         dma_tile(rows_rsrc(seq, ld, q0, qcol, s), stage, voff_q, w);
         dma_tile(rows_rsrc(dseq, ldo, q0, head * D, s), stage + TILE, voff_o, w);
@@ -351,17 +356,6 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_dkv_kernel(
                                                      4u * lane, 0, 0, 0);
         }
     };
-    // row reads: dims 16kk + 8h of row 32t + l32 sit at rd0 ^ (kk << 5) (the
-    // unit index 2kk + h XOR-ed by swz(l32); kk moves only unit bits 1-3)
-    const unsigned rd0 = tile_off(l32, 8 * h);
-    const int G = lane >> 4, gi = lane & 15;
-    unsigned tlo[4], thi[4];
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-        const int col = 32 * dt + 16 * (G & 1) + 4 * (gi & 3);
-        tlo[dt] = tile_off(4 * h + (gi >> 2), col);
-        thi[dt] = tile_off(8 + 4 * h + (gi >> 2), col);
-    }
 
     f32x16 dk[4], dv[4];
 #pragma unroll
@@ -372,6 +366,22 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_dkv_kernel(
 
     auto compute = [&](const char* base, int q0) {
         if (causal && q0 + T64 - 1 < kw0) return;   // every query before the wave's keys
+        // LDS read addresses, derived per tile from an opaque lane index: held
+        // across the loop they pushed two K/V fragments out to scratch.
+        // Row reads: dims 16kk + 8h of row 32t + l32 sit at rd0 ^ (kk << 5)
+        // (the unit index 2kk + h XOR-ed by swz(l32); kk moves only unit bits
+        // 1-3); transpose reads of 4 key rows x 16 dims per 16-lane group.
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const unsigned rd0 = tile_off(ln & 31, 8 * (ln >> 5));
+        const int G = ln >> 4, gi = ln & 15, hh = ln >> 5;
+        unsigned tlo[4], thi[4];
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+            const int col = 32 * dt + 16 * (G & 1) + 4 * (gi & 3);
+            tlo[dt] = tile_off(4 * hh + (gi >> 2), col);
+            thi[dt] = tile_off(8 + 4 * hh + (gi >> 2), col);
+        }
         const float* Ls = (const float*)(base + 2 * TILE);
         const float* Ds = Ls + T64;
         const bool edge = (causal && q0 < kw0 + 31) || q0 + T64 > s;
@@ -395,11 +405,12 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_dkv_kernel(
                     sacc[r] = (q >= s || (causal && q < my_k)) ? -INFINITY : sacc[r];
                 }
             }
-            // P and dS one 16-query step at a time (accumulator elements
-            // 8·half .. +7), each consumed by its MFMAs right away
+            // P and dS of both 16-query steps (accumulator elements 8·half ..
+            // +7) first, so that the f32 scores are dead before the dV and dK
+            // MFMAs (keeping them live across those spilled a K/V fragment)
+            bf16x8 pk[2], dsk[2];
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
-                bf16x8 pk, dsk;
 #pragma unroll
                 for (int rq2 = 0; rq2 < 2; ++rq2) {
                     const int rq4 = 2 * half + rq2;
@@ -410,17 +421,20 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_dkv_kernel(
                     for (int e = 0; e < 4; ++e) {
                         const int r = 4 * rq4 + e;
                         const float p = __builtin_amdgcn_exp2f(fmaf(sacc[r], scale_log2, -Lv[e]));
-                        pk[r & 7] = (__bf16)p;
-                        dsk[r & 7] = (__bf16)(p * (pacc[r] - Dv[e]));
+                        pk[half][r & 7] = (__bf16)p;
+                        dsk[half][r & 7] = (__bf16)(p * (pacc[r] - Dv[e]));
                     }
                 }
+            }
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
                 const char* qb_base = base + (32 * t + 16 * half) * 256;
 #pragma unroll
                 for (int dt = 0; dt < 4; ++dt) {
                     dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        tr_read(qb_base + TILE, tlo[dt], thi[dt]), pk, dv[dt], 0, 0, 0);
+                        tr_read(qb_base + TILE, tlo[dt], thi[dt]), pk[half], dv[dt], 0, 0, 0);
                     dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        tr_read(qb_base, tlo[dt], thi[dt]), dsk, dk[dt], 0, 0, 0);
+                        tr_read(qb_base, tlo[dt], thi[dt]), dsk[half], dk[dt], 0, 0, 0);
                 }
             }
         }
