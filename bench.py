@@ -831,8 +831,21 @@ def cpu_baseline(w, rows_req, env):
     log(f"oracle: {dt:.1f} s")
     return {"value": round(fl / dt / 1e12, 4), "unit": "TFLOP/s",
             "cores": max(oracle.num_threads(), blas_threads()), "kind": "oracle",
+            "cpu_model": host_cpu_model(), "host_cpus": os.cpu_count(),
             "sample": sample, "seconds": round(dt, 2),
             "note": "fp64; matmuls via the host BLAS, other steps plain C loops"}
+
+
+def host_cpu_model() -> str:
+    """The host CPU's model name, from /proc/cpuinfo (None if unreadable)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 if __name__ == "__main__":

@@ -90,7 +90,8 @@ def f64(t) -> np.ndarray:
             t = t.detach().cpu().contiguous()
             if t.dtype == torch.bfloat16:
                 bits = t.view(torch.int16).numpy().astype(np.uint16).astype(np.uint32)
-                return np.ascontiguousarray((bits << 16).view(np.float32).astype(np.float64))
+                with np.errstate(invalid="ignore"):     # NaN payloads widen quietly
+                    return np.ascontiguousarray((bits << 16).view(np.float32).astype(np.float64))
             return np.ascontiguousarray(t.numpy().astype(np.float64))
     except ImportError:  # pragma: no cover
         pass

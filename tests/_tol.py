@@ -2,16 +2,20 @@
 
 * f32 path:  max_i |g_i - r_i| / max(|r_i|, rms(r)) <= 1e-4
 * bf16 path: ||g - r||_F / ||r||_F <= 1e-2 over the compared tensor, and
-             max_i |g_i - r_i| <= 3e-2 * rms(r_row(i)), where r_row(i) is the
-             output row (one token's vector) that holds element i.
+             max_i |g_i - r_i| <= 3e-2 * rms(r) with the rms over the whole
+             compared tensor -- the literal bar, asserted for every output
+             whose rows share one scale (GEMM, MLP, LayerNorm, partial sums,
+             their gradients).
 
-The rms in the bf16 max-abs bar is taken per token row: every step of the path
-is defined per token (per query for attention), and causal attention's rows
-differ in scale by an order of magnitude (the first query averages one value,
-the last averages thousands).  With a tensor-wide rms no implementation that
-keeps Q, K, V or O in bf16 meets the bar on the first rows (rounding V alone
-gives 0.054 * rms at s=2048), while per row an exact emulation of the bf16
-roundings gives 0.019 * rms_row.
+Attention-derived tensors (``per_row=True``) take the max-abs bar against the
+rms of the output row (one token's vector) that holds each element instead:
+causal attention's rows differ in scale by an order of magnitude (the first
+query averages one value, the last averages thousands).  With a tensor-wide
+rms no implementation that keeps Q, K, V or O in bf16 meets the bar on the
+first rows -- the exact output correctly rounded to bf16 already gives
+0.07 * rms at s=2048 -- while per row an emulation of the GPU path's bf16
+roundings gives 0.019 * rms_row (tests/test_tolerance_reading.py computes
+both in float64).
 
 A reference row that is exactly zero has no scale of its own; such rows occur
 where the mathematics fixes a zero (under a causal mask the first query
@@ -44,7 +48,11 @@ def errors(g, r):
     fro = float(np.linalg.norm(g2 - r2) / max(np.linalg.norm(r2), 1e-300))
     out = {"fro": fro, "rms": rms, "finite": bool(np.isfinite(g2).all())}
     if r2.size:
-        out["max_rel"] = float(np.max(d / np.maximum(np.abs(r2), rms)))
+        # an all-zero reference has no scale: any nonzero error is infinite
+        # relative error, an exact zero none
+        with np.errstate(divide="ignore", invalid="ignore"):
+            rel = np.where(d == 0.0, 0.0, d / np.maximum(np.abs(r2), rms))
+        out["max_rel"] = float(np.max(rel))
         out["max_abs"] = float(d.max())
         out["max_abs_over_rms"] = float(d.max() / max(rms, 1e-300))
         ratio = d.max(axis=1, keepdims=True) / np.maximum(rms_row, 1e-300)
@@ -64,9 +72,14 @@ def assert_f32(g, r, bar=F32_MAX_REL):
     return e
 
 
-def assert_bf16(g, r, fro=BF16_FRO, max_abs_rms=BF16_MAX_ABS_RMS):
+def assert_bf16(g, r, fro=BF16_FRO, max_abs_rms=BF16_MAX_ABS_RMS, per_row=False):
+    """The bf16 bars.  per_row=False (the default): max abs against the whole
+    tensor's rms, and against each row's rms as well.  per_row=True, for
+    attention-derived tensors only: against each row's rms."""
     e = errors(g, r)
     assert e["finite"], e
     assert e["fro"] <= fro, e
     assert e["max_abs_over_row_rms"] <= max_abs_rms, e
+    if not per_row:
+        assert e["max_abs_over_rms"] <= max_abs_rms, e
     return e

@@ -1,0 +1,66 @@
+"""Register budgets of the hot kernels, as the compiler reports them (CPU).
+
+The MFMA kernels are laid out for two waves per SIMD with their accumulators
+and operand fragments in registers; a compiler that starts spilling them to
+scratch memory (or drops the occupancy) slows them down without changing a
+single result, so no parity test would notice.  This compiles the three hot
+sources for gfx950 (device code only, the library's own flags) and checks
+each kernel's scratch use and occupancy against the budget it was tuned at.
+"""
+import concurrent.futures as cf
+import re
+
+import pytest
+
+from transformer_tensor_shard_amd import build as tpbuild
+
+
+def _have_hipcc():
+    try:
+        return bool(tpbuild.hipcc())
+    except RuntimeError:
+        return False
+
+
+pytestmark = pytest.mark.skipif(not _have_hipcc(), reason="hipcc (ROCm) not installed")
+
+SOURCES = ("gemm_bf16.hip", "attention.hip", "attention_bwd.hip")
+
+
+@pytest.fixture(scope="module")
+def usage():
+    with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        return dict(zip(SOURCES, ex.map(tpbuild.resource_usage, SOURCES)))
+
+
+def _kernels(u, pattern):
+    ks = {k: v for k, v in u.items() if re.search(pattern, k)}
+    assert ks, pattern
+    return ks
+
+
+def test_gemm_main_loop_variants_do_not_spill(usage):
+    # gemm_bf16_kernel<layout, epilogue, out_bf16, CHECK_K>: the variants
+    # without the K-tail checks run every product whose K is a multiple of 64
+    for name, r in _kernels(usage["gemm_bf16.hip"], r"gemm_bf16_kernelILi\dELi\dELb\dELb0E").items():
+        assert r["ScratchSize"] == 0 and r["VGPRs Spill"] == 0, (name, r)
+        assert r["Occupancy"] >= 2, (name, r)
+        assert r["LDS Size"] <= 160 * 1024, (name, r)
+
+
+def test_attention_forward_and_dq_do_not_spill(usage):
+    for name, r in {**_kernels(usage["attention.hip"], "attn_fwd_kernel"),
+                    **_kernels(usage["attention_bwd.hip"], "attn_bwd_dq_kernel")}.items():
+        assert r["ScratchSize"] == 0 and r["VGPRs Spill"] == 0, (name, r)
+        assert r["Occupancy"] >= 2, (name, r)
+
+
+def test_attention_dkv_spill_stays_at_two_dwords(usage):
+    """The dK/dV kernel holds K, V and both accumulators across its loop and
+    fills the 256-VGPR budget of two waves per SIMD; the per-tile addresses
+    are derived inside the loop so that only two dwords spill.  When the
+    compiler hoisted them out of the loop instead, 13 dwords spilled and the
+    core backward ran 0.593 ms against 0.536 ms at the 175B layer shape."""
+    (name, r), = _kernels(usage["attention_bwd.hip"], "attn_bwd_dkv_kernel").items()
+    assert r["VGPRs Spill"] <= 2 and r["ScratchSize"] <= 12, (name, r)
+    assert r["Occupancy"] >= 2, (name, r)

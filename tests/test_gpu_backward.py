@@ -254,7 +254,7 @@ def test_attention_core_backward(b, s, Hl, causal):
                 scale = float(np.sqrt(np.mean(oracle.f64(dO) ** 2)))
                 assert float(g.abs().max()) <= 1e-4 * scale
             else:
-                assert_bf16(g, ref[k])
+                assert_bf16(g, ref[k], per_row=True)
 
 
 def test_attention_train_forward_unchanged():
@@ -286,11 +286,11 @@ def test_attn_shard_backward(b, s, h, Hl, causal, dx):
     dX, dWqkv, dWo = tts.tp_attn_shard_backward(Xd, Wqd, Wod, qkv, O, lse, dZ.to(DEV), b, s, Hl,
                                                 causal=causal, dx_dtype=dx)
     torch.cuda.synchronize()
-    assert_bf16(Z, oracle.attn_shard_rows(X, b, s, Wqkv, Wo, Hl, 128, causal))
+    assert_bf16(Z, oracle.attn_shard_rows(X, b, s, Wqkv, Wo, Hl, 128, causal), per_row=True)
     rX, rWqkv, rWo = oracle.attn_shard_backward(X, b, s, Wqkv, Wo, dZ, Hl, 128, causal)
-    assert_bf16(dX, rX)
-    assert_bf16(dWqkv, rWqkv)
-    assert_bf16(dWo, rWo)
+    assert_bf16(dX, rX, per_row=True)
+    assert_bf16(dWqkv, rWqkv, per_row=True)
+    assert_bf16(dWo, rWo, per_row=True)
 
 
 def test_attn_backward_deterministic_and_ranks_sum():
@@ -320,7 +320,7 @@ def test_attn_backward_deterministic_and_ranks_sum():
     torch.cuda.synchronize()
     Wqkv_full = torch.cat([Wq, Wk, Wv], dim=1)
     rX = oracle.attn_shard_backward(X, b, s, Wqkv_full, Wo, dZ, H, 128, True)[0]
-    assert_bf16(dX, rX)
+    assert_bf16(dX, rX, per_row=True)
 
 
 @pytest.mark.parametrize("ta,tb,shapes,K", [

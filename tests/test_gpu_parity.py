@@ -241,7 +241,7 @@ def test_attention_core(b, s, Hl, causal):
     eye = np.eye(n3)
     ref = oracle.attn_shard_rows(qkv, b, s, eye, np.ascontiguousarray(eye[:Hl * d]), Hl, d,
                                  causal)[:, :Hl * d]
-    assert_bf16(O, ref)
+    assert_bf16(O, ref, per_row=True)
 
 
 @pytest.mark.parametrize("causal", [True, False])
@@ -262,7 +262,7 @@ def test_attention_core_moving_max(causal):
     eye = np.eye(n3)
     ref = oracle.attn_shard_rows(qkv, b, s, eye, np.ascontiguousarray(eye[:Hl * d]), Hl, d,
                                  causal)[:, :Hl * d]
-    assert_bf16(O, ref)
+    assert_bf16(O, ref, per_row=True)
 
 
 def test_attention_single_token_is_value():
@@ -281,7 +281,7 @@ def test_attn_shard_small(b, s, h, Hl):
     Wqkv, Wo = _qkv_weights(h, Hl, d, 53)
     Z = tts.tp_attn_shard(X.to(DEV), Wqkv.to(DEV), Wo.to(DEV), b, s, Hl, d, True)
     torch.cuda.synchronize()
-    assert_bf16(Z, oracle.attn_shard_rows(X, b, s, Wqkv, Wo, Hl, d, True))
+    assert_bf16(Z, oracle.attn_shard_rows(X, b, s, Wqkv, Wo, Hl, d, True), per_row=True)
 
 
 def test_attn_heads_sum_to_full_mha():
@@ -305,7 +305,7 @@ def test_attn_heads_sum_to_full_mha():
     Z = tts.tp_partial_sum(parts)
     torch.cuda.synchronize()
     full = oracle.attn_shard_rows(X, b, s, torch.cat([Wq, Wk, Wv], 1), Wo, H, d, True)
-    assert_bf16(Z, full)
+    assert_bf16(Z, full, per_row=True)
 
 
 # ------------------------------------------------------------------ block
@@ -328,10 +328,10 @@ def test_block_small_all_ranks():
                              ln1=(g1.to(DEV), b1.to(DEV)), x1=x1)
     torch.cuda.synchronize()
     x1_ref, out_ref = oracle.block_rows(x, b, s, Wqkv, Wo, A, B, H, d, ln1=(g1, b1))
-    assert_bf16(x1, x1_ref)
-    assert_bf16(out, out_ref)
+    assert_bf16(x1, x1_ref, per_row=True)
+    assert_bf16(out, out_ref, per_row=True)
     # the residual dominates out: check the block's own contributions too
-    assert_bf16(x1.cpu().double() - oracle.f64(x), x1_ref - oracle.f64(x))
+    assert_bf16(x1.cpu().double() - oracle.f64(x), x1_ref - oracle.f64(x), per_row=True)
     assert_bf16(out.cpu().double() - x1.cpu().double(), out_ref - x1_ref)
 
 

@@ -25,6 +25,84 @@ def rel(a, b):
     return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
 
 
+# --------------------------------------------------------------- input conversion
+def _bf16_from_definition(bits: int) -> float:
+    """Value of a bfloat16 bit pattern from the format's definition: 1 sign
+    bit, 8 exponent bits (bias 127), 7 fraction bits; exponent 0 encodes
+    zero and subnormals (fraction * 2^-133), exponent 255 infinities (zero
+    fraction) and NaNs."""
+    sign = -1.0 if bits & 0x8000 else 1.0
+    e = (bits >> 7) & 0xFF
+    frac = bits & 0x7F
+    if e == 0xFF:
+        return sign * math.inf if frac == 0 else math.nan
+    if e == 0:
+        return sign * math.ldexp(frac, -133)
+    return sign * math.ldexp(128 + frac, e - 134)
+
+
+def test_f64_widens_every_bf16_pattern_exactly():
+    """Every GPU comparison feeds the oracle the shared bf16 inputs through
+    oracle.f64; all 65536 bit patterns (both zeros, subnormals, the largest
+    finite values, both infinities, NaNs) must widen to exactly the value the
+    format defines, and agree bit for bit with torch's own widening."""
+    bits = torch.arange(-32768, 32768, dtype=torch.int32).to(torch.int16)
+    t = bits.view(torch.bfloat16)
+    got = oracle.f64(t)
+    assert got.dtype == np.float64 and got.shape == (65536,)
+    lib = t.double().numpy()
+    nan = np.isnan(lib)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint64), lib[~nan].view(np.uint64))
+    for i, b in enumerate(bits.numpy().astype(np.uint16).tolist()):
+        want = _bf16_from_definition(b)
+        if math.isnan(want):
+            assert math.isnan(got[i]), hex(b)
+        else:
+            assert got[i] == want and math.copysign(1.0, got[i]) == math.copysign(1.0, want), hex(b)
+    # landmarks, spelled out
+    by_bits = {int(b): float(v) for b, v in zip(bits.numpy().astype(np.uint16), got)}
+    assert by_bits[0x3F80] == 1.0 and by_bits[0xC000] == -2.0
+    assert by_bits[0x0001] == 2.0 ** -133 and by_bits[0x8001] == -(2.0 ** -133)
+    assert by_bits[0x7F7F] == (2.0 - 2.0 ** -7) * 2.0 ** 127
+    assert by_bits[0x7F80] == math.inf and by_bits[0xFF80] == -math.inf
+    assert by_bits[0x0000] == 0.0 and math.copysign(1.0, by_bits[0x8000]) == -1.0
+
+
+def test_f64_widens_f32_exactly():
+    g = torch.Generator().manual_seed(77)
+    t = torch.randn(100000, generator=g) * torch.exp2(torch.randint(-140, 120, (100000,),
+                                                                    generator=g).float())
+    special = torch.tensor([0.0, -0.0, float("inf"), float("-inf"), float("nan"),
+                            3.4028234663852886e38, -3.4028234663852886e38, 1.401298464324817e-45,
+                            -1.401298464324817e-45, 1.1754943508222875e-38])
+    t = torch.cat([t, special])
+    got = oracle.f64(t)
+    lib = t.double().numpy()
+    nan = np.isnan(lib)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint64), lib[~nan].view(np.uint64))
+    # a binary32 value is the rational its bits define: compare with the
+    # struct module's own decoding of the same bytes
+    import struct
+    raw = t.numpy().tobytes()
+    for i in range(0, 100010, 997):
+        (v,) = struct.unpack_from("<f", raw, 4 * i)
+        assert (math.isnan(v) and math.isnan(got[i])) or got[i] == v
+
+
+def test_f64_random_bf16_round_trip():
+    """1e5 random bf16 values of every magnitude: widening is exact, so
+    rounding back to bf16 returns the same bits."""
+    g = torch.Generator().manual_seed(78)
+    t = (torch.randn(100000, generator=g) *
+         torch.exp2(torch.randint(-130, 127, (100000,), generator=g).float())).to(torch.bfloat16)
+    got = oracle.f64(t)
+    back = torch.from_numpy(got).to(torch.bfloat16)
+    assert torch.equal(back.view(torch.int16), t.view(torch.int16))
+    assert np.array_equal(got, t.double().numpy())
+
+
 # --------------------------------------------------------------- matmul
 def test_matmul_matches_library():
     X = RNG.standard_normal((13, 29))

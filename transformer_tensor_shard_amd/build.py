@@ -57,6 +57,38 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
+def resource_usage(name: str) -> dict:
+    """Per-kernel register and scratch use of csrc/<name>, as the compiler
+    reports it (device code only, same flags as the library build):
+    {mangled kernel name: {"VGPRs": int, "AGPRs": int, "ScratchSize": int
+    (bytes per lane), "VGPRs Spill": int, "Occupancy": int (waves per SIMD),
+    "LDS Size": int (bytes per workgroup)}}."""
+    import re
+    import tempfile
+    src = os.path.join(CSRC, name)
+    with tempfile.TemporaryDirectory() as tmp:
+        cmd = [hipcc(), *_flags(), *FILE_FLAGS.get(name, []), "--cuda-device-only",
+               "-Rpass-analysis=kernel-resource-usage", "-c", src, "-o",
+               os.path.join(tmp, "dev.o")]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
+    out, cur = {}, None
+    for line in r.stderr.splitlines():
+        m = re.search(r"remark:\s+(.*?)\s*\[-Rpass-analysis", line)
+        if not m:
+            continue
+        text = m.group(1)
+        if text.startswith("Function Name:"):
+            cur = out.setdefault(text.split(":", 1)[1].strip(), {})
+            continue
+        key, _, val = text.rpartition(":")
+        key = re.sub(r"\s*\[.*\]", "", key).strip()
+        if cur is not None and val.strip().isdigit():
+            cur[key] = int(val)
+    return out
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))

@@ -59,6 +59,8 @@ hipError_t gemm_bf16_grouped(const GemmBatch& batch, int layout, int epi, int64_
 // O = P·V.  (sequence, head) pairs run kKvChunk at a time; rows up to kKvMaxS.
 constexpr int kKvChunk = 16;
 constexpr int kKvMaxS = 8192;
+// a chunk's O = P·V products run as one grouped GEMM launch
+static_assert(kKvChunk <= kMaxBatch, "a K/V-split chunk must fit one grouped GEMM launch");
 int64_t kv_split_workspace_bytes(int64_t pairs, int64_t s, int64_t d, int P);
 hipError_t kv_split_attention(const __bf16* qkv, int64_t ld, __bf16* O, int64_t ldo, int b, int s,
                               int H, int d, int P, bool causal, void* ws, hipStream_t stream);
