@@ -49,7 +49,9 @@ typedef enum tp_status {
     TP_ERR_DTYPE = 3,     /* dtype code not accepted by this entry point         */
     TP_ERR_ALIGN = 4,     /* a pointer is not 16-byte aligned                    */
     TP_ERR_WORKSPACE = 5, /* workspace NULL or smaller than the *_workspace size */
-    TP_ERR_LAUNCH = 6     /* the HIP runtime rejected a kernel launch            */
+    TP_ERR_LAUNCH = 6,    /* the HIP runtime rejected a kernel launch            */
+    TP_ERR_SCRATCH = 7    /* too large for the fixed scratch of an allocation-free
+                             entry point (tp_mlp_shard_noalloc)                  */
 } tp_status;
 
 typedef enum tp_dtype {
@@ -82,6 +84,23 @@ size_t tp_mlp_shard_workspace(int64_t M, int64_t f, int in);
 tp_status tp_mlp_shard(const void* X, const void* A_i, const void* a_i, const void* B_i,
                        void* Z_i, void* ws, size_t ws_bytes,
                        int64_t M, int64_t h, int64_t f, int in, int out, void* stream);
+
+/* tp_mlp_shard_noalloc -- tp_mlp_shard for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments, results and precision as
+ * tp_mlp_shard (bit for bit), with no workspace argument: Y'_i lives in a
+ * fixed 64 MiB device array inside the library, which every GPU the library
+ * runs on holds until the process ends.  The share runs on blocks of token
+ * rows whose Y'_i fits that array (rows are independent), so any M is
+ * accepted; f is limited to f·256·sizeof(in) <= 64 MiB (f <= 131072 for
+ * TP_BF16, 65536 for TP_F32), else TP_ERR_SCRATCH before anything is
+ * launched.  The call allocates and frees nothing and never synchronises.
+ * All calls on one GPU share its array and nothing in it needs to start at
+ * zero; calls that overlap on one GPU (two streams, two host threads) race
+ * on it and must be ordered by the caller. */
+tp_status tp_mlp_shard_noalloc(const void* X, const void* A_i, const void* a_i,
+                               const void* B_i, void* Z_i, int64_t M, int64_t h, int64_t f,
+                               int in, int out, void* stream);
 
 /* ------------------------------------------------------------------------
  * Training: the MLP share's forward keeping its activations, and its

@@ -74,6 +74,29 @@ def test_mlp_shard_rejects(kw, status):
     assert mlp(**kw) == status
 
 
+def mlp_noalloc(**kw):
+    a = dict(X=FAKE, A=FAKE, a=None, B=FAKE, Z=FAKE, M=64, h=64, f=32, i=_lib.TP_BF16,
+             o=_lib.TP_F32)
+    a.update(kw)
+    return tts.lib().tp_mlp_shard_noalloc(a["X"], a["A"], a["a"], a["B"], a["Z"], a["M"], a["h"],
+                                          a["f"], a["i"], a["o"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(X=None), _lib.TP_ERR_NULL),
+    (dict(M=0), _lib.TP_ERR_SHAPE),
+    (dict(h=12), _lib.TP_ERR_SHAPE),
+    (dict(o=2), _lib.TP_ERR_DTYPE),
+    (dict(Z=FAKE_ODD), _lib.TP_ERR_ALIGN),
+    # Y'_i of one 256-row tile must fit the fixed 64 MiB scratch
+    (dict(f=131080), _lib.TP_ERR_SCRATCH),
+    (dict(f=65544, i=_lib.TP_F32), _lib.TP_ERR_SCRATCH),
+])
+def test_mlp_shard_noalloc_rejects(kw, status):
+    assert mlp_noalloc(**kw) == status
+    assert b"scratch" in tts.lib().tp_status_string(_lib.TP_ERR_SCRATCH)
+
+
 def test_mlp_workspace_size():
     L = tts.lib()
     assert L.tp_mlp_shard_workspace(100, 64, _lib.TP_BF16) == 12800

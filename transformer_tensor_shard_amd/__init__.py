@@ -27,7 +27,7 @@ __all__ = [
     "tp_attn_shard_train_fwd", "tp_attn_shard_backward", "tp_attn_shard_backward_workspace",
     "tp_vocab_embedding_shard", "tp_vocab_ce_shard", "tp_vocab_ce_shard_workspace",
     "tp_vocab_ce_combine", "tp_vocab_parallel_ce", "tp_vocab_parallel_ce_workspace",
-    "tp_attention_kv_split", "tp_attention_kv_split_workspace", "lib",
+    "tp_attention_kv_split", "tp_attention_kv_split_workspace", "tp_mlp_shard_noalloc", "lib",
 ]
 
 
@@ -114,6 +114,21 @@ def tp_mlp_shard(X, A_i, B_i, a_i=None, *, out=None, out_dtype=torch.float32, ws
                                   _dev(B_i, "B_i"), _dev(out, "out"), _dev(ws, "ws"), _bytes(ws),
                                   M, h, f, _code(X.dtype), _code(out.dtype), _stream(stream))
     _check(st, "tp_mlp_shard")
+    return out
+
+
+def tp_mlp_shard_noalloc(X, A_i, B_i, a_i=None, *, out=None, out_dtype=torch.float32,
+                         stream=None):
+    """tp_mlp_shard without a workspace: Y'_i lives in the library's fixed
+    device scratch (f·256·sizeof(X) <= 64 MiB); returns Z_i [M,h]."""
+    M, h = X.shape
+    f = A_i.shape[1]
+    if out is None:
+        out = torch.empty(M, h, dtype=out_dtype, device=X.device)
+    st = _lib.load().tp_mlp_shard_noalloc(_dev(X, "X"), _dev(A_i, "A_i"), _dev(a_i, "a_i"),
+                                          _dev(B_i, "B_i"), _dev(out, "out"), M, h, f,
+                                          _code(X.dtype), _code(out.dtype), _stream(stream))
+    _check(st, "tp_mlp_shard_noalloc")
     return out
 
 

@@ -18,7 +18,8 @@ import torch  # noqa: F401  (must be loaded first: see the module docstring)
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtp.so")
 
-TP_OK, TP_ERR_NULL, TP_ERR_SHAPE, TP_ERR_DTYPE, TP_ERR_ALIGN, TP_ERR_WORKSPACE, TP_ERR_LAUNCH = range(7)
+(TP_OK, TP_ERR_NULL, TP_ERR_SHAPE, TP_ERR_DTYPE, TP_ERR_ALIGN, TP_ERR_WORKSPACE, TP_ERR_LAUNCH,
+ TP_ERR_SCRATCH) = range(8)
 TP_F32, TP_BF16 = 0, 1
 TP_EPI_NONE, TP_EPI_GELU, TP_EPI_GELU_BWD, TP_EPI_GELU_SAVE = 0, 1, 2, 3
 
@@ -33,6 +34,7 @@ SIGNATURES = {
     "tp_abi_version": (_int, []),
     "tp_mlp_shard_workspace": (_sz, [_i64, _i64, _int]),
     "tp_mlp_shard": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _sz, _i64, _i64, _i64, _int, _int, _vp]),
+    "tp_mlp_shard_noalloc": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _vp]),
     "tp_attn_shard_workspace": (_sz, [_i64, _i64, _i64, _i64]),
     "tp_attn_shard": (_int, [_vp, _vp, _vp, _vp, _vp, _sz, _i64, _i64, _i64, _i64, _i64, _int,
                              _int, _vp]),

@@ -8,6 +8,8 @@
 
 #include <stdint.h>
 
+#include <mutex>
+
 #define TP_EXPORT extern "C" __attribute__((visibility("default")))
 
 namespace {
@@ -266,6 +268,7 @@ TP_EXPORT const char* tp_status_string(int status) {
         case TP_ERR_ALIGN: return "pointer not 16-byte aligned";
         case TP_ERR_WORKSPACE: return "workspace missing or too small";
         case TP_ERR_LAUNCH: return "kernel launch failed";
+        case TP_ERR_SCRATCH: return "size exceeds the fixed scratch of an allocation-free call";
         default: return "unknown status";
     }
 }
@@ -330,6 +333,77 @@ TP_EXPORT tp_status tp_mlp_shard(const void* X, const void* A_i, const void* a_i
     if (!ws || ws_bytes < (size_t)mlp_ws(M, f, in)) return TP_ERR_WORKSPACE;
     if (!aligned16(ws)) return TP_ERR_ALIGN;
     return launched(run_mlp(X, A_i, a_i, B_i, Z_i, ws, M, h, f, in, out, as_stream(stream)));
+}
+
+// ---- allocation-free MLP share ---------------------------------------------
+// The scratch of tp_mlp_shard_noalloc: a fixed device array that every GPU the
+// library runs on holds until the process ends.  Host code never passes
+// `scratch` itself to a kernel (on the host the name is only a stand-in); it
+// looks up each device's address once with hipGetSymbolAddress and passes
+// that.
+constexpr int64_t kNoAllocScratchBytes = 64ll << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The address of `scratch` on the device that `stream` runs on (looked up
+// with that device current, once per device).
+hipError_t scratch_on_device(hipStream_t stream, void** out) {
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    hipDevice_t dev = cur;
+    if (stream) {
+        e = hipStreamGetDevice(stream, &dev);
+        if (e != hipSuccess) return e;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
+// Token rows of Y'_i that fit the scratch at width f: a multiple of 256 (the
+// GEMM's tile height), 0 when not even one tile row fits.
+int64_t noalloc_rows(int64_t f, int in) {
+    return (kNoAllocScratchBytes / (f * esize(in))) / 256 * 256;
+}
+}  // namespace
+
+TP_EXPORT tp_status tp_mlp_shard_noalloc(const void* X, const void* A_i, const void* a_i,
+                                         const void* B_i, void* Z_i, int64_t M, int64_t h,
+                                         int64_t f, int in, int out, void* stream) {
+    tp_status s = check_mlp(X, A_i, a_i, B_i, Z_i, M, h, f, in, out);
+    if (s != TP_OK) return s;
+    const int64_t rows = noalloc_rows(f, in);
+    if (rows < 256) return TP_ERR_SCRATCH;
+    hipStream_t st = as_stream(stream);
+    void* ws = nullptr;
+    if (scratch_on_device(st, &ws) != hipSuccess) return TP_ERR_LAUNCH;
+    // Token rows are independent: the share runs on row blocks whose Y'_i fits
+    // the scratch, each with the kernels (and the per-element summation order)
+    // of tp_mlp_shard, so the result is the same bit for bit.
+    for (int64_t m0 = 0; m0 < M; m0 += rows) {
+        const int64_t mc = M - m0 < rows ? M - m0 : rows;
+        const hipError_t e = run_mlp((const char*)X + m0 * h * esize(in), A_i, a_i, B_i,
+                                     (char*)Z_i + m0 * h * esize(out), ws, mc, h, f, in, out, st);
+        if (e != hipSuccess) return TP_ERR_LAUNCH;
+    }
+    return TP_OK;
 }
 
 TP_EXPORT tp_status tp_matmul(const void* A, int64_t lda, int trans_a, const void* B,
