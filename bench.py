@@ -601,6 +601,10 @@ def main():
             components[name] = c
             log(f"component {name}: {c}")
 
+    shards = None
+    if w.kind == "block":
+        shards = rank0_shards(w, tts, torch, x, A[0], B[0], Wqkv[0], Wo[0], dev, stream)
+
     training = None
     if w.kind == "block" and not args.no_training:
         training = mlp_backward_rank0(w, wl, tts, torch, x, A[0], B[0], dev, stream)
@@ -667,9 +671,45 @@ def main():
             "traffic": None, "algorithmic_bytes_per_launch": by,
             "frac_of_copy": round(gbs / calib["hbm_copy"]["gbs"], 4),
             "avg_launch_ms": round(kern_ms, 4), "launches_timed": len(kern_all)}
+    if shards is not None:
+        result["rank0_shards"] = shards
     if training is not None:
         result["training"] = training
     print(json.dumps(result), flush=True)
+
+
+def rank0_shards(w, tts, torch, x, A0, B0, Wqkv0, Wo0, dev, stream):
+    """One rank's shares at the block's shape, each as a single call on rank 0's
+    slices (no grouped launch over ranks): tp_mlp_shard (the 175B-layer MLP
+    shard, [16384 x 12288] x [12288 x 6144] then x [6144 x 12288]) and
+    tp_attn_shard (8 sequences of 2048, 12 local heads of 128), timed with HIP
+    events like the step."""
+    M, h, f = w.M, w.h, w.f
+    out = torch.empty(M, h, dtype=torch.float32, device=dev)
+    ws_m = torch.empty(tts.tp_mlp_shard_workspace(M, f, x.dtype), dtype=torch.uint8, device=dev)
+    ws_a = torch.empty(tts.tp_attn_shard_workspace(w.b, w.s, w.Hl, w.d), dtype=torch.uint8,
+                       device=dev)
+    att = w.attn_flops_rank()
+    items = {
+        "mlp_shard_rank0": (lambda: tts.tp_mlp_shard(x, A0, B0, out=out, ws=ws_m),
+                            w.mlp_flops_rank(),
+                            "tp_mlp_shard, rank 0 of tp=8: %d tokens, h=%d, f=%d" % (M, h, f)),
+        "attn_shard_rank0": (lambda: tts.tp_attn_shard(x, Wqkv0, Wo0, w.b, w.s, w.Hl, w.d, True,
+                                                       out=out, ws=ws_a),
+                             att["total"],
+                             "tp_attn_shard, rank 0 of tp=8: %d sequences of %d, %d local heads "
+                             "of %d, causal" % (w.b, w.s, w.Hl, w.d)),
+    }
+    res = {}
+    for name, (fn, fl, what) in items.items():
+        fn()
+        t, _ = event_time(fn, 5, stream)
+        res[name] = {"ms": round(t, 4), "tflops": round(fl / (t * 1e-3) / 1e12, 1),
+                     "pct_peak": round(100 * fl / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+                     "flops": fl, "what": what}
+        log(f"shard {name}: {res[name]}")
+    del out, ws_m, ws_a
+    return res
 
 
 def mlp_backward_rank0(w, wl, tts, torch, x, A0, B0, dev, stream):
