@@ -426,6 +426,22 @@ tp_status tp_vocab_parallel_ce(const void* H, const void* const* E, int P,
  * Measurement support (not part of the method).
  * ====================================================================== */
 
+/* tp_block_shard_timed -- tp_block_shard (same arguments, same launches,
+ * same results) that also records two HIP events (hipEvent_t handles, created
+ * by the caller with timing enabled) on `stream`: ev_begin immediately before
+ * and ev_end immediately after the launch of the MLP's column-parallel GEMM
+ * with GeLU over all ranks, the block's dominant kernel.  hipEventElapsedTime
+ * between them is that kernel's duration inside the step, as the benchmark
+ * reports it.  Both events must be non-NULL (TP_ERR_NULL otherwise). */
+tp_status tp_block_shard_timed(const void* x, void* out, int out_dtype, void* x1,
+                               const void* ln1_g, const void* ln1_b,
+                               const void* ln2_g, const void* ln2_b, float eps,
+                               const void* const* W_qkv, const void* const* W_o,
+                               const void* const* A, const void* const* B, int P,
+                               void* ws, size_t ws_bytes, int64_t b, int64_t s, int64_t h,
+                               int64_t H, int64_t d, int64_t F, void* stream,
+                               void* ev_begin, void* ev_end);
+
 /* tp_probe_mfma -- a register-only loop of MFMA 16x16x32 bf16 instructions:
  * `blocks` workgroups of 8 waves (two per SIMD), each wave issuing
  * 32 * iters independent MFMAs on values held in registers; nothing is loaded

@@ -335,6 +335,30 @@ def test_block_small_all_ranks():
     assert_bf16(out.cpu().double() - x1.cpu().double(), out_ref - x1_ref)
 
 
+def test_block_timed_matches_block_and_times_the_gelu_gemm():
+    """Measurement support: tp_block_shard_timed gives tp_block_shard's bits and
+    its events bracket the grouped GeLU GEMM, a part of the whole call."""
+    banner("block timed entry point")
+    P, b, s, H, d, F = 2, 2, 160, 4, 128, 1024
+    h, seed = H * d, 71
+    x = gen((b * s, h), 1.0, seed, "x").to(DEV)
+    rs = lambda r: synth.rank_seed(seed, r)
+    Wqkv = [gen((h, 3 * (H // P) * d), 1 / math.sqrt(h), rs(r), "Wqkv").to(DEV) for r in range(P)]
+    Wo = [gen(((H // P) * d, h), 1 / math.sqrt(h), rs(r), "Wo").to(DEV) for r in range(P)]
+    A = [gen((h, F // P), 1 / math.sqrt(h), rs(r), "A").to(DEV) for r in range(P)]
+    B = [gen((F // P, h), 1 / math.sqrt(F), rs(r), "B").to(DEV) for r in range(P)]
+    ref = tts.tp_block_shard(x, Wqkv, Wo, A, B, b, s, H, d)
+    ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    whole = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    whole[0].record()
+    got = tts.tp_block_shard(x, Wqkv, Wo, A, B, b, s, H, d, gelu_gemm_events=ev)
+    whole[1].record()
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)
+    t = ev[0].elapsed_time(ev[1])
+    assert 0.0 < t < whole[0].elapsed_time(whole[1])
+
+
 def test_probe_mfma_runs():
     """Measurement support: the register-only MFMA loop launches and returns
     finite sums (its values carry no meaning)."""

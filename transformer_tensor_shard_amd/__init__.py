@@ -229,24 +229,41 @@ def _ptr_array(ts: Sequence[torch.Tensor], name: str):
 
 def tp_block_shard(x, W_qkv: Sequence, W_o: Sequence, A: Sequence, B: Sequence, b: int, s: int,
                    H: int, d: int = 128, *, ln1=(None, None), ln2=(None, None), eps=1e-5,
-                   out=None, out_dtype=torch.float32, x1=None, ws=None, stream=None):
+                   out=None, out_dtype=torch.float32, x1=None, ws=None, stream=None,
+                   gelu_gemm_events=None):
     """Pre-LN block with every rank's share run in turn on this GPU.
 
     Returns out [b·s, h]; pass an f32 ``x1`` tensor to also receive the
-    residual stream after attention."""
+    residual stream after attention.  ``gelu_gemm_events``, a pair of
+    torch.cuda.Event(enable_timing=True), calls tp_block_shard_timed: the
+    events are recorded around the MLP's grouped GeLU GEMM launch."""
     P = len(W_qkv)
     h = x.shape[1]
     F = A[0].shape[1] * P
     if out is None:
         out = torch.empty(b * s, h, dtype=out_dtype, device=x.device)
     ws = _ws(ws, tp_block_shard_workspace(b, s, h, H, d, F, P), x.device)
-    st = _lib.load().tp_block_shard(
-        _dev(x, "x"), _dev(out, "out"), _code(out.dtype), _dev(x1, "x1"),
-        _dev(ln1[0], "ln1_g"), _dev(ln1[1], "ln1_b"), _dev(ln2[0], "ln2_g"), _dev(ln2[1], "ln2_b"),
-        float(eps), _ptr_array(W_qkv, "W_qkv"), _ptr_array(W_o, "W_o"), _ptr_array(A, "A"),
-        _ptr_array(B, "B"), P, _dev(ws, "ws"), _bytes(ws), b, s, h, H, d, F, _stream(stream))
-    _check(st, "tp_block_shard")
+    args = (_dev(x, "x"), _dev(out, "out"), _code(out.dtype), _dev(x1, "x1"),
+            _dev(ln1[0], "ln1_g"), _dev(ln1[1], "ln1_b"), _dev(ln2[0], "ln2_g"),
+            _dev(ln2[1], "ln2_b"), float(eps), _ptr_array(W_qkv, "W_qkv"), _ptr_array(W_o, "W_o"),
+            _ptr_array(A, "A"), _ptr_array(B, "B"), P, _dev(ws, "ws"), _bytes(ws), b, s, h, H, d,
+            F, _stream(stream))
+    if gelu_gemm_events is None:
+        st = _lib.load().tp_block_shard(*args)
+        _check(st, "tp_block_shard")
+    else:
+        ev = [_event(e) for e in gelu_gemm_events]
+        st = _lib.load().tp_block_shard_timed(*args, ev[0], ev[1])
+        _check(st, "tp_block_shard_timed")
     return out
+
+
+def _event(e):
+    """The raw hipEvent_t of a torch.cuda.Event (torch creates it lazily, on
+    its first record, so an unused event is recorded once here)."""
+    if not e.cuda_event:
+        e.record()
+    return ctypes.c_void_p(e.cuda_event)
 
 
 # ------------------------------------------------------------------ components

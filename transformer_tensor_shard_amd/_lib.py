@@ -44,6 +44,10 @@ SIGNATURES = {
                               ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.POINTER(_vp),
                               ctypes.POINTER(_vp), _int, _vp, _sz, _i64, _i64, _i64, _i64, _i64,
                               _i64, _vp]),
+    "tp_block_shard_timed": (_int, [_vp, _vp, _int, _vp, _vp, _vp, _vp, _vp, ctypes.c_float,
+                                    ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.POINTER(_vp),
+                                    ctypes.POINTER(_vp), _int, _vp, _sz, _i64, _i64, _i64, _i64,
+                                    _i64, _i64, _vp, _vp, _vp]),
     "tp_linear": (_int, [_vp, _i64, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _int, _int, _int,
                          _vp]),
     "tp_linear_batched": (_int, [ctypes.POINTER(_vp), _i64, ctypes.POINTER(_vp), _i64,

@@ -847,13 +847,15 @@ TP_EXPORT size_t tp_block_shard_workspace(int64_t b, int64_t s, int64_t h, int64
     return (size_t)block_ws(b, s, h, H, d, F, P).total;
 }
 
-TP_EXPORT tp_status tp_block_shard(const void* x, void* out, int out_dtype, void* x1,
-                                   const void* ln1_g, const void* ln1_b, const void* ln2_g,
-                                   const void* ln2_b, float eps, const void* const* W_qkv,
-                                   const void* const* W_o, const void* const* A,
-                                   const void* const* B, int P, void* ws, size_t ws_bytes,
-                                   int64_t b, int64_t s, int64_t h, int64_t H, int64_t d,
-                                   int64_t F, void* stream) {
+namespace {
+// The block; ev_begin / ev_end (both or neither) are recorded on the stream
+// around the launches of the MLP's column-parallel GEMM with GeLU.
+tp_status block_shard(const void* x, void* out, int out_dtype, void* x1, const void* ln1_g,
+                      const void* ln1_b, const void* ln2_g, const void* ln2_b, float eps,
+                      const void* const* W_qkv, const void* const* W_o, const void* const* A,
+                      const void* const* B, int P, void* ws, size_t ws_bytes, int64_t b,
+                      int64_t s, int64_t h, int64_t H, int64_t d, int64_t F, void* stream,
+                      hipEvent_t ev_begin, hipEvent_t ev_end) {
     if (!x || !out || !W_qkv || !W_o || !A || !B) return TP_ERR_NULL;
     if (!is_dtype(out_dtype)) return TP_ERR_DTYPE;
     if (P <= 0 || H <= 0 || F <= 0 || H % P || F % P || h != H * d || !(eps > 0.0f))
@@ -908,9 +910,11 @@ TP_EXPORT tp_status tp_block_shard(const void* x, void* out, int out_dtype, void
                      (const float*)ln2_g, (const float*)ln2_b, eps, st))
         return TP_ERR_LAUNCH;
     // out = x1 + sum_r MLP_r(LN2(x1)): Y'_r = GeLU(LN2(x1)·A_r), Z_r = Y'_r·B_r (§2.1)
+    if (ev_begin && hipEventRecord(ev_begin, st) != hipSuccess) return TP_ERR_LAUNCH;
     if (grouped(P, [&](int) { return (const void*)xn; }, [&](int r) { return A[r]; },
                 [&](int r) { return (void*)(Y + r * y_r * 2); }, h, f, f, M, f, h, true, true, st))
         return TP_ERR_LAUNCH;
+    if (ev_end && hipEventRecord(ev_end, st) != hipSuccess) return TP_ERR_LAUNCH;
     if (grouped(P, [&](int r) { return (const void*)(Y + r * y_r * 2); },
                 [&](int r) { return B[r]; }, [&](int r) { return (void*)(parts + r * n); },
                 f, h, h, M, h, f, false, false, st))
@@ -919,6 +923,31 @@ TP_EXPORT tp_status tp_block_shard(const void* x, void* out, int out_dtype, void
                      nullptr, nullptr, nullptr, 0.0f, st))
         return TP_ERR_LAUNCH;
     return TP_OK;
+}
+}  // namespace
+
+TP_EXPORT tp_status tp_block_shard(const void* x, void* out, int out_dtype, void* x1,
+                                   const void* ln1_g, const void* ln1_b, const void* ln2_g,
+                                   const void* ln2_b, float eps, const void* const* W_qkv,
+                                   const void* const* W_o, const void* const* A,
+                                   const void* const* B, int P, void* ws, size_t ws_bytes,
+                                   int64_t b, int64_t s, int64_t h, int64_t H, int64_t d,
+                                   int64_t F, void* stream) {
+    return block_shard(x, out, out_dtype, x1, ln1_g, ln1_b, ln2_g, ln2_b, eps, W_qkv, W_o, A, B,
+                       P, ws, ws_bytes, b, s, h, H, d, F, stream, nullptr, nullptr);
+}
+
+TP_EXPORT tp_status tp_block_shard_timed(const void* x, void* out, int out_dtype, void* x1,
+                                         const void* ln1_g, const void* ln1_b, const void* ln2_g,
+                                         const void* ln2_b, float eps, const void* const* W_qkv,
+                                         const void* const* W_o, const void* const* A,
+                                         const void* const* B, int P, void* ws, size_t ws_bytes,
+                                         int64_t b, int64_t s, int64_t h, int64_t H, int64_t d,
+                                         int64_t F, void* stream, void* ev_begin, void* ev_end) {
+    if (!ev_begin || !ev_end) return TP_ERR_NULL;
+    return block_shard(x, out, out_dtype, x1, ln1_g, ln1_b, ln2_g, ln2_b, eps, W_qkv, W_o, A, B,
+                       P, ws, ws_bytes, b, s, h, H, d, F, stream, (hipEvent_t)ev_begin,
+                       (hipEvent_t)ev_end);
 }
 
 TP_EXPORT tp_status tp_probe_mfma(float* out, int blocks, int iters, void* stream) {
