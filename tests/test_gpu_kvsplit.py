@@ -87,3 +87,15 @@ def test_kv_split_fullsize_sampled():
         ref = oracle.attention_kv_split(Q, K, V, P, True)[1]
         assert_bf16(O[rows, hd * d:(hd + 1) * d], ref, per_row=True)
     assert torch.isfinite(O).all()
+
+
+def test_kv_split_longest_sequence():
+    """s = 8192, the longest sequence the K/V split accepts: one (sequence,
+    head) pair, all rows against the oracle."""
+    b, s, H, d, P = 1, 8192, 1, 128, 4
+    banner(f"longest sequence: b={b} s={s} H={H} d={d} P={P}")
+    qkv = synth.normal((b * s, 3 * H * d), 1.0, 64, "x", torch.bfloat16)
+    O = tts.tp_attention_kv_split(qkv.to(DEV), b, s, H, P, d, True).cpu()
+    torch.cuda.synchronize()
+    ref = oracle.attention_kv_split(qkv[:, :d], qkv[:, d:2 * d], qkv[:, 2 * d:], P, True)[1]
+    assert_bf16(O, ref, per_row=True)

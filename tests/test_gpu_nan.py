@@ -97,6 +97,25 @@ def test_nan_token_through_block():
     _check_sequence_rows(outc, outb, b, s, beta, t0)
 
 
+def test_nan_token_through_mlp_shard():
+    """Token rows are independent in the MLP share: a NaN in one row of X
+    makes exactly that row of Z_i NaN."""
+    M, h, f = 300, 256, 512
+    banner(f"mlp shard NaN at one token: M={M} h={h} f={f}")
+    X = gen((M, h), 1.0, 304, "x")
+    A = gen((h, f), 1 / math.sqrt(h), 304, "A").to(DEV)
+    B = gen((f, h), 1 / math.sqrt(f), 304, "B").to(DEV)
+    Xbad = X.clone()
+    Xbad[123, 7] = float("nan")
+    clean = tts.tp_mlp_shard(X.to(DEV), A, B).cpu()
+    bad = tts.tp_mlp_shard(Xbad.to(DEV), A, B).cpu()
+    assert torch.isfinite(clean).all()
+    assert torch.isnan(bad[123]).all()
+    keep = torch.ones(M, dtype=torch.bool)
+    keep[123] = False
+    assert torch.equal(bad[keep], clean[keep])
+
+
 @pytest.mark.parametrize("part_dtype", [torch.float32, torch.bfloat16])
 def test_inf_nan_in_one_partial_stay_local(part_dtype):
     P, M, h = 3, 64, 264

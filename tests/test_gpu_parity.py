@@ -169,7 +169,8 @@ def test_mlp_bf16_small(M, h, f, bias):
 
 
 # ------------------------------------------------------------------ partial sum
-@pytest.mark.parametrize("P,M,h", [(8, 33, 520), (1, 5, 4), (3, 1000, 64), (2, 3, 16392)])
+@pytest.mark.parametrize("P,M,h", [(8, 33, 520), (1, 5, 4), (3, 1000, 64), (2, 3, 16392),
+                                   (8, 7, 16384)])     # the row kernel at its widest row
 def test_partial_sum_f32(P, M, h):
     banner(f"partial sum f32 P={P} M={M} h={h}")
     parts = gen((P, M, h), 1.0, 31, "partials", torch.float32)
@@ -207,7 +208,8 @@ def test_partial_sum_mixed_dtypes_and_alias():
 @pytest.mark.parametrize("M,h,dtype,affine", [(64, 4096, torch.bfloat16, False),
                                               (37, 520, torch.float32, True),
                                               (3, 12288, torch.float32, False),
-                                              (5, 20000, torch.bfloat16, True)])
+                                              (5, 20000, torch.bfloat16, True),
+                                              (2, 32768, torch.bfloat16, True)])   # widest row
 def test_layernorm(M, h, dtype, affine):
     banner(f"layernorm M={M} h={h} {dtype} affine={affine}")
     x = gen((M, h), 2.0, 41, "x", dtype) + 0.5
@@ -308,7 +310,46 @@ def test_attn_heads_sum_to_full_mha():
     assert_bf16(Z, full, per_row=True)
 
 
+def test_attention_core_long_sequence():
+    """s = 4100: 33 query blocks and 65 key tiles, a ragged end; sampled rows
+    on both sides of tile boundaries far into the sequence."""
+    b, s, Hl, d = 1, 4100, 1, 128
+    banner(f"attention core long b={b} s={s} Hl={Hl}")
+    n3 = 3 * Hl * d
+    qkv = gen((b * s, n3), 1.0, 57, "x")
+    O = tts.tp_attention_core(qkv.to(DEV), b, s, Hl, d, True).cpu()
+    rows = np.array([0, 1, 63, 64, 127, 128, 2047, 2048, 4095, 4096, 4099] +
+                    list(np.random.default_rng(57).integers(0, s, 9)), dtype=np.int64)
+    eye = np.eye(n3)
+    ref = oracle.attn_shard_rows(qkv, b, s, eye, np.ascontiguousarray(eye[:Hl * d]), Hl, d, True,
+                                 rows)[:, :Hl * d]
+    assert_bf16(O[torch.from_numpy(rows)], ref, per_row=True)
+
+
 # ------------------------------------------------------------------ block
+@pytest.mark.parametrize("P,H", [(1, 2), (3, 3)])
+def test_block_one_and_three_ranks(P, H):
+    """Degenerate and odd rank counts: P = 1 is the unsharded block; P = 3
+    splits F and H three ways."""
+    b, s, d, F = 2, 96, 128, 768
+    h, seed = H * d, 62 + P
+    banner(f"block P={P} H={H} h={h} F={F}")
+    x = gen((b * s, h), 1.0, seed, "x")
+    rs = lambda r: synth.rank_seed(seed, r)
+    Wqkv = [gen((h, 3 * (H // P) * d), 1 / math.sqrt(h), rs(r), "Wqkv") for r in range(P)]
+    Wo = [gen(((H // P) * d, h), 1 / math.sqrt(h), rs(r), "Wo") for r in range(P)]
+    A = [gen((h, F // P), 1 / math.sqrt(h), rs(r), "A") for r in range(P)]
+    B = [gen((F // P, h), 1 / math.sqrt(F), rs(r), "B") for r in range(P)]
+    x1 = torch.empty(b * s, h, device=DEV)
+    dev = lambda ts: [t.to(DEV) for t in ts]
+    out = tts.tp_block_shard(x.to(DEV), dev(Wqkv), dev(Wo), dev(A), dev(B), b, s, H, d, x1=x1)
+    torch.cuda.synchronize()
+    x1_ref, out_ref = oracle.block_rows(x, b, s, Wqkv, Wo, A, B, H, d)
+    assert_bf16(x1, x1_ref, per_row=True)
+    assert_bf16(out, out_ref, per_row=True)
+    assert_bf16(out.cpu().double() - x1.cpu().double(), out_ref - x1_ref)
+
+
 def test_block_small_all_ranks():
     banner("block P=2 small")
     P, b, s, H, d, F = 2, 2, 160, 4, 128, 1024
