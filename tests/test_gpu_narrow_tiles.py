@@ -1,0 +1,111 @@
+"""GPU parity of the forward GEMM with 192-column output tiles.
+
+A forward (NN) product whose 256-column tiles would leave the last wave of
+workgroups mostly empty runs with 192-column tiles instead (the launcher's
+choice; with 256 compute units it is taken for every shape below, and for
+none of the smaller shapes in test_gpu_parity.py).  The arithmetic per
+output is the same K loop, so each case is held to the same bar as the
+256-column kernel: f32 output within 1e-4 of the oracle, bf16 output within
+the bf16 bar.  The shapes cover ragged M, N and K, bias, GeLU, the training
+forward's two outputs, the shared-X band order and a grouped launch whose
+products differ in M and N.
+"""
+import math
+
+import pytest
+import torch
+
+import oracle
+import synth
+import transformer_tensor_shard_amd as tts
+from _tol import assert_bf16, assert_f32
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def banner(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def gen(shape, sigma, seed, sub, dtype=torch.bfloat16):
+    return synth.normal(shape, sigma, seed, sub, dtype)
+
+
+def tiles(M, N, w):
+    return -(-M // 256) * -(-N // w)
+
+
+def test_shapes_take_the_narrow_tiles():
+    """The cases below are in the regime the launcher's rule selects: with
+    256 compute units, 256-column tiles need w4 waves and 192-column ones
+    w3, and 7·w3 < 8·w4 - 1."""
+    cus = 256
+    for prods in ([(2304, 7680)], [(2250, 7560)], [(2048, 3072)] * 3,
+                  [(2304, 3840), (2100, 3896)]):
+        w4 = -(-sum(tiles(m, n, 256) for m, n in prods) // cus)
+        w3 = -(-sum(tiles(m, n, 192) for m, n in prods) // cus)
+        assert 7 * w3 < 8 * w4 - 1, prods
+
+
+def test_narrow_bias_gelu_bf16():
+    M, N, K = 2304, 7680, 136                   # K tail: 136 = 2·64 + 8
+    banner(f"narrow tiles linear bias+gelu bf16 M={M} N={N} K={K}")
+    X = gen((M, K), 1.0, 501, "x")
+    W = gen((K, N), 1 / math.sqrt(K), 501, "A")
+    bias = gen((N,), 0.5, 501, "bias", torch.float32)
+    C = tts.tp_linear(X.to(DEV), W.to(DEV), bias.to(DEV), gelu=True, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert_bf16(C, oracle.gelu(oracle.matmul(X, W, bias)))
+
+
+def test_narrow_f32_ragged():
+    M, N, K = 2250, 7560, 200                   # M, N and K all ragged
+    banner(f"narrow tiles linear f32 M={M} N={N} K={K}")
+    X = gen((M, K), 1.0, 502, "x")
+    W = gen((K, N), 1 / math.sqrt(K), 502, "A")
+    C = tts.tp_linear(X.to(DEV), W.to(DEV), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    e = assert_f32(C, oracle.matmul(X, W), bar=1e-4)
+    assert e["fro"] < 1e-5, e
+
+
+def test_narrow_gelu_save():
+    """The training forward's epilogue: C = GeLU(v) and aux = v, both bf16."""
+    M, N, K = 2304, 7680, 64
+    banner(f"narrow tiles gelu_save M={M} N={N} K={K}")
+    X = gen((M, K), 1.0, 503, "x")
+    W = gen((K, N), 1 / math.sqrt(K), 503, "A")
+    bias = gen((N,), 0.5, 503, "bias", torch.float32)
+    C, aux = tts.tp_matmul(X.to(DEV), W.to(DEV), bias.to(DEV), epilogue="gelu_save",
+                           out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    v = oracle.matmul(X, W, bias)
+    assert_bf16(aux, v)
+    assert_bf16(C, oracle.gelu(v))
+
+
+def test_narrow_shared_x_band_order():
+    count, M, N, K = 3, 2048, 3072, 64
+    banner(f"narrow tiles shared X count={count} M={M} N={N} K={K}")
+    X = gen((M, K), 1.0, 504, "x")
+    Ws = [gen((K, N), 1 / math.sqrt(K), 504 + g, "A") for g in range(count)]
+    Xd = X.to(DEV)
+    outs = tts.tp_linear_batched([Xd] * count, [W.to(DEV) for W in Ws], gelu=True,
+                                 out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    for g in range(count):
+        assert_bf16(outs[g], oracle.gelu(oracle.matmul(X, Ws[g])))
+
+
+def test_narrow_grouped_different_shapes():
+    K = 96
+    shapes = [(2304, 3840), (2100, 3896)]
+    banner(f"narrow tiles grouped shapes={shapes} K={K}")
+    As = [gen((m, K), 1.0, 505 + g, "x") for g, (m, _) in enumerate(shapes)]
+    Bs = [gen((K, n), 1 / math.sqrt(K), 505 + g, "A") for g, (_, n) in enumerate(shapes)]
+    outs = tts.tp_matmul_grouped([A.to(DEV) for A in As], [B.to(DEV) for B in Bs],
+                                 out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for A, B, C in zip(As, Bs, outs):
+        assert_f32(C, oracle.matmul(A, B), bar=1e-4)

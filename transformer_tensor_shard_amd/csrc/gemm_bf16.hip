@@ -65,6 +65,8 @@
 // 4-stage BK=32 version measured the same), and cache-policy bits do not
 // either (non-temporal loads halve throughput: they defeat the L2 sharing
 // that the tile order sets up).
+#include <atomic>
+
 #include "tp_kernels.h"
 
 namespace tpk {
@@ -76,14 +78,18 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
-constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int BM = 256, BN = 256, BK = 64;    // BN: the LDS tile's width (a tile may use 192)
 constexpr int NWAVES = 8, NTHREADS = NWAVES * 64;
 constexpr int A_BYTES = BM * BK * 2;          // 32 KiB
 constexpr int B_BYTES = BK * BN * 2;          // 32 KiB
 constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
 constexpr int GROUP_M = 4;
 constexpr unsigned OOB = 0x80000000u;         // any offset >= num_records reads 0
-constexpr int NI = 8, NJ = 4;                 // 16x16 MFMA blocks per wave (rows, cols)
+constexpr int NI = 8;                         // 16x16 MFMA blocks per wave along M
+// Blocks per wave along N: 4 (a 256-column tile) or 3 (192 columns, for
+// products whose 256-column tile count leaves the last wave of workgroups
+// mostly empty; see the launcher).
+constexpr int NJ_MAX = 4;
 constexpr int LOADS = 4;                      // A (and B) loads per wave per K tile
 
 // Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
@@ -96,24 +102,25 @@ constexpr int SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100;
 // slower).
 constexpr int DMA_WINDOW = 20;
 
-// One 32-wide k-step of a wave: 32 MFMAs (A block mi = I/4 against the 4 B
-// blocks); the next k-step's B reads (DB LDS instructions per block) go out
+// One 32-wide k-step of a wave: 8·NJ MFMAs (A block mi = I/NJ against the NJ
+// B blocks); the next k-step's B reads (DB LDS instructions per block) go out
 // over the first 8 MFMAs and each A block's reload (DA instructions) right
 // after its last MFMA; V direct-to-LDS loads are spread evenly over the
-// first DMA_WINDOW MFMAs.
-template <int V, int DA, int DB, int I>
+// first DMA_WINDOW·NJ/4 MFMAs (the same share of the k-step).
+template <int V, int DA, int DB, int NJ, int I>
 __device__ __forceinline__ void sched_step() {
+    constexpr int window = DMA_WINDOW * NJ / NJ_MAX;
     __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-    constexpr int nb = I < 8 ? ((I + 1) * 4 * DB) / 8 - (I * 4 * DB) / 8 : 0;
-    constexpr int nds = nb + (I % 4 == 3 ? DA : 0);
+    constexpr int nb = I < 8 ? ((I + 1) * NJ * DB) / 8 - (I * NJ * DB) / 8 : 0;
+    constexpr int nds = nb + (I % NJ == NJ - 1 ? DA : 0);
     if constexpr (nds > 0) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, nds, 0);
-    constexpr int nv = I < DMA_WINDOW ? ((I + 1) * V) / DMA_WINDOW - (I * V) / DMA_WINDOW : 0;
+    constexpr int nv = I < window ? ((I + 1) * V) / window - (I * V) / window : 0;
     if constexpr (nv > 0) __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, nv, 0);
-    if constexpr (I + 1 < 32) sched_step<V, DA, DB, I + 1>();
+    if constexpr (I + 1 < NI * NJ) sched_step<V, DA, DB, NJ, I + 1>();
 }
-template <int V, int DA, int DB>
+template <int V, int DA, int DB, int NJ>
 __device__ __forceinline__ void sched_kstep() {
-    sched_step<V, DA, DB, 0>();
+    sched_step<V, DA, DB, NJ, 0>();
     __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -151,12 +158,12 @@ __device__ __forceinline__ float gelu_grad(float x) {
 // at the same time and one group's tail overlaps the next group's head.
 // Inside a range, tiles walk the output GROUP_M tile-rows at a time.  Returns
 // false for the few padding workgroups of XCDs with fewer tiles.
-__device__ __forceinline__ bool tile_coords(int pid, const GemmBatch& b, int& g, int& tm,
+__device__ __forceinline__ bool tile_coords(int pid, const GemmBatch& b, int bn, int& g, int& tm,
                                             int& tn) {
     const int xcd = pid & 7;
     int local = pid >> 3;
     for (g = 0; g < b.count; ++g) {
-        const int tiles_m = (b.M[g] + BM - 1) / BM, tiles_n = (b.N[g] + BN - 1) / BN;
+        const int tiles_m = (b.M[g] + BM - 1) / BM, tiles_n = (b.N[g] + bn - 1) / bn;
         const int ntiles = tiles_m * tiles_n;
         const int per = ntiles >> 3, rem = ntiles & 7;
         const int cnt = per + (xcd < rem ? 1 : 0);          // this XCD's tiles of group g
@@ -225,12 +232,18 @@ __device__ __forceinline__ int kc_kpos(int lane, int j) {
 template <typename T>
 __device__ __forceinline__ void st_out(T v, T* p) { __builtin_nontemporal_store(v, p); }
 
-template <int LAYOUT, int EPI, bool OUT_BF16, bool CHECK_K>
+template <int LAYOUT, int EPI, bool OUT_BF16, bool CHECK_K, int NJ>
 __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
     GemmBatch batch, int64_t ldaux, int K)
 {
     constexpr bool A_MC = LAYOUT == GEMM_TN;    // A stored [K,M]: M contiguous
     constexpr bool B_KC = LAYOUT == GEMM_NT;    // B stored [N,K]: K contiguous
+    // Output tile BM x TN.  With NJ = 3 the tile is 192 columns wide: the LDS
+    // layout stays 256 wide and its last 64 columns are loaded as zeros (their
+    // lanes get out-of-range offsets) and never read.
+    constexpr int TN = 64 * NJ;
+    static_assert(NJ == 3 || NJ == NJ_MAX, "256- or 192-column tiles");
+    static_assert(EPI != EPI_CE_STATS || NJ == NJ_MAX, "the statistics use 256-column tiles");
     // Two stages as two separate LDS objects: every access below names its
     // stage statically, which lets the compiler see that reads of one stage
     // do not depend on the direct-to-LDS loads still landing in the other.
@@ -239,12 +252,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
 
     int grp, tm, tn;
     if (batch.band ? !tile_coords_band(blockIdx.x, batch.count, (batch.M[0] + BM - 1) / BM,
-                                       (batch.N[0] + BN - 1) / BN, grp, tm, tn)
-                   : !tile_coords(blockIdx.x, batch, grp, tm, tn))
+                                       (batch.N[0] + TN - 1) / TN, grp, tm, tn)
+                   : !tile_coords(blockIdx.x, batch, TN, grp, tm, tn))
         return;
     const int M = batch.M[grp], N = batch.N[grp];
     const int64_t lda = batch.lda[grp], ldb = batch.ldb[grp], ldc = batch.ldc[grp];
-    const int m0 = tm * BM, n0 = tn * BN;
+    const int m0 = tm * BM, n0 = tn * TN;
     const __bf16* __restrict__ A = batch.A[grp];
     const __bf16* __restrict__ B = batch.B[grp];
     const float* __restrict__ bias = batch.bias[grp];
@@ -281,9 +294,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
         else
             a_off[j] = (m0 + r) < M ? (unsigned)(r * lda + u * 8) * 2u : OOB;
         if (B_KC)
-            b_off[j] = (n0 + r) < N ? (unsigned)(r * ldb + u * 8) * 2u : OOB;
+            b_off[j] = (n0 + r) < N && (NJ == NJ_MAX || r < TN) ? (unsigned)(r * ldb + u * 8) * 2u : OOB;
         else
-            b_off[j] = (n0 + ub * 8) < N ? (unsigned)(kr * ldb + ub * 8) * 2u : OOB;
+            b_off[j] = (n0 + ub * 8) < N && ub * 8 < TN ? (unsigned)(kr * ldb + ub * 8) * 2u : OOB;
     }
     auto dma_tile = [&](int k0, char* stage) {
         // A tile past the last one gets an empty range: all loads write zeros.
@@ -339,12 +352,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
     // XOR-ed by mi (the 16-column blocks differ only in the swizzled unit
     // bits 1-3).
     const unsigned a_rd0 = A_MC ? mc_rd(wm * 128) : wm * 128 * 128 + kc_rd;
+    // wave columns: wn·32·NJ + wh·16·NJ (+ 16·nj), i.e. wn·128 + wh·64 for 256-column tiles
+    const int wcol = wn * 32 * NJ + wh * 16 * NJ;
     unsigned b_rd[B_KC ? 1 : NJ];
     if constexpr (B_KC) {
-        b_rd[0] = A_BYTES + (wn * 128 + wh * 64) * 128 + kc_rd;
+        b_rd[0] = A_BYTES + wcol * 128 + kc_rd;
     } else {
 #pragma unroll
-        for (int nj = 0; nj < NJ; ++nj) b_rd[nj] = A_BYTES + mc_rd(wn * 128 + wh * 64 + 16 * nj);
+        for (int nj = 0; nj < NJ; ++nj) b_rd[nj] = A_BYTES + mc_rd(wcol + 16 * nj);
     }
     auto read_kc = [&](const char* base, unsigned addr, int blk, int kk) -> bf16x8 {
         // 16-byte unit (4kk + lane>>4) of the row: XOR with kk*4 keeps the swizzle
@@ -401,12 +416,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
     // tile sits before the second, whose operand reloads read the next tile
     auto tile = [&](const char* cur_c, char* cur, const char* nxt, int k_next2) {
         kstep(fb[0], fb[1], cur_c, 1);
-        sched_kstep<0, A_MC ? 2 : 1, B_KC ? 1 : 2>();
+        sched_kstep<0, A_MC ? 2 : 1, B_KC ? 1 : 2, NJ>();
         __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();                            // next tile visible; `cur` free
         dma_tile(k_next2, cur);                     // empty range past the last tile
         kstep(fb[1], fb[0], nxt, 0);
-        sched_kstep<2 * LOADS, A_MC ? 2 : 1, B_KC ? 1 : 2>();
+        sched_kstep<2 * LOADS, A_MC ? 2 : 1, B_KC ? 1 : 2, NJ>();
     };
     int kt = 0;
     for (; kt + 1 < nk; kt += 2) {
@@ -421,7 +436,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
     // Lane holds column (lane & 15) and rows 4*(lane >> 4) + i of each 16x16
     // block.  Staged rows r and r+4, r+8, r+12 (one store instruction) get
     // their units XOR-ed apart so the LDS writes do not conflict.
-    const int lcol = wn * 128 + wh * 64 + (lane & 15);        // + 16*nj
+    const int lcol = wcol + (lane & 15);                     // + 16*nj
     float bv[NJ];
 #pragma unroll
     for (int nj = 0; nj < NJ; ++nj)
@@ -452,7 +467,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
             const char* src = (row < 128 ? lds0 : lds1) + lr * 512 +
                               ((unit ^ (((lr >> 2) & 3) << 1)) << 4);
             const int grow = m0 + row, gcol = n0 + unit * 8;
-            if (grow < M && gcol < N)
+            if (grow < M && gcol < N && unit * 8 < TN)
                 st_out(*(const bf16x8*)src, (bf16x8*)((__bf16*)C + (int64_t)grow * ldc + gcol));
         }
     } else {
@@ -559,7 +574,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
                     const f32x4 v0 = *(const f32x4*)(rowp + (((2 * u2) ^ sw) << 4));
                     const f32x4 v1 = *(const f32x4*)(rowp + (((2 * u2 + 1) ^ sw) << 4));
                     const int grow = m0 + (lrow >> 6) * 128 + 64 * p + q, gcol = n0 + u2 * 8;
-                    if (grow < M && gcol < N) {
+                    if (grow < M && gcol < N && u2 * 8 < TN) {
                         float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
                         const int64_t o = (int64_t)grow * ldc + gcol;
                         if constexpr (EPI == EPI_GELU_BWD) {
@@ -593,7 +608,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
                 const char* src = (lrow < 64 ? lds0 : lds1) + q * 1024 +
                                   ((unit ^ (((q >> 2) & 3) << 2)) << 4);
                 const int grow = m0 + (lrow >> 6) * 128 + 64 * p + q, gcol = n0 + unit * 4;
-                if (grow < M && gcol < N) {
+                if (grow < M && gcol < N && unit * 4 < TN) {
                     f32x4 v = *(const f32x4*)src;
                     const int64_t o = (int64_t)grow * ldc + gcol;
                     if constexpr (EPI == EPI_GELU_BWD) {
@@ -612,35 +627,80 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
 }  // namespace
 
 namespace {
+// Compute units of the current device (256 on MI355X), for the tile-width
+// choice; queried once per device.
+int cu_count() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        n = 256;
+    cached[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+// Workgroups of a launch with tiles tn_w columns wide (one 256 x tn_w tile each).
+int64_t tile_count(const GemmBatch& b, int tn_w) {
+    int64_t t = 0;
+    for (int g = 0; g < b.count; ++g)
+        t += (int64_t)((b.M[g] + BM - 1) / BM) * ((b.N[g] + tn_w - 1) / tn_w);
+    return t;
+}
+
+// 192-column tiles for a forward (NN) product whose 256-column tiles fill the
+// last of their waves of workgroups (one per CU) badly.  The cost model: a
+// wave of 256-column tiles takes 1, a wave of 192-column tiles 7/8 (the K
+// loop is bound by the L2 requests of a tile's A and B panels, 256 + 192
+// rows against 256 + 256).  Measured on MI355X at [8192 x 4096]·[4096 x 3072]
+// (384 tiles of 256 columns, 1.5 waves; 512 of 192, 2 waves).
+bool narrow_tiles(const GemmBatch& b, int layout, int epi) {
+    if (layout != GEMM_NN || epi == EPI_CE_STATS) return false;
+    if (tile_count(b, 192) > 0x7fffffff / 16) return false;     // keep the grid size in range
+    const int64_t cus = cu_count();
+    const int64_t w4 = (tile_count(b, 256) + cus - 1) / cus;
+    const int64_t w3 = (tile_count(b, 192) + cus - 1) / cus;
+    return 7 * w3 < 8 * w4 - 1;       // 7/8·w3 < w4 by more than 1/8 of a wave
+}
+
 hipError_t launch(const GemmBatch& b, int layout, int epi, int64_t ldaux, int64_t K,
                   bool out_bf16, hipStream_t stream)
 {
+    const int nj = narrow_tiles(b, layout, epi) ? 3 : 4;
+    const int tn_w = 64 * nj;
     int per_xcd = 0;
     if (b.band) {
-        const int tiles_m = (b.M[0] + BM - 1) / BM, tiles_n = (b.N[0] + BN - 1) / BN;
+        const int tiles_m = (b.M[0] + BM - 1) / BM, tiles_n = (b.N[0] + tn_w - 1) / tn_w;
         per_xcd = ((tiles_m / 8 + GROUP_M - 1) / GROUP_M) * GROUP_M * tiles_n * b.count;
     } else {
         for (int g = 0; g < b.count; ++g)
-            per_xcd += (((b.M[g] + BM - 1) / BM) * ((b.N[g] + BN - 1) / BN) + 7) / 8;
+            per_xcd += (((b.M[g] + BM - 1) / BM) * ((b.N[g] + tn_w - 1) / tn_w) + 7) / 8;
     }
     if (per_xcd == 0) return hipSuccess;
     const dim3 grid(8 * per_xcd), block(NTHREADS);
     const bool ck = (K % BK) != 0;
-#define TP_GEMM(L, E, OB)                                                                      \
+#define TP_GEMM_NJ(L, E, OB, NJ)                                                               \
     do {                                                                                       \
         if (ck)                                                                                \
-            hipLaunchKernelGGL((gemm_bf16_kernel<L, E, OB, true>), grid, block, 0, stream, b,  \
-                               ldaux, (int)K);                                                 \
+            hipLaunchKernelGGL((gemm_bf16_kernel<L, E, OB, true, NJ>), grid, block, 0, stream, \
+                               b, ldaux, (int)K);                                              \
         else                                                                                   \
-            hipLaunchKernelGGL((gemm_bf16_kernel<L, E, OB, false>), grid, block, 0, stream, b, \
-                               ldaux, (int)K);                                                 \
+            hipLaunchKernelGGL((gemm_bf16_kernel<L, E, OB, false, NJ>), grid, block, 0,        \
+                               stream, b, ldaux, (int)K);                                      \
         return hipGetLastError();                                                              \
+    } while (0)
+#define TP_GEMM(L, E, OB) TP_GEMM_NJ(L, E, OB, NJ_MAX)
+#define TP_GEMM_NN(E, OB)                                                                      \
+    do {                                                                                       \
+        if (nj == 3) TP_GEMM_NJ(GEMM_NN, E, OB, 3);                                            \
+        TP_GEMM_NJ(GEMM_NN, E, OB, NJ_MAX);                                                    \
     } while (0)
     switch (layout) {
     case GEMM_NN:
-        if (epi == EPI_NONE) { if (out_bf16) TP_GEMM(GEMM_NN, EPI_NONE, true); TP_GEMM(GEMM_NN, EPI_NONE, false); }
-        if (epi == EPI_GELU) { if (out_bf16) TP_GEMM(GEMM_NN, EPI_GELU, true); TP_GEMM(GEMM_NN, EPI_GELU, false); }
-        if (epi == EPI_DUAL && out_bf16) TP_GEMM(GEMM_NN, EPI_DUAL, true);
+        if (epi == EPI_NONE) { if (out_bf16) TP_GEMM_NN(EPI_NONE, true); TP_GEMM_NN(EPI_NONE, false); }
+        if (epi == EPI_GELU) { if (out_bf16) TP_GEMM_NN(EPI_GELU, true); TP_GEMM_NN(EPI_GELU, false); }
+        if (epi == EPI_DUAL && out_bf16) TP_GEMM_NN(EPI_DUAL, true);
         break;
     case GEMM_NT:
         if (epi == EPI_NONE) { if (out_bf16) TP_GEMM(GEMM_NT, EPI_NONE, true); TP_GEMM(GEMM_NT, EPI_NONE, false); }
@@ -651,7 +711,9 @@ hipError_t launch(const GemmBatch& b, int layout, int epi, int64_t ldaux, int64_
         if (epi == EPI_NONE) { if (out_bf16) TP_GEMM(GEMM_TN, EPI_NONE, true); TP_GEMM(GEMM_TN, EPI_NONE, false); }
         break;
     }
+#undef TP_GEMM_NN
 #undef TP_GEMM
+#undef TP_GEMM_NJ
     return hipErrorInvalidValue;      // a layout / epilogue pair with no kernel
 }
 }  // namespace
@@ -659,7 +721,8 @@ hipError_t launch(const GemmBatch& b, int layout, int epi, int64_t ldaux, int64_
 hipError_t gemm_bf16_grouped(const GemmBatch& batch, int layout, int epi, int64_t ldaux,
                              int64_t K, bool out_bf16, hipStream_t stream)
 {
-    if (batch.count <= 0 || batch.count > kMaxBatch || K <= 0) return hipSuccess;
+    if (batch.count > kMaxBatch || K <= 0) return hipErrorInvalidValue;
+    if (batch.count <= 0) return hipSuccess;
     GemmBatch b = batch;
     b.band = 0;
     return launch(b, layout, epi, ldaux, K, out_bf16, stream);
@@ -669,6 +732,7 @@ hipError_t gemm_bf16_batched(const GemmBatch& batch, int layout, int epi, int64_
                              int64_t ldb, int64_t ldc, int64_t ldaux, int64_t M, int64_t N,
                              int64_t K, bool out_bf16, hipStream_t stream)
 {
+    if (batch.count > kMaxBatch || K <= 0) return hipErrorInvalidValue;
     if (M <= 0 || N <= 0 || batch.count <= 0) return hipSuccess;
     GemmBatch b = batch;
     for (int g = 0; g < b.count; ++g) {
