@@ -310,6 +310,43 @@ def test_attn_heads_sum_to_full_mha():
     assert_bf16(Z, full, per_row=True)
 
 
+def _core_ref(qkv, b, s, Hl, d, causal):
+    """The oracle's attention over qkv = [Q | K | V] of each sequence."""
+    HD = Hl * d
+    out = np.empty((b * s, HD))
+    for beta in range(b):
+        seq = qkv[beta * s:(beta + 1) * s]
+        out[beta * s:(beta + 1) * s] = oracle.attention_rows(
+            seq[:, :HD], seq[:, HD:2 * HD], seq[:, 2 * HD:], np.arange(s), Hl, d, causal)
+    return out
+
+
+def _one_workgroup_per_block(n_bh, s, causal, cus=256):
+    """The launcher's rule: query blocks of 128 take one 4-wave workgroup each
+    unless the key tiles of all blocks, spread over two such workgroups per
+    CU, come to less than 0.7 of the longest block's; then every block's
+    keys are split over an 8-wave workgroup."""
+    n_max = -(-s // 64)
+    nqb = -(-s // 128)
+    per_head = sum(-(-min(s, 128 * (q + 1)) // 64) if causal else n_max for q in range(nqb))
+    return 10 * n_bh * per_head >= 7 * n_max * 2 * cus
+
+
+@pytest.mark.parametrize("b,s,Hl,causal", [(8, 320, 30, True), (4, 200, 64, False)])
+def test_attention_core_many_heads(b, s, Hl, causal):
+    """Enough query blocks that each runs as one 4-wave workgroup (the
+    block-shape path); the small cases above split every block's keys over
+    an 8-wave workgroup."""
+    banner(f"attention core many heads b={b} s={s} Hl={Hl} causal={causal}")
+    assert _one_workgroup_per_block(b * Hl, s, causal)
+    assert not _one_workgroup_per_block(2 * 2, 256, True)
+    d = 128
+    qkv = gen((b * s, 3 * Hl * d), 1.0, 58, "x")
+    O = tts.tp_attention_core(qkv.to(DEV), b, s, Hl, d, causal)
+    torch.cuda.synchronize()
+    assert_bf16(O, _core_ref(qkv, b, s, Hl, d, causal), per_row=True)
+
+
 def test_attention_core_long_sequence():
     """s = 4100: 33 query blocks and 65 key tiles, a ragged end; sampled rows
     on both sides of tile boundaries far into the sequence."""

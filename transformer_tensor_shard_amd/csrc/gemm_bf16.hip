@@ -626,7 +626,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
 
 }  // namespace
 
-namespace {
 // Compute units of the current device (256 on MI355X), for the tile-width
 // choice; queried once per device.
 int cu_count() {
@@ -641,6 +640,7 @@ int cu_count() {
     return n;
 }
 
+namespace {
 // Workgroups of a launch with tiles tn_w columns wide (one 256 x tn_w tile each).
 int64_t tile_count(const GemmBatch& b, int tn_w) {
     int64_t t = 0;

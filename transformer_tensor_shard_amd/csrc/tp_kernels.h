@@ -139,6 +139,10 @@ hipError_t ce_rank_reduce(const float* tiles, int ntn, int64_t M, float* stats,
 hipError_t ce_combine(const float* stats, int P, int64_t M, float* loss, float* loss_mean,
                       hipStream_t stream);
 
+// Compute units of the current device (256 on MI355X; queried once per
+// device), for launch-shape choices.
+int cu_count();
+
 // Register-only MFMA 16x16x32 bf16 loop: `blocks` workgroups of 8 waves, each
 // wave issuing 32 * iters MFMAs; out receives blocks * 512 floats.
 hipError_t mfma_probe(float* out, int blocks, int iters, hipStream_t stream);
