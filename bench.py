@@ -104,6 +104,16 @@ def measured_traffic(path=TRAFFIC_FILE, source_hash=None):
     return c.get("hbm_bytes_per_launch") if c else None
 
 
+def component_time(fn, stream):
+    """Average ms of fn() alone: after a warm-up of about 0.05 s, over enough
+    launches for about 0.1 s (3 to 500)."""
+    import torch
+    t1, _ = event_time(fn, 1, stream)
+    n = int(min(500, max(3, 0.05e3 / max(t1, 1e-3))))
+    event_time(fn, n, stream)
+    return event_time(fn, int(min(500, max(3, 0.1e3 / max(t1, 1e-3)))), stream)
+
+
 def event_time(fn, reps, stream):
     """Average ms of fn() over reps launches, bracketed by HIP events."""
     import torch
@@ -277,15 +287,18 @@ def dominant_kernel(w, tts, torch, X, Ws, dev):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: at least 20 and about 0.25 s of steps, at most 2000)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps first (default: at least 3 and about 0.1 s of steps)")
     ap.add_argument("--workload", default="block_bf16_h12288_tp8")
     ap.add_argument("--no-training", action="store_true",
                     help="skip the MLP-backward measurement added to the block line")
     ap.add_argument("--mode", default="step", choices=["step", "kernel", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=768,
-                    help="tokens of sequence 0 the oracle computes for the CPU baseline")
+    ap.add_argument("--cpu-rows", type=int, default=None,
+                    help="tokens the oracle computes for the CPU baseline (default: sized for "
+                         "10-30 s on 16 host threads, or the whole workload where that is less)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -305,6 +318,9 @@ def main():
     stream = torch.cuda.current_stream()
     tts.lib()
 
+    if args.mode in ("copy", "kernel"):
+        args.warmup = 1 if args.warmup is None else args.warmup
+        args.steps = 3 if args.steps is None else args.steps
     if args.mode == "copy":
         src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
@@ -345,8 +361,7 @@ def main():
 
         # the dominant kernel (the grouped GeLU GEMM) is timed inside every
         # timed step, by events the library records around its launch
-        kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)]
+        kev = []            # one pair per timed step, made once the step count is known
 
         def step(i=None):
             tts.tp_block_shard(x, Wqkv, Wo, A, B, w.b, w.s, w.H, w.d, out=out, ws=ws,
@@ -450,10 +465,28 @@ def main():
     kernel, kern_flops, kern_name = dominant_kernel(w, tts, torch, X_k, W_k, dev)
 
     # ---------------------------------------------------------------- timing
-    log(f"warmup {args.warmup} step(s)")
-    for _ in range(args.warmup):
-        step()
+    # Short steps get more of both by default, so that the clocks have settled
+    # and the mean covers a quarter second: the warm-up runs at least 3 steps
+    # and 0.1 s, the timed region at least 20 steps and 0.25 s (at most 2000).
+    auto_warm = args.warmup is None
+    n_warm = 3 if auto_warm else args.warmup
     torch.cuda.synchronize()
+    tw = time.time()
+    done = 0
+    while done < n_warm or (auto_warm and time.time() - tw < 0.1):
+        step()
+        done += 1
+        if auto_warm:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    est = (time.time() - tw) / max(done, 1)
+    args.warmup = done
+    if args.steps is None:
+        args.steps = int(min(2000, max(20, 0.25 / max(est, 1e-6))))
+    log(f"warmup {args.warmup} step(s), {1000 * est:.3f} ms each")
+    if w.kind == "block":
+        kev.extend((torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.steps))
     log(f"timing {args.steps} step(s)")
     # one event after every step: the whole region gives the mean, the
     # differences the per-step spread
@@ -536,7 +569,7 @@ def main():
         }
         for name, (fn, fl, by) in items.items():
             fn()
-            t, _ = event_time(fn, 3, stream)
+            t, _ = component_time(fn, stream)
             c = {"ms": round(t, 4)}
             if fl:
                 c["tflops"] = round(fl / (t * 1e-3) / 1e12, 1)
@@ -547,6 +580,33 @@ def main():
             components[name] = c
             log(f"component {name}: {c}")
         del qkv_all, o_all, y_all, parts
+    if w.kind in ("mlp", "attn"):
+        # the launches of one shard call, one by one
+        if w.kind == "mlp":
+            Yc = torch.empty(M, f, dtype=torch.bfloat16, device=dev)
+            items = {
+                "gelu_gemm": (lambda: tts.tp_linear(x, A0, gelu=True, out=Yc), 2 * M * h * f),
+                "row_gemm_f32_partial": (lambda: tts.tp_linear(Yc, B0, out=out), 2 * M * h * f),
+            }
+        else:
+            HD = w.Hl * w.d
+            att = w.attn_flops_rank()
+            qkv_c = torch.empty(M, 3 * HD, dtype=torch.bfloat16, device=dev)
+            o_c = torch.empty(M, HD, dtype=torch.bfloat16, device=dev)
+            items = {
+                "qkv_gemm": (lambda: tts.tp_linear(x, Wqkv0, out=qkv_c), att["qkv"]),
+                "attention_core": (lambda: tts.tp_attention_core(qkv_c, w.b, w.s, w.Hl, w.d, True,
+                                                                 out=o_c), att["core"]),
+                "wo_gemm_f32_partial": (lambda: tts.tp_linear(o_c, Wo0, out=out), att["wo"]),
+            }
+        for name, (fn, fl) in items.items():
+            fn()
+            t, _ = component_time(fn, stream)
+            c = {"ms": round(t, 4), "tflops": round(fl / (t * 1e-3) / 1e12, 1),
+                 "pct_peak": round(100 * fl / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 1)}
+            components[name] = c
+            log(f"component {name}: {c}")
+        del items
     if w.kind == "mlp_bwd":
         fl1 = 2 * M * h * f
         dYc = torch.empty(M, f, dtype=torch.bfloat16, device=dev)
@@ -562,7 +622,7 @@ def main():
         }
         for name, (fn, fl, by) in items.items():
             fn()
-            t, _ = event_time(fn, 3, stream)
+            t, _ = component_time(fn, stream)
             c = {"ms": round(t, 4), "tflops": round(fl / (t * 1e-3) / 1e12, 1),
                  "pct_peak": round(100 * fl / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 1)}
             components[name] = c
@@ -586,7 +646,7 @@ def main():
         }
         for name, (fn, flc) in items.items():
             fn()
-            t, _ = event_time(fn, 3, stream)
+            t, _ = component_time(fn, stream)
             c = {"ms": round(t, 4), "tflops": round(flc / (t * 1e-3) / 1e12, 1),
                  "pct_peak": round(100 * flc / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 1)}
             components[name] = c
@@ -606,7 +666,7 @@ def main():
         }
         for name, (fn, fl, by) in items.items():
             fn()
-            t, _ = event_time(fn, 3, stream)
+            t, _ = component_time(fn, stream)
             c = {"ms": round(t, 4)}
             if fl:
                 c["tflops"] = round(fl / (t * 1e-3) / 1e12, 1)
@@ -787,12 +847,24 @@ def attn_backward_rank0(w, wl, tts, torch, x, Wqkv0, Wo0, dev, stream):
     return res
 
 
+# Default CPU-baseline samples (tokens), sized from the oracle's rates on 16
+# host threads for 10-30 s each, or the whole workload where that is less:
+# block, all of sequence 0 (~15 s); the MLP and attention shards, every token
+# (C3 ~7 s, the others under 3 s); the backward of the attention share, four
+# whole sequences (~14 s); the MLP backward and the vocabulary ends, 4096
+# tokens (~12 s); the K/V split takes all its (sequence, head) pairs (~9 s).
+CPU_SAMPLE_TOKENS = {"block": 2048, "attn_bwd": 4 * 2048, "mlp_bwd": 4096, "vocab": 4096}
+
+
 def cpu_baseline(w, rows_req, env):
-    """The fp64 oracle, as it stands, on the first tokens of sequence 0."""
+    """The fp64 oracle, as it stands, on a bounded sample of the workload:
+    the first tokens (sequence-major) of its batch."""
     import numpy as np
     import oracle
     from synth import workloads as wl
 
+    if rows_req is None:
+        rows_req = CPU_SAMPLE_TOKENS.get(w.kind, 1 << 62)
     if w.kind == "block":
         R = min(rows_req, w.s)
         rows = np.arange(R)
@@ -833,7 +905,7 @@ def cpu_baseline(w, rows_req, env):
         sample = (f"tokens 0..{R - 1}: the embedding lookup and the cross-entropy of all {w.P} "
                   f"ranks; {fl / 1e12:.3f} TFLOP")
     elif w.kind == "kvsplit":
-        n = min(96, w.b * w.H)                      # about 10 s of host time
+        n = w.b * w.H                               # every (sequence, head) pair
         qkv_cpu = env["qkv_cpu"]
         HD = w.H * w.d
         log(f"oracle: K/V-split attention of {n} (sequence, head) pairs")
@@ -850,18 +922,22 @@ def cpu_baseline(w, rows_req, env):
         sample = (f"{n} (sequence, head) pairs, all {w.P} ranks' partial scores, the softmax and "
                   f"the output slices; {fl / 1e12:.4f} TFLOP counted as on the GPU")
     elif w.kind == "attn_bwd":
-        # whole sequences: the backward of a causal sequence involves all of it
-        R = min(rows_req, w.s)
+        # whole sequences (the backward of a causal sequence involves all of
+        # it), or sequence 0 cut to fewer tokens
+        nseq = max(1, min(w.b, rows_req // w.s))
+        R = w.s if rows_req >= w.s else rows_req
         X_cpu, Wqkv_cpu, Wo_cpu, dZ_cpu = (env[k] for k in ("X_cpu", "Wqkv_cpu", "Wo_cpu",
                                                              "dZ_cpu"))
-        log(f"oracle: attention backward over sequence 0 truncated to {R} tokens")
+        log(f"oracle: attention backward over {nseq} sequence(s) of {R} tokens")
         t0 = time.time()
-        oracle.attn_shard_backward(X_cpu[:R], 1, R, Wqkv_cpu, Wo_cpu, dZ_cpu[:R], w.Hl, w.d, True)
+        oracle.attn_shard_backward(X_cpu[:nseq * R], nseq, R, Wqkv_cpu, Wo_cpu, dZ_cpu[:nseq * R],
+                                   w.Hl, w.d, True)
         dt = time.time() - t0
         HD = w.Hl * w.d
-        fl = 2 * (2 * R * w.h * 3 * HD) + 2 * (2 * R * HD * w.h) + 10 * w.Hl * w.d * R * (R + 1) // 2
-        sample = (f"the attention-share backward of one sequence of {R} tokens (its causal "
-                  f"prefix of sequence 0); {fl / 1e12:.3f} TFLOP counted, the oracle's "
+        fl = nseq * (2 * (2 * R * w.h * 3 * HD) + 2 * (2 * R * HD * w.h)
+                     + 10 * w.Hl * w.d * R * (R + 1) // 2)
+        sample = (f"the attention-share backward of {nseq} sequence(s) of {R} tokens (the causal "
+                  f"prefix of each); {fl / 1e12:.3f} TFLOP counted, the oracle's "
                   f"recomputation of the forward not counted")
     elif w.kind == "mlp_bwd":
         R = min(rows_req, w.M)
@@ -876,16 +952,19 @@ def cpu_baseline(w, rows_req, env):
                   f"batch); {fl / 1e12:.3f} TFLOP counted, the oracle's recomputation of Y "
                   f"(a further {2 * R * w.h * w.f / 1e12:.3f} TFLOP) not counted")
     else:
-        R = min(rows_req, w.s)
+        R = min(rows_req, w.b * w.s)                # tokens, sequence-major
         X_cpu, Wqkv_cpu, Wo_cpu = env["X_cpu"], env["Wqkv_cpu"], env["Wo_cpu"]
-        log(f"oracle: attention shard rows 0..{R - 1} of sequence 0")
+        log(f"oracle: attention shard rows 0..{R - 1}")
         t0 = time.time()
         oracle.attn_shard_rows(X_cpu, w.b, w.s, Wqkv_cpu, Wo_cpu, w.Hl, w.d, True,
                                np.arange(R))
         dt = time.time() - t0
         HD = w.Hl * w.d
-        fl = 2 * R * w.h * 3 * HD + 4 * HD * R * (R + 1) // 2 + 2 * R * HD * w.h
-        sample = f"tokens 0..{R - 1} of sequence 0 of the attention shard; {fl / 1e12:.3f} TFLOP"
+        full, part = divmod(R, w.s)                 # whole sequences, then a prefix
+        pairs = full * w.s * (w.s + 1) // 2 + part * (part + 1) // 2
+        fl = 2 * R * w.h * 3 * HD + 4 * HD * pairs + 2 * R * HD * w.h
+        sample = (f"tokens 0..{R - 1} of the attention shard ({full} whole sequence(s)"
+                  f"{f' and {part} tokens of the next' if part else ''}); {fl / 1e12:.3f} TFLOP")
     log(f"oracle: {dt:.1f} s")
     return {"value": round(fl / dt / 1e12, 4), "unit": "TFLOP/s",
             "cores": max(oracle.num_threads(), blas_threads()), "kind": "oracle",
