@@ -1,14 +1,15 @@
-"""GPU parity of the forward GEMM with 192-column output tiles.
+"""GPU parity of the GEMM with 192-column output tiles.
 
-A forward (NN) product whose 256-column tiles would leave the last wave of
-workgroups mostly empty runs with 192-column tiles instead (the launcher's
+A product whose 256-column tiles would leave the last wave of workgroups
+mostly empty runs with 192-column tiles instead (the launcher's
 choice; with 256 compute units it is taken for every shape below, and for
 none of the smaller shapes in test_gpu_parity.py).  The arithmetic per
 output is the same K loop, so each case is held to the same bar as the
 256-column kernel: f32 output within 1e-4 of the oracle, bf16 output within
 the bf16 bar.  The shapes cover ragged M, N and K, bias, GeLU, the training
-forward's two outputs, the shared-X band order and a grouped launch whose
-products differ in M and N.
+forward's two outputs, the shared-X band order, a grouped launch whose
+products differ in M and N, and the transposed-operand layouts of the
+backward (with the GeLU-backward epilogue).
 """
 import math
 
@@ -109,3 +110,31 @@ def test_narrow_grouped_different_shapes():
     torch.cuda.synchronize()
     for A, B, C in zip(As, Bs, outs):
         assert_f32(C, oracle.matmul(A, B), bar=1e-4)
+
+
+def test_narrow_nt_and_gelu_bwd():
+    """B stored [N,K] (the input-gradient layout), plain and with the GeLU
+    backward epilogue C = (A·B^T) ⊙ GeLU'(aux)."""
+    M, N, K = 2304, 7680, 136
+    banner(f"narrow tiles NT M={M} N={N} K={K}")
+    A = gen((M, K), 1.0, 506, "x")
+    B = gen((N, K), 1 / math.sqrt(K), 506, "A")
+    aux = gen((M, N), 1.0, 506, "preact")
+    C = tts.tp_matmul(A.to(DEV), B.to(DEV), trans_b=True, out_dtype=torch.float32)
+    G = tts.tp_matmul(A.to(DEV), B.to(DEV), trans_b=True, epilogue="gelu_bwd", aux=aux.to(DEV),
+                      out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    ref = oracle.matmul(A, B.t().contiguous())
+    assert_f32(C, ref, bar=1e-4)
+    assert_bf16(G, ref * oracle.gelu_grad(aux))
+
+
+def test_narrow_tn():
+    """A stored [K,M] (the weight-gradient layout)."""
+    M, N, K = 2304, 7680, 200
+    banner(f"narrow tiles TN M={M} N={N} K={K}")
+    A = gen((K, M), 1.0, 507, "x")
+    B = gen((K, N), 1 / math.sqrt(K), 507, "A")
+    C = tts.tp_matmul(A.to(DEV), B.to(DEV), trans_a=True, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert_f32(C, oracle.matmul(A.t().contiguous(), B), bar=1e-4)

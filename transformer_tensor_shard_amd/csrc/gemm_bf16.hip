@@ -649,14 +649,14 @@ int64_t tile_count(const GemmBatch& b, int tn_w) {
     return t;
 }
 
-// 192-column tiles for a forward (NN) product whose 256-column tiles fill the
-// last of their waves of workgroups (one per CU) badly.  The cost model: a
+// 192-column tiles for a product whose 256-column tiles fill the last of their
+// waves of workgroups (one per CU) badly.  The cost model: a
 // wave of 256-column tiles takes 1, a wave of 192-column tiles 7/8 (the K
 // loop is bound by the L2 requests of a tile's A and B panels, 256 + 192
 // rows against 256 + 256).  Measured on MI355X at [8192 x 4096]·[4096 x 3072]
 // (384 tiles of 256 columns, 1.5 waves; 512 of 192, 2 waves).
 bool narrow_tiles(const GemmBatch& b, int layout, int epi) {
-    if (layout != GEMM_NN || epi == EPI_CE_STATS) return false;
+    if (epi == EPI_CE_STATS) return false;
     if (tile_count(b, 192) > 0x7fffffff / 16) return false;     // keep the grid size in range
     const int64_t cus = cu_count();
     const int64_t w4 = (tile_count(b, 256) + cus - 1) / cus;
@@ -690,28 +690,26 @@ hipError_t launch(const GemmBatch& b, int layout, int epi, int64_t ldaux, int64_
                                stream, b, ldaux, (int)K);                                      \
         return hipGetLastError();                                                              \
     } while (0)
-#define TP_GEMM(L, E, OB) TP_GEMM_NJ(L, E, OB, NJ_MAX)
-#define TP_GEMM_NN(E, OB)                                                                      \
+#define TP_GEMM(L, E, OB)                                                                      \
     do {                                                                                       \
-        if (nj == 3) TP_GEMM_NJ(GEMM_NN, E, OB, 3);                                            \
-        TP_GEMM_NJ(GEMM_NN, E, OB, NJ_MAX);                                                    \
+        if (nj == 3) TP_GEMM_NJ(L, E, OB, 3);                                                  \
+        TP_GEMM_NJ(L, E, OB, NJ_MAX);                                                          \
     } while (0)
     switch (layout) {
     case GEMM_NN:
-        if (epi == EPI_NONE) { if (out_bf16) TP_GEMM_NN(EPI_NONE, true); TP_GEMM_NN(EPI_NONE, false); }
-        if (epi == EPI_GELU) { if (out_bf16) TP_GEMM_NN(EPI_GELU, true); TP_GEMM_NN(EPI_GELU, false); }
-        if (epi == EPI_DUAL && out_bf16) TP_GEMM_NN(EPI_DUAL, true);
+        if (epi == EPI_NONE) { if (out_bf16) TP_GEMM(GEMM_NN, EPI_NONE, true); TP_GEMM(GEMM_NN, EPI_NONE, false); }
+        if (epi == EPI_GELU) { if (out_bf16) TP_GEMM(GEMM_NN, EPI_GELU, true); TP_GEMM(GEMM_NN, EPI_GELU, false); }
+        if (epi == EPI_DUAL && out_bf16) TP_GEMM(GEMM_NN, EPI_DUAL, true);
         break;
     case GEMM_NT:
         if (epi == EPI_NONE) { if (out_bf16) TP_GEMM(GEMM_NT, EPI_NONE, true); TP_GEMM(GEMM_NT, EPI_NONE, false); }
         if (epi == EPI_GELU_BWD) { if (out_bf16) TP_GEMM(GEMM_NT, EPI_GELU_BWD, true); TP_GEMM(GEMM_NT, EPI_GELU_BWD, false); }
-        if (epi == EPI_CE_STATS && !out_bf16) TP_GEMM(GEMM_NT, EPI_CE_STATS, false);
+        if (epi == EPI_CE_STATS && !out_bf16) TP_GEMM_NJ(GEMM_NT, EPI_CE_STATS, false, NJ_MAX);
         break;
     case GEMM_TN:
         if (epi == EPI_NONE) { if (out_bf16) TP_GEMM(GEMM_TN, EPI_NONE, true); TP_GEMM(GEMM_TN, EPI_NONE, false); }
         break;
     }
-#undef TP_GEMM_NN
 #undef TP_GEMM
 #undef TP_GEMM_NJ
     return hipErrorInvalidValue;      // a layout / epilogue pair with no kernel
