@@ -690,6 +690,10 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, args.cpu_rows, locals())
+        if cpu["value"] > 0:
+            # labelled as extrapolated: the oracle's rate on the sample applied to
+            # one whole step's FLOPs, not a timed run of the whole step
+            cpu["extrapolated_step_s"] = round(flops / (cpu["value"] * 1e12), 1)
 
     result = {
         "metric": METRIC,
