@@ -765,7 +765,7 @@ def rank0_shards(w, tts, torch, x, A0, B0, Wqkv0, Wo0, dev, stream):
     slices (no grouped launch over ranks): tp_mlp_shard (the 175B-layer MLP
     shard, [16384 x 12288] x [12288 x 6144] then x [6144 x 12288]) and
     tp_attn_shard (8 sequences of 2048, 12 local heads of 128), timed with HIP
-    events like the step."""
+    events after a warm-up of their own, like the components."""
     M, h, f = w.M, w.h, w.f
     out = torch.empty(M, h, dtype=torch.float32, device=dev)
     ws_m = torch.empty(tts.tp_mlp_shard_workspace(M, f, x.dtype), dtype=torch.uint8, device=dev)
@@ -785,7 +785,7 @@ def rank0_shards(w, tts, torch, x, A0, B0, Wqkv0, Wo0, dev, stream):
     res = {}
     for name, (fn, fl, what) in items.items():
         fn()
-        t, _ = event_time(fn, 5, stream)
+        t, _ = component_time(fn, stream)
         res[name] = {"ms": round(t, 4), "tflops": round(fl / (t * 1e-3) / 1e12, 1),
                      "pct_peak": round(100 * fl / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
                      "flops": fl, "what": what}
@@ -810,7 +810,7 @@ def mlp_backward_rank0(w, wl, tts, torch, x, A0, B0, dev, stream):
                                device=dev))
     fn = lambda: tts.tp_mlp_shard_backward(x, A0, B0, Y, Yp, dZ, **outs)
     fn()
-    t, _ = event_time(fn, 5, stream)
+    t, _ = component_time(fn, stream)
     fl = 8 * M * h * f
     res = {"mlp_shard_backward_rank0": {
         "ms": round(t, 4), "tflops": round(fl / (t * 1e-3) / 1e12, 1),
@@ -837,7 +837,7 @@ def attn_backward_rank0(w, wl, tts, torch, x, Wqkv0, Wo0, dev, stream):
     fn = lambda: tts.tp_attn_shard_backward(x, Wqkv0, Wo0, qkv, O, lse, dZ, w.b, w.s, w.Hl,
                                             w.d, **outs)
     fn()
-    t, _ = event_time(fn, 5, stream)
+    t, _ = component_time(fn, stream)
     fl = w.attn_bwd_flops_rank()["total"]
     res = {"attn_shard_backward_rank0": {
         "ms": round(t, 4), "tflops": round(fl / (t * 1e-3) / 1e12, 1),
@@ -854,10 +854,10 @@ def attn_backward_rank0(w, wl, tts, torch, x, Wqkv0, Wo0, dev, stream):
 # Default CPU-baseline samples (tokens), sized from the oracle's rates on 16
 # host threads for 10-30 s each, or the whole workload where that is less:
 # block, all of sequence 0 (~15 s); the MLP and attention shards, every token
-# (C3 ~7 s, the others under 3 s); the backward of the attention share, four
-# whole sequences (~14 s); the MLP backward and the vocabulary ends, 4096
-# tokens (~12 s); the K/V split takes all its (sequence, head) pairs (~9 s).
-CPU_SAMPLE_TOKENS = {"block": 2048, "attn_bwd": 4 * 2048, "mlp_bwd": 4096, "vocab": 4096}
+# (3 s or less); the backward of the attention share, all 8 sequences
+# (~18 s); the MLP backward, 12288 tokens (~11 s); the vocabulary ends, 8192
+# tokens (~10 s); the K/V split takes all its (sequence, head) pairs (~9 s).
+CPU_SAMPLE_TOKENS = {"block": 2048, "attn_bwd": 8 * 2048, "mlp_bwd": 12288, "vocab": 8192}
 
 
 def cpu_baseline(w, rows_req, env):

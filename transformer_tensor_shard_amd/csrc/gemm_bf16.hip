@@ -19,7 +19,10 @@
 // cross-entropy statistics of vocab-parallel logits (per row and column tile
 // the maximum and the exp-sum, plus the target's logit; no logits stored).
 //
-// Design: one 256x256 output tile per workgroup of 8 waves (two per SIMD).
+// Design: one 256x256 output tile per workgroup of 8 waves (two per SIMD);
+// a launch whose 256-column tiles would leave the last wave of workgroups
+// mostly empty uses 256x192 tiles instead (8x3 blocks per wave, see the
+// launcher).
 //  * wave w owns a 128x64 sub-tile: rows 128*((w&3)>>1), columns
 //    128*(w&1) + 64*(w>>2); that is 8x4 MFMA 16x16x32 bf16 blocks with 128
 //    f32 accumulators per lane.  The two waves on a SIMD (w and w+4) take the
