@@ -278,8 +278,10 @@ def dominant_kernel(w, tts, torch, X, Ws, dev):
     else:
         def launch():
             tts.tp_linear(X, Ws[0], gelu=gelu, out=outs[0])
-    name = "gemm_bf16_kernel<bf16 out, %s> %s[%dx%d]x[%dx%d]" % (
-        "GeLU" if gelu else "no epilogue",
+    cols = tts.tp_gemm_tile_cols([(M, N)] * len(Ws), K, epilogue="gelu" if gelu else "none")
+    kern = "gemm_bf16_w384_kernel" if cols == 384 else "gemm_bf16_kernel"
+    name = "%s<bf16 out, %s> (256x%d tiles) %s[%dx%d]x[%dx%d]" % (
+        kern, "GeLU" if gelu else "no epilogue", cols,
         ("grouped over %d ranks, each " % len(Ws)) if len(Ws) > 1 else "", M, K, K, N)
     return launch, 2 * M * N * K * len(Ws), name
 

@@ -311,6 +311,19 @@ tp_status tp_matmul_grouped(const void* const* A, const int64_t* lda, int trans_
                             void* const* C, const int64_t* ldc, const int64_t* M,
                             const int64_t* N, int count, int64_t K, int out, void* stream);
 
+/* tp_gemm_tile_cols -- the output-tile width, in columns, that the bf16 GEMM
+ * behind tp_linear, tp_linear_batched, tp_matmul and tp_matmul_grouped uses
+ * for a launch of `count` products (host arrays M[count], N[count]) with
+ * inner size K, layout (trans_a, trans_b) and epilogue as in tp_matmul, on
+ * the current device: 256, or 192 or 384 where fewer or better-filled waves
+ * of workgroups make the launch faster.  The width changes the speed only,
+ * never a result: every output element sees the same MFMA sequence over K.
+ * Host logic only (nothing is launched); with no GPU present it answers for
+ * 256 compute units.  Returns 0 for invalid arguments (count outside 1..16,
+ * a size <= 0, both operands transposed, an unknown epilogue). */
+int tp_gemm_tile_cols(int trans_a, int trans_b, int epilogue, int count, const int64_t* M,
+                      const int64_t* N, int64_t K);
+
 /* tp_attention_kv_split -- attention with Q, K and V split along the feature
  * dimension over P emulated ranks ("strategy B", K/V splitting, of the
  * ops-transformer article [ops-transformer] §3.1): rank r holds the features

@@ -48,6 +48,18 @@ def test_gemm_main_loop_variants_do_not_spill(usage):
         assert r["LDS Size"] <= 160 * 1024, (name, r)
 
 
+def test_gemm_384_column_variants_do_not_spill(usage):
+    """The 256x384-tile kernel holds 192 accumulators per lane and uses 253 of
+    the 256 VGPRs two waves per SIMD allow; a spill, or an accumulator array
+    left in scratch memory, would cost far more than the wider tile gains."""
+    ks = _kernels(usage["gemm_bf16.hip"], r"gemm_bf16_w384_kernel")
+    assert len(ks) == 4, sorted(ks)
+    for name, r in ks.items():
+        assert r["ScratchSize"] == 0 and r["VGPRs Spill"] == 0, (name, r)
+        assert r["Occupancy"] >= 2, (name, r)
+        assert r["LDS Size"] <= 160 * 1024, (name, r)
+
+
 def test_attention_forward_and_dq_do_not_spill(usage):
     for name, r in {**_kernels(usage["attention.hip"], "attn_fwd_kernel"),
                     **_kernels(usage["attention_bwd.hip"], "attn_bwd_dq_kernel")}.items():

@@ -2,8 +2,9 @@
 
 A product whose 256-column tiles would leave the last wave of workgroups
 mostly empty runs with 192-column tiles instead (the launcher's
-choice; with 256 compute units it is taken for every shape below, and for
-none of the smaller shapes in test_gpu_parity.py).  The arithmetic per
+choice; with 256 compute units it is taken for every shape below -- their K
+tails or layouts keep them off the 384-column kernel -- and for none of the
+smaller shapes in test_gpu_parity.py).  The arithmetic per
 output is the same K loop, so each case is held to the same bar as the
 256-column kernel: f32 output within 1e-4 of the oracle, bf16 output within
 the bf16 bar.  The shapes cover ragged M, N and K, bias, GeLU, the training
@@ -19,6 +20,7 @@ import torch
 import oracle
 import synth
 import transformer_tensor_shard_amd as tts
+from _tiles import tile_cols
 from _tol import assert_bf16, assert_f32
 
 pytestmark = pytest.mark.gpu
@@ -33,20 +35,17 @@ def gen(shape, sigma, seed, sub, dtype=torch.bfloat16):
     return synth.normal(shape, sigma, seed, sub, dtype)
 
 
-def tiles(M, N, w):
-    return -(-M // 256) * -(-N // w)
-
-
 def test_shapes_take_the_narrow_tiles():
-    """The cases below are in the regime the launcher's rule selects: with
-    256 compute units, 256-column tiles need w4 waves and 192-column ones
-    w3, and 7·w3 < 8·w4 - 1."""
-    cus = 256
-    for prods in ([(2304, 7680)], [(2250, 7560)], [(2048, 3072)] * 3,
-                  [(2304, 3840), (2100, 3896)]):
-        w4 = -(-sum(tiles(m, n, 256) for m, n in prods) // cus)
-        w3 = -(-sum(tiles(m, n, 192) for m, n in prods) // cus)
-        assert 7 * w3 < 8 * w4 - 1, prods
+    """The cases below are in the regime where the launcher's rule (restated
+    in _tiles.py) picks 192-column tiles, and the library agrees."""
+    for prods, K, kw in (([(2304, 7680)], 136, dict(epilogue="gelu")), ([(2250, 7560)], 200, {}),
+                         ([(2304, 7680)], 64, dict(epilogue="gelu_save")),
+                         ([(2048, 3072)] * 3, 72, dict(epilogue="gelu")),
+                         ([(2304, 3840), (2100, 3896)], 96, {}),
+                         ([(2304, 7680)], 136, dict(trans_b=True, epilogue="gelu_bwd")),
+                         ([(2304, 7680)], 200, dict(trans_a=True))):
+        assert tile_cols(prods, K, **kw) == 192, prods
+        assert tts.tp_gemm_tile_cols(prods, K, **kw) == 192, prods
 
 
 def test_narrow_bias_gelu_bf16():
@@ -87,7 +86,7 @@ def test_narrow_gelu_save():
 
 
 def test_narrow_shared_x_band_order():
-    count, M, N, K = 3, 2048, 3072, 64
+    count, M, N, K = 3, 2048, 3072, 72          # K tail: 72 = 64 + 8
     banner(f"narrow tiles shared X count={count} M={M} N={N} K={K}")
     X = gen((M, K), 1.0, 504, "x")
     Ws = [gen((K, N), 1 / math.sqrt(K), 504 + g, "A") for g in range(count)]

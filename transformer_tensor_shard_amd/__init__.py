@@ -22,7 +22,7 @@ __all__ = [
     "TpError", "tp_abi_version", "tp_mlp_shard", "tp_mlp_shard_workspace", "tp_attn_shard",
     "tp_attn_shard_workspace", "tp_partial_sum", "tp_block_shard", "tp_block_shard_workspace",
     "tp_linear", "tp_linear_batched", "tp_attention_core", "tp_layernorm", "tp_probe_mfma",
-    "tp_matmul", "tp_matmul_grouped", "tp_mlp_shard_train_fwd", "tp_mlp_shard_backward",
+    "tp_matmul", "tp_matmul_grouped", "tp_gemm_tile_cols", "tp_mlp_shard_train_fwd", "tp_mlp_shard_backward",
     "tp_mlp_shard_backward_workspace", "tp_attention_core_train", "tp_attention_core_backward",
     "tp_attn_shard_train_fwd", "tp_attn_shard_backward", "tp_attn_shard_backward_workspace",
     "tp_vocab_embedding_shard", "tp_vocab_ce_shard", "tp_vocab_ce_shard_workspace",
@@ -330,6 +330,21 @@ def tp_matmul(A, B, bias=None, *, trans_a=False, trans_b=False, epilogue="none",
         _stream(stream))
     _check(st, "tp_matmul")
     return (out, aux) if epilogue == "gelu_save" else out
+
+
+def tp_gemm_tile_cols(shapes, K: int, *, trans_a=False, trans_b=False, epilogue="none") -> int:
+    """Output-tile width (192, 256 or 384 columns) the bf16 GEMM uses for one
+    launch of the products `shapes` = [(M, N), ...] with inner size K on the
+    current device (256 compute units when there is none).  Host logic only."""
+    count = len(shapes)
+    I64 = ctypes.c_int64 * max(count, 1)
+    cols = _lib.load().tp_gemm_tile_cols(int(bool(trans_a)), int(bool(trans_b)),
+                                         _EPILOGUES[epilogue], count,
+                                         I64(*[m for m, _ in shapes]), I64(*[n for _, n in shapes]),
+                                         int(K))
+    if cols == 0:
+        raise ValueError(f"tp_gemm_tile_cols: invalid launch {shapes}, K={K}")
+    return cols
 
 
 def tp_matmul_grouped(As, Bs, *, trans_a=False, trans_b=False, outs=None,

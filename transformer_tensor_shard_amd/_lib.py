@@ -59,6 +59,8 @@ SIGNATURES = {
                                       _vp, _sz, _vp]),
     "tp_layernorm": (_int, [_vp, _int, _vp, _vp, _vp, ctypes.c_float, _i64, _i64, _vp]),
     "tp_probe_mfma": (_int, [_vp, _int, _int, _vp]),
+    "tp_gemm_tile_cols": (_int, [_int, _int, _int, _int, ctypes.POINTER(_i64),
+                                 ctypes.POINTER(_i64), _i64]),
     "tp_matmul": (_int, [_vp, _i64, _int, _vp, _i64, _int, _vp, _vp, _i64, _vp, _i64, _i64, _i64,
                          _i64, _int, _int, _vp]),
     "tp_matmul_grouped": (_int, [ctypes.POINTER(_vp), ctypes.POINTER(_i64), _int,

@@ -69,6 +69,7 @@
 // either (non-temporal loads halve throughput: they defeat the L2 sharing
 // that the tile order sets up).
 #include <atomic>
+#include <type_traits>
 
 #include "tp_kernels.h"
 
@@ -627,6 +628,283 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
     }
 }
 
+// ---- 256 x 384 output tiles ------------------------------------------------
+// The K loop of the 256 x 256 kernel is bound by the L2 requests of its
+// operand panels, so a wider tile, which needs fewer operand bytes per FLOP
+// ((256 + 384) / (256·384) against (256 + 256) / (256·256): 5/6), runs the
+// forward products faster: measured at the 175B layer shape, grouped over 8
+// ranks, 4-5% on the GeLU and QKV products, 6% on the row product and 7% on
+// W_o, with results bit-identical to the 256-column kernel (each output sees
+// the same MFMA sequence over K).
+//  * eight waves, wave w owning 128 x 96: rows 128·((w&3)>>1), columns
+//    192·(w&1) + 96·(w>>2), i.e. 8 x 6 MFMA 16x16x32 blocks with 192 f32
+//    accumulators per lane.  Two waves per SIMD give a wave 256 VGPRs, so the
+//    operands are held lean: the six B blocks of the k-step (24 VGPRs) and two
+//    A blocks (8).  Row mi's MFMAs run while the A block of row mi+1 is read;
+//    in the last row each B block is re-read for the next k-step right after
+//    its MFMA (253 VGPRs, no spills);
+//  * two 80 KiB stages (A 32 KiB, B 48 KiB) fill the 160 KiB of LDS.  A is
+//    staged as in the 256-column kernel; B as 64 K rows of 768 bytes with the
+//    same XOR swizzle (it depends on K row bits 0, 1 and 3 only, and keeps a
+//    unit inside its aligned group of 16);
+//  * the loads of the next K tile go out over the first 30 of the 48 MFMAs of
+//    a tile's first k-step (a window of 20 was 1-2% slower, 40 the same); the
+//    barrier that publishes them sits before the last row of the second
+//    k-step, after the last reads of the current stage;
+//  * the output tile is staged through the LDS in two (bf16) or four (f32)
+//    passes in which all eight waves take part.
+// NN layout only (the forward products), K a multiple of 64, no causal K
+// bound; the launcher picks it by the cost model of tile_cols().
+constexpr int W_NJ = 6, W_TN = 64 * W_NJ;              // 384 columns
+constexpr int W_ROWB = W_TN * 2;                        // 768 B per K row of the B tile
+constexpr int W_B_BYTES = BK * W_ROWB;                  // 48 KiB
+constexpr int W_STAGE = A_BYTES + W_B_BYTES;            // 80 KiB
+constexpr int W_BLOADS = W_B_BYTES / (NTHREADS * 16);   // B loads per wave per K tile
+constexpr int W_WINDOW = 30;
+static_assert(W_BLOADS == 6 && 2 * W_STAGE <= 160 * 1024, "two 80 KiB stages");
+template <int V>
+using IC = std::integral_constant<int, V>;
+
+// Schedule of one 32-wide k-step, MFMAs I .. R1·6-1 (row mi = I / 6): the A
+// read of the next row after each row's first MFMA, the B re-reads (two
+// transpose reads each) after the last row's MFMAs, and V direct-to-LDS loads
+// spread over the first W_WINDOW MFMAs.
+template <int V, int I, int R1>
+__device__ __forceinline__ void w_sched() {
+    constexpr int mi = I / W_NJ, nj = I % W_NJ;
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+    constexpr int nds = (nj == 0 ? 1 : 0) + (mi == NI - 1 ? 2 : 0);
+    if constexpr (nds > 0) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, nds, 0);
+    constexpr int nv = I < W_WINDOW ? ((I + 1) * V) / W_WINDOW - (I * V) / W_WINDOW : 0;
+    if constexpr (nv > 0) __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, nv, 0);
+    if constexpr (I + 1 < R1 * W_NJ) w_sched<V, I + 1, R1>();
+}
+
+template <int EPI, bool OUT_BF16>
+__global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_w384_kernel(GemmBatch batch, int K)
+{
+    static_assert(EPI == EPI_NONE || EPI == EPI_GELU, "plain and GeLU epilogues");
+    __shared__ __attribute__((aligned(1024))) char lds0[W_STAGE];
+    __shared__ __attribute__((aligned(1024))) char lds1[W_STAGE];
+
+    int grp, tm, tn;
+    if (batch.band ? !tile_coords_band(blockIdx.x, batch.count, (batch.M[0] + BM - 1) / BM,
+                                       (batch.N[0] + W_TN - 1) / W_TN, grp, tm, tn)
+                   : !tile_coords(blockIdx.x, batch, W_TN, grp, tm, tn))
+        return;
+    const int M = batch.M[grp], N = batch.N[grp];
+    const int64_t lda = batch.lda[grp], ldb = batch.ldb[grp], ldc = batch.ldc[grp];
+    const int m0 = tm * BM, n0 = tn * W_TN;
+    const __bf16* __restrict__ A = batch.A[grp];
+    const __bf16* __restrict__ B = batch.B[grp];
+    const float* __restrict__ bias = batch.bias[grp];
+    void* __restrict__ C = batch.C[grp];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+    const int wm = (wid & 3) >> 1, wn = wid & 1, wh = wid >> 2;
+    const __bf16* a_tile = A + (int64_t)m0 * lda;
+    const __bf16* b_tile = B + n0;
+
+    // direct-to-LDS loads.  A (256 rows of 128 B): load j of wave w fills rows
+    // 32w + 8j .. +7, as in the 256-column kernel.  B (64 K rows of 48 units):
+    // load j of wave w fills the physical units (6w + j)·64 .. +63 of the tile;
+    // physical unit p is K row p / 48, unit p % 48, and holds logical unit
+    // (p % 48) ^ mc_swz(row).  Columns past N read zeros.
+    unsigned a_off[LOADS], b_off[W_BLOADS];
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+        const int r = 32 * wid + 8 * j + (lane >> 3);
+        const int u = (lane & 7) ^ ((r >> 1) & 7);
+        a_off[j] = (m0 + r) < M ? (unsigned)(r * lda + u * 8) * 2u : OOB;
+    }
+#pragma unroll
+    for (int j = 0; j < W_BLOADS; ++j) {
+        const int p = (W_BLOADS * wid + j) * 64 + lane;
+        const int r = p / 48, u = (p % 48) ^ mc_swz(r);
+        b_off[j] = (n0 + u * 8) < N ? (unsigned)(r * ldb + u * 8) * 2u : OOB;
+    }
+    auto dma_tile = [&](int k0, char* stage) __attribute__((always_inline)) {
+        const int nrec = k0 < K ? 0x7ffffff0 : 0;     // past the last K tile: zeros
+        const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<__bf16*>(a_tile + k0), (short)0, nrec, 0x00020000);
+        const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<__bf16*>(b_tile + (int64_t)k0 * ldb), (short)0, nrec, 0x00020000);
+        char* sa = stage + wid * 4096;
+        char* sb = stage + A_BYTES + wid * (W_BLOADS * 1024);
+#pragma unroll
+        for (int j = 0; j < LOADS; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, LDS_PTR(void, sa + j * 1024), 16,
+                                                     a_off[j], 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < W_BLOADS; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(br, LDS_PTR(void, sb + j * 1024), 16,
+                                                     b_off[j], 0, 0, 0);
+    };
+    const int nk = K / BK;
+
+    // operand reads: A with 16-byte reads as in the 256-column kernel, B with
+    // transpose reads from the 768-byte rows
+    const int g = lane >> 4, gi = lane & 15;
+    const unsigned kc_rd = (lane & 15) * 128 + (((lane >> 4) ^ (((lane & 15) >> 1) & 7)) << 4);
+    const unsigned a_rd0 = wm * 128 * 128 + kc_rd;
+    const int wcol = wn * 192 + wh * 96;
+    unsigned b_rd[W_NJ];
+#pragma unroll
+    for (int nj = 0; nj < W_NJ; ++nj) {
+        const int row = 8 * g + (gi >> 2);
+        const int c = wcol + 16 * nj + 4 * (gi & 3);
+        b_rd[nj] = A_BYTES + row * W_ROWB + (((c >> 3) ^ mc_swz(row)) << 4) + (c & 7) * 2;
+    }
+
+    f32x4 acc[NI][W_NJ];
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int j = 0; j < W_NJ; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.0f;
+
+    bf16x8 fa[2], fb[W_NJ];
+    auto ld_a = [&](int slot, const char* base, int mi, int kk) __attribute__((always_inline)) {
+        fa[slot] = *(const bf16x8*)(base + ((a_rd0 + mi * 16 * 128) ^ (kk << 6)));
+    };
+    auto ld_b = [&](int nj, const char* base, int kk) __attribute__((always_inline)) {
+        const char* p = base + b_rd[nj] + kk * 32 * W_ROWB;
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, p));
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, p + 4 * W_ROWB));
+        fb[nj] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    // rows [R0, R1) of a 32-wide k-step whose operands come from (cb, ckk);
+    // the next k-step's come from (nb, nkk).  The row bounds are compile-time
+    // constants so that every accumulator index is one.
+    auto rows = [&](auto R0, auto R1, const char* cb, int ckk, const char* nb, int nkk)
+                    __attribute__((always_inline)) {
+        constexpr int r0 = decltype(R0)::value, r1 = decltype(R1)::value;
+#pragma unroll
+        for (int mi = r0; mi < r1; ++mi) {
+            if (mi < NI - 1) ld_a((mi + 1) & 1, cb, mi + 1, ckk);
+            else ld_a(0, nb, 0, nkk);
+#pragma unroll
+            for (int nj = 0; nj < W_NJ; ++nj) {
+                acc[mi][nj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[mi & 1], fb[nj],
+                                                                      acc[mi][nj], 0, 0, 0);
+                if (mi == NI - 1) ld_b(nj, nb, nkk);
+            }
+        }
+    };
+    // One K tile in stage `cur`.  Its first k-step issues the loads of the
+    // next K tile into `oth`, whose last reads came before the previous
+    // tile's barrier; the barrier before this tile's last row publishes them.
+    auto tile = [&](const char* cur, char* oth, int k_next) __attribute__((always_inline)) {
+        dma_tile(k_next, oth);
+        rows(IC<0>{}, IC<NI>{}, cur, 0, cur, 1);
+        w_sched<LOADS + W_BLOADS, 0, NI>();
+        __builtin_amdgcn_sched_barrier(0);
+        rows(IC<0>{}, IC<NI - 1>{}, cur, 1, cur, 1);
+        w_sched<0, 0, NI - 1>();
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(0x0F70);        // vmcnt(0): this wave's loads have landed
+        __syncthreads();                           // `oth` complete; `cur` no longer read
+        rows(IC<NI - 1>{}, IC<NI>{}, cur, 1, oth, 0);
+        w_sched<0, (NI - 1) * W_NJ, NI>();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    dma_tile(0, lds0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+#pragma unroll
+    for (int nj = 0; nj < W_NJ; ++nj) ld_b(nj, lds0, 0);
+    ld_a(0, lds0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+        tile(lds0, lds1, (kt + 1) * BK);
+        tile(lds1, lds0, (kt + 2) * BK);
+    }
+    if (kt < nk) tile(lds0, lds1, (kt + 1) * BK);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+
+    // ---- epilogue ------------------------------------------------------------
+    // Lane holds column (lane & 15) and rows 4·(lane >> 4) + r of each 16x16
+    // block.  Each pass stages some row blocks of every wave (the waves with
+    // wm = 0 into lds0, wm = 1 into lds1; rows four apart get their units
+    // XOR-ed apart), then the workgroup writes the staged rows with 16-byte
+    // row-contiguous stores.
+    const int lcol = wcol + (lane & 15);                     // + 16·nj
+    float bv[W_NJ];
+#pragma unroll
+    for (int nj = 0; nj < W_NJ; ++nj)
+        bv[nj] = (bias && n0 + lcol + 16 * nj < N) ? bias[n0 + lcol + 16 * nj] : 0.0f;
+    auto value = [&](int mi, int nj, int r) __attribute__((always_inline)) {
+        const float v = acc[mi][nj][r] + bv[nj];
+        return EPI == EPI_GELU ? gelu(v) : v;
+    };
+    char* half = wm ? lds1 : lds0;
+    if constexpr (OUT_BF16) {
+        // two passes of row blocks 4p .. 4p+3 (64 rows of each 128-row half)
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+#pragma unroll
+            for (int nj = 0; nj < W_NJ; ++nj) {
+                const int lc = lcol + 16 * nj;
+#pragma unroll
+                for (int m2 = 0; m2 < 4; ++m2)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int q = m2 * 16 + 4 * (lane >> 4) + r;
+                        *(__bf16*)(half + q * W_ROWB + (((lc >> 3) ^ (((q >> 2) & 3) << 1)) << 4) +
+                                   (lc & 7) * 2) = (__bf16)value(4 * p + m2, nj, r);
+                    }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < 128 * 48 / NTHREADS; ++i) {
+                const int idx = i * NTHREADS + tid;
+                const int lrow = idx / 48, unit = idx % 48, q = lrow & 63;
+                const char* src = (lrow < 64 ? lds0 : lds1) + q * W_ROWB +
+                                  ((unit ^ (((q >> 2) & 3) << 1)) << 4);
+                const int grow = m0 + (lrow >> 6) * 128 + 64 * p + q, gcol = n0 + unit * 8;
+                if (grow < M && gcol < N)
+                    st_out(*(const bf16x8*)src, (bf16x8*)((__bf16*)C + (int64_t)grow * ldc + gcol));
+            }
+            if (p == 0) __syncthreads();
+        }
+    } else {
+        // four passes of row blocks 2p, 2p+1 (32 rows of each half, 1536 B per row)
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+#pragma unroll
+            for (int nj = 0; nj < W_NJ; ++nj) {
+                const int lc = lcol + 16 * nj;
+#pragma unroll
+                for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int q = m2 * 16 + 4 * (lane >> 4) + r;
+                        *(float*)(half + q * 1536 + (((lc >> 2) ^ (((q >> 2) & 3) << 2)) << 4) +
+                                  (lc & 3) * 4) = value(2 * p + m2, nj, r);
+                    }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < 64 * 96 / NTHREADS; ++i) {
+                const int idx = i * NTHREADS + tid;
+                const int lrow = idx / 96, unit = idx % 96, q = lrow & 31;
+                const char* src = (lrow < 32 ? lds0 : lds1) + q * 1536 +
+                                  ((unit ^ (((q >> 2) & 3) << 2)) << 4);
+                const int grow = m0 + (lrow >> 5) * 128 + 32 * p + q, gcol = n0 + unit * 4;
+                if (grow < M && gcol < N)
+                    st_out(*(const f32x4*)src, (f32x4*)((float*)C + (int64_t)grow * ldc + gcol));
+            }
+            if (p < 3) __syncthreads();
+        }
+    }
+}
+
 }  // namespace
 
 // Compute units of the current device (256 on MI355X), for the tile-width
@@ -652,26 +930,47 @@ int64_t tile_count(const GemmBatch& b, int tn_w) {
     return t;
 }
 
-// 192-column tiles for a product whose 256-column tiles fill the last of their
-// waves of workgroups (one per CU) badly.  The cost model: a
-// wave of 256-column tiles takes 1, a wave of 192-column tiles 7/8 (the K
-// loop is bound by the L2 requests of a tile's A and B panels, 256 + 192
-// rows against 256 + 256).  Measured on MI355X at [8192 x 4096]·[4096 x 3072]
-// (384 tiles of 256 columns, 1.5 waves; 512 of 192, 2 waves).
-bool narrow_tiles(const GemmBatch& b, int layout, int epi) {
-    if (epi == EPI_CE_STATS) return false;
-    if (tile_count(b, 192) > 0x7fffffff / 16) return false;     // keep the grid size in range
-    const int64_t cus = cu_count();
-    const int64_t w4 = (tile_count(b, 256) + cus - 1) / cus;
-    const int64_t w3 = (tile_count(b, 192) + cus - 1) / cus;
-    return 7 * w3 < 8 * w4 - 1;       // 7/8·w3 < w4 by more than 1/8 of a wave
+// Whether a launch can take 256 x 384 tiles: the kernel covers the forward
+// layout with the plain and GeLU epilogues, K a multiple of 64, no causal K
+// bound.
+bool wide_ok(const GemmBatch& b, int layout, int epi, int64_t K) {
+    return layout == GEMM_NN && (epi == EPI_NONE || epi == EPI_GELU) && K % BK == 0 &&
+           !b.causal_k;
 }
 
+}  // namespace
+
+// Output-tile width of a launch: 256 columns, or 192 or 384 where a cost model
+// of the waves of workgroups (one workgroup per CU) says so.  The cost of a
+// wave, in sixteenths of a wave of 256-column tiles: 14 for 192 columns (the
+// K loop is bound by the L2 requests of a tile's A and B panels, 256 + 192
+// rows against 256 + 256), 23 for 384 (1.5 times the work, measured 4-7%
+// faster per FLOP).  Another width is taken only where it saves more than
+// 1/8 of a 256-column wave; ties keep the narrower tile.  Measured on MI355X:
+// [8192 x 4096]·[4096 x 3072] (384 tiles of 256 columns, 1.5 waves; 512 of
+// 192, 2 waves) and the 175B layer shape's products (48 waves of 256-column
+// tiles, 32 of 384).
+int gemm_tile_cols(const GemmBatch& b, int layout, int epi, int64_t K) {
+    if (epi == EPI_CE_STATS) return 256;
+    if (tile_count(b, 192) > 0x7fffffff / 16) return 256;     // keep the grid size in range
+    const int64_t cus = cu_count();
+    auto waves = [&](int w) { return (tile_count(b, w) + cus - 1) / cus; };
+    int best = 256;
+    int64_t cost = 16 * waves(256);
+    if (14 * waves(192) < cost - 2) {
+        best = 192;
+        cost = 14 * waves(192);
+    }
+    if (wide_ok(b, layout, epi, K) && 23 * waves(384) < cost - 2) best = 384;
+    return best;
+}
+
+namespace {
 hipError_t launch(const GemmBatch& b, int layout, int epi, int64_t ldaux, int64_t K,
                   bool out_bf16, hipStream_t stream)
 {
-    const int nj = narrow_tiles(b, layout, epi) ? 3 : 4;
-    const int tn_w = 64 * nj;
+    const int tn_w = gemm_tile_cols(b, layout, epi, K);
+    const int nj = tn_w / 64;
     int per_xcd = 0;
     if (b.band) {
         const int tiles_m = (b.M[0] + BM - 1) / BM, tiles_n = (b.N[0] + tn_w - 1) / tn_w;
@@ -682,6 +981,20 @@ hipError_t launch(const GemmBatch& b, int layout, int epi, int64_t ldaux, int64_
     }
     if (per_xcd == 0) return hipSuccess;
     const dim3 grid(8 * per_xcd), block(NTHREADS);
+    if (tn_w == W_TN) {
+        if (epi == EPI_GELU) {
+            if (out_bf16)
+                hipLaunchKernelGGL((gemm_bf16_w384_kernel<EPI_GELU, true>), grid, block, 0, stream, b, (int)K);
+            else
+                hipLaunchKernelGGL((gemm_bf16_w384_kernel<EPI_GELU, false>), grid, block, 0, stream, b, (int)K);
+        } else {
+            if (out_bf16)
+                hipLaunchKernelGGL((gemm_bf16_w384_kernel<EPI_NONE, true>), grid, block, 0, stream, b, (int)K);
+            else
+                hipLaunchKernelGGL((gemm_bf16_w384_kernel<EPI_NONE, false>), grid, block, 0, stream, b, (int)K);
+        }
+        return hipGetLastError();
+    }
     const bool ck = (K % BK) != 0;
 #define TP_GEMM_NJ(L, E, OB, NJ)                                                               \
     do {                                                                                       \

@@ -435,6 +435,21 @@ TP_EXPORT tp_status tp_matmul_grouped(const void* const* A, const int64_t* lda, 
     return launched(run_grouped(p, count, K, trans_a, trans_b, out, as_stream(stream)));
 }
 
+TP_EXPORT int tp_gemm_tile_cols(int trans_a, int trans_b, int epilogue, int count,
+                                const int64_t* M, const int64_t* N, int64_t K) {
+    if (!M || !N || count <= 0 || count > tpk::kMaxBatch || K <= 0) return 0;
+    if ((trans_a && trans_b) || epilogue < TP_EPI_NONE || epilogue > TP_EPI_GELU_SAVE) return 0;
+    tpk::GemmBatch gb = {};
+    gb.count = count;
+    for (int g = 0; g < count; ++g) {
+        if (M[g] <= 0 || N[g] <= 0 || M[g] >= kI32 || N[g] >= kI32) return 0;
+        gb.M[g] = (int)M[g];
+        gb.N[g] = (int)N[g];
+    }
+    const int layout = trans_a ? tpk::GEMM_TN : (trans_b ? tpk::GEMM_NT : tpk::GEMM_NN);
+    return tpk::gemm_tile_cols(gb, layout, gemm_epi(epilogue), K);
+}
+
 // ---- MLP shard: training forward and backward ------------------------------
 namespace {
 struct MlpBwdWs {

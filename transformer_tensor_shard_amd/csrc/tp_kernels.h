@@ -143,6 +143,10 @@ hipError_t ce_combine(const float* stats, int P, int64_t M, float* loss, float* 
 // device), for launch-shape choices.
 int cu_count();
 
+// Output-tile width (192, 256 or 384 columns) that gemm_bf16_grouped /
+// gemm_bf16_batched use for this launch on the current device.
+int gemm_tile_cols(const GemmBatch& b, int layout, int epi, int64_t K);
+
 // Register-only MFMA 16x16x32 bf16 loop: `blocks` workgroups of 8 waves, each
 // wave issuing 32 * iters MFMAs; out receives blocks * 512 floats.
 hipError_t mfma_probe(float* out, int blocks, int iters, hipStream_t stream);
