@@ -4,8 +4,10 @@ A launch is costed in waves of workgroups (one 256-row tile per workgroup,
 one workgroup per compute unit): a wave of 256-column tiles counts 16, of
 192-column tiles 14, of 384-column tiles 23.  A width other than 256 is
 taken only when it saves more than 2 (1/8 of a 256-column wave), 192 before
-384; 384-column tiles exist for the forward layout with the plain and GeLU
-epilogues and K a multiple of 64, and the cross-entropy statistics keep 256.
+384; 384-column tiles exist for the forward layout (plain, GeLU and the
+dual-store epilogues) and the input-gradient layout (B transposed: plain and
+GeLU backward) with K a multiple of 64, not for the weight-gradient layout
+(A transposed); the cross-entropy statistics keep 256.
 """
 
 
@@ -23,7 +25,8 @@ def tile_cols(prods, K, *, trans_a=False, trans_b=False, epilogue="none", cus=25
     best, cost = 256, 16 * waves(prods, 256, cus)
     if 14 * waves(prods, 192, cus) < cost - 2:
         best, cost = 192, 14 * waves(prods, 192, cus)
-    wide_ok = not trans_a and not trans_b and epilogue in ("none", "gelu") and K % 64 == 0
+    epis = ("none", "gelu_bwd") if trans_b else ("none", "gelu", "gelu_save")
+    wide_ok = not trans_a and epilogue in epis and K % 64 == 0
     if wide_ok and 23 * waves(prods, 384, cus) < cost - 2:
         best = 384
     return best

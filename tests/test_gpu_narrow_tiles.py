@@ -39,7 +39,7 @@ def test_shapes_take_the_narrow_tiles():
     """The cases below are in the regime where the launcher's rule (restated
     in _tiles.py) picks 192-column tiles, and the library agrees."""
     for prods, K, kw in (([(2304, 7680)], 136, dict(epilogue="gelu")), ([(2250, 7560)], 200, {}),
-                         ([(2304, 7680)], 64, dict(epilogue="gelu_save")),
+                         ([(2304, 7680)], 72, dict(epilogue="gelu_save")),
                          ([(2048, 3072)] * 3, 72, dict(epilogue="gelu")),
                          ([(2304, 3840), (2100, 3896)], 96, {}),
                          ([(2304, 7680)], 136, dict(trans_b=True, epilogue="gelu_bwd")),
@@ -72,7 +72,7 @@ def test_narrow_f32_ragged():
 
 def test_narrow_gelu_save():
     """The training forward's epilogue: C = GeLU(v) and aux = v, both bf16."""
-    M, N, K = 2304, 7680, 64
+    M, N, K = 2304, 7680, 72                    # K tail: 72 = 64 + 8
     banner(f"narrow tiles gelu_save M={M} N={N} K={K}")
     X = gen((M, K), 1.0, 503, "x")
     W = gen((K, N), 1 / math.sqrt(K), 503, "A")

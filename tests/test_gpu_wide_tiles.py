@@ -1,8 +1,10 @@
 """GPU parity of the GEMM with 256x384 output tiles.
 
-Forward-layout products (plain or GeLU epilogue, K a multiple of 64) whose
-waves of workgroups the wider tile fills better run on the 384-column
-kernel (the launcher's choice; each shape below is checked to take it).  Per
+Products in the forward layout (plain, GeLU and dual-store epilogues) and
+the input-gradient layout (B stored [N,K]: plain and GeLU-backward
+epilogues), K a multiple of 64, whose waves of workgroups the wider tile
+fills better run on the 384-column kernel (the launcher's choice; each shape
+below is checked to take it).  Per
 output element the K loop is the same MFMA sequence as in the 256-column
 kernel, so each case meets the same bars: f32 output within 1e-4 of the
 oracle, bf16 output within the bf16 bar; and a sub-block computed by the
@@ -148,3 +150,64 @@ def test_wide_nan_row_stays_in_its_row():
     cols[5000] = False
     ref = oracle.gelu(oracle.matmul(X[keep].contiguous(), W[:, cols].contiguous()))
     assert_f32(C[keep][:, cols], ref, bar=1e-4)
+
+
+def test_wide_gelu_save_matches_narrow_kernel_bitwise():
+    """The training forward's dual store: C = GeLU(v) and aux = v, both bf16."""
+    M, N, K = 2304, 7680, 128
+    wide([(M, N)], K, epilogue="gelu_save")
+    banner(f"wide tiles gelu_save M={M} N={N} K={K}")
+    X = gen((M, K), 1.0, 608, "x")
+    W = gen((K, N), 1 / math.sqrt(K), 608, "A")
+    bias = gen((N,), 0.5, 608, "bias", torch.float32)
+    Xd, Wd, bd = X.to(DEV), W.to(DEV), bias.to(DEV)
+    C, aux = tts.tp_matmul(Xd, Wd, bd, epilogue="gelu_save", out_dtype=torch.bfloat16)
+    assert tts.tp_gemm_tile_cols([(256, N)], K, epilogue="gelu_save") == 256
+    C0, aux0 = tts.tp_matmul(Xd[:256].contiguous(), Wd, bd, epilogue="gelu_save",
+                             out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(C[:256].view(torch.int16), C0.view(torch.int16))
+    assert torch.equal(aux[:256].view(torch.int16), aux0.view(torch.int16))
+    v = oracle.matmul(X, W, bias)
+    assert_bf16(aux, v)
+    assert_bf16(C, oracle.gelu(v))
+
+
+def test_wide_nt_f32_ragged_matches_narrow_kernel_bitwise():
+    """B stored [N,K] (the input-gradient layout dY·W^T), ragged M and N."""
+    M, N, K = 2250, 7560, 192
+    wide([(M, N)], K, trans_b=True)
+    banner(f"wide tiles NT f32 M={M} N={N} K={K}")
+    A = gen((M, K), 1.0, 609, "x")
+    B = gen((N, K), 1 / math.sqrt(K), 609, "A")
+    Ad, Bd = A.to(DEV), B.to(DEV)
+    C = tts.tp_matmul(Ad, Bd, trans_b=True, out_dtype=torch.float32)
+    C0 = tts.tp_matmul(Ad[2048:].contiguous(), Bd, trans_b=True, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(C[2048:], C0)
+    e = assert_f32(C, oracle.matmul(A, B.t().contiguous()), bar=1e-4)
+    assert e["fro"] < 1e-5, e
+
+
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+def test_wide_nt_gelu_bwd(out):
+    """C = (A·B^T) ⊙ GeLU'(aux), the GeLU's backward with the saved
+    pre-activation; N ragged against 384 and K over 17 K tiles."""
+    M, N, K = 2304, 7560, 1088
+    wide([(M, N)], K, trans_b=True, epilogue="gelu_bwd")
+    banner(f"wide tiles NT gelu_bwd {out} M={M} N={N} K={K}")
+    A = gen((M, K), 1.0, 610, "x")
+    B = gen((N, K), 1 / math.sqrt(K), 610, "A")
+    aux = gen((M, N), 1.0, 610, "preact")
+    odt = torch.bfloat16 if out == "bf16" else torch.float32
+    Ad, Bd, auxd = A.to(DEV), B.to(DEV), aux.to(DEV)
+    G = tts.tp_matmul(Ad, Bd, trans_b=True, epilogue="gelu_bwd", aux=auxd, out_dtype=odt)
+    G0 = tts.tp_matmul(Ad[:256].contiguous(), Bd, trans_b=True, epilogue="gelu_bwd",
+                       aux=auxd[:256].contiguous(), out_dtype=odt)
+    torch.cuda.synchronize()
+    assert torch.equal(G[:256], G0)
+    ref = oracle.matmul(A, B.t().contiguous()) * oracle.gelu_grad(aux)
+    if out == "bf16":
+        assert_bf16(G, ref)
+    else:
+        assert_f32(G, ref, bar=1e-4)

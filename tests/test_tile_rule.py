@@ -50,8 +50,13 @@ def test_rule_on_the_benchmarked_products(lib):
     assert tts.tp_gemm_tile_cols([(8192, 4096)], 2048) == 256
     assert tts.tp_gemm_tile_cols([(8192, 3072)], 4096) == 384
     assert tts.tp_gemm_tile_cols([(8192, 4096)], 1024) == 256
-    # the training forward's dual store has no 384-column kernel
-    assert tts.tp_gemm_tile_cols([(16384, 6144)], 12288, epilogue="gelu_save") == 256
+    # the training forward's dual store and the backward's input gradients
+    # take 384 too; the weight gradients (A transposed) keep 256
+    assert tts.tp_gemm_tile_cols([(16384, 6144)], 12288, epilogue="gelu_save") == 384
+    assert tts.tp_gemm_tile_cols([(16384, 6144)], 12288, trans_b=True, epilogue="gelu_bwd") == 384
+    assert tts.tp_gemm_tile_cols([(16384, 12288)], 6144, trans_b=True) == 384
+    assert tts.tp_gemm_tile_cols([(16384, 12288)], 4608, trans_b=True) == 384
+    assert tts.tp_gemm_tile_cols([(6144, 12288), (12288, 6144)], 16384, trans_a=True) == 256
 
 
 def test_rule_rejects_invalid_launches(lib):

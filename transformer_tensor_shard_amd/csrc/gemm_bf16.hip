@@ -21,8 +21,10 @@
 //
 // Design: one 256x256 output tile per workgroup of 8 waves (two per SIMD);
 // a launch whose 256-column tiles would leave the last wave of workgroups
-// mostly empty uses 256x192 tiles instead (8x3 blocks per wave, see the
-// launcher).
+// mostly empty uses 256x192 tiles instead (8x3 blocks per wave), and the
+// large forward and input-gradient products use 256x384 tiles (a kernel of
+// their own, gemm_bf16_w384_kernel below: 5/6 of the operand bytes per
+// FLOP); the launcher's cost model picks the width.
 //  * wave w owns a 128x64 sub-tile: rows 128*((w&3)>>1), columns
 //    128*(w&1) + 64*(w>>2); that is 8x4 MFMA 16x16x32 bf16 blocks with 128
 //    f32 accumulators per lane.  The two waves on a SIMD (w and w+4) take the
@@ -58,9 +60,10 @@
 //    written with 16-byte row-contiguous stores; all output stores carry the
 //    non-temporal hint (they stream past the L2);
 //
-// Measured on MI355X (rocprofv3 counters, GeLU GEMM at the 175B layer shape):
-// the shader clock settles at ~1.7 GHz under the power limit and the matrix
-// cores are busy ~77% of it.  What idles them is mostly the global -> LDS stream:
+// Measured on MI355X (rocprofv3 counters, GeLU GEMM at the 175B layer shape,
+// 256x256 tiles): the shader clock settles at ~1.7 GHz under the power limit
+// and the matrix cores are busy ~77% of it (~81% with 256x384 tiles, whose
+// clock then settles ~0.1 GHz lower).  What idles them is mostly the global -> LDS stream:
 // without the K loop's loads (a probe that reuses stale tiles) MFMA busy
 // reaches ~85% at the same clock.  The texture data path that carries the
 // loads is busy ~96% of the time, over half of it waiting on the L2 (~400
@@ -632,31 +635,37 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
 // The K loop of the 256 x 256 kernel is bound by the L2 requests of its
 // operand panels, so a wider tile, which needs fewer operand bytes per FLOP
 // ((256 + 384) / (256·384) against (256 + 256) / (256·256): 5/6), runs the
-// forward products faster: measured at the 175B layer shape, grouped over 8
+// large products faster: measured at the 175B layer shape, grouped over 8
 // ranks, 4-5% on the GeLU and QKV products, 6% on the row product and 7% on
-// W_o, with results bit-identical to the 256-column kernel (each output sees
-// the same MFMA sequence over K).
+// W_o; one rank's input gradients (B stored [N,K]) 6-7%, with results
+// bit-identical to the 256-column kernel (each output sees the same MFMA
+// sequence over K).
 //  * eight waves, wave w owning 128 x 96: rows 128·((w&3)>>1), columns
 //    192·(w&1) + 96·(w>>2), i.e. 8 x 6 MFMA 16x16x32 blocks with 192 f32
 //    accumulators per lane.  Two waves per SIMD give a wave 256 VGPRs, so the
 //    operands are held lean: the six B blocks of the k-step (24 VGPRs) and two
 //    A blocks (8).  Row mi's MFMAs run while the A block of row mi+1 is read;
 //    in the last row each B block is re-read for the next k-step right after
-//    its MFMA (253 VGPRs, no spills);
-//  * two 80 KiB stages (A 32 KiB, B 48 KiB) fill the 160 KiB of LDS.  A is
-//    staged as in the 256-column kernel; B as 64 K rows of 768 bytes with the
-//    same XOR swizzle (it depends on K row bits 0, 1 and 3 only, and keeps a
+//    its MFMA;
+//  * two 80 KiB stages (A 32 KiB, B 48 KiB) fill the 160 KiB of LDS.  The
+//    operand tiles are staged and read as in the 256-column kernel, in the
+//    layout their memory has: a K-contiguous tile as rows of 128 bytes read
+//    with 16-byte reads, an M/N-contiguous one as 64 K rows (512 bytes for A,
+//    768 for B) read with transpose reads, both with the same XOR swizzles
+//    (the M/N-contiguous one depends on K row bits 0, 1 and 3 only and keeps a
 //    unit inside its aligned group of 16);
 //  * the loads of the next K tile go out over the first 30 of the 48 MFMAs of
 //    a tile's first k-step (a window of 20 was 1-2% slower, 40 the same); the
 //    barrier that publishes them sits before the last row of the second
 //    k-step, after the last reads of the current stage;
-//  * the output tile is staged through the LDS in two (bf16) or four (f32)
-//    passes in which all eight waves take part.
-// NN layout only (the forward products), K a multiple of 64, no causal K
-// bound; the launcher picks it by the cost model of tile_cols().
+//  * the output tile is staged through the LDS in two (bf16 values) or four
+//    (f32 values) passes in which all eight waves take part; the epilogues
+//    that need a second operand or output (GeLU backward, the dual store)
+//    work from the f32 stage like the 256-column kernel's.
+// K must be a multiple of 64 and there is no causal K bound; the launcher
+// picks this kernel by the cost model of gemm_tile_cols().
 constexpr int W_NJ = 6, W_TN = 64 * W_NJ;              // 384 columns
-constexpr int W_ROWB = W_TN * 2;                        // 768 B per K row of the B tile
+constexpr int W_ROWB = W_TN * 2;                        // 768 B per K row of an N-contiguous B tile
 constexpr int W_B_BYTES = BK * W_ROWB;                  // 48 KiB
 constexpr int W_STAGE = A_BYTES + W_B_BYTES;            // 80 KiB
 constexpr int W_BLOADS = W_B_BYTES / (NTHREADS * 16);   // B loads per wave per K tile
@@ -666,24 +675,30 @@ template <int V>
 using IC = std::integral_constant<int, V>;
 
 // Schedule of one 32-wide k-step, MFMAs I .. R1·6-1 (row mi = I / 6): the A
-// read of the next row after each row's first MFMA, the B re-reads (two
-// transpose reads each) after the last row's MFMAs, and V direct-to-LDS loads
-// spread over the first W_WINDOW MFMAs.
-template <int V, int I, int R1>
+// read of the next row (DA LDS instructions) after each row's first MFMA, the
+// B re-reads (DB instructions each) after the last row's MFMAs, and V
+// direct-to-LDS loads spread over the first W_WINDOW MFMAs.
+template <int V, int DA, int DB, int I, int R1>
 __device__ __forceinline__ void w_sched() {
     constexpr int mi = I / W_NJ, nj = I % W_NJ;
     __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-    constexpr int nds = (nj == 0 ? 1 : 0) + (mi == NI - 1 ? 2 : 0);
+    constexpr int nds = (nj == 0 ? DA : 0) + (mi == NI - 1 ? DB : 0);
     if constexpr (nds > 0) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, nds, 0);
     constexpr int nv = I < W_WINDOW ? ((I + 1) * V) / W_WINDOW - (I * V) / W_WINDOW : 0;
     if constexpr (nv > 0) __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, nv, 0);
-    if constexpr (I + 1 < R1 * W_NJ) w_sched<V, I + 1, R1>();
+    if constexpr (I + 1 < R1 * W_NJ) w_sched<V, DA, DB, I + 1, R1>();
 }
 
-template <int EPI, bool OUT_BF16>
-__global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_w384_kernel(GemmBatch batch, int K)
+template <int LAYOUT, int EPI, bool OUT_BF16>
+__global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_w384_kernel(GemmBatch batch,
+                                                                     int64_t ldaux, int K)
 {
-    static_assert(EPI == EPI_NONE || EPI == EPI_GELU, "plain and GeLU epilogues");
+    constexpr bool A_MC = LAYOUT == GEMM_TN;    // A stored [K,M]: M contiguous
+    constexpr bool B_KC = LAYOUT == GEMM_NT;    // B stored [N,K]: K contiguous
+    static_assert(EPI == EPI_NONE || (LAYOUT == GEMM_NN && (EPI == EPI_GELU || EPI == EPI_DUAL)) ||
+                  (LAYOUT == GEMM_NT && EPI == EPI_GELU_BWD), "epilogue");
+    static_assert(EPI != EPI_DUAL || OUT_BF16, "the dual store is bf16");
+    constexpr int DA = A_MC ? 2 : 1, DB = B_KC ? 1 : 2;     // LDS reads per operand block
     __shared__ __attribute__((aligned(1024))) char lds0[W_STAGE];
     __shared__ __attribute__((aligned(1024))) char lds1[W_STAGE];
 
@@ -699,38 +714,58 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_w384_kernel(GemmBatch b
     const __bf16* __restrict__ B = batch.B[grp];
     const float* __restrict__ bias = batch.bias[grp];
     void* __restrict__ C = batch.C[grp];
+    __bf16* aux = batch.aux[grp];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int wm = (wid & 3) >> 1, wn = wid & 1, wh = wid >> 2;
-    const __bf16* a_tile = A + (int64_t)m0 * lda;
-    const __bf16* b_tile = B + n0;
+    const __bf16* a_tile = A_MC ? A + m0 : A + (int64_t)m0 * lda;
+    const __bf16* b_tile = B_KC ? B + (int64_t)n0 * ldb : B + n0;
 
-    // direct-to-LDS loads.  A (256 rows of 128 B): load j of wave w fills rows
-    // 32w + 8j .. +7, as in the 256-column kernel.  B (64 K rows of 48 units):
-    // load j of wave w fills the physical units (6w + j)·64 .. +63 of the tile;
-    // physical unit p is K row p / 48, unit p % 48, and holds logical unit
-    // (p % 48) ^ mc_swz(row).  Columns past N read zeros.
+    // direct-to-LDS loads; rows or columns past M or N get an offset beyond
+    // the buffer's range and read zeros.
+    //  A, K-contiguous (256 rows of 128 B): load j of wave w fills rows
+    //    32w + 8j .. +7, unit (lane%8) ^ ((row>>1)&7);
+    //  A, M-contiguous (64 K rows of 32 units): K row 8w + 2j + lane/32, unit
+    //    (lane%32) ^ mc_swz(row);
+    //  B, N-contiguous (64 K rows of 48 units): load j of wave w fills the
+    //    physical units (6w + j)·64 .. +63 of the tile; physical unit p is K
+    //    row p / 48, unit p % 48, and holds logical unit (p % 48) ^ mc_swz(row);
+    //  B, K-contiguous (384 rows of 128 B): rows 48w + 8j .. +7.
     unsigned a_off[LOADS], b_off[W_BLOADS];
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
-        const int r = 32 * wid + 8 * j + (lane >> 3);
-        const int u = (lane & 7) ^ ((r >> 1) & 7);
-        a_off[j] = (m0 + r) < M ? (unsigned)(r * lda + u * 8) * 2u : OOB;
+        if constexpr (A_MC) {
+            const int kr = 8 * wid + 2 * j + (lane >> 5);
+            const int ub = (lane & 31) ^ mc_swz(kr);
+            a_off[j] = (m0 + ub * 8) < M ? (unsigned)(kr * lda + ub * 8) * 2u : OOB;
+        } else {
+            const int r = 32 * wid + 8 * j + (lane >> 3);
+            const int u = (lane & 7) ^ ((r >> 1) & 7);
+            a_off[j] = (m0 + r) < M ? (unsigned)(r * lda + u * 8) * 2u : OOB;
+        }
     }
 #pragma unroll
     for (int j = 0; j < W_BLOADS; ++j) {
-        const int p = (W_BLOADS * wid + j) * 64 + lane;
-        const int r = p / 48, u = (p % 48) ^ mc_swz(r);
-        b_off[j] = (n0 + u * 8) < N ? (unsigned)(r * ldb + u * 8) * 2u : OOB;
+        if constexpr (B_KC) {
+            const int r = 48 * wid + 8 * j + (lane >> 3);
+            const int u = (lane & 7) ^ ((r >> 1) & 7);
+            b_off[j] = (n0 + r) < N ? (unsigned)(r * ldb + u * 8) * 2u : OOB;
+        } else {
+            const int p = (W_BLOADS * wid + j) * 64 + lane;
+            const int r = p / 48, u = (p % 48) ^ mc_swz(r);
+            b_off[j] = (n0 + u * 8) < N ? (unsigned)(r * ldb + u * 8) * 2u : OOB;
+        }
     }
     auto dma_tile = [&](int k0, char* stage) __attribute__((always_inline)) {
         const int nrec = k0 < K ? 0x7ffffff0 : 0;     // past the last K tile: zeros
         const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<__bf16*>(a_tile + k0), (short)0, nrec, 0x00020000);
+            const_cast<__bf16*>(A_MC ? a_tile + (int64_t)k0 * lda : a_tile + k0), (short)0, nrec,
+            0x00020000);
         const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<__bf16*>(b_tile + (int64_t)k0 * ldb), (short)0, nrec, 0x00020000);
+            const_cast<__bf16*>(B_KC ? b_tile + k0 : b_tile + (int64_t)k0 * ldb), (short)0, nrec,
+            0x00020000);
         char* sa = stage + wid * 4096;
         char* sb = stage + A_BYTES + wid * (W_BLOADS * 1024);
 #pragma unroll
@@ -744,19 +779,30 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_w384_kernel(GemmBatch b
     };
     const int nk = K / BK;
 
-    // operand reads: A with 16-byte reads as in the 256-column kernel, B with
-    // transpose reads from the 768-byte rows
+    // operand reads, as in the 256-column kernel: 16-byte reads of a
+    // K-contiguous tile, transpose reads of an M/N-contiguous one (rows of
+    // 512 bytes for A, 768 for B)
     const int g = lane >> 4, gi = lane & 15;
     const unsigned kc_rd = (lane & 15) * 128 + (((lane >> 4) ^ (((lane & 15) >> 1) & 7)) << 4);
-    const unsigned a_rd0 = wm * 128 * 128 + kc_rd;
-    const int wcol = wn * 192 + wh * 96;
-    unsigned b_rd[W_NJ];
-#pragma unroll
-    for (int nj = 0; nj < W_NJ; ++nj) {
+    auto mc_rd = [&](int col, int rowb) -> unsigned {      // col: first column of the block
         const int row = 8 * g + (gi >> 2);
-        const int c = wcol + 16 * nj + 4 * (gi & 3);
-        b_rd[nj] = A_BYTES + row * W_ROWB + (((c >> 3) ^ mc_swz(row)) << 4) + (c & 7) * 2;
+        const int c = col + 4 * (gi & 3);
+        return row * rowb + (((c >> 3) ^ mc_swz(row)) << 4) + (c & 7) * 2;
+    };
+    const unsigned a_rd0 = A_MC ? mc_rd(wm * 128, 512) : wm * 128 * 128 + kc_rd;
+    const int wcol = wn * 192 + wh * 96;
+    unsigned b_rd[B_KC ? 1 : W_NJ];
+    if constexpr (B_KC) {
+        b_rd[0] = A_BYTES + wcol * 128 + kc_rd;
+    } else {
+#pragma unroll
+        for (int nj = 0; nj < W_NJ; ++nj) b_rd[nj] = A_BYTES + mc_rd(wcol + 16 * nj, W_ROWB);
     }
+    auto tr_read = [&](const char* p, int rowb) __attribute__((always_inline)) -> bf16x8 {
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, p));
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, p + 4 * rowb));
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
 
     f32x4 acc[NI][W_NJ];
 #pragma unroll
@@ -768,13 +814,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_w384_kernel(GemmBatch b
 
     bf16x8 fa[2], fb[W_NJ];
     auto ld_a = [&](int slot, const char* base, int mi, int kk) __attribute__((always_inline)) {
-        fa[slot] = *(const bf16x8*)(base + ((a_rd0 + mi * 16 * 128) ^ (kk << 6)));
+        // an M-contiguous block mi is block 0's address with bits 5-7 XOR-ed
+        // by mi (the 16-column blocks differ only in the swizzled unit bits 1-3)
+        if constexpr (A_MC) fa[slot] = tr_read(base + (a_rd0 ^ (mi << 5)) + kk * 32 * 512, 512);
+        else fa[slot] = *(const bf16x8*)(base + ((a_rd0 + mi * 16 * 128) ^ (kk << 6)));
     };
     auto ld_b = [&](int nj, const char* base, int kk) __attribute__((always_inline)) {
-        const char* p = base + b_rd[nj] + kk * 32 * W_ROWB;
-        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, p));
-        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, p + 4 * W_ROWB));
-        fb[nj] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        if constexpr (B_KC) fb[nj] = *(const bf16x8*)(base + ((b_rd[0] + nj * 16 * 128) ^ (kk << 6)));
+        else fb[nj] = tr_read(base + b_rd[nj] + kk * 32 * W_ROWB, W_ROWB);
     };
     // rows [R0, R1) of a 32-wide k-step whose operands come from (cb, ckk);
     // the next k-step's come from (nb, nkk).  The row bounds are compile-time
@@ -800,15 +847,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_w384_kernel(GemmBatch b
     auto tile = [&](const char* cur, char* oth, int k_next) __attribute__((always_inline)) {
         dma_tile(k_next, oth);
         rows(IC<0>{}, IC<NI>{}, cur, 0, cur, 1);
-        w_sched<LOADS + W_BLOADS, 0, NI>();
+        w_sched<LOADS + W_BLOADS, DA, DB, 0, NI>();
         __builtin_amdgcn_sched_barrier(0);
         rows(IC<0>{}, IC<NI - 1>{}, cur, 1, cur, 1);
-        w_sched<0, 0, NI - 1>();
+        w_sched<0, DA, DB, 0, NI - 1>();
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_waitcnt(0x0F70);        // vmcnt(0): this wave's loads have landed
         __syncthreads();                           // `oth` complete; `cur` no longer read
         rows(IC<NI - 1>{}, IC<NI>{}, cur, 1, oth, 0);
-        w_sched<0, (NI - 1) * W_NJ, NI>();
+        w_sched<0, DA, DB, (NI - 1) * W_NJ, NI>();
         __builtin_amdgcn_sched_barrier(0);
     };
 
@@ -844,7 +891,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_w384_kernel(GemmBatch b
         return EPI == EPI_GELU ? gelu(v) : v;
     };
     char* half = wm ? lds1 : lds0;
-    if constexpr (OUT_BF16) {
+    if constexpr (OUT_BF16 && (EPI == EPI_NONE || EPI == EPI_GELU)) {
         // two passes of row blocks 4p .. 4p+3 (64 rows of each 128-row half)
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
@@ -874,9 +921,20 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_w384_kernel(GemmBatch b
             if (p == 0) __syncthreads();
         }
     } else {
-        // four passes of row blocks 2p, 2p+1 (32 rows of each half, 1536 B per row)
+        // four passes of row blocks 2p, 2p+1 (32 rows of each half, 1536 B per
+        // row).  The store phase applies the element-wise epilogues that need a
+        // second operand or output; with bf16 output a lane takes the staged
+        // units 2·u2 and 2·u2 + 1 of a row (the XOR keeps them adjacent), 8
+        // outputs per 16-byte store.  GeLU backward: the pass's saved
+        // pre-activations are loaded right after its staging (whose
+        // accumulators are then dead), so that their latency overlaps the
+        // barrier; units past M or N read zeros.
+        constexpr int UNITS = OUT_BF16 ? 48 : 96;             // per staged row and lane step
+        constexpr int PER = 64 * UNITS / NTHREADS;            // store steps per lane per pass
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
+            [[maybe_unused]] bf16x8 ypre8[OUT_BF16 ? PER : 1];
+            [[maybe_unused]] bf16x4 ypre4[OUT_BF16 ? 1 : PER];
 #pragma unroll
             for (int nj = 0; nj < W_NJ; ++nj) {
                 const int lc = lcol + 16 * nj;
@@ -889,16 +947,68 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_w384_kernel(GemmBatch b
                                   (lc & 3) * 4) = value(2 * p + m2, nj, r);
                     }
             }
+            if constexpr (EPI == EPI_GELU_BWD) {
+                const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
+                    aux + (int64_t)m0 * ldaux + n0, (short)0, 0x7ffffff0, 0x00020000);
+#pragma unroll
+                for (int i = 0; i < PER; ++i) {
+                    const int idx = i * NTHREADS + tid;
+                    const int lrow = idx / UNITS, u = idx % UNITS, q = lrow & 31;
+                    const int r = (lrow >> 5) * 128 + 32 * p + q, c = u * (OUT_BF16 ? 8 : 4);
+                    const unsigned off = (m0 + r < M && n0 + c < N)
+                                             ? (unsigned)(((int64_t)r * ldaux + c) * 2) : OOB;
+                    if constexpr (OUT_BF16)
+                        ypre8[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(yr, off, 0, 0));
+                    else
+                        ypre4[i] = __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(yr, off, 0, 0));
+                }
+            }
             __syncthreads();
 #pragma unroll
-            for (int i = 0; i < 64 * 96 / NTHREADS; ++i) {
+            for (int i = 0; i < PER; ++i) {
                 const int idx = i * NTHREADS + tid;
-                const int lrow = idx / 96, unit = idx % 96, q = lrow & 31;
-                const char* src = (lrow < 32 ? lds0 : lds1) + q * 1536 +
-                                  ((unit ^ (((q >> 2) & 3) << 2)) << 4);
-                const int grow = m0 + (lrow >> 5) * 128 + 32 * p + q, gcol = n0 + unit * 4;
-                if (grow < M && gcol < N)
-                    st_out(*(const f32x4*)src, (f32x4*)((float*)C + (int64_t)grow * ldc + gcol));
+                const int lrow = idx / UNITS, u = idx % UNITS, q = lrow & 31;
+                const char* rowp = (lrow < 32 ? lds0 : lds1) + q * 1536;
+                const int sw = ((q >> 2) & 3) << 2;
+                const int grow = m0 + (lrow >> 5) * 128 + 32 * p + q;
+                if constexpr (OUT_BF16) {
+                    const int gcol = n0 + u * 8;
+                    if (grow < M && gcol < N) {
+                        const f32x4 v0 = *(const f32x4*)(rowp + (((2 * u) ^ sw) << 4));
+                        const f32x4 v1 = *(const f32x4*)(rowp + (((2 * u + 1) ^ sw) << 4));
+                        float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+                        const int64_t o = (int64_t)grow * ldc + gcol;
+                        if constexpr (EPI == EPI_GELU_BWD) {
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) v[e] *= gelu_grad((float)ypre8[i][e]);
+                        }
+                        if constexpr (EPI == EPI_DUAL) {
+                            bf16x8 y, yp;
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) {
+                                y[e] = (__bf16)v[e];
+                                yp[e] = (__bf16)gelu(v[e]);
+                            }
+                            st_out(y, (bf16x8*)(aux + (int64_t)grow * ldaux + gcol));
+                            st_out(yp, (bf16x8*)((__bf16*)C + o));
+                        } else {
+                            bf16x8 c;
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) c[e] = (__bf16)v[e];
+                            st_out(c, (bf16x8*)((__bf16*)C + o));
+                        }
+                    }
+                } else {
+                    const int gcol = n0 + u * 4;
+                    if (grow < M && gcol < N) {
+                        f32x4 v = *(const f32x4*)(rowp + ((u ^ sw) << 4));
+                        if constexpr (EPI == EPI_GELU_BWD) {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) v[e] *= gelu_grad((float)ypre4[i][e]);
+                        }
+                        st_out(v, (f32x4*)((float*)C + (int64_t)grow * ldc + gcol));
+                    }
+                }
             }
             if (p < 3) __syncthreads();
         }
@@ -930,12 +1040,20 @@ int64_t tile_count(const GemmBatch& b, int tn_w) {
     return t;
 }
 
-// Whether a launch can take 256 x 384 tiles: the kernel covers the forward
-// layout with the plain and GeLU epilogues, K a multiple of 64, no causal K
-// bound.
+// Whether a launch can take 256 x 384 tiles: the forward (NN) and input-gradient
+// (NT) layouts with every epilogue but the cross-entropy statistics (whose
+// output format is per 256-column tile), K a multiple of 64 and no causal K
+// bound.  The weight-gradient layout (TN: both operands M/N-contiguous, eight
+// transpose-read addresses for A) does not fit the register budget.
 bool wide_ok(const GemmBatch& b, int layout, int epi, int64_t K) {
-    return layout == GEMM_NN && (epi == EPI_NONE || epi == EPI_GELU) && K % BK == 0 &&
-           !b.causal_k;
+    if (layout == GEMM_TN) return false;
+    const bool epi_ok = epi == EPI_NONE || (layout == GEMM_NN && (epi == EPI_GELU || epi == EPI_DUAL)) ||
+                        (layout == GEMM_NT && epi == EPI_GELU_BWD);
+    if (!epi_ok || K % BK != 0 || b.causal_k) return false;
+    // a K-contiguous B tile spans 384 rows, addressed with 32-bit byte offsets
+    for (int g = 0; layout == GEMM_NT && g < b.count; ++g)
+        if (b.ldb[g] * 2 * W_TN >= 0x7fffffff) return false;
+    return true;
 }
 
 }  // namespace
@@ -982,18 +1100,27 @@ hipError_t launch(const GemmBatch& b, int layout, int epi, int64_t ldaux, int64_
     if (per_xcd == 0) return hipSuccess;
     const dim3 grid(8 * per_xcd), block(NTHREADS);
     if (tn_w == W_TN) {
-        if (epi == EPI_GELU) {
-            if (out_bf16)
-                hipLaunchKernelGGL((gemm_bf16_w384_kernel<EPI_GELU, true>), grid, block, 0, stream, b, (int)K);
-            else
-                hipLaunchKernelGGL((gemm_bf16_w384_kernel<EPI_GELU, false>), grid, block, 0, stream, b, (int)K);
-        } else {
-            if (out_bf16)
-                hipLaunchKernelGGL((gemm_bf16_w384_kernel<EPI_NONE, true>), grid, block, 0, stream, b, (int)K);
-            else
-                hipLaunchKernelGGL((gemm_bf16_w384_kernel<EPI_NONE, false>), grid, block, 0, stream, b, (int)K);
+#define TP_GEMM_W(L, E, OB)                                                                    \
+    do {                                                                                       \
+        hipLaunchKernelGGL((gemm_bf16_w384_kernel<L, E, OB>), grid, block, 0, stream, b, ldaux, \
+                           (int)K);                                                            \
+        return hipGetLastError();                                                              \
+    } while (0)
+        switch (layout) {
+        case GEMM_NN:
+            if (epi == EPI_NONE) { if (out_bf16) TP_GEMM_W(GEMM_NN, EPI_NONE, true); TP_GEMM_W(GEMM_NN, EPI_NONE, false); }
+            if (epi == EPI_GELU) { if (out_bf16) TP_GEMM_W(GEMM_NN, EPI_GELU, true); TP_GEMM_W(GEMM_NN, EPI_GELU, false); }
+            if (epi == EPI_DUAL && out_bf16) TP_GEMM_W(GEMM_NN, EPI_DUAL, true);
+            break;
+        case GEMM_NT:
+            if (epi == EPI_NONE) { if (out_bf16) TP_GEMM_W(GEMM_NT, EPI_NONE, true); TP_GEMM_W(GEMM_NT, EPI_NONE, false); }
+            if (epi == EPI_GELU_BWD) { if (out_bf16) TP_GEMM_W(GEMM_NT, EPI_GELU_BWD, true); TP_GEMM_W(GEMM_NT, EPI_GELU_BWD, false); }
+            break;
+        default:
+            break;
         }
-        return hipGetLastError();
+#undef TP_GEMM_W
+        return hipErrorInvalidValue;
     }
     const bool ck = (K % BK) != 0;
 #define TP_GEMM_NJ(L, E, OB, NJ)                                                               \
