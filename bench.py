@@ -242,8 +242,13 @@ def dominant_kernel(w, tts, torch, X, Ws, dev):
         def launch():
             tts.tp_vocab_parallel_ce(X, Es, targets, loss=loss, loss_mean=mean, ws=ws)
         V = sum(E.shape[0] for E in Es)
-        name = ("gemm_bf16_kernel<NT, epi=ce_stats> grouped over %d ranks, each [%dx%d]x[%dx%d]^T "
-                "(+ statistics combine)" % (len(Es), M, K, Es[0].shape[0], K))
+        # the statistics epilogue takes the input-gradient layout's width rule,
+        # 384 or 256 columns (it has no 192-column kernel)
+        cols = tts.tp_gemm_tile_cols([(M, Es[0].shape[0])] * len(Es), K, trans_b=True)
+        cols = 256 if cols == 192 else cols
+        name = ("%s<NT, epi=ce_stats> (256x%d tiles) grouped over %d ranks, each [%dx%d]x[%dx%d]^T "
+                "(+ statistics combine)" % ("gemm_bf16_w384_kernel" if cols == 384 else "gemm_bf16_kernel",
+                                            cols, len(Es), M, K, Es[0].shape[0], K))
         return launch, 2 * M * K * V, name
     N = Ws[0].shape[1]
     if w.kind == "mlp_bwd":

@@ -408,7 +408,7 @@ tp_status tp_vocab_embedding_shard(const int32_t* tokens, int64_t M, const void*
  *   stats[2M..3M)  t_r = the target's logit if the target is in the rank's
  *                  range, else 0.
  *   H [M, h] bf16, targets [M] int32, stats f32 [3·M];
- *   ws >= tp_vocab_ce_shard_workspace(M, V_r) bytes (per-tile statistics).
+ *   ws >= tp_vocab_ce_shard_workspace(M, V_r) bytes (statistics per row and 128-column piece).
  * h % 8 == 0, V_r % 8 == 0. */
 size_t tp_vocab_ce_shard_workspace(int64_t M, int64_t V_r);
 tp_status tp_vocab_ce_shard(const void* H, const void* E_r, const int32_t* targets, int64_t M,

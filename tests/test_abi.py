@@ -326,7 +326,7 @@ def test_vocab_rejects():
     assert ce(ws=None) == _lib.TP_ERR_WORKSPACE
     assert ce(wsb=8) == _lib.TP_ERR_WORKSPACE
     assert ce(stats=FAKE_ODD) == _lib.TP_ERR_ALIGN
-    assert L.tp_vocab_ce_shard_workspace(300, 520) == 7424   # 300 rows x 3 tiles x 8 B, to 256 B
+    assert L.tp_vocab_ce_shard_workspace(300, 520) == 12032  # 300 rows x 5 pieces of 128 columns x 8 B, to 256 B
     assert L.tp_vocab_ce_combine(None, 2, 10, FAKE, None, None) == _lib.TP_ERR_NULL
     assert L.tp_vocab_ce_combine(FAKE, 0, 10, FAKE, None, None) == _lib.TP_ERR_SHAPE
     two = (ctypes.c_void_p * 2)(FAKE.value, FAKE.value)

@@ -11,6 +11,7 @@ import torch
 import oracle
 import synth
 import transformer_tensor_shard_amd as tts
+from _tiles import tile_cols
 from _tol import assert_bf16, assert_f32
 
 pytestmark = pytest.mark.gpu
@@ -371,11 +372,17 @@ def test_vocab_embedding(M, h, V_r, P, out):
 
 
 @pytest.mark.parametrize("M,h,V_r,P", [(300, 264, 520, 3), (512, 512, 6400 // 8, 8),
-                                       (1, 64, 8, 2), (700, 128, 1032, 1)])
+                                       (1, 64, 8, 2), (700, 128, 1032, 1), (2304, 128, 3840, 2)])
 def test_vocab_cross_entropy(M, h, V_r, P):
     """Per-rank statistics and the combined loss against the oracle; the
-    all-ranks entry point equals the per-rank path bit for bit."""
+    all-ranks entry point equals the per-rank path bit for bit.  In the last
+    case the per-rank launches take 256-column output tiles and the all-ranks
+    launch 384-column ones: the statistics, kept per 128-column piece, do not
+    depend on the width."""
     banner(f"vocab cross-entropy M={M} h={h} V_r={V_r} P={P}")
+    if (M, V_r, P) == (2304, 3840, 2):
+        assert tile_cols([(M, V_r)], h, trans_b=True, epilogue="ce_stats") == 256
+        assert tile_cols([(M, V_r)] * P, h, trans_b=True, epilogue="ce_stats") == 384
     V = V_r * P
     H = gen((M, h), 1.0, 241, "x")
     E = gen((V, h), 0.02 * math.sqrt(4096 / h), 241, "E")

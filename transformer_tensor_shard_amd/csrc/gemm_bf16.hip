@@ -239,6 +239,28 @@ __device__ __forceinline__ int kc_kpos(int lane, int j) {
 template <typename T>
 __device__ __forceinline__ void st_out(T v, T* p) { __builtin_nontemporal_store(v, p); }
 
+// Cross-entropy statistics of one 128-column piece of a logits row, held by
+// 32 lanes (lanes 0..31 or 32..63 of the wave; lane's 4 columns from gcol): the
+// maximum m over the columns below N and sum_j exp(logit_j - m), reduced over
+// the 32 lanes in a fixed order; the half's first lane writes (m, sum) at
+// out + 2·(lane >> 5).  Both output-tile widths build their statistics from
+// these pieces, so the statistics do not depend on the width.
+__device__ __forceinline__ void ce_half_stats(const f32x4& v, int gcol, int N, int lane, float* out) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) mx = fmaxf(mx, gcol + e < N ? v[e] : -INFINITY);
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    float sm = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        sm += gcol + e < N ? __builtin_amdgcn_exp2f((v[e] - mx) * 1.44269504088896341f) : 0.0f;
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) sm += __shfl_xor(sm, o);
+    // a piece that starts at or past N has no columns and is not written
+    if ((lane & 31) == 0 && gcol < N) *(float2*)(out + 2 * (lane >> 5)) = make_float2(mx, sm);
+}
+
 template <int LAYOUT, int EPI, bool OUT_BF16, bool CHECK_K, int NJ>
 __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
     GemmBatch batch, int64_t ldaux, int K)
@@ -538,9 +560,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
             __syncthreads();
             if constexpr (EPI == EPI_CE_STATS) {
                 // one wave holds one whole row of the tile per iteration (its
-                // 64 lanes the row's 64 units): the row's maximum and exp-sum
-                // over the tile's columns, and the target's logit
-                const int ntn = (N + BN - 1) / BN;
+                // 64 lanes the row's 64 units); each 32-lane half reduces its
+                // 128 columns (ce_half_stats) and the target's logit is kept
+                const int nsub = (N + 127) / 128;
 #pragma unroll 2
                 for (int i = 0; i < 8192 / NTHREADS; ++i) {
                     const int lrow = i * (NTHREADS / 64) + wid, q = lrow & 63;
@@ -548,20 +570,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
                     if (grow >= M) continue;                // wave-uniform
                     const f32x4 v = *(const f32x4*)((lrow < 64 ? lds0 : lds1) + q * 1024 +
                                                      ((lane ^ (((q >> 2) & 3) << 2)) << 4));
-                    float mx = -INFINITY;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) mx = fmaxf(mx, gcol + e < N ? v[e] : -INFINITY);
-#pragma unroll
-                    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-                    float sm = 0.0f;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        sm += gcol + e < N ? __builtin_amdgcn_exp2f((v[e] - mx) * 1.44269504088896341f)
-                                           : 0.0f;
-#pragma unroll
-                    for (int o = 32; o >= 1; o >>= 1) sm += __shfl_xor(sm, o);
-                    if (lane == 0)
-                        *(float2*)((float*)C + ((int64_t)grow * ntn + tn) * 2) = make_float2(mx, sm);
+                    ce_half_stats(v, gcol, N, lane, (float*)C + ((int64_t)grow * nsub + 2 * tn) * 2);
                     const int tl = batch.targets[grow] - batch.vstart[grp] - gcol;
                     if (tl >= 0 && tl < 4 && gcol + tl < N) ((float*)aux)[grow] = v[tl];
                 }
@@ -696,7 +705,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_w384_kernel(GemmBatch b
     constexpr bool A_MC = LAYOUT == GEMM_TN;    // A stored [K,M]: M contiguous
     constexpr bool B_KC = LAYOUT == GEMM_NT;    // B stored [N,K]: K contiguous
     static_assert(EPI == EPI_NONE || (LAYOUT == GEMM_NN && (EPI == EPI_GELU || EPI == EPI_DUAL)) ||
-                  (LAYOUT == GEMM_NT && EPI == EPI_GELU_BWD), "epilogue");
+                  (LAYOUT == GEMM_NT && (EPI == EPI_GELU_BWD || EPI == EPI_CE_STATS)), "epilogue");
+    static_assert(EPI != EPI_CE_STATS || !OUT_BF16, "the statistics are f32");
     static_assert(EPI != EPI_DUAL || OUT_BF16, "the dual store is bf16");
     constexpr int DA = A_MC ? 2 : 1, DB = B_KC ? 1 : 2;     // LDS reads per operand block
     __shared__ __attribute__((aligned(1024))) char lds0[W_STAGE];
@@ -964,6 +974,36 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_w384_kernel(GemmBatch b
                 }
             }
             __syncthreads();
+            if constexpr (EPI == EPI_CE_STATS) {
+                // one wave per staged row (64 rows per pass, 8 per wave): all 64
+                // lanes take columns 0..255 (4 each), then lanes 0..31 take
+                // 256..383 -- three 128-column pieces, each reduced by
+                // ce_half_stats as the 256-column kernel does
+                const int nsub = (N + 127) / 128;
+#pragma unroll 2
+                for (int i = 0; i < 64 / NWAVES; ++i) {
+                    const int lrow = i * NWAVES + wid, q = lrow & 31;
+                    const int grow = m0 + (lrow >> 5) * 128 + 32 * p + q;
+                    if (grow >= M) continue;                // wave-uniform
+                    const char* rowp = (lrow < 32 ? lds0 : lds1) + q * 1536;
+                    const int sw = ((q >> 2) & 3) << 2;
+                    float* out = (float*)C + ((int64_t)grow * nsub + 3 * tn) * 2;
+                    const int tgt = batch.targets[grow] - batch.vstart[grp];
+                    const int gc0 = n0 + lane * 4;
+                    const f32x4 v0 = *(const f32x4*)(rowp + ((lane ^ sw) << 4));
+                    ce_half_stats(v0, gc0, N, lane, out);
+                    if (tgt - gc0 >= 0 && tgt - gc0 < 4 && tgt < N) ((float*)aux)[grow] = v0[tgt - gc0];
+                    const int gc1 = n0 + 256 + (lane & 31) * 4;
+                    const f32x4 v1 = *(const f32x4*)(rowp + (((64 + (lane & 31)) ^ sw) << 4));
+                    // lanes 32..63 see columns past every piece (gcol >= N for
+                    // their reduction half, nothing written)
+                    ce_half_stats(v1, lane < 32 ? gc1 : N, N, lane, out + 4);
+                    if (lane < 32 && tgt - gc1 >= 0 && tgt - gc1 < 4 && tgt < N)
+                        ((float*)aux)[grow] = v1[tgt - gc1];
+                }
+                if (p < 3) __syncthreads();
+                continue;
+            }
 #pragma unroll
             for (int i = 0; i < PER; ++i) {
                 const int idx = i * NTHREADS + tid;
@@ -1041,14 +1081,12 @@ int64_t tile_count(const GemmBatch& b, int tn_w) {
 }
 
 // Whether a launch can take 256 x 384 tiles: the forward (NN) and input-gradient
-// (NT) layouts with every epilogue but the cross-entropy statistics (whose
-// output format is per 256-column tile), K a multiple of 64 and no causal K
-// bound.  The weight-gradient layout (TN: both operands M/N-contiguous, eight
+// (NT) layouts with every epilogue, K a multiple of 64 and no causal K bound.  The weight-gradient layout (TN: both operands M/N-contiguous, eight
 // transpose-read addresses for A) does not fit the register budget.
 bool wide_ok(const GemmBatch& b, int layout, int epi, int64_t K) {
     if (layout == GEMM_TN) return false;
     const bool epi_ok = epi == EPI_NONE || (layout == GEMM_NN && (epi == EPI_GELU || epi == EPI_DUAL)) ||
-                        (layout == GEMM_NT && epi == EPI_GELU_BWD);
+                        (layout == GEMM_NT && (epi == EPI_GELU_BWD || epi == EPI_CE_STATS));
     if (!epi_ok || K % BK != 0 || b.causal_k) return false;
     // a K-contiguous B tile spans 384 rows, addressed with 32-bit byte offsets
     for (int g = 0; layout == GEMM_NT && g < b.count; ++g)
@@ -1069,13 +1107,13 @@ bool wide_ok(const GemmBatch& b, int layout, int epi, int64_t K) {
 // 192, 2 waves) and the 175B layer shape's products (48 waves of 256-column
 // tiles, 32 of 384).
 int gemm_tile_cols(const GemmBatch& b, int layout, int epi, int64_t K) {
-    if (epi == EPI_CE_STATS) return 256;
     if (tile_count(b, 192) > 0x7fffffff / 16) return 256;     // keep the grid size in range
     const int64_t cus = cu_count();
     auto waves = [&](int w) { return (tile_count(b, w) + cus - 1) / cus; };
     int best = 256;
     int64_t cost = 16 * waves(256);
-    if (14 * waves(192) < cost - 2) {
+    // (the cross-entropy statistics have no 192-column kernel)
+    if (epi != EPI_CE_STATS && 14 * waves(192) < cost - 2) {
         best = 192;
         cost = 14 * waves(192);
     }
@@ -1115,6 +1153,7 @@ hipError_t launch(const GemmBatch& b, int layout, int epi, int64_t ldaux, int64_
         case GEMM_NT:
             if (epi == EPI_NONE) { if (out_bf16) TP_GEMM_W(GEMM_NT, EPI_NONE, true); TP_GEMM_W(GEMM_NT, EPI_NONE, false); }
             if (epi == EPI_GELU_BWD) { if (out_bf16) TP_GEMM_W(GEMM_NT, EPI_GELU_BWD, true); TP_GEMM_W(GEMM_NT, EPI_GELU_BWD, false); }
+            if (epi == EPI_CE_STATS && !out_bf16) TP_GEMM_W(GEMM_NT, EPI_CE_STATS, false);
             break;
         default:
             break;

@@ -707,7 +707,7 @@ TP_EXPORT tp_status tp_attn_shard_backward(const void* X, const void* W_qkv_i, c
 
 // ---- vocabulary ends: vocab-parallel embedding and cross-entropy -----------
 namespace {
-int64_t ce_ntn(int64_t V_r) { return (V_r + 255) / 256; }
+int64_t ce_ntn(int64_t V_r) { return (V_r + 127) / 128; }   // 128-column pieces per row
 int64_t ce_tiles_bytes(int64_t M, int64_t V_r) { return align_up(M * ce_ntn(V_r) * 2 * 4); }
 int64_t ce_stats_bytes(int64_t M) { return align_up(3 * M * 4); }
 
@@ -722,6 +722,8 @@ tp_status check_vocab(int64_t M, int64_t h, int64_t V_r) {
 hipError_t run_ce_ranks(const void* H, const void* const* E, int count, const int* targets,
                         int64_t M, int64_t h, int64_t V_r, int64_t vstart0, float* stats,
                         float* tiles, hipStream_t st) {
+    // each rank's logits rows leave statistics per 128-column piece (the same
+    // values whichever output-tile width the GEMM takes)
     const int64_t ntn = ce_ntn(V_r);
     for (int g0 = 0; g0 < count; g0 += tpk::kMaxBatch) {
         const int n = count - g0 < tpk::kMaxBatch ? count - g0 : tpk::kMaxBatch;

@@ -14,10 +14,11 @@ enum GemmLayout { GEMM_NN = 0, GEMM_NT = 1, GEMM_TN = 2 };
 // GELU_BWD  C = v · GeLU'(aux) (aux: the saved bf16 pre-activation);
 // DUAL  C = bf16 GeLU(v) and aux = bf16 v (the training forward).
 // CE_STATS (the vocab-parallel cross-entropy's logits, NT, f32): no C is
-// written; for every output row and 256-column tile tn, C[g] (as float*)
-// receives at [(row·ceil(N/256) + tn)·2] the tile's row maximum m and
-// sum_j exp(logit_j - m); aux[g] (as float*) receives logit[row][targets[row]
-// - vstart[g]] at [row] when that column is in range (the caller zeroes it).
+// written; for every output row and 128-column piece j of the row, C[g] (as
+// float*) receives at [(row·ceil(N/128) + j)·2] the piece's maximum m and
+// sum_i exp(logit_i - m), computed the same way whatever the output-tile
+// width; aux[g] (as float*) receives logit[row][targets[row] - vstart[g]] at
+// [row] when that column is in range (the caller zeroes it).
 enum GemmEpi { EPI_NONE = 0, EPI_GELU = 1, EPI_GELU_BWD = 2, EPI_DUAL = 3, EPI_CE_STATS = 4 };
 
 // Up to kMaxBatch independent GEMMs launched together: group g computes

@@ -5,10 +5,10 @@
 //    row, and the sum over ranks (the all-reduce) is the full lookup.  One
 //    256-thread workgroup per token row, 16-byte loads and stores;
 //  * cross-entropy: the logits H·E_r^T come from the MFMA GEMM with the
-//    CE-statistics epilogue (gemm_bf16.hip), which leaves per row and 256-wide
-//    column tile the maximum m_t and sum_j exp(l_j - m_t), and the target's
-//    logit.  Here, in the stable form: the rank's row statistics
-//        m_r = max_t m_t,   s_r = sum_t s_t·exp(m_t - m_r)   (tiles in order);
+//    CE-statistics epilogue (gemm_bf16.hip), which leaves per row and
+//    128-column piece t the maximum m_t and sum_j exp(l_j - m_t), and the
+//    target's logit.  Here, in the stable form: the rank's row statistics
+//        m_r = max_t m_t,   s_r = sum_t s_t·exp(m_t - m_r)   (pieces in order);
 //    the cross-rank combine (the all-reduces of the max, the exp-sum and the
 //    target logit) and the loss
 //        m = max_r m_r,  s = sum_r s_r·exp(m_r - m),  t = sum_r t_r,
@@ -52,7 +52,7 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, i
     if (i < n) p[i] = 0.0f;
 }
 
-// tile statistics [M][ntn][2] -> the rank's m_r, s_r (stats[0..M), stats[M..2M))
+// piece statistics [M][ntn][2] -> the rank's m_r, s_r (stats[0..M), stats[M..2M))
 __global__ __launch_bounds__(256) void ce_rank_reduce_kernel(const float* __restrict__ tiles,
                                                              int ntn, int64_t M,
                                                              float* __restrict__ stats)
