@@ -227,6 +227,7 @@ def matmul(**kw):
     (dict(tb=1, ldb=32), _lib.TP_ERR_SHAPE),               # B^T stored [N,K]: ldb < K
     (dict(ta=1, lda=16), _lib.TP_ERR_SHAPE),               # A^T stored [K,M]: lda < M
     (dict(lda=1 << 23), _lib.TP_ERR_SHAPE),                # 256 rows past 32-bit offsets
+    (dict(tb=1, epi=_lib.TP_EPI_GELU_BWD, aux=FAKE, ldaux=1 << 23), _lib.TP_ERR_SHAPE),  # aux rows too
     (dict(B=FAKE_ODD), _lib.TP_ERR_ALIGN),
     (dict(tb=1, epi=_lib.TP_EPI_GELU_BWD, aux=FAKE_ODD, ldaux=64), _lib.TP_ERR_ALIGN),
 ])

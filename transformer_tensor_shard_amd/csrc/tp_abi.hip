@@ -100,7 +100,10 @@ tp_status check_matmul(const void* A, int64_t lda, int ta, const void* B, int64_
     if ((ta ? M : K) % 8 || (tb ? K : N) % 8 || N % 8 || lda % 8 || ldb % 8 || ldc % 8 ||
         (uses_aux && ldaux % 8))
         return TP_ERR_SHAPE;
+    // the GeLU-backward epilogue reads a tile's 256 rows of aux with 32-bit
+    // byte offsets, as the K-contiguous operands are read
     if (!operand_fits(lda, !ta) || !operand_fits(ldb, tb != 0) ||
+        (epi == TP_EPI_GELU_BWD && !operand_fits(ldaux, true)) ||
         ((M + 255) / 256) * ((N + 255) / 256) > kI32 / 8)
         return TP_ERR_SHAPE;
     if (!aligned16(A) || !aligned16(B) || !aligned16(C) || (bias && !aligned16(bias)) ||
