@@ -268,7 +268,7 @@ tp_status tp_linear(const void* X, int64_t ldx, const void* W, int64_t ldw,
  * the identical per-rank products of several emulated tensor-parallel ranks
  * ([Megatron explainer] §2.1, §3.2: every rank applies the same operation to
  * its own slice) without a tail per rank.  bf16 inputs run as one grouped
- * MFMA launch per 16 products; f32 inputs run one product after another. */
+ * MFMA launch per 32 products; f32 inputs run one product after another. */
 tp_status tp_linear_batched(const void* const* X, int64_t ldx, const void* const* W,
                             int64_t ldw, const void* const* bias, void* const* C, int64_t ldc,
                             int count, int64_t M, int64_t N, int64_t K, int in, int out,
@@ -334,7 +334,7 @@ int tp_gemm_tile_cols(int trans_a, int trans_b, int epilogue, int count, const i
  * scores are materialised in f32 ([s, s] per rank and head), the softmax
  * weights in bf16 (unnormalised, the row maximum's weight exactly 1), the
  * products with V in f32, divided by the sum of the same rounded weights;
- * (sequence, head) pairs run 16 at a time.
+ * (sequence, head) pairs run 32 at a time.
  *   qkv  [b·s, ld_qkv] bf16, columns [Q | K | V], each H·d wide, head-major
  *   O    [b·s, ldo] bf16: head h's features at columns h·d .. h·d + d - 1, the
  *        ranks' slices in rank order

@@ -24,7 +24,8 @@ def banner(msg):
     (1, 64, 3, 128, 1, True),      # P = 1: plain attention
     (1, 128, 2, 128, 8, True),     # d/P = 16
     (3, 8, 2, 64, 8, False),       # tiny s, d/P = 8
-    (1, 520, 20, 128, 4, True),    # 20 pairs: a second chunk of pairs, ragged s
+    (1, 520, 20, 128, 4, True),    # 20 pairs: one partial chunk of pairs, ragged s
+    (3, 136, 12, 128, 4, False),   # 36 pairs: a second chunk of pairs, ragged s
     (1, 2056, 2, 128, 4, True),    # s > 2048: the softmax's second row unit, wide score grids
 ])
 def test_kv_split(b, s, H, d, P, causal):
@@ -65,7 +66,7 @@ def test_kv_split_agrees_with_head_sharded_core():
 def test_kv_split_fullsize_sampled():
     """The benchmark's workload (4 sequences of 2048, 32 heads of 128, P = 4),
     launched as the benchmark launches it; every row of eight (sequence, head)
-    pairs -- both sides of the 16-pair chunk boundary among them -- against
+    pairs -- both sides of the 32-pair chunk boundary among them -- against
     the oracle, which computes each pair on its own."""
     from synth import workloads as wl
     w = wl.WORKLOADS["kvsplit_bf16_h4096_tp4"]
@@ -75,7 +76,7 @@ def test_kv_split_fullsize_sampled():
     O = tts.tp_attention_kv_split(qkv.to(DEV), b, s, H, P, d, True).cpu()
     torch.cuda.synchronize()
     rng = np.random.default_rng(w.seed)
-    pairs = {(0, 0), (0, 15), (0, 16), (b - 1, H - 1)}
+    pairs = {(0, 0), (0, 31), (1, 0), (b - 1, H - 1)}
     while len(pairs) < 8:
         pairs.add((int(rng.integers(0, b)), int(rng.integers(0, H))))
     HD = H * d

@@ -19,6 +19,7 @@ constexpr int64_t kHeadDim = 128;          // the attention kernel's head tile
 constexpr int64_t kMaxLnWidth = 16384;     // the block's row kernels keep a row in registers
 constexpr int64_t kMaxLnWidthWide = 32768; // tp_layernorm's wide-row kernel keeps it in LDS
 constexpr int64_t kI32 = 0x7fffffffLL;
+constexpr int kMaxGroup = 16;             // products per tp_matmul_grouped call
 
 inline int64_t align_up(int64_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -426,8 +427,8 @@ TP_EXPORT tp_status tp_matmul_grouped(const void* const* A, const int64_t* lda, 
                                       const int64_t* N, int count, int64_t K, int out,
                                       void* stream) {
     if (!A || !lda || !B || !ldb || !C || !ldc || !M || !N) return TP_ERR_NULL;
-    if (count <= 0 || count > tpk::kMaxBatch) return TP_ERR_SHAPE;
-    Product p[tpk::kMaxBatch];
+    if (count <= 0 || count > kMaxGroup) return TP_ERR_SHAPE;
+    Product p[kMaxGroup];
     for (int g = 0; g < count; ++g) {
         const tp_status s = check_matmul(A[g], lda[g], trans_a, B[g], ldb[g], trans_b, nullptr,
                                          C[g], ldc[g], nullptr, 0, M[g], N[g], K, out,
@@ -440,7 +441,7 @@ TP_EXPORT tp_status tp_matmul_grouped(const void* const* A, const int64_t* lda, 
 
 TP_EXPORT int tp_gemm_tile_cols(int trans_a, int trans_b, int epilogue, int count,
                                 const int64_t* M, const int64_t* N, int64_t K) {
-    if (!M || !N || count <= 0 || count > tpk::kMaxBatch || K <= 0) return 0;
+    if (!M || !N || count <= 0 || count > kMaxGroup || K <= 0) return 0;
     if ((trans_a && trans_b) || epilogue < TP_EPI_NONE || epilogue > TP_EPI_GELU_SAVE) return 0;
     tpk::GemmBatch gb = {};
     gb.count = count;

@@ -26,7 +26,7 @@ enum GemmEpi { EPI_NONE = 0, EPI_GELU = 1, EPI_GELU_BWD = 2, EPI_DUAL = 3, EPI_C
 // leading dimensions lda[g], ldb[g], ldc[g]; layout, epilogue, K and output
 // type are common.  Used for the emulated ranks of a block (identical
 // shapes) and for the weight gradients of a backward (different shapes).
-constexpr int kMaxBatch = 16;
+constexpr int kMaxBatch = 32;
 struct GemmBatch {
     const __bf16* A[kMaxBatch];
     const __bf16* B[kMaxBatch];
@@ -58,7 +58,7 @@ hipError_t gemm_bf16_grouped(const GemmBatch& batch, int layout, int epi, int64_
 // Attention with Q, K, V split along the feature dimension over P ranks
 // (kv_split.hip): partial scores per rank, their sum and the softmax, then
 // O = P·V.  (sequence, head) pairs run kKvChunk at a time; rows up to kKvMaxS.
-constexpr int kKvChunk = 16;
+constexpr int kKvChunk = 32;
 constexpr int kKvMaxS = 8192;
 // a chunk's O = P·V products run as one grouped GEMM launch
 static_assert(kKvChunk <= kMaxBatch, "a K/V-split chunk must fit one grouped GEMM launch");
