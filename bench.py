@@ -264,16 +264,20 @@ def dominant_kernel(w, tts, torch, X, Ws, dev):
                 "X^T·dY [%dx%d]x[%dx%d]" % (f, M, M, h, h, M, M, f))
         return launch, 2 * (2 * M * h * f), name
     if w.kind == "attn_bwd":
-        # dW_qkv,i = X^T·dqkv and dW_o,i = O^T·dZ in one grouped launch
+        # dW_qkv,i = X^T·dqkv and dW_o,i = O^T·dZ in one grouped launch, with
+        # the spare memory the backward gives it (its dO buffer, dead by then),
+        # which lets the launch split its last wave of tiles over K
         dqkv, O, dZ = Ws
         h, n3, HD = K, dqkv.shape[1], O.shape[1]
         dWqkv = torch.empty(h, n3, dtype=torch.float32, device=dev)
         dWo = torch.empty(HD, h, dtype=torch.float32, device=dev)
+        spare = torch.empty(M * HD * 2, dtype=torch.uint8, device=dev)
 
         def launch():
-            tts.tp_matmul_grouped([X, O], [dqkv, dZ], trans_a=True, outs=[dWqkv, dWo])
+            tts.tp_matmul_grouped([X, O], [dqkv, dZ], trans_a=True, outs=[dWqkv, dWo], ws=spare)
         name = ("gemm_bf16_kernel<TN, f32 out> grouped: X^T·dqkv [%dx%d]x[%dx%d] and "
-                "O^T·dZ [%dx%d]x[%dx%d]" % (h, M, M, n3, HD, M, M, h))
+                "O^T·dZ [%dx%d]x[%dx%d] (+ the last wave's split-K sum)"
+                % (h, M, M, n3, HD, M, M, h))
         return launch, 2 * M * h * n3 + 2 * M * HD * h, name
     gelu = w.kind != "attn"
     outs = [torch.empty(M, N, dtype=torch.bfloat16, device=dev) for _ in Ws]
@@ -647,7 +651,8 @@ def main():
                 qkv0, O0, dO_c, lse0, w.b, w.s, w.Hl, w.d, dqkv=dqkv_c, D_ws=Dws), fl["core"]),
             "dWqkv_dWo_gemm_tn_grouped": (lambda: tts.tp_matmul_grouped(
                 [x, O0], [dqkv_c, dZ], trans_a=True,
-                outs=[bwd_out["dWqkv_out"], bwd_out["dWo_out"]]), (fl["qkv"] + fl["wo"]) // 2),
+                outs=[bwd_out["dWqkv_out"], bwd_out["dWo_out"]], ws=dO_c),
+                (fl["qkv"] + fl["wo"]) // 2),
             "dX_gemm_nt": (lambda: tts.tp_matmul(dqkv_c, Wqkv0, trans_b=True,
                                                  out=bwd_out["dX_out"]), fl["qkv"] // 2),
         }

@@ -62,7 +62,8 @@ typedef enum tp_dtype {
 /* Human-readable name of a status code (static string, never NULL). */
 const char* tp_status_string(int status);
 
-/* ABI version of this header: 1. */
+/* ABI version of this header: 2 (tp_matmul_grouped took its optional
+ * workspace arguments in version 2). */
 int tp_abi_version(void);
 
 /* ------------------------------------------------------------------------
@@ -303,13 +304,24 @@ tp_status tp_matmul(const void* A, int64_t lda, int trans_a, const void* B, int6
  * dimensions, in a single launch.  A backward pass's weight gradients
  * ([Megatron explainer] §2.2, §3.2: every rank forms the gradients of its
  * own weight slices) are such a set: launched together, one product's tiles
- * fill the partly idle last wave of the other's.  All arguments are HOST
- * arrays of `count` entries (device pointers, sizes); each group must
- * satisfy tp_matmul's conditions. */
+ * fill the partly idle last wave of the other's.  A, lda, B, ldb, C, ldc,
+ * M, N are HOST arrays of `count` entries (device pointers, sizes); each
+ * group must satisfy tp_matmul's conditions.
+ *   ws, ws_bytes: optional device memory (16-byte aligned; NULL for none)
+ *     that the launch may use, f32 output only: when its last wave of
+ *     workgroups fills at most half (a quarter) of the compute units and
+ *     K >= 4096 (8192), each tile of that wave runs as 2 (4) workgroups over
+ *     equal K ranges, the first writing C, the others a block of ws each,
+ *     and a second launch adds those blocks to C in range order.  Results
+ *     stay deterministic for a given device, shapes and ws_bytes; they can
+ *     differ in the last bits from a launch without ws (the sum over K is
+ *     split in two (four) partial sums).  ws is not read before it is
+ *     written and may hold anything. */
 tp_status tp_matmul_grouped(const void* const* A, const int64_t* lda, int trans_a,
                             const void* const* B, const int64_t* ldb, int trans_b,
                             void* const* C, const int64_t* ldc, const int64_t* M,
-                            const int64_t* N, int count, int64_t K, int out, void* stream);
+                            const int64_t* N, int count, int64_t K, int out, void* ws,
+                            size_t ws_bytes, void* stream);
 
 /* tp_gemm_tile_cols -- the output-tile width, in columns, that the bf16 GEMM
  * behind tp_linear, tp_linear_batched, tp_matmul and tp_matmul_grouped uses

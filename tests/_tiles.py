@@ -9,6 +9,14 @@ dual-store epilogues) and the input-gradient layout (B transposed: plain and
 GeLU backward; also the cross-entropy statistics, which have no 192-column
 kernel) with K a multiple of 64, not for the weight-gradient layout (A
 transposed).
+
+A launch with f32 output and no epilogue, on 256- or 192-column tiles, whose
+caller offers spare device memory may split its last, partly filled wave:
+with W = 8·sum_g ceil(tiles_g / 8) workgroups (each XCD takes its share of
+every product's tiles) the last
+wave holds t = W mod CUs; 4 ways when 4t <= CUs and K >= 8192, else 2 ways
+when 2t <= CUs and K >= 4096, K a multiple of 64·ways, and (ways - 1)·t
+blocks of 256 x width f32 fitting the spare memory.
 """
 
 
@@ -31,3 +39,21 @@ def tile_cols(prods, K, *, trans_a=False, trans_b=False, epilogue="none", cus=25
     if wide_ok and 23 * waves(prods, 384, cus) < cost - 2:
         best = 384
     return best
+
+
+def workgroups(prods, w):
+    def cdiv(a, b):
+        return -(-a // b)
+    return 8 * sum(cdiv(cdiv(m, 256) * cdiv(n, w), 8) for m, n in prods)
+
+
+def split_ways(prods, K, spare_bytes, w=256, cus=256):
+    tail = workgroups(prods, w) % cus
+    if tail == 0:
+        return 0
+    for ways in (4, 2):
+        if ways * tail > cus or K % (64 * ways) or K < 2048 * ways:
+            continue
+        if (ways - 1) * tail * 256 * w * 4 <= spare_bytes:
+            return ways
+    return 0

@@ -38,7 +38,7 @@ def test_header_symbols_exported():
 
 def test_loads_and_reports_version():
     L = tts.lib()
-    assert L.tp_abi_version() == 1
+    assert L.tp_abi_version() == 2
     assert L.tp_status_string(0) == b"ok"
     assert L.tp_status_string(99) == b"unknown status"
 
@@ -293,9 +293,10 @@ def test_matmul_grouped_rejects():
     I2 = ctypes.c_int64 * 2
     ok, hole = P2(FAKE.value, FAKE.value), P2(FAKE.value, None)
     odd = P2(FAKE.value, FAKE_ODD.value)
-    call = lambda A=ok, lda=I2(64, 128), ta=1, C=ok, M=I2(64, 128), N=I2(32, 64), count=2, K=100: \
+    call = lambda A=ok, lda=I2(64, 128), ta=1, C=ok, M=I2(64, 128), N=I2(32, 64), count=2, K=100, \
+        ws=None: \
         L.tp_matmul_grouped(A, lda, ta, ok, I2(64, 64), 0, C, I2(64, 64), M, N, count, K,
-                            _lib.TP_F32, None)
+                            _lib.TP_F32, ws, 1 << 20, None)
     assert call(A=hole) == _lib.TP_ERR_NULL
     assert call(count=0) == _lib.TP_ERR_SHAPE
     assert call(count=17) == _lib.TP_ERR_SHAPE
@@ -303,8 +304,9 @@ def test_matmul_grouped_rejects():
     assert call(lda=I2(64, 32)) == _lib.TP_ERR_SHAPE    # group 1's lda < M
     assert call(ta=2) == _lib.TP_ERR_DTYPE
     assert call(C=odd) == _lib.TP_ERR_ALIGN
+    assert call(ws=FAKE_ODD) == _lib.TP_ERR_ALIGN        # the optional workspace, misaligned
     assert L.tp_matmul_grouped(None, I2(64, 64), 1, ok, I2(64, 64), 0, ok, I2(64, 64), I2(64, 64),
-                               I2(64, 64), 2, 64, 0, None) == _lib.TP_ERR_NULL
+                               I2(64, 64), 2, 64, 0, None, 0, None) == _lib.TP_ERR_NULL
 
 
 def test_vocab_rejects():

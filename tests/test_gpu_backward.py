@@ -11,7 +11,7 @@ import torch
 import oracle
 import synth
 import transformer_tensor_shard_amd as tts
-from _tiles import tile_cols
+from _tiles import split_ways, tile_cols
 from _tol import assert_bf16, assert_f32
 
 pytestmark = pytest.mark.gpu
@@ -292,6 +292,72 @@ def test_attn_shard_backward(b, s, h, Hl, causal, dx):
     assert_bf16(dX, rX, per_row=True)
     assert_bf16(dWqkv, rWqkv, per_row=True)
     assert_bf16(dWo, rWo, per_row=True)
+
+
+@pytest.mark.parametrize("ta,tb,shapes,K,ways", [
+    (1, 0, [(512, 768), (256, 520)], 4096, 2),     # weight-gradient layout, N ragged
+    (0, 0, [(300, 264), (512, 256)], 8192, 4),     # forward layout, M ragged
+    (0, 1, [(256, 512), (40, 264)], 4096, 2)])     # input-gradient layout
+def test_matmul_grouped_split_last_wave(ta, tb, shapes, K, ways):
+    """Given spare memory, a launch whose one wave fills few compute units runs
+    every tile as `ways` workgroups over equal K ranges and adds the ranges'
+    f32 blocks to C in range order: each element equals, bit for bit, that
+    ordered sum of `ways` launches over the K ranges alone (without spare
+    memory); and the whole against the oracle."""
+    spare = (ways - 1) * 16 * 256 * 256 * 4
+    assert split_ways(shapes, K, spare) == ways
+    banner(f"matmul grouped split ta={ta} tb={tb} shapes={shapes} K={K} ways={ways}")
+    As = [gen((K, m) if ta else (m, K), 1.0, 240 + g, "x") for g, (m, n) in enumerate(shapes)]
+    Bs = [gen((n, K) if tb else (K, n), 1 / math.sqrt(K), 240 + g, "A")
+          for g, (m, n) in enumerate(shapes)]
+    Ad, Bd = [A.to(DEV) for A in As], [B.to(DEV) for B in Bs]
+    ws = torch.full((spare,), 0x7F, dtype=torch.uint8, device=DEV)   # garbage: written first
+    outs = tts.tp_matmul_grouped(Ad, Bd, trans_a=bool(ta), trans_b=bool(tb), ws=ws)
+
+    def k_range(t, k0, k1, k_rows):
+        return (t[k0:k1] if k_rows else t[:, k0:k1]).contiguous()
+    kr = K // ways
+    ref = None
+    for p in range(ways):
+        k0, k1 = p * kr, (p + 1) * kr
+        part = tts.tp_matmul_grouped([k_range(A, k0, k1, ta) for A in Ad],
+                                     [k_range(B, k0, k1, not tb) for B in Bd],
+                                     trans_a=bool(ta), trans_b=bool(tb))
+        ref = part if ref is None else [r + q for r, q in zip(ref, part)]
+    torch.cuda.synchronize()
+    for g in range(len(shapes)):
+        assert torch.equal(outs[g], ref[g]), g
+        a = oracle.f64(As[g]).T if ta else As[g]
+        b = oracle.f64(Bs[g]).T if tb else Bs[g]
+        assert_f32(outs[g], oracle.matmul(a, b), bar=1e-4)
+
+
+def test_attn_shard_backward_split_last_wave():
+    """16 sequences of 256 tokens, 8 local heads, h = 512: the weight-gradient
+    launch (dW_qkv 24 tiles, dW_o 8: 32 workgroups, under half the CUs, K =
+    4096 tokens) runs each tile as two workgroups over the halves of K and
+    adds the second half into C afterwards, in the dO buffer's memory.  Every
+    gradient against the oracle, and a repeat bit for bit."""
+    b, s, h, Hl = 16, 256, 512, 8
+    HD = Hl * 128
+    assert tile_cols([(h, 3 * HD), (HD, h)], b * s, trans_a=True) == 256
+    assert split_ways([(h, 3 * HD), (HD, h)], b * s, b * s * HD * 2) == 2
+    banner(f"attn shard backward, split last wave: b={b} s={s} h={h} Hl={Hl}")
+    X = gen((b * s, h), 1.0, 226, "x")
+    Wqkv = gen((h, 3 * HD), 1 / math.sqrt(h), 226, "Wqkv")
+    Wo = gen((HD, h), 1 / math.sqrt(h), 226, "Wo")
+    dZ = gen((b * s, h), 1.0, 226, "dZ")
+    Xd, Wqd, Wod, dZd = X.to(DEV), Wqkv.to(DEV), Wo.to(DEV), dZ.to(DEV)
+    _, qkv, O, lse = tts.tp_attn_shard_train_fwd(Xd, Wqd, Wod, b, s, Hl)
+    g1 = tts.tp_attn_shard_backward(Xd, Wqd, Wod, qkv, O, lse, dZd, b, s, Hl)
+    g2 = tts.tp_attn_shard_backward(Xd, Wqd, Wod, qkv, O, lse, dZd, b, s, Hl)
+    torch.cuda.synchronize()
+    for u, v in zip(g1, g2):
+        assert torch.equal(u, v)
+    rX, rWqkv, rWo = oracle.attn_shard_backward(X, b, s, Wqkv, Wo, dZ, Hl, 128, True)
+    assert_bf16(g1[0], rX, per_row=True)
+    assert_bf16(g1[1], rWqkv, per_row=True)
+    assert_bf16(g1[2], rWo, per_row=True)
 
 
 def test_attn_backward_deterministic_and_ranks_sum():

@@ -348,9 +348,11 @@ def tp_gemm_tile_cols(shapes, K: int, *, trans_a=False, trans_b=False, epilogue=
 
 
 def tp_matmul_grouped(As, Bs, *, trans_a=False, trans_b=False, outs=None,
-                      out_dtype=torch.float32, stream=None):
+                      out_dtype=torch.float32, ws=None, stream=None):
     """C[g] = op(A[g])·op(B[g]) for every g in one launch; the products share
-    layout and K but may differ in M and N.  Returns the list of C[g]."""
+    layout and K but may differ in M and N.  ws: optional device memory the
+    launch may use to split its last wave of workgroups over K (f32 output).
+    Returns the list of C[g]."""
     count = len(As)
     if len(Bs) != count or (outs is not None and len(outs) != count):
         raise ValueError("As, Bs and outs must have the same length")
@@ -368,7 +370,8 @@ def tp_matmul_grouped(As, Bs, *, trans_a=False, trans_b=False, outs=None,
         _ptr_array(As, "A"), I64(*[A.shape[1] for A in As]), int(bool(trans_a)),
         _ptr_array(Bs, "B"), I64(*[B.shape[1] for B in Bs]), int(bool(trans_b)),
         _ptr_array(outs, "out"), I64(*[C.shape[1] for C in outs]), I64(*Ms), I64(*Ns), count, K,
-        _code(outs[0].dtype), _stream(stream))
+        _code(outs[0].dtype), _dev(ws, "ws"), _bytes(ws) if ws is not None else 0,
+        _stream(stream))
     _check(st, "tp_matmul_grouped")
     return outs
 

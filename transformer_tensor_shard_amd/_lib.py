@@ -66,7 +66,7 @@ SIGNATURES = {
     "tp_matmul_grouped": (_int, [ctypes.POINTER(_vp), ctypes.POINTER(_i64), _int,
                                  ctypes.POINTER(_vp), ctypes.POINTER(_i64), _int,
                                  ctypes.POINTER(_vp), ctypes.POINTER(_i64), ctypes.POINTER(_i64),
-                                 ctypes.POINTER(_i64), _int, _i64, _int, _vp]),
+                                 ctypes.POINTER(_i64), _int, _i64, _int, _vp, _sz, _vp]),
     "tp_vocab_embedding_shard": (_int, [_vp, _i64, _vp, _i64, _i64, _i64, _vp, _int, _vp]),
     "tp_vocab_ce_shard_workspace": (_sz, [_i64, _i64]),
     "tp_vocab_ce_shard": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _vp, _sz, _vp]),

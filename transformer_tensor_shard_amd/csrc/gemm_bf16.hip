@@ -72,6 +72,7 @@
 // either (non-temporal loads halve throughput: they defeat the L2 sharing
 // that the tile order sets up).
 #include <atomic>
+#include <cstdint>
 #include <type_traits>
 
 #include "tp_kernels.h"
@@ -279,19 +280,49 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
     __shared__ __attribute__((aligned(1024))) char lds0[STAGE_BYTES];
     __shared__ __attribute__((aligned(1024))) char lds1[STAGE_BYTES];
 
+    // With a split last wave (f32 output, no epilogue, whole K steps) the
+    // tail workgroups id = split_from + part·split_tail + j all take tile
+    // split_from + j, part `part` of its K range; the id stays congruent to
+    // the tile's own modulo 8 when split_tail is a multiple of 8 (the CU
+    // count is), so the tile keeps its XCD.
+    constexpr bool SPLITS = EPI == EPI_NONE && !OUT_BF16 && !CHECK_K;
+    int pid = blockIdx.x, part = 0;
+    const bool split_wg = SPLITS && batch.split_ways > 1 && pid >= batch.split_from;
+    if (split_wg) {
+        const int j = pid - batch.split_from;
+        part = j / batch.split_tail;
+        pid = batch.split_from + j % batch.split_tail;
+    }
     int grp, tm, tn;
-    if (batch.band ? !tile_coords_band(blockIdx.x, batch.count, (batch.M[0] + BM - 1) / BM,
+    if (batch.band ? !tile_coords_band(pid, batch.count, (batch.M[0] + BM - 1) / BM,
                                        (batch.N[0] + TN - 1) / TN, grp, tm, tn)
-                   : !tile_coords(blockIdx.x, batch, TN, grp, tm, tn))
+                   : !tile_coords(pid, batch, TN, grp, tm, tn))
         return;
     const int M = batch.M[grp], N = batch.N[grp];
-    const int64_t lda = batch.lda[grp], ldb = batch.ldb[grp], ldc = batch.ldc[grp];
+    const int64_t lda = batch.lda[grp], ldb = batch.ldb[grp];
+    int64_t ldc = batch.ldc[grp];
     const int m0 = tm * BM, n0 = tn * TN;
     const __bf16* __restrict__ A = batch.A[grp];
     const __bf16* __restrict__ B = batch.B[grp];
     const float* __restrict__ bias = batch.bias[grp];
     void* __restrict__ C = batch.C[grp];
     __bf16* aux = batch.aux[grp];
+    if (split_wg) {
+        const int kr = K / batch.split_ways, k0 = part * kr;
+        A += A_MC ? (int64_t)k0 * lda : k0;
+        B += B_KC ? k0 : (int64_t)k0 * ldb;
+        K = kr;
+        if (part > 0) {
+            // block (part - 1, j) of the workspace, addressed so that the
+            // epilogue's C + row·ldc + col lands on the tile's element
+            // (row - m0, col - n0) of that block
+            const int64_t blk = (int64_t)(part - 1) * batch.split_tail + (pid - batch.split_from);
+            C = (void*)((uintptr_t)(batch.split_ws + blk * (BM * TN)) -
+                        (uintptr_t)(((int64_t)m0 * TN + n0) * 4));
+            ldc = TN;
+            bias = nullptr;
+        }
+    }
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -1072,6 +1103,33 @@ int cu_count() {
 }
 
 namespace {
+// Second launch of a split last wave: C += block p of tail tile j for p = 1,
+// 2, ... in that order (range 0 is already in C), one workgroup per 64-row
+// quarter of a tile, 16-byte units (every group's N and ldc a multiple of 4,
+// C 16-byte aligned: checked by the launcher).
+__global__ __launch_bounds__(256) void split_fixup_kernel(GemmBatch batch, int tile_cols) {
+    const int j = blockIdx.x >> 2, quarter = blockIdx.x & 3;
+    int grp, tm, tn;
+    if (!tile_coords(batch.split_from + j, batch, tile_cols, grp, tm, tn)) return;
+    const int r0 = 64 * quarter, m0 = tm * BM + r0, n0 = tn * tile_cols;
+    const int rows = min(64, batch.M[grp] - m0), cols = min(tile_cols, batch.N[grp] - n0);
+    if (rows <= 0) return;
+    float* C = (float*)batch.C[grp] + (int64_t)m0 * batch.ldc[grp] + n0;
+    const int units = tile_cols / 4;
+    const int64_t blk = (int64_t)BM * tile_cols;
+    const float* ws = batch.split_ws + (int64_t)j * blk + (int64_t)r0 * tile_cols;
+    for (int idx = threadIdx.x; idx < 64 * units; idx += 256) {
+        const int r = idx / units, c = 4 * (idx - r * units);
+        if (r >= rows || c >= cols) continue;
+        f32x4* dst = (f32x4*)(C + (int64_t)r * batch.ldc[grp] + c);
+        f32x4 acc = *dst;
+        for (int p = 1; p < batch.split_ways; ++p)
+            acc += *(const f32x4*)(ws + (int64_t)(p - 1) * batch.split_tail * blk +
+                                   (int64_t)r * tile_cols + c);
+        *dst = acc;
+    }
+}
+
 // Workgroups of a launch with tiles tn_w columns wide (one 256 x tn_w tile each).
 int64_t tile_count(const GemmBatch& b, int tn_w) {
     int64_t t = 0;
@@ -1122,21 +1180,12 @@ int gemm_tile_cols(const GemmBatch& b, int layout, int epi, int64_t K) {
 }
 
 namespace {
-hipError_t launch(const GemmBatch& b, int layout, int epi, int64_t ldaux, int64_t K,
-                  bool out_bf16, hipStream_t stream)
+// The tile kernel of a launch whose width, grid and split are set.
+hipError_t launch_tiles(const GemmBatch& b, int tn_w, dim3 grid, int layout, int epi,
+                        int64_t ldaux, int64_t K, bool out_bf16, hipStream_t stream)
 {
-    const int tn_w = gemm_tile_cols(b, layout, epi, K);
     const int nj = tn_w / 64;
-    int per_xcd = 0;
-    if (b.band) {
-        const int tiles_m = (b.M[0] + BM - 1) / BM, tiles_n = (b.N[0] + tn_w - 1) / tn_w;
-        per_xcd = ((tiles_m / 8 + GROUP_M - 1) / GROUP_M) * GROUP_M * tiles_n * b.count;
-    } else {
-        for (int g = 0; g < b.count; ++g)
-            per_xcd += (((b.M[g] + BM - 1) / BM) * ((b.N[g] + tn_w - 1) / tn_w) + 7) / 8;
-    }
-    if (per_xcd == 0) return hipSuccess;
-    const dim3 grid(8 * per_xcd), block(NTHREADS);
+    const dim3 block(NTHREADS);
     if (tn_w == W_TN) {
 #define TP_GEMM_W(L, E, OB)                                                                    \
     do {                                                                                       \
@@ -1195,6 +1244,62 @@ hipError_t launch(const GemmBatch& b, int layout, int epi, int64_t ldaux, int64_
 #undef TP_GEMM
 #undef TP_GEMM_NJ
     return hipErrorInvalidValue;      // a layout / epilogue pair with no kernel
+}
+
+// Ways to split each tile of a launch's last wave over K, 0 for none.  With
+// W workgroups on C compute units (one each) the last wave holds
+// t = W mod C tiles; when t <= C/2 (C/4) the wave can run as 2t (4t)
+// workgroups of half (a quarter of) the K loop, taking half (a quarter of)
+// a tile's time, at the price of (ways - 1)·t f32 tile blocks written,
+// read back and added to C.  Taken from K = 4096 (8192) on, where the
+// saved K loop outweighs that traffic, and only with f32 output and no
+// epilogue, whole K steps and a caller-provided workspace that holds the
+// blocks.
+int split_ways(const GemmBatch& b, int tn_w, int64_t workgroups, int epi, int64_t K,
+               bool out_bf16) {
+    if (!b.split_ws || epi != EPI_NONE || out_bf16 || tn_w == W_TN || b.band || b.causal_k)
+        return 0;
+    const int64_t cus = cu_count();
+    const int64_t tail = workgroups % cus;
+    if (tail == 0) return 0;
+    for (int g = 0; g < b.count; ++g)
+        if (b.N[g] % 4 || b.ldc[g] % 4 || ((uintptr_t)b.C[g] & 15)) return 0;
+    for (int ways = 4; ways >= 2; ways /= 2) {
+        if (ways * tail > cus || K % (ways * BK) != 0 || K < 2048 * ways) continue;
+        if ((ways - 1) * tail * BM * tn_w * 4 <= b.split_ws_bytes) return ways;
+    }
+    return 0;
+}
+
+hipError_t launch(const GemmBatch& b_in, int layout, int epi, int64_t ldaux, int64_t K,
+                  bool out_bf16, hipStream_t stream)
+{
+    const int tn_w = gemm_tile_cols(b_in, layout, epi, K);
+    GemmBatch b = b_in;
+    b.split_ways = 0;
+    int per_xcd = 0;
+    if (b.band) {
+        const int tiles_m = (b.M[0] + BM - 1) / BM, tiles_n = (b.N[0] + tn_w - 1) / tn_w;
+        per_xcd = ((tiles_m / 8 + GROUP_M - 1) / GROUP_M) * GROUP_M * tiles_n * b.count;
+    } else {
+        for (int g = 0; g < b.count; ++g)
+            per_xcd += (((b.M[g] + BM - 1) / BM) * ((b.N[g] + tn_w - 1) / tn_w) + 7) / 8;
+    }
+    if (per_xcd == 0) return hipSuccess;
+    int64_t workgroups = 8 * (int64_t)per_xcd;
+    const int ways = split_ways(b, tn_w, workgroups, epi, K, out_bf16);
+    if (ways > 1) {
+        b.split_tail = (int)(workgroups % cu_count());
+        b.split_from = (int)(workgroups - b.split_tail);
+        b.split_ways = ways;
+        workgroups = b.split_from + (int64_t)ways * b.split_tail;
+    }
+    if (hipError_t e = launch_tiles(b, tn_w, dim3((unsigned)workgroups), layout, epi, ldaux, K,
+                                    out_bf16, stream))
+        return e;
+    if (ways < 2) return hipSuccess;
+    hipLaunchKernelGGL(split_fixup_kernel, dim3(4 * b.split_tail), dim3(256), 0, stream, b, tn_w);
+    return hipGetLastError();
 }
 }  // namespace
 

@@ -129,15 +129,19 @@ hipError_t run_matmul(const void* A, int64_t lda, int ta, const void* B, int64_t
 }
 
 // `n` bf16 products of one layout, output type and K but their own shapes in
-// one grouped launch (no epilogue); the caller has validated every group
+// one grouped launch (no epilogue); the caller has validated every group.
+// `spare` (spare_bytes, or NULL) is device memory free for the launch, which
+// may then split its last wave of workgroups over K (f32 output).
 struct Product {
     const void* A; int64_t lda; const void* B; int64_t ldb; void* C; int64_t ldc;
     int64_t M, N;
 };
 hipError_t run_grouped(const Product* p, int n, int64_t K, int ta, int tb, int out,
-                       hipStream_t st) {
+                       hipStream_t st, void* spare = nullptr, int64_t spare_bytes = 0) {
     tpk::GemmBatch gb = {};
     gb.count = n;
+    gb.split_ws = (float*)spare;
+    gb.split_ws_bytes = spare ? spare_bytes : 0;
     for (int i = 0; i < n; ++i) {
         gb.A[i] = (const __bf16*)p[i].A;
         gb.B[i] = (const __bf16*)p[i].B;
@@ -277,7 +281,7 @@ TP_EXPORT const char* tp_status_string(int status) {
     }
 }
 
-TP_EXPORT int tp_abi_version(void) { return 1; }
+TP_EXPORT int tp_abi_version(void) { return 2; }
 
 TP_EXPORT tp_status tp_linear(const void* X, int64_t ldx, const void* W, int64_t ldw,
                               const void* bias, void* C, int64_t ldc, int64_t M, int64_t N,
@@ -425,9 +429,10 @@ TP_EXPORT tp_status tp_matmul_grouped(const void* const* A, const int64_t* lda, 
                                       const void* const* B, const int64_t* ldb, int trans_b,
                                       void* const* C, const int64_t* ldc, const int64_t* M,
                                       const int64_t* N, int count, int64_t K, int out,
-                                      void* stream) {
+                                      void* ws, size_t ws_bytes, void* stream) {
     if (!A || !lda || !B || !ldb || !C || !ldc || !M || !N) return TP_ERR_NULL;
     if (count <= 0 || count > kMaxGroup) return TP_ERR_SHAPE;
+    if (ws && !aligned16(ws)) return TP_ERR_ALIGN;
     Product p[kMaxGroup];
     for (int g = 0; g < count; ++g) {
         const tp_status s = check_matmul(A[g], lda[g], trans_a, B[g], ldb[g], trans_b, nullptr,
@@ -436,7 +441,8 @@ TP_EXPORT tp_status tp_matmul_grouped(const void* const* A, const int64_t* lda, 
         if (s != TP_OK) return s;
         p[g] = {A[g], lda[g], B[g], ldb[g], C[g], ldc[g], M[g], N[g]};
     }
-    return launched(run_grouped(p, count, K, trans_a, trans_b, out, as_stream(stream)));
+    const int64_t spare = ws_bytes > (size_t)INT64_MAX ? INT64_MAX : (int64_t)ws_bytes;
+    return launched(run_grouped(p, count, K, trans_a, trans_b, out, as_stream(stream), ws, spare));
 }
 
 TP_EXPORT int tp_gemm_tile_cols(int trans_a, int trans_b, int epilogue, int count,
@@ -700,10 +706,12 @@ TP_EXPORT tp_status tp_attn_shard_backward(const void* X, const void* W_qkv_i, c
     if (tpk::attention_bwd(qkv, n3, O, dO, lse, Dv, dqkv, b, s, H_l, causal != 0, stm))
         return TP_ERR_LAUNCH;
     // dW_qkv,i = X^T·dqkv [h, 3·H_l·d] and dW_o,i = O^T·dZ [H_l·d, h], f32, in
-    // one grouped launch (dW_o,i alone has too few tiles to fill the GPU)
+    // one grouped launch (dW_o,i alone has too few tiles to fill the GPU);
+    // dO is dead by now and its buffer serves a split of the launch's last
+    // wave over K
     const Product wgrad[2] = {{X, h, dqkv, n3, dW_qkv_i, n3, h, n3},
                               {O, HD, dZ, h, dW_o_i, h, HD, h}};
-    if (run_grouped(wgrad, 2, M, 1, 0, TP_F32, stm)) return TP_ERR_LAUNCH;
+    if (run_grouped(wgrad, 2, M, 1, 0, TP_F32, stm, dO, M * HD * 2)) return TP_ERR_LAUNCH;
     // dX_i = dqkv·W_qkv,i^T                      [M, h] partial over ranks
     return launched(run_matmul(dqkv, n3, 0, W_qkv_i, n3, 1, nullptr, dX_i, h, nullptr, 0, M, h,
                                n3, dx_dtype, TP_EPI_NONE, stm));

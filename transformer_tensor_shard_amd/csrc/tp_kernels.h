@@ -41,6 +41,17 @@ struct GemmBatch {
     int band;       // set by the launcher: tile order for groups sharing A
     int causal_k;   // A is zero past its diagonal (A[m][k] = 0 for k > m, NN layout): a
                     // tile's K loop stops after its last row (only zero terms are dropped)
+    // Split of the last, partly filled wave of workgroups (f32 output, no
+    // epilogue): the caller offers split_ws (split_ws_bytes of device memory
+    // free for the launch); the launcher may then run every tile of workgroup
+    // id >= split_from as split_ways workgroups over equal K ranges, range 0
+    // writing C and range p >= 1 the BM x (tile width) f32 block p-1 of tile
+    // (id - split_from) in split_ws, and adds those blocks to C in order p = 1,
+    // 2, ... in a second launch (set by the launcher: split_from, split_ways,
+    // split_tail = the number of tail workgroups).
+    float* split_ws;
+    int64_t split_ws_bytes;
+    int split_from, split_ways, split_tail;
 };
 // Supported (layout, epilogue, output) combinations: NN with NONE / GELU
 // (bf16 or f32) and DUAL (bf16); NT with NONE / GELU_BWD (bf16 or f32) and
