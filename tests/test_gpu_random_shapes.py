@@ -16,6 +16,7 @@ import torch
 import oracle
 import synth
 import transformer_tensor_shard_amd as tts
+from _tiles import split_ways
 from _tol import assert_bf16, assert_f32
 
 pytestmark = pytest.mark.gpu
@@ -80,6 +81,51 @@ def test_gemm_random(i, layout, epi, out, M, N, K):
         assert_bf16(res, ref)
     else:
         assert_f32(res, ref, bar=1e-4)
+
+
+def _split_cases(n=6):
+    rng = np.random.default_rng(SEED + 2)
+    cases = []
+    for i in range(n):
+        layout = ["nn", "nt", "tn"][i % 3]
+        count = int(rng.integers(1, 4))
+        shapes = [(8 * int(rng.integers(1, 80)), 8 * int(rng.integers(1, 80))) for _ in range(count)]
+        K = 256 * int(rng.integers(16, 48))          # 4096 .. 12032: two or four K ranges
+        cases.append((i, layout, shapes, K))
+    return cases
+
+
+@pytest.mark.parametrize("i,layout,shapes,K", _split_cases())
+def test_matmul_grouped_split_random(i, layout, shapes, K):
+    """Grouped f32 products given spare memory, on random shapes small enough
+    that their one wave of workgroups takes at most half the compute units:
+    the split over K must equal, bit for bit, the ordered sum of the K
+    ranges' own launches, and the oracle within the f32 bar."""
+    spare = 3 * 256 * 256 * 256 * 4                 # room for any tail of this size
+    ways = split_ways(shapes, K, spare)
+    assert ways in (2, 4)
+    banner(f"random split #{i}: {layout} shapes={shapes} K={K} ways={ways}")
+    ta, tb = layout == "tn", layout == "nt"
+    seeds = [SEED + 100 + 10 * i + g for g in range(len(shapes))]
+    As = [gen((K, m) if ta else (m, K), 1.0, sd, "x") for sd, (m, n) in zip(seeds, shapes)]
+    Bs = [gen((n, K) if tb else (K, n), 1 / math.sqrt(K), sd, "A") for sd, (m, n) in zip(seeds, shapes)]
+    Ad, Bd = [A.to(DEV) for A in As], [B.to(DEV) for B in Bs]
+    ws = torch.full((spare,), 0xFF, dtype=torch.uint8, device=DEV)   # NaN bits: written first
+    outs = tts.tp_matmul_grouped(Ad, Bd, trans_a=ta, trans_b=tb, ws=ws)
+    kr = K // ways
+    ref = None
+    for p in range(ways):
+        k0, k1 = p * kr, (p + 1) * kr
+        part = tts.tp_matmul_grouped(
+            [(A[k0:k1] if ta else A[:, k0:k1]).contiguous() for A in Ad],
+            [(B[:, k0:k1] if tb else B[k0:k1]).contiguous() for B in Bd], trans_a=ta, trans_b=tb)
+        ref = part if ref is None else [r + q for r, q in zip(ref, part)]
+    torch.cuda.synchronize()
+    for g in range(len(shapes)):
+        assert torch.equal(outs[g], ref[g]), g
+        a = As[g].t().contiguous() if ta else As[g]
+        b = Bs[g].t().contiguous() if tb else Bs[g]
+        assert_f32(outs[g], oracle.matmul(a, b), bar=1e-4)
 
 
 def _attn_cases(n=10):
