@@ -31,7 +31,11 @@ shape), with the weight-gradient product X^T·dY as its dominant kernel;
 dW_o,i, the attention-core backward, dW_qkv,i, dX_i) with its grouped
 weight-gradient launch as its dominant kernel; --workload vocab_bf16_h12288_tp8
 the vocab-parallel ends of all 8 ranks (embedding lookup and partial sum, the
-stable cross-entropy) with the grouped logits GEMM as its dominant kernel.
+stable cross-entropy) with the grouped logits GEMM as its dominant kernel;
+--workload kvsplit_bf16_h4096_tp4 the K/V-split attention of 4 ranks, HBM bound
+as a whole: each of its steps is timed on its own with the 256 MB last-level
+cache flushed before it (a 1 GiB write outside the events), and so are the
+HBM-bound components of every workload (LayerNorm, partial sums, embedding).
 
 Modes for profiler runs: --mode kernel launches only the dominant kernel,
 --mode copy only a plain device copy of a known size (counter calibration).
@@ -104,22 +108,41 @@ def measured_traffic(path=TRAFFIC_FILE, source_hash=None):
     return c.get("hbm_bytes_per_launch") if c else None
 
 
-def component_time(fn, stream):
+class CacheFlush:
+    """Writes a 1 GiB device buffer: run between the timed launches of an
+    HBM-bound kernel (outside their events), it evicts the 256 MB last-level
+    cache, so that no launch reads what the one before left there."""
+    BYTES = 1 << 30
+
+    def __init__(self, torch, dev):
+        self.buf = torch.empty(self.BYTES // 4, dtype=torch.float32, device=dev)
+        self.n = 0
+
+    def __call__(self):
+        self.n += 1
+        self.buf.fill_(float(self.n & 1))
+
+
+def component_time(fn, stream, flush=None):
     """Average ms of fn() alone: after a warm-up of about 0.05 s, over enough
-    launches for about 0.1 s (3 to 500)."""
+    launches for about 0.1 s (3 to 500); with `flush`, the cache is flushed
+    before every launch (outside the timing)."""
     import torch
-    t1, _ = event_time(fn, 1, stream)
+    t1, _ = event_time(fn, 1, stream, flush)
     n = int(min(500, max(3, 0.05e3 / max(t1, 1e-3))))
-    event_time(fn, n, stream)
-    return event_time(fn, int(min(500, max(3, 0.1e3 / max(t1, 1e-3)))), stream)
+    event_time(fn, n, stream, flush)
+    return event_time(fn, int(min(500, max(3, 0.1e3 / max(t1, 1e-3)))), stream, flush)
 
 
-def event_time(fn, reps, stream):
-    """Average ms of fn() over reps launches, bracketed by HIP events."""
+def event_time(fn, reps, stream, flush=None):
+    """Average ms of fn() over reps launches, bracketed by HIP events (and
+    preceded by `flush()`, outside the events, when given)."""
     import torch
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(reps)]
     for a, b in evs:
+        if flush is not None:
+            flush()
         a.record(stream)
         fn()
         b.record(stream)
@@ -474,6 +497,10 @@ def main():
     log(f"inputs ready in {time.time() - t0:.1f} s")
 
     kernel, kern_flops, kern_name = dominant_kernel(w, tts, torch, X_k, W_k, dev)
+    # HBM-bound kernels and steps are timed with the last-level cache flushed
+    # before each launch; the K/V split is HBM bound as a whole
+    flush = CacheFlush(torch, dev)
+    hbm_bound = w.kind == "kvsplit"
 
     # ---------------------------------------------------------------- timing
     # Short steps get more of both by default, so that the clocks have settled
@@ -499,19 +526,33 @@ def main():
         kev.extend((torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                    for _ in range(args.steps))
     log(f"timing {args.steps} step(s)")
-    # one event after every step: the whole region gives the mean, the
-    # differences the per-step spread
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     wall0 = time.time()
-    evs[0].record(stream)
-    for i in range(args.steps):
-        step(i)
-        evs[i + 1].record(stream)
-    torch.cuda.synchronize()
+    if hbm_bound:
+        # each step bracketed by its own events, the last-level cache flushed
+        # before it (outside the events): the mean of the steps' own times
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for i, (a, b) in enumerate(evs):
+            flush()
+            a.record(stream)
+            step(i)
+            b.record(stream)
+        torch.cuda.synchronize()
+        per_step = sorted(a.elapsed_time(b) for a, b in evs)
+        ms = sum(per_step) / args.steps
+    else:
+        # one event after every step: the whole region gives the mean, the
+        # differences the per-step spread
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        evs[0].record(stream)
+        for i in range(args.steps):
+            step(i)
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+        ms = evs[0].elapsed_time(evs[-1]) / args.steps
+        per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
     wall = time.time() - wall0
-    ms = evs[0].elapsed_time(evs[-1]) / args.steps
-    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
     step_stats = {"min": round(per_step[0], 4),
                   "median": round(per_step[len(per_step) // 2] if len(per_step) % 2
                                   else 0.5 * (per_step[len(per_step) // 2 - 1]
@@ -524,7 +565,7 @@ def main():
 
     # the dominant kernel: its own launches inside the timed steps where the
     # step's entry point records them (the block), else separate launches
-    iso_ms, iso_all = event_time(kernel, max(args.steps, 5), stream)
+    iso_ms, iso_all = event_time(kernel, max(args.steps, 5), stream, flush if hbm_bound else None)
     if w.kind == "block":
         kern_all = [a.elapsed_time(b) for a, b in kev]
         kern_ms = sum(kern_all) / len(kern_all)
@@ -580,7 +621,7 @@ def main():
         }
         for name, (fn, fl, by) in items.items():
             fn()
-            t, _ = component_time(fn, stream)
+            t, _ = component_time(fn, stream, flush if by and not fl else None)
             c = {"ms": round(t, 4)}
             if fl:
                 c["tflops"] = round(fl / (t * 1e-3) / 1e12, 1)
@@ -633,7 +674,7 @@ def main():
         }
         for name, (fn, fl, by) in items.items():
             fn()
-            t, _ = component_time(fn, stream)
+            t, _ = component_time(fn, stream, flush if by and not fl else None)
             c = {"ms": round(t, 4), "tflops": round(fl / (t * 1e-3) / 1e12, 1),
                  "pct_peak": round(100 * fl / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 1)}
             components[name] = c
@@ -678,7 +719,7 @@ def main():
         }
         for name, (fn, fl, by) in items.items():
             fn()
-            t, _ = component_time(fn, stream)
+            t, _ = component_time(fn, stream, flush if by and not fl else None)
             c = {"ms": round(t, 4)}
             if fl:
                 c["tflops"] = round(fl / (t * 1e-3) / 1e12, 1)
@@ -764,7 +805,9 @@ def main():
             "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
             "traffic": None, "algorithmic_bytes_per_launch": by,
             "frac_of_copy": round(gbs / calib["hbm_copy"]["gbs"], 4),
-            "avg_launch_ms": round(kern_ms, 4), "launches_timed": len(kern_all)}
+            "avg_launch_ms": round(kern_ms, 4), "launches_timed": len(kern_all),
+            "cache": "1 GiB written before every timed step and launch (outside the "
+                     "events), evicting the 256 MB last-level cache"}
     if shards is not None:
         result["rank0_shards"] = shards
     if training is not None:
