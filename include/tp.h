@@ -181,7 +181,12 @@ tp_status tp_attn_shard_train_fwd(const void* X, const void* W_qkv_i, const void
  *   qkv, O, lse: from tp_attn_shard_train_fwd
  *   dX_i [b·s, h] in dtype `dx_dtype` (this rank's partial);
  *   dW_qkv_i [h, 3·H_l·d], dW_o_i [H_l·d, h]: f32
- *   ws >= tp_attn_shard_backward_workspace(b, s, H_l, d) bytes (dO, dqkv, D). */
+ *   ws >= tp_attn_shard_backward_workspace(b, s, H_l, d) bytes (dO, dqkv, D).
+ * The two weight gradients run as one grouped launch (tp_matmul_grouped's),
+ * given the dO part of ws once dO is consumed: where its last wave of tiles
+ * fills at most half the GPU, those tiles' sums over the b·s tokens are split
+ * into two (or four) ordered partial sums.  Results are deterministic for a
+ * given device and shape. */
 size_t tp_attn_shard_backward_workspace(int64_t b, int64_t s, int64_t H_l, int64_t d);
 tp_status tp_attn_shard_backward(const void* X, const void* W_qkv_i, const void* W_o_i,
                                  const void* qkv, const void* O, const float* lse,
