@@ -332,8 +332,9 @@ tp_status tp_matmul_grouped(const void* const* A, const int64_t* lda, int trans_
  * behind tp_linear, tp_linear_batched, tp_matmul and tp_matmul_grouped uses
  * for a launch of `count` products (host arrays M[count], N[count]) with
  * inner size K, layout (trans_a, trans_b) and epilogue as in tp_matmul, on
- * the current device: 256, or 192 or 384 where fewer or better-filled waves
- * of workgroups make the launch faster.  The width changes the speed only,
+ * the current device: 128 when no product is wider than 128 columns, else
+ * 256, or 192 or 384 where fewer or better-filled waves of workgroups make
+ * the launch faster.  The width changes the speed only,
  * never a result: every output element sees the same MFMA sequence over K.
  * Host logic only (nothing is launched); with no GPU present it answers for
  * 256 compute units.  Returns 0 for invalid arguments (count outside 1..16,

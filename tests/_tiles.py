@@ -1,6 +1,7 @@
 """The bf16 GEMM's choice of output-tile width, restated for the tests.
 
-A launch is costed in waves of workgroups (one 256-row tile per workgroup,
+A launch whose products are all at most 128 columns wide takes 128-column
+tiles (not the cross-entropy statistics).  Otherwise a launch is costed in waves of workgroups (one 256-row tile per workgroup,
 one workgroup per compute unit): a wave of 256-column tiles counts 16, of
 192-column tiles 14, of 384-column tiles 23.  A width other than 256 is
 taken only when it saves more than 2 (1/8 of a 256-column wave), 192 before
@@ -31,6 +32,8 @@ def waves(prods, w, cus=256):
 def tile_cols(prods, K, *, trans_a=False, trans_b=False, epilogue="none", cus=256):
     if tiles(prods, 192) > 0x7FFFFFFF // 16:
         return 256
+    if epilogue != "ce_stats" and all(n <= 128 for m, n in prods):
+        return 128
     best, cost = 256, 16 * waves(prods, 256, cus)
     if epilogue != "ce_stats" and 14 * waves(prods, 192, cus) < cost - 2:
         best, cost = 192, 14 * waves(prods, 192, cus)

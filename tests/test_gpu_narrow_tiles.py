@@ -137,3 +137,69 @@ def test_narrow_tn():
     C = tts.tp_matmul(A.to(DEV), B.to(DEV), trans_a=True, out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert_f32(C, oracle.matmul(A.t().contiguous(), B), bar=1e-4)
+
+
+# --------------------------------------------------------------- 128 columns
+def test_products_at_most_128_wide_take_128_column_tiles():
+    """A launch whose products are all at most 128 columns wide takes
+    128-column tiles (the rule restated in _tiles.py; the library agrees), a
+    launch with one wider product does not (the cross-entropy statistics, an
+    internal epilogue, keep 256 columns: restated only)."""
+    for prods, K, kw, want in (([(2048, 128)], 2048, {}, 128),
+                               ([(2048, 128)] * 16, 2048, {}, 128),
+                               ([(300, 8), (64, 120)], 72, dict(trans_b=True), 128),
+                               ([(2048, 128), (2048, 136)], 2048, {}, 256)):
+        assert tile_cols(prods, K, **kw) == want, prods
+        assert tts.tp_gemm_tile_cols(prods, K, **kw) == want, prods
+    assert tile_cols([(4096, 128)], 512, trans_b=True, epilogue="ce_stats") == 256
+
+
+@pytest.mark.parametrize("ta,tb,out", [(0, 0, torch.float32), (0, 1, torch.bfloat16),
+                                       (1, 0, torch.float32), (0, 0, torch.bfloat16)])
+def test_128_column_tiles_match_wider_tiles_bitwise(ta, tb, out):
+    """The same product (N = 120, ragged M and K) alone, on 128-column tiles,
+    and grouped with a 520-column product, which puts the launch on wider
+    tiles: the per-element K loop is the same MFMA sequence, so the two
+    results agree bit for bit; and the oracle within the bar."""
+    M, N, K = 1000, 120, 328 if not ta else 320
+    assert tile_cols([(M, N)], K, trans_a=bool(ta), trans_b=bool(tb)) == 128
+    assert tile_cols([(M, N), (M, 520)], K, trans_a=bool(ta), trans_b=bool(tb)) != 128
+    banner(f"128-column tiles ta={ta} tb={tb} out={out} M={M} N={N} K={K}")
+    A = gen((K, M) if ta else (M, K), 1.0, 511, "x")
+    B = gen((N, K) if tb else (K, N), 1 / math.sqrt(K), 511, "A")
+    A2 = gen((K, M) if ta else (M, K), 1.0, 512, "x")
+    B2 = gen((520, K) if tb else (K, 520), 1 / math.sqrt(K), 512, "A")
+    Ad, Bd = A.to(DEV), B.to(DEV)
+    alone = tts.tp_matmul_grouped([Ad], [Bd], trans_a=bool(ta), trans_b=bool(tb), out_dtype=out)[0]
+    pair = tts.tp_matmul_grouped([Ad, A2.to(DEV)], [Bd, B2.to(DEV)], trans_a=bool(ta),
+                                 trans_b=bool(tb), out_dtype=out)[0]
+    torch.cuda.synchronize()
+    assert torch.equal(alone, pair)
+    ref = oracle.matmul(A.t().contiguous() if ta else A, B.t().contiguous() if tb else B)
+    if out == torch.float32:
+        assert_f32(alone, ref, bar=1e-4)
+    else:
+        assert_bf16(alone, ref)
+
+
+def test_128_column_tiles_gelu_and_gelu_bwd():
+    """The forward epilogues (bias + GeLU, bf16; the training forward's two
+    outputs) and the GeLU-backward epilogue on 128-column tiles."""
+    M, N, K = 2056, 128, 264
+    banner(f"128-column tiles epilogues M={M} N={N} K={K}")
+    X = gen((M, K), 1.0, 513, "x")
+    W = gen((K, N), 1 / math.sqrt(K), 513, "A")
+    bias = gen((N,), 0.5, 513, "bias", torch.float32)
+    aux = gen((M, N), 1.0, 513, "preact")
+    Xd, Wd = X.to(DEV), W.to(DEV)
+    G = tts.tp_linear(Xd, Wd, bias.to(DEV), gelu=True, out_dtype=torch.bfloat16)
+    Y, Yp = tts.tp_matmul(Xd, Wd, bias.to(DEV), epilogue="gelu_save", out_dtype=torch.bfloat16)
+    Bt = W.t().contiguous()
+    dY = tts.tp_matmul(Xd, Bt.to(DEV), trans_b=True, epilogue="gelu_bwd", aux=aux.to(DEV),
+                       out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    v = oracle.matmul(X, W, bias)
+    assert_bf16(G, oracle.gelu(v))
+    assert_bf16(Y, oracle.gelu(v))
+    assert_bf16(Yp, v)
+    assert_bf16(dY, oracle.matmul(X, W) * oracle.gelu_grad(aux))

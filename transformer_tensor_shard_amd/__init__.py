@@ -333,7 +333,7 @@ def tp_matmul(A, B, bias=None, *, trans_a=False, trans_b=False, epilogue="none",
 
 
 def tp_gemm_tile_cols(shapes, K: int, *, trans_a=False, trans_b=False, epilogue="none") -> int:
-    """Output-tile width (192, 256 or 384 columns) the bf16 GEMM uses for one
+    """Output-tile width (128, 192, 256 or 384 columns) the bf16 GEMM uses for one
     launch of the products `shapes` = [(M, N), ...] with inner size K on the
     current device (256 compute units when there is none).  Host logic only."""
     count = len(shapes)

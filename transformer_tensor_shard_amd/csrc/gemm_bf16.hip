@@ -94,9 +94,10 @@ constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
 constexpr int GROUP_M = 4;
 constexpr unsigned OOB = 0x80000000u;         // any offset >= num_records reads 0
 constexpr int NI = 8;                         // 16x16 MFMA blocks per wave along M
-// Blocks per wave along N: 4 (a 256-column tile) or 3 (192 columns, for
+// Blocks per wave along N: 4 (a 256-column tile), 3 (192 columns, for
 // products whose 256-column tile count leaves the last wave of workgroups
-// mostly empty; see the launcher).
+// mostly empty) or 2 (128 columns, for products at most 128 wide, which a
+// 256-column tile would leave half idle); see the launcher.
 constexpr int NJ_MAX = 4;
 constexpr int LOADS = 4;                      // A (and B) loads per wave per K tile
 
@@ -268,11 +269,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(
 {
     constexpr bool A_MC = LAYOUT == GEMM_TN;    // A stored [K,M]: M contiguous
     constexpr bool B_KC = LAYOUT == GEMM_NT;    // B stored [N,K]: K contiguous
-    // Output tile BM x TN.  With NJ = 3 the tile is 192 columns wide: the LDS
-    // layout stays 256 wide and its last 64 columns are loaded as zeros (their
-    // lanes get out-of-range offsets) and never read.
+    // Output tile BM x TN.  With NJ = 3 (2) the tile is 192 (128) columns
+    // wide: the LDS layout stays 256 wide and its last 64 (128) columns are
+    // loaded as zeros (their lanes get out-of-range offsets) and never read.
     constexpr int TN = 64 * NJ;
-    static_assert(NJ == 3 || NJ == NJ_MAX, "256- or 192-column tiles");
+    static_assert(NJ >= 2 && NJ <= NJ_MAX, "128-, 192- or 256-column tiles");
     static_assert(EPI != EPI_CE_STATS || NJ == NJ_MAX, "the statistics use 256-column tiles");
     // Two stages as two separate LDS objects: every access below names its
     // stage statically, which lets the compiler see that reads of one stage
@@ -1154,8 +1155,11 @@ bool wide_ok(const GemmBatch& b, int layout, int epi, int64_t K) {
 
 }  // namespace
 
-// Output-tile width of a launch: 256 columns, or 192 or 384 where a cost model
-// of the waves of workgroups (one workgroup per CU) says so.  The cost of a
+// Output-tile width of a launch: 128 columns when no product is wider (a
+// 256-column tile would do the same number of tiles with half its MFMAs on
+// zero columns; not for the cross-entropy statistics), else 256 columns, or
+// 192 or 384 where a cost model of the waves of workgroups (one workgroup per
+// CU) says so.  The cost of a
 // wave, in sixteenths of a wave of 256-column tiles: 14 for 192 columns (the
 // K loop is bound by the L2 requests of a tile's A and B panels, 256 + 192
 // rows against 256 + 256), 23 for 384 (1.5 times the work, measured 4-7%
@@ -1166,6 +1170,11 @@ bool wide_ok(const GemmBatch& b, int layout, int epi, int64_t K) {
 // tiles, 32 of 384).
 int gemm_tile_cols(const GemmBatch& b, int layout, int epi, int64_t K) {
     if (tile_count(b, 192) > 0x7fffffff / 16) return 256;     // keep the grid size in range
+    if (epi != EPI_CE_STATS) {
+        bool narrow = true;
+        for (int g = 0; g < b.count; ++g) narrow = narrow && b.N[g] <= 128;
+        if (narrow) return 128;
+    }
     const int64_t cus = cu_count();
     auto waves = [&](int w) { return (tile_count(b, w) + cus - 1) / cus; };
     int best = 256;
@@ -1223,6 +1232,7 @@ hipError_t launch_tiles(const GemmBatch& b, int tn_w, dim3 grid, int layout, int
     } while (0)
 #define TP_GEMM(L, E, OB)                                                                      \
     do {                                                                                       \
+        if (nj == 2) TP_GEMM_NJ(L, E, OB, 2);                                                  \
         if (nj == 3) TP_GEMM_NJ(L, E, OB, 3);                                                  \
         TP_GEMM_NJ(L, E, OB, NJ_MAX);                                                          \
     } while (0)
