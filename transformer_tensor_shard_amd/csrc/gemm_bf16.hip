@@ -21,10 +21,13 @@
 //
 // Design: one 256x256 output tile per workgroup of 8 waves (two per SIMD);
 // a launch whose 256-column tiles would leave the last wave of workgroups
-// mostly empty uses 256x192 tiles instead (8x3 blocks per wave), and the
+// mostly empty uses 256x192 tiles instead (8x3 blocks per wave), products at
+// most 128 columns wide use 256x128 tiles (8x2 blocks per wave), and the
 // large forward and input-gradient products use 256x384 tiles (a kernel of
 // their own, gemm_bf16_w384_kernel below: 5/6 of the operand bytes per
-// FLOP); the launcher's cost model picks the width.
+// FLOP); the launcher's rule picks the width.  Given spare device memory, a
+// launch with f32 output may also split the tiles of its partly filled last
+// wave over K (see split_ways).
 //  * wave w owns a 128x64 sub-tile: rows 128*((w&3)>>1), columns
 //    128*(w&1) + 64*(w>>2); that is 8x4 MFMA 16x16x32 bf16 blocks with 128
 //    f32 accumulators per lane.  The two waves on a SIMD (w and w+4) take the
