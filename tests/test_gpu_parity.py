@@ -90,7 +90,7 @@ def test_linear_batched(count, M, N, K, gelu):
 
 
 @pytest.mark.parametrize("count,M,N,K,gelu", [(3, 2048, 264, 200, True), (5, 4096, 520, 328, False),
-                                              (18, 2048, 256, 64, True)])
+                                              (34, 2048, 256, 64, True)])
 def test_linear_batched_shared_x(count, M, N, K, gelu):
     """Every group shares X (the column-parallel products of all ranks), with
     whole tile-row bands per XCD: the band tile order, including ragged N and
