@@ -438,15 +438,17 @@ def test_vocab_embedding(M, h, V_r, P, out):
 
 
 @pytest.mark.parametrize("M,h,V_r,P", [(300, 264, 520, 3), (512, 512, 6400 // 8, 8),
-                                       (1, 64, 8, 2), (700, 128, 1032, 1), (2304, 128, 3840, 2)])
+                                       (1, 64, 8, 2), (700, 128, 1032, 1), (2304, 128, 3840, 2),
+                                       (2304, 128, 3848, 2)])
 def test_vocab_cross_entropy(M, h, V_r, P):
     """Per-rank statistics and the combined loss against the oracle; the
     all-ranks entry point equals the per-rank path bit for bit.  In the last
-    case the per-rank launches take 256-column output tiles and the all-ranks
-    launch 384-column ones: the statistics, kept per 128-column piece, do not
-    depend on the width."""
+    two cases the per-rank launches take 256-column output tiles and the
+    all-ranks launch 384-column ones: the statistics, kept per 128-column
+    piece, do not depend on the width (V_r = 3848: each rank's last
+    384-column tile holds 8 columns, one partial piece)."""
     banner(f"vocab cross-entropy M={M} h={h} V_r={V_r} P={P}")
-    if (M, V_r, P) == (2304, 3840, 2):
+    if (M, P) == (2304, 2):
         assert tile_cols([(M, V_r)], h, trans_b=True, epilogue="ce_stats") == 256
         assert tile_cols([(M, V_r)] * P, h, trans_b=True, epilogue="ce_stats") == 384
     V = V_r * P
