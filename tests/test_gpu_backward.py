@@ -332,6 +332,24 @@ def test_matmul_grouped_split_last_wave(ta, tb, shapes, K, ways):
         assert_f32(outs[g], oracle.matmul(a, b), bar=1e-4)
 
 
+def test_matmul_grouped_spare_too_small_means_no_split():
+    """Spare memory smaller than the split's blocks (here 1 MiB against the
+    4 MiB two K ranges of 16 tail tiles need) leaves the launch unsplit: its
+    result equals, bit for bit, the launch given no spare memory."""
+    shapes, K = [(512, 768), (256, 520)], 4096
+    assert split_ways(shapes, K, 4 << 20) == 2 and split_ways(shapes, K, 1 << 20) == 0
+    banner(f"matmul grouped, spare too small: shapes={shapes} K={K}")
+    As = [gen((K, m), 1.0, 245 + g, "x").to(DEV) for g, (m, n) in enumerate(shapes)]
+    Bs = [gen((K, n), 1 / math.sqrt(K), 245 + g, "A").to(DEV) for g, (m, n) in enumerate(shapes)]
+    ws = torch.full((1 << 20,), 0x7F, dtype=torch.uint8, device=DEV)
+    small = tts.tp_matmul_grouped(As, Bs, trans_a=True, ws=ws)
+    plain = tts.tp_matmul_grouped(As, Bs, trans_a=True)
+    torch.cuda.synchronize()
+    for u, v in zip(small, plain):
+        assert torch.equal(u, v)
+    assert torch.equal(ws, torch.full_like(ws, 0x7F))      # never touched
+
+
 def test_attn_shard_backward_split_last_wave():
     """16 sequences of 256 tokens, 8 local heads, h = 512: the weight-gradient
     launch (dW_qkv 24 tiles, dW_o 8: 32 workgroups, under half the CUs, K =
