@@ -349,7 +349,8 @@ int tp_gemm_tile_cols(int trans_a, int trans_b, int epilogue, int count, const i
  * scores S_r = Q_r·K_r^T (the exchange step sums them over the ranks before
  * the softmax, which is not linear), and forms its feature slice of the head
  * output, O[:, F_r] = softmax(S/sqrt(d) + causal mask)·V_r.  The partial
- * scores are materialised in f32 ([s, s] per rank and head), the softmax
+ * scores are materialised in f32 ([s, s] per rank and head, stored as
+ * 128x128 tiles, s rounded up to a multiple of 128), the softmax
  * weights in bf16 (unnormalised, the row maximum's weight exactly 1), the
  * products with V in f32, divided by the sum of the same rounded weights;
  * (sequence, head) pairs run 32 at a time.

@@ -364,9 +364,13 @@ def test_kv_split_rejects():
 def test_kv_split_workspace_size():
     L = tts.lib()
     # 32 pairs at most in flight
-    # per pair: P f32 partial-score matrices and a bf16 weight matrix of s x s,
-    # the f32 product with V [s, d] and the row sums [s]
-    assert L.tp_attention_kv_split_workspace(2, 64, 4, 128, 4) == 8 * (64 * 64 * 18 + 64 * 516)
+    # per pair: P f32 partial-score matrices stored as 128 x 128 tiles (s
+    # rounded up to a multiple of 128), a bf16 weight matrix of s x s, the f32
+    # product with V [s, d] and the row sums [s]
+    assert L.tp_attention_kv_split_workspace(2, 64, 4, 128, 4) == \
+        8 * (4 * 4 * 128 * 128 + 2 * 64 * 64 + 64 * 516)
+    assert L.tp_attention_kv_split_workspace(1, 136, 1, 64, 2) == \
+        1 * (4 * 2 * 256 * 256 + 2 * 136 * 136 + 136 * 260)
     assert L.tp_attention_kv_split_workspace(4, 2048, 32, 128, 4) == \
         32 * (2048 * 2048 * 18 + 2048 * 516)
     assert L.tp_attention_kv_split_workspace(0, 64, 4, 128, 4) == 0

@@ -7,7 +7,8 @@
 // its feature slice of the output, O[:, F_r] = softmax(S/sqrt(d) + mask)·V_r.
 // On one GPU, per (sequence, head) pair:
 //  * kv_scores_kernel forms the P partial-score products, K = d/P (f32 out,
-//    one [s, s] matrix per rank), operands loaded straight into registers;
+//    one [s, s] matrix per rank, stored as 128x128 tiles), operands loaded
+//    straight into registers;
 //    under the causal mask the 128x128 tiles that lie wholly past the
 //    diagonal are skipped (no query reads them);
 //  * kv_softmax_kernel sums a query row's P partial rows in rank order,
@@ -54,15 +55,28 @@ __device__ __forceinline__ float wg_reduce(float v, float* red, bool is_max) {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 constexpr unsigned KV_OOB = 0x80000000u;     // buffer offset past any range: reads 0
 
+// A partial-score matrix is stored tile by tile: 128x128 f32 tiles in
+// row-major tile order, each tile row-major in 64 KiB of its own (a ragged
+// last tile row or column padded), so that the workgroup forming a tile
+// writes one contiguous block instead of 128 row pieces 4·s bytes apart.
+__host__ __device__ inline int64_t kv_part_floats(int64_t s) {
+    const int64_t nt = (s + 127) / 128;
+    return nt * nt * 16384;
+}
+__device__ __forceinline__ int64_t kv_part_index(int s, int row, int key) {
+    const int nt = (s + 127) / 128;
+    return ((int64_t)(row >> 7) * nt + (key >> 7)) * 16384 + (row & 127) * 128 + (key & 127);
+}
+
 // Partial scores of a small feature slice: S_r = Q_r·K_r^T, [s, s] f32 per
-// (chunk pair, rank), w = d/P <= 128 features.  One workgroup of 4 waves per
+// (chunk pair, rank) in 128x128 tiles, w = d/P <= 128 features.  One workgroup of 4 waves per
 // 128x128 tile (wave: 64 query rows x 64 keys as 4x4 MFMA 16x16x32 blocks).
 // With a K of one to four 32-wide steps there is nothing to stage: each lane
 // loads its MFMA operand fragments (16 bytes of one row) straight from
 // memory, features past w read as zeros, and each wave's f32 block is staged
 // through 8 KiB of LDS (32 KiB per workgroup, so several workgroups share a
 // CU and their stores overlap) and stored with the non-temporal hint in whole
-// 256-byte row segments.  Under the causal mask a tile wholly past the
+// 256-byte row segments of the workgroup's 64 KiB tile.  Under the causal mask a tile wholly past the
 // diagonal is not computed (no query reads it).
 __global__ __launch_bounds__(256) void kv_scores_kernel(const __bf16* __restrict__ qkv, int64_t ld,
                                                         int s, int H, int d, int P, int pair0,
@@ -120,8 +134,7 @@ __global__ __launch_bounds__(256) void kv_scores_kernel(const __bf16* __restrict
     // The 16-byte unit of a staged row is XOR-ed with bits 2-3 of the row:
     // the four row groups of one LDS write then hit distinct banks.  s % 8 == 0,
     // so a unit's four keys are all inside or all past the row's end.
-    const int64_t ss = (int64_t)s * s;
-    float* out = parts + k * ss;
+    float* out = parts + k * kv_part_floats(s);
     char* const st = stage[wv];
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
@@ -145,15 +158,15 @@ __global__ __launch_bounds__(256) void kv_scores_kernel(const __bf16* __restrict
             const f32x4 v = *(const f32x4*)(st + rl * 256 + ((unit ^ (((rl >> 2) & 3) << 2)) << 4));
             const int row = m0 + 32 * p + rl, key = n0 + 4 * unit;
             if (row < s && key < s)
-                __builtin_nontemporal_store(v, (f32x4*)(out + (int64_t)row * s + key));
+                __builtin_nontemporal_store(v, (f32x4*)(out + kv_part_index(s, row, key)));
         }
         __builtin_amdgcn_s_waitcnt(0xC07F);               // reads done before the next pass writes
         __builtin_amdgcn_wave_barrier();
     }
 }
 
-// One workgroup per query row t of chunk pair p: parts [n][P][s][s] f32,
-// weights [n][s][s] bf16, rowsum [n][s] f32.  Keys past the diagonal
+// One workgroup per query row t of chunk pair p: parts [n][P] tiled partial
+// scores (kv_part_index), weights [n][s][s] bf16, rowsum [n][s] f32.  Keys past the diagonal
 // (causal) are neither read nor given weight.
 template <int PT>   // the rank count when known at compile time (loads all in flight), else 0
 __global__ __launch_bounds__(256) void kv_softmax_kernel(const float* __restrict__ parts, int P,
@@ -166,8 +179,8 @@ __global__ __launch_bounds__(256) void kv_softmax_kernel(const float* __restrict
     const int64_t p = row / s;
     const int t = (int)(row % s);
     const int nv = s / 4;
-    const int64_t ss = (int64_t)s * s;
-    const float* base = parts + p * P * ss + (int64_t)t * s;
+    const int64_t ss = (int64_t)s * s, ps = kv_part_floats(s);
+    const float* base = parts + p * P * ps;
     f32x4 acc[KV_MAXV];
     float mx = -INFINITY;
 #pragma unroll
@@ -175,14 +188,15 @@ __global__ __launch_bounds__(256) void kv_softmax_kernel(const float* __restrict
         const int c = threadIdx.x + 256 * i;
         acc[i] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
         if (c >= nv || (causal && 4 * c > t)) continue;
-        f32x4 v = __builtin_nontemporal_load((const f32x4*)base + c);
+        const float* pc = base + kv_part_index(s, t, 4 * c);    // 4 keys of one tile row
+        f32x4 v = __builtin_nontemporal_load((const f32x4*)pc);
         if constexpr (PT > 0) {
 #pragma unroll
             for (int r = 1; r < PT; ++r)
-                v += __builtin_nontemporal_load((const f32x4*)(base + r * ss) + c);
+                v += __builtin_nontemporal_load((const f32x4*)(pc + r * ps));
         } else {
             for (int r = 1; r < P; ++r)
-                v += __builtin_nontemporal_load((const f32x4*)(base + r * ss) + c);
+                v += __builtin_nontemporal_load((const f32x4*)(pc + r * ps));
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -237,7 +251,7 @@ __global__ __launch_bounds__(256) void kv_normalize_kernel(const float* __restri
 
 int64_t kv_split_workspace_bytes(int64_t pairs, int64_t s, int64_t d, int P) {
     const int64_t n = pairs < kKvChunk ? pairs : kKvChunk;
-    return n * s * s * (4 * (int64_t)P + 2) + n * s * (4 * d + 4);
+    return n * (4 * (int64_t)P * kv_part_floats(s) + 2 * s * s) + n * s * (4 * d + 4);
 }
 
 hipError_t kv_split_attention(const __bf16* qkv, int64_t ld, __bf16* O, int64_t ldo, int b, int s,
@@ -246,11 +260,11 @@ hipError_t kv_split_attention(const __bf16* qkv, int64_t ld, __bf16* O, int64_t 
     const int pairs = b * H, w = d / P;
     const int64_t ss = (int64_t)s * s;
     const int64_t HD = (int64_t)H * d;
-    // workspace: partial scores [n][P][s][s] f32, then e·V [n][s][d] f32 and
+    // workspace: partial scores [n][P] (tiled, kv_part_floats(s) each) f32, then e·V [n][s][d] f32 and
     // the row sums [n][s] f32, then the weights [n][s][s] bf16
     float* parts = (float*)ws;
     const int64_t n_max = pairs < kKvChunk ? pairs : kKvChunk;
-    float* accv = parts + n_max * P * ss;
+    float* accv = parts + n_max * P * kv_part_floats(s);
     float* rowsum = accv + n_max * s * d;
     __bf16* probs = (__bf16*)(rowsum + n_max * s);
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
