@@ -409,7 +409,7 @@ def test_block_small_all_ranks():
     assert_bf16(x1, x1_ref, per_row=True)
     assert_bf16(out, out_ref, per_row=True)
     # the residual dominates out: check the block's own contributions too
-    assert_bf16(x1.cpu().double() - oracle.f64(x), x1_ref - oracle.f64(x), per_row=True)
+    assert_bf16(x1.cpu().double().numpy() - oracle.f64(x), x1_ref - oracle.f64(x), per_row=True)
     assert_bf16(out.cpu().double() - x1.cpu().double(), out_ref - x1_ref)
 
 
